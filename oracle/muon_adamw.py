@@ -1,0 +1,400 @@
+"""Plain, slow fp64 reference of the hybrid MuonAdamW optimizer step.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  It is written for a
+reader checking it against the OpenDM training-stack page by eye: one function
+per step of the method, NumPy float64 arithmetic, matrix products through
+NumPy's BLAS, no blocking, fusion or reordering.  Inputs and stored state are
+float32 (the storage contract of the GPU library); every step computes in
+float64 and rounds stored state back to float32 once, at the end of the step.
+
+Citations name the page and the part of it a function follows:
+  [routing]      Muon/AdamW hybrid section, "how parameters are split" table
+                 (2-D, under action_expert ... layers, ends in .weight, with
+                 embeddings and norms excluded; everything else goes to AdamW;
+                 the optim switch muon_adamw / adamw)
+  [NS]           Muon/AdamW hybrid section, Newton-Schulz paragraph
+                 (a 5-step Newton-Schulz iteration approximates the zeroth
+                 power of the matrix instead of an SVD)
+  [hparams]      hyperparameter table of DM05OptimizerConfig (momentum 0.95,
+                 Nesterov on, 5 NS steps, moonlight coefficient 0.2, base lr
+                 2.5e-5) and the sentence after it giving the Muon learning rate
+                 lr * muon_lr_scale * 0.2 * sqrt(max(shape))
+  [FSDP-plan]    the MuonShardPlan paragraph: NS always acts on the whole
+                 matrix, never on a shard
+  [frozen]       FSDP section: the VLM token embedding and its tied lm_head are
+                 frozen by default
+  [defaults]     defaults quick-reference table (max_grad_norm 1.0)
+
+Readings where the page is silent (each also listed in the design notes):
+  * NS quintic coefficients: the page gives none.  Default (3.2608, -3.6447,
+    1.3650), a fixed triple whose 5-fold composition keeps every singular value
+    of a Frobenius-normalised input with sigma/||X||_F in [1e-2, 1] inside
+    [0.934, 1.215]; the widely published (3.4445, -4.7750, 2.0315) is accepted
+    as an option.
+  * Canonical orientation: rows <= cols, the Gram matrix is X X^T; a matrix
+    stored with more rows than columns is transposed before NS and back after.
+  * Normalisation epsilon 1e-7 added to the Frobenius norm.
+  * Nesterov in sum form: buf = mu*buf + g ; u = g + mu*buf.
+  * muon_lr_scale = 1.0; "shape" is the stored (m, n); the shape factor is
+    computed in float64 and rounded once to float32.
+  * Muon weight decay 0 unless given (then decoupled, scaled by the base lr).
+  * AdamW is the decoupled-decay algorithm of torch.optim.AdamW with one step
+    counter for the group; decay applies to every AdamW tensor.
+  * Clipping is global over every trainable gradient of both groups, with the
+    1e-6 guard of the usual clip_grad_norm_, and is applied before both
+    updates; max_grad_norm <= 0 disables it; non-finite norms propagate.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "MUON", "ADAMW", "NONE", "GROUP_NAMES",
+    "MODE_MUON_ADAMW", "MODE_ADAMW",
+    "DEFAULT_NS_COEFFS", "PUBLISHED_NS_COEFFS",
+    "HParams",
+    "route_one", "route", "lr_shape_scale", "plan_dump",
+    "global_grad_norm", "clip_coefficient",
+    "adamw_update", "nesterov_momentum", "frobenius_normalise",
+    "newton_schulz", "newton_schulz_bf16_emulated", "bf16_round",
+    "muon_matrix_update", "optimizer_step",
+]
+
+MUON, ADAMW, NONE = 0, 1, 2
+GROUP_NAMES = {MUON: "MUON", ADAMW: "ADAMW", NONE: "NONE"}
+MODE_MUON_ADAMW, MODE_ADAMW = 0, 1
+
+DEFAULT_NS_COEFFS = (3.2608, -3.6447, 1.3650)
+PUBLISHED_NS_COEFFS = (3.4445, -4.7750, 2.0315)
+
+
+@dataclass
+class HParams:
+    """Defaults from [hparams] and [defaults]; AdamW's betas, eps and decay
+    are the ones stated for the tiny hybrid workload."""
+    lr: float = 2.5e-5
+    muon_lr_scale: float = 1.0
+    muon_momentum: float = 0.95
+    muon_nesterov: bool = True
+    muon_ns_steps: int = 5
+    ns_coeffs: Tuple[float, float, float] = DEFAULT_NS_COEFFS
+    ns_eps: float = 1e-7
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.01
+    muon_weight_decay: float = 0.0
+    max_grad_norm: float = 1.0
+    moonlight_coefficient: float = 0.2
+
+
+# --------------------------------------------------------------------------
+# Routing and the plan  [routing], [frozen], [hparams], [FSDP-plan]
+# --------------------------------------------------------------------------
+
+_EXCLUDED_SUBSTRINGS = ("embed", "lm_head", "norm")
+
+
+def route_one(name: str, shape: Sequence[int], trainable: bool,
+              mode: int = MODE_MUON_ADAMW) -> int:
+    """Group of one parameter.  [routing]
+
+    Frozen parameters take no update and no part in the clip norm ([frozen]:
+    the routing scans trainable parameters only).  With the optim switch set
+    to plain AdamW every trainable tensor is AdamW.  Otherwise a tensor is
+    Muon when it is a matrix (two dimensions) whose dotted name contains
+    'action_expert' in one component, has a component exactly 'layers' after
+    that one, ends with '.weight', and whose lower-cased name contains none of
+    'embed', 'lm_head', 'norm' (the page's exclusion of embeddings and of
+    every norm layer).  Anything else trainable is AdamW.
+    """
+    if not trainable:
+        return NONE
+    if mode == MODE_ADAMW:
+        return ADAMW
+    if len(shape) != 2:
+        return ADAMW
+    if not name.endswith(".weight"):
+        return ADAMW
+    parts = name.split(".")
+    ae = None
+    for i, part in enumerate(parts):
+        if "action_expert" in part:
+            ae = i
+            break
+    if ae is None:
+        return ADAMW
+    if "layers" not in parts[ae + 1:]:
+        return ADAMW
+    lowered = name.lower()
+    for bad in _EXCLUDED_SUBSTRINGS:
+        if bad in lowered:
+            return ADAMW
+    return MUON
+
+
+def route(names: Sequence[str], shapes: Sequence[Sequence[int]],
+          trainable: Sequence[bool], mode: int = MODE_MUON_ADAMW) -> List[int]:
+    return [route_one(n, s, t, mode) for n, s, t in zip(names, shapes, trainable)]
+
+
+def lr_shape_scale(m: int, n: int, moonlight_coefficient: float = 0.2) -> np.float32:
+    """The shape factor moonlight_coefficient * sqrt(max(m, n)) of the Muon
+    learning rate, in float64, rounded once to float32.  [hparams]"""
+    return np.float32(moonlight_coefficient * math.sqrt(float(max(m, n))))
+
+
+def _f32_bits(x: np.float32) -> str:
+    return "%08x" % int(np.array([x], dtype=np.float32).view(np.uint32)[0])
+
+
+def plan_dump(names: Sequence[str], shapes: Sequence[Sequence[int]],
+              trainable: Sequence[bool], mode: int = MODE_MUON_ADAMW,
+              moonlight_coefficient: float = 0.2) -> str:
+    """Canonical text of a plan: the routing of every entry, the stored and
+    canonical (rows <= cols) shape of every Muon matrix, its orientation flag,
+    its shape-bucket (distinct canonical shapes, numbered in order of first
+    appearance), the bits of its float32 shape factor, and the running offset
+    of every AdamW tensor in the concatenated AdamW element space.
+
+    This format is an interface: the library's plan dump must produce the
+    same bytes for the same table.
+    """
+    groups = route(names, shapes, trainable, mode)
+    buckets: Dict[Tuple[int, int], int] = {}
+    bucket_count: Dict[int, int] = {}
+    lines = []
+    adam_off = 0
+    n_m = n_a = n_n = 0
+    for i, (name, shape, g) in enumerate(zip(names, shapes, groups)):
+        numel = 1
+        for d in shape:
+            numel *= int(d)
+        if g == MUON:
+            n_m += 1
+            m, n = int(shape[0]), int(shape[1])
+            r, c = min(m, n), max(m, n)
+            if (r, c) not in buckets:
+                buckets[(r, c)] = len(buckets)
+            b = buckets[(r, c)]
+            bucket_count[b] = bucket_count.get(b, 0) + 1
+            lines.append("%d MUON %d %d %d %d %d %d %s %d -1" % (
+                i, b, m, n, r, c, 1 if m > n else 0,
+                _f32_bits(lr_shape_scale(m, n, moonlight_coefficient)), numel))
+        elif g == ADAMW:
+            n_a += 1
+            lines.append("%d ADAMW -1 0 0 0 0 0 00000000 %d %d" % (i, numel, adam_off))
+            adam_off += numel
+        else:
+            n_n += 1
+            lines.append("%d NONE -1 0 0 0 0 0 00000000 %d -1" % (i, numel))
+    head = ["muon_adamw_plan v1 mode=%d entries=%d muon=%d adamw=%d none=%d "
+            "buckets=%d adamw_numel=%d" % (mode, len(groups), n_m, n_a, n_n,
+                                          len(buckets), adam_off)]
+    for (r, c), b in sorted(buckets.items(), key=lambda kv: kv[1]):
+        head.append("bucket %d r=%d c=%d count=%d" % (b, r, c, bucket_count[b]))
+    return "\n".join(head + lines) + "\n"
+
+
+# --------------------------------------------------------------------------
+# Global gradient-norm clipping  [defaults]
+# --------------------------------------------------------------------------
+
+def global_grad_norm(grads: Sequence[np.ndarray]) -> float:
+    """sqrt of the sum of squares of every element of every given gradient,
+    accumulated in float64."""
+    total = 0.0
+    for g in grads:
+        g64 = np.asarray(g, dtype=np.float64).ravel()
+        total += float(np.dot(g64, g64))
+    return math.sqrt(total)
+
+
+def clip_coefficient(norm: float, max_grad_norm: float) -> float:
+    """Factor applied to every gradient before the update: 1 when clipping is
+    off (max_grad_norm <= 0), else min(1, max_grad_norm / (norm + 1e-6))."""
+    if max_grad_norm <= 0.0:
+        return 1.0
+    return min(1.0, max_grad_norm / (norm + 1e-6))
+
+
+# --------------------------------------------------------------------------
+# AdamW group  [routing] (tensors not selected for Muon go to AdamW)
+# --------------------------------------------------------------------------
+
+def adamw_update(p, g, m, v, t: int, coef: float, hp: HParams):
+    """One decoupled-weight-decay Adam step (the AdamW of torch.optim), in
+    float64, on arrays of any shape.  t is the 1-based step count.
+
+    g' = coef*g
+    p  = p*(1 - lr*wd)
+    m  = beta1*m + (1-beta1)*g'
+    v  = beta2*v + (1-beta2)*g'^2
+    p  = p - (lr / (1-beta1^t)) * m / (sqrt(v)/sqrt(1-beta2^t) + eps)
+
+    Returns float32 (p, m, v).
+    """
+    p = np.asarray(p, np.float64)
+    g = np.asarray(g, np.float64) * coef
+    m = np.asarray(m, np.float64)
+    v = np.asarray(v, np.float64)
+    bc1 = 1.0 - hp.beta1 ** t
+    bc2 = 1.0 - hp.beta2 ** t
+    p = p * (1.0 - hp.lr * hp.weight_decay)
+    m = hp.beta1 * m + (1.0 - hp.beta1) * g
+    v = hp.beta2 * v + (1.0 - hp.beta2) * g * g
+    denom = np.sqrt(v) / math.sqrt(bc2) + hp.eps
+    p = p - (hp.lr / bc1) * m / denom
+    return p.astype(np.float32), m.astype(np.float32), v.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Muon group  [hparams], [NS], [FSDP-plan]
+# --------------------------------------------------------------------------
+
+def nesterov_momentum(g, buf, coef: float, mu: float, nesterov: bool):
+    """Momentum with coefficient mu on the clipped gradient; with Nesterov on,
+    the direction looks one step ahead along the new buffer.
+
+    buf = mu*buf + coef*g
+    u   = coef*g + mu*buf   (Nesterov)   or   u = buf
+
+    Returns (u float64, new buf float64)."""
+    g = np.asarray(g, np.float64) * coef
+    buf = mu * np.asarray(buf, np.float64) + g
+    u = g + mu * buf if nesterov else buf
+    return u, buf
+
+
+def frobenius_normalise(x, eps: float):
+    """x / (||x||_F + eps)."""
+    x = np.asarray(x, np.float64)
+    return x / (math.sqrt(float(np.sum(x * x))) + eps)
+
+
+def newton_schulz(u, steps: int, coeffs=DEFAULT_NS_COEFFS, eps: float = 1e-7):
+    """Quintic Newton-Schulz iteration towards the orthogonal polar factor of
+    the whole matrix u (the 'zeroth power' of [NS]), in float64.
+
+    The matrix is put in the orientation with rows <= columns, so the Gram
+    matrix X X^T is the smaller square; it is scaled to unit Frobenius norm;
+    then each step is
+        A = X X^T ;  B = b*A + c*(A A) ;  X = a*X + B X
+    and the result is turned back to the input's orientation.
+    """
+    u = np.asarray(u, np.float64)
+    if u.ndim != 2:
+        raise ValueError("newton_schulz needs a matrix")
+    a, b, c = (float(v) for v in coeffs)
+    tall = u.shape[0] > u.shape[1]
+    x = u.T if tall else u
+    x = frobenius_normalise(x, eps)
+    for _ in range(steps):
+        gram = x @ x.T
+        poly = b * gram + c * (gram @ gram)
+        x = a * x + poly @ x
+    return x.T if tall else x
+
+
+def bf16_round(x) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even), returned
+    as float32.  Diagnostic helper for the bf16-emulating NS below."""
+    f = np.ascontiguousarray(np.asarray(x, np.float32))
+    bits = f.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> np.uint64(16)) & np.uint64(1)
+    rounded = ((bits + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)).astype(np.uint32)
+    nan = np.isnan(f)
+    out = rounded.view(np.float32).copy()
+    out[nan] = np.nan
+    return out.reshape(f.shape)
+
+
+def newton_schulz_bf16_emulated(u, steps: int, coeffs=DEFAULT_NS_COEFFS,
+                                eps: float = 1e-7):
+    """Diagnostic only, not a parity target: the NS iteration with the
+    products' operands rounded to bfloat16 and float32 results, keeping a
+    float32 copy of X for the linear a*X term.  It tells how much of a bf16
+    GPU result's distance from `newton_schulz` is inherent to bf16."""
+    u = np.asarray(u, np.float64)
+    a, b, c = (float(v) for v in coeffs)
+    tall = u.shape[0] > u.shape[1]
+    x = (u.T if tall else u)
+    x32 = frobenius_normalise(x, eps).astype(np.float32)
+    for _ in range(steps):
+        xb = bf16_round(x32).astype(np.float64)
+        gram_b = bf16_round((xb @ xb.T).astype(np.float32)).astype(np.float64)
+        poly = (b * gram_b + c * (gram_b @ gram_b)).astype(np.float32)
+        poly_b = bf16_round(poly).astype(np.float64)
+        x32 = (a * x32.astype(np.float64) + (poly_b @ xb).astype(np.float32)).astype(np.float32)
+    x = x32.astype(np.float64)
+    return x.T if tall else x
+
+
+def muon_matrix_update(p, g, buf, coef: float, hp: HParams, shape_scale):
+    """The whole Muon update of one matrix parameter (float64 inside).
+
+    u, buf = nesterov_momentum(...)            [hparams]
+    O      = newton_schulz(u, ns_steps)        [NS], on the full matrix [FSDP-plan]
+    delta  = lr * muon_lr_scale * shape_scale * O   [hparams]
+    p      = p*(1 - lr*muon_wd) - delta
+
+    Returns (p float32, buf float32, delta float64)."""
+    u, buf = nesterov_momentum(g, buf, coef, hp.muon_momentum, hp.muon_nesterov)
+    o = newton_schulz(u, hp.muon_ns_steps, hp.ns_coeffs, hp.ns_eps)
+    lr_eff = float(hp.lr) * float(hp.muon_lr_scale) * float(shape_scale)
+    delta = lr_eff * o
+    p = np.asarray(p, np.float64) * (1.0 - hp.lr * hp.muon_weight_decay) - delta
+    return p.astype(np.float32), buf.astype(np.float32), delta
+
+
+@dataclass
+class StepResult:
+    params: List[Optional[np.ndarray]]
+    muon_momentum: List[Optional[np.ndarray]]
+    adam_m: List[Optional[np.ndarray]]
+    adam_v: List[Optional[np.ndarray]]
+    deltas: List[Optional[np.ndarray]]
+    grad_norm: float
+    clip_coef: float
+    groups: List[int] = field(default_factory=list)
+
+
+def optimizer_step(names, params, grads, trainable, muon_momentum, adam_m,
+                   adam_v, t: int, hp: HParams, mode: int = MODE_MUON_ADAMW,
+                   groups: Optional[Sequence[int]] = None) -> StepResult:
+    """One hybrid step over a whole parameter table, in the page's order:
+    route (once), clip over all trainable gradients, then AdamW for the AdamW
+    group and momentum -> NS -> scaled update for the Muon group.
+
+    params/grads/state are lists indexed like `names` (None where unused).
+    Nothing is modified in place; new float32 arrays are returned."""
+    shapes = [np.shape(p) if p is not None else np.shape(g) for p, g in zip(params, grads)]
+    if groups is None:
+        groups = route(names, shapes, trainable, mode)
+    live = [g for g, grp in zip(grads, groups) if grp != NONE]
+    norm = global_grad_norm(live)
+    coef = clip_coefficient(norm, hp.max_grad_norm)
+    n = len(names)
+    out_p: List[Optional[np.ndarray]] = [None] * n
+    out_buf: List[Optional[np.ndarray]] = [None] * n
+    out_m: List[Optional[np.ndarray]] = [None] * n
+    out_v: List[Optional[np.ndarray]] = [None] * n
+    deltas: List[Optional[np.ndarray]] = [None] * n
+    for i in range(n):
+        grp = groups[i]
+        if grp == ADAMW:
+            out_p[i], out_m[i], out_v[i] = adamw_update(
+                params[i], grads[i], adam_m[i], adam_v[i], t, coef, hp)
+        elif grp == MUON:
+            m, nn = shapes[i]
+            scale = lr_shape_scale(m, nn, hp.moonlight_coefficient)
+            out_p[i], out_buf[i], deltas[i] = muon_matrix_update(
+                params[i], grads[i], muon_momentum[i], coef, hp, scale)
+        else:
+            out_p[i] = None if params[i] is None else np.asarray(params[i], np.float32).copy()
+    return StepResult(out_p, out_buf, out_m, out_v, deltas, norm, coef, list(groups))

@@ -1,0 +1,414 @@
+"""Pins of the CPU oracle to facts fixed outside the oracle itself.
+
+Each test names what pins it: a closed form, an invariant, a special case that
+reduces to a library routine, brute force on tiny inputs (SVD), or a value the
+OpenDM training-stack page states.  Chosen so that a dropped term, a wrong
+sign, index or coefficient, or a transposed operand in the oracle fails one.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _phi(s, coeffs, k):
+    """k-fold composition of the scalar quintic s -> a s + b s^3 + c s^5."""
+    a, b, c = coeffs
+    for _ in range(k):
+        s = a * s + b * s ** 3 + c * s ** 5
+    return s
+
+
+# --------------------------------------------------------------------------
+# Newton-Schulz
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("coeffs", [O.DEFAULT_NS_COEFFS, O.PUBLISHED_NS_COEFFS])
+@pytest.mark.parametrize("shape", [(5, 9), (9, 5), (7, 7), (1, 6), (6, 1), (16, 64), (40, 24)])
+def test_ns_equals_svd_spectral_map(shape, coeffs):
+    """Closed form: for X = U S V^T normalised to unit Frobenius norm, k steps
+    of X <- aX + (b XX^T + c (XX^T)^2) X give U phi^k(S) V^T, with phi the
+    scalar quintic.  SVD from LAPACK, independent of the iteration."""
+    rng = np.random.default_rng(sum(shape))
+    g = rng.standard_normal(shape)
+    for k in (1, 3, 5):
+        got = O.newton_schulz(g, k, coeffs, eps=0.0)
+        u, s, vt = np.linalg.svd(g, full_matrices=False)
+        s = s / math.sqrt(float(np.sum(s * s)))
+        want = (u * _phi(s, coeffs, k)) @ vt
+        assert np.linalg.norm(got - want) <= 1e-9 * np.linalg.norm(want)
+
+
+def test_phi5_values_distinguish_step_count():
+    """ns_steps = 5 (hyperparameter table of the page).  The fixed point of
+    the map is not reached, so 4, 5 and 6 steps give visibly different gains
+    on a unit singular value.  Numbers are the scalar compositions, recorded
+    at survey time for both triples."""
+    d, p = O.DEFAULT_NS_COEFFS, O.PUBLISHED_NS_COEFFS
+    assert _phi(1.0, d, 5) == pytest.approx(0.984131, abs=2e-6)
+    assert _phi(1.0, d, 4) == pytest.approx(0.996466, abs=2e-6)
+    assert _phi(1.0, d, 6) == pytest.approx(0.995206, abs=2e-6)
+    assert _phi(1.0, p, 5) == pytest.approx(0.696436, abs=2e-6)
+    assert _phi(1.0, p, 4) == pytest.approx(1.089974, abs=2e-6)
+    assert _phi(1.0, p, 6) == pytest.approx(1.118768, abs=2e-6)
+    hp = O.HParams()
+    assert hp.muon_ns_steps == 5
+
+
+@pytest.mark.parametrize("shape", [(8, 32), (32, 8), (1, 17), (17, 1), (12, 12)])
+def test_rank_one_input(shape):
+    """Special case: a rank-1 matrix x y^T has one singular value, equal to
+    its Frobenius norm, so NS returns phi^5(1) * x y^T / (|x||y|)."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(shape[0])
+    y = rng.standard_normal(shape[1])
+    got = O.newton_schulz(np.outer(x, y), 5, eps=0.0)
+    want = 0.984131 * np.outer(x / np.linalg.norm(x), y / np.linalg.norm(y))
+    np.testing.assert_allclose(got, want, atol=3e-6)
+
+
+@pytest.mark.parametrize("r,c,gain", [(4, 16, 0.958947), (16, 64, 1.037006), (64, 256, 0.949313)])
+def test_orthonormal_rows(r, c, gain):
+    """Special case: X = Q with orthonormal rows has r singular values 1, which
+    normalisation maps to 1/sqrt(r); the result is phi^5(1/sqrt(r)) Q."""
+    rng = np.random.default_rng(r)
+    q, _ = np.linalg.qr(rng.standard_normal((c, r)))
+    q = q.T
+    got = O.newton_schulz(q, 5, eps=0.0)
+    np.testing.assert_allclose(got, gain * q, atol=2e-6)
+    np.testing.assert_allclose(O.newton_schulz(q.T, 5, eps=0.0), gain * q.T, atol=2e-6)
+
+
+def test_alignment_with_polar_factor():
+    """Brute force on tiny inputs: NS of a Gaussian matrix points along its
+    orthogonal polar factor U V^T (SVD), cosine >= 0.99 for shapes with
+    r <= c/4, and every output singular value lies in the band of the default
+    triple, [0.934, 1.215] for sigma/||X||_F in [1e-2, 1]."""
+    rng = np.random.default_rng(11)
+    worst = 1.0
+    for r in (4, 8, 16, 32, 64):
+        for c in (4 * r, 8 * r):
+            for t in range(40):
+                g = rng.standard_normal((r, c))
+                if t % 2:
+                    g = g.T
+                u, s, vt = np.linalg.svd(g, full_matrices=False)
+                polar = u @ vt
+                out = O.newton_schulz(g, 5)
+                cos = float(np.sum(out * polar) / np.linalg.norm(out) / np.linalg.norm(polar))
+                worst = min(worst, cos)
+                rel = s / np.linalg.norm(s)
+                sv = np.linalg.svd(out, compute_uv=False)
+                inside = rel >= 1e-2
+                if inside.all():
+                    assert sv.min() >= 0.934 and sv.max() <= 1.215
+    assert worst >= 0.99
+
+
+def test_band_of_default_coefficients():
+    """The recorded band of the default triple over sigma in [1e-2, 1]."""
+    s = np.linspace(1e-2, 1.0, 200001)
+    v = _phi(s, O.DEFAULT_NS_COEFFS, 5)
+    assert 0.934 <= v.min() <= 0.9345
+    assert 1.2145 <= v.max() <= 1.215
+
+
+@pytest.mark.parametrize("shape", [(6, 20), (20, 6), (9, 9)])
+def test_orientation_invariance(shape):
+    """Invariant: NS(G^T) = NS(G)^T; the oracle transposes tall matrices, so a
+    wrong back-transpose or a Gram on the wrong side breaks it."""
+    rng = np.random.default_rng(5)
+    g = rng.standard_normal(shape)
+    a = O.newton_schulz(g.T, 5)
+    b = O.newton_schulz(g, 5).T
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_scale_invariance_and_zero():
+    """Invariants: NS(alpha G) = NS(G) for alpha > 0 (normalisation), and the
+    zero matrix maps to zero (the epsilon guards the division)."""
+    rng = np.random.default_rng(6)
+    g = rng.standard_normal((10, 30))
+    np.testing.assert_allclose(O.newton_schulz(37.5 * g, 5, eps=0.0),
+                               O.newton_schulz(g, 5, eps=0.0), atol=1e-12)
+    assert np.all(O.newton_schulz(np.zeros((4, 8)), 5) == 0.0)
+
+
+def test_frobenius_normalise():
+    """Special case reducing to a library routine: ||x||_F from numpy."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((13, 7))
+    got = O.frobenius_normalise(x, 1e-7)
+    np.testing.assert_allclose(got, x / (np.linalg.norm(x) + 1e-7), rtol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# momentum, learning-rate factor, whole Muon update
+# --------------------------------------------------------------------------
+
+def test_nesterov_closed_forms():
+    """Closed forms with a zero buffer, mu = 0.95 (hyperparameter table),
+    coef 1: step 1 u = 1.95 g1; step 2 u = 1.95 g2 + 0.9025 g1; buffers
+    g1 and g2 + 0.95 g1.  Without Nesterov u is the buffer."""
+    rng = np.random.default_rng(8)
+    g1, g2 = rng.standard_normal((2, 5, 4))
+    u1, b1 = O.nesterov_momentum(g1, np.zeros((5, 4)), 1.0, 0.95, True)
+    np.testing.assert_allclose(u1, 1.95 * g1, rtol=1e-15)
+    np.testing.assert_allclose(b1, g1, rtol=1e-15)
+    u2, b2 = O.nesterov_momentum(g2, b1, 1.0, 0.95, True)
+    np.testing.assert_allclose(u2, 1.95 * g2 + 0.9025 * g1, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(b2, g2 + 0.95 * g1, rtol=1e-15)
+    u3, _ = O.nesterov_momentum(g2, b1, 1.0, 0.95, False)
+    np.testing.assert_allclose(u3, g2 + 0.95 * g1, rtol=1e-15)
+    u4, b4 = O.nesterov_momentum(g1, np.zeros((5, 4)), 0.25, 0.95, True)
+    np.testing.assert_allclose(b4, 0.25 * g1, rtol=1e-15)
+
+
+def test_lr_shape_scale_values():
+    """Closed form 0.2*sqrt(max(m,n)) (the Muon learning-rate sentence of the
+    page): exact squares give 3.2, 6.4, 12.8; 8192 and 14336 worked by hand
+    (sqrt(8192) = 64 sqrt 2, sqrt(14336) = 32 sqrt 14)."""
+    assert O.lr_shape_scale(256, 256) == np.float32(3.2)
+    assert O.lr_shape_scale(1024, 256) == np.float32(6.4)
+    assert O.lr_shape_scale(256, 1024) == np.float32(6.4)
+    assert O.lr_shape_scale(4096, 1024) == np.float32(12.8)
+    assert O.lr_shape_scale(8192, 8192) == np.float32(12.8 * math.sqrt(2.0))
+    assert O.lr_shape_scale(14336, 4096) == np.float32(6.4 * math.sqrt(14.0))
+    assert O.lr_shape_scale(1, 1) == np.float32(0.2)
+
+
+@pytest.mark.parametrize("shape", [(24, 96), (96, 24)])
+def test_muon_update_rank_one(shape):
+    """Whole Muon update of a rank-1 gradient at step 1 from a zero buffer:
+    delta = lr * 0.2 sqrt(max(m,n)) * phi^5(1) * x y^T / (|x||y|), whatever
+    the clip factor and the Nesterov factor 1.95 (both cancel in the
+    normalisation); p moves by -delta exactly, the buffer holds coef*g."""
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal(shape[0])
+    y = rng.standard_normal(shape[1])
+    g = np.outer(x, y).astype(np.float32)
+    p0 = rng.standard_normal(shape).astype(np.float32) * np.float32(0.02)
+    hp = O.HParams()
+    coef = 0.125
+    scale = O.lr_shape_scale(*shape)
+    p1, buf, delta = O.muon_matrix_update(p0, g, np.zeros(shape, np.float32), coef, hp, scale)
+    want = 2.5e-5 * 0.2 * math.sqrt(max(shape)) * 0.984131 * np.outer(
+        x / np.linalg.norm(x), y / np.linalg.norm(y))
+    np.testing.assert_allclose(delta, want, rtol=0, atol=2.5e-5 * 5.0 * 3e-6)
+    np.testing.assert_allclose(p1, (p0.astype(np.float64) - delta).astype(np.float32), rtol=0, atol=0)
+    np.testing.assert_allclose(buf, (coef * g.astype(np.float64)).astype(np.float32), rtol=0, atol=0)
+
+
+# --------------------------------------------------------------------------
+# AdamW and clipping
+# --------------------------------------------------------------------------
+
+def _load_adamw_golden():
+    rows = []
+    with open(os.path.join(GOLDEN, "adamw_one_step.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            rows.append([float(v) for v in line.split()])
+    return np.array(rows)
+
+
+def test_adamw_first_step_worked_values():
+    """Closed form of the first AdamW step from zero moments (worked values
+    in tests/golden/adamw_one_step.txt); the eps-sensitive row pins where eps
+    enters the denominator."""
+    rows = _load_adamw_golden()
+    hp = O.HParams()
+    p0, g, p1, m1, v1 = (rows[:, i] for i in range(5))
+    z = np.zeros_like(p0)
+    p, m, v = O.adamw_update(p0.astype(np.float32), g.astype(np.float32), z, z, 1, 1.0, hp)
+    # inputs pass through float32, so compare to the closed form evaluated on
+    # the float32-rounded inputs
+    p0f = p0.astype(np.float32).astype(np.float64)
+    gf = g.astype(np.float32).astype(np.float64)
+    want = p0f * (1 - 2.5e-7) - 2.5e-5 * gf / (np.abs(gf) + 1e-8)
+    np.testing.assert_allclose(p, want.astype(np.float32), rtol=0, atol=0)
+    np.testing.assert_allclose(p, p1, rtol=2e-7, atol=1e-12)
+    np.testing.assert_allclose(m, m1, rtol=2e-7, atol=0)
+    np.testing.assert_allclose(v, v1, rtol=4e-7, atol=0)
+
+
+def test_adamw_constant_gradient_steps():
+    """Closed form: with a constant gradient the bias-corrected moments equal
+    g and g^2 at every step, so each step is p <- p(1-lr wd) - lr g/(|g|+eps)."""
+    hp = O.HParams()
+    g = np.array([1e-3, -4e-4, 2e-9, 0.5], np.float32)
+    p = np.array([0.02, -0.01, 0.03, 0.0], np.float32)
+    m = np.zeros(4, np.float32)
+    v = np.zeros(4, np.float32)
+    ref = p.astype(np.float64)
+    g64 = g.astype(np.float64)
+    for t in range(1, 6):
+        p, m, v = O.adamw_update(p, g, m, v, t, 1.0, hp)
+        ref = ref * (1 - hp.lr * hp.weight_decay) - hp.lr * g64 / (np.abs(g64) + hp.eps)
+        np.testing.assert_allclose(p, ref, rtol=1e-6, atol=1e-12)
+
+
+def test_adamw_zero_gradient_is_pure_decay():
+    hp = O.HParams()
+    p0 = np.array([0.5, -2.0], np.float32)
+    p, m, v = O.adamw_update(p0, np.zeros(2, np.float32), np.zeros(2), np.zeros(2), 1, 1.0, hp)
+    np.testing.assert_allclose(p, p0 * (1 - 2.5e-7), rtol=1e-7)
+    assert np.all(m == 0) and np.all(v == 0)
+
+
+def test_global_norm_is_library_norm():
+    """Special case reducing to a library routine: the global norm is the
+    2-norm of the concatenation of all gradients."""
+    rng = np.random.default_rng(12)
+    gs = [rng.standard_normal(s).astype(np.float32) for s in [(3, 4), (7,), (2, 2, 2)]]
+    flat = np.concatenate([g.ravel().astype(np.float64) for g in gs])
+    assert O.global_grad_norm(gs) == pytest.approx(np.linalg.norm(flat), rel=1e-14)
+
+
+def test_clip_coefficient_closed_forms():
+    """max_grad_norm 1.0 (defaults table): no clipping at or below the limit,
+    coef*N = 1*N/(N+1e-6) above it, off for max_grad_norm <= 0, NaN
+    propagates."""
+    assert O.clip_coefficient(0.5, 1.0) == 1.0
+    assert O.clip_coefficient(1.0 - 1e-6, 1.0) == 1.0
+    n = 464.0
+    assert O.clip_coefficient(n, 1.0) * n == pytest.approx(n / (n + 1e-6), rel=1e-15)
+    assert O.clip_coefficient(1e9, 0.0) == 1.0
+    assert math.isnan(O.clip_coefficient(float("nan"), 1.0)) or O.clip_coefficient(float("nan"), 1.0) == 1.0
+    assert O.HParams().max_grad_norm == 1.0
+
+
+def test_step_clip_scope_and_order():
+    """Whole-step special case.  A Muon matrix with a rank-1 gradient of norm
+    10, a tiny AdamW gradient (1e-8 per element) and a frozen tensor with a
+    huge gradient.  The norm must skip the frozen tensor (N = 10 exactly up to
+    the AdamW part), the clip must reach AdamW before its moments (then
+    coef*g = 1e-9, comparable to eps, so the update is lr*1e-9/(1e-9+1e-8)),
+    and the Muon delta is the rank-1 closed form."""
+    names = ["action_expert.layers.0.mlp.down_proj.weight", "vlm.model.norm.weight",
+             "vlm.model.embed_tokens.weight"]
+    x = np.zeros(16); x[3] = 1.0
+    y = np.zeros(64); y[10] = 10.0
+    gm = np.outer(x, y).astype(np.float32)
+    ga = np.full(8, 1e-8, np.float32)
+    gn = np.full((4, 4), 1e6, np.float32)
+    params = [np.zeros((16, 64), np.float32), np.full(8, 0.1, np.float32), np.zeros((4, 4), np.float32)]
+    hp = O.HParams()
+    res = O.optimizer_step(names, params, [gm, ga, gn], [True, True, False],
+                           [np.zeros((16, 64), np.float32), None, None],
+                           [None, np.zeros(8, np.float32), None],
+                           [None, np.zeros(8, np.float32), None], 1, hp)
+    assert res.groups == [O.MUON, O.ADAMW, O.NONE]
+    assert res.grad_norm == pytest.approx(math.sqrt(100.0 + 8 * 1e-16), rel=1e-12)
+    coef = 1.0 / (res.grad_norm + 1e-6)
+    assert res.clip_coef == pytest.approx(coef, rel=1e-15)
+    cg = coef * float(np.float32(1e-8))
+    want_a = 0.1 * (1 - 2.5e-7) - 2.5e-5 * cg / (cg + 1e-8)
+    np.testing.assert_allclose(res.params[1], np.float32(want_a), rtol=1e-7)
+    want_d = 2.5e-5 * 0.2 * 8.0 * 0.984131 * np.outer(x, y / 10.0)
+    np.testing.assert_allclose(res.deltas[0], want_d, atol=1e-10)
+    np.testing.assert_allclose(res.muon_momentum[0], (coef * gm).astype(np.float32), rtol=1e-7)
+    np.testing.assert_array_equal(res.params[2], params[2])
+
+
+# --------------------------------------------------------------------------
+# routing and plan
+# --------------------------------------------------------------------------
+
+def _routing_rows():
+    rows = []
+    with open(os.path.join(GOLDEN, "routing_table.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            grp, tr, shape, name = line.rstrip("\n").split("\t")
+            rows.append((grp, tr == "1", tuple(int(s) for s in shape.split(",")), name))
+    return rows
+
+
+def test_routing_table():
+    """The page's routing rule on an adversarial table (golden file with its
+    reading of every edge)."""
+    for grp, tr, shape, name in _routing_rows():
+        got = O.GROUP_NAMES[O.route_one(name, shape, tr)]
+        assert got == grp, name
+
+
+def test_routing_adamw_mode():
+    """The optim switch: plain AdamW sends every trainable tensor to AdamW."""
+    for grp, tr, shape, name in _routing_rows():
+        want = "NONE" if not tr else "ADAMW"
+        assert O.GROUP_NAMES[O.route_one(name, shape, tr, O.MODE_ADAMW)] == want
+
+
+def test_workload_group_counts():
+    """Group sizes of the synthetic workloads follow from the routing rule:
+    tiny 14 Muon / 13 AdamW; 18-layer 126 / 0; full hybrid 126 / 253 / 1
+    frozen; stress 68 / 0; and the element totals of the workload text."""
+    import workloads as W
+    expect = {
+        "tiny_hybrid_fp32": (14, 13, 0, 2_097_152, 259_072),
+        "ae18_muon_bf16": (126, 0, 0, 273_678_336, 0),
+        "vla_hybrid_bf16": (126, 253, 1, 273_678_336, 1_879_164_928),
+        "ragged_stress_bf16": (68, 0, 0, 186_646_528, 0),
+    }
+    for name, (nm, na, nn, em, ea) in expect.items():
+        w = W.WORKLOADS[name]()
+        groups = O.route(w.names, w.shapes, w.trainable)
+        assert groups.count(O.MUON) == nm
+        assert groups.count(O.ADAMW) == na
+        assert groups.count(O.NONE) == nn
+        numel = [p.numel for p in w.params]
+        assert sum(n for n, g in zip(numel, groups) if g == O.MUON) == em
+        assert sum(n for n, g in zip(numel, groups) if g == O.ADAMW) == ea
+
+
+def test_plan_dump_shape():
+    """Plan dump header and bucket lines on the 18-layer table: three
+    canonical buckets (1024,1024)x36, (256,1024)x36, (1024,4096)x54 and the
+    shape factors 6.4 / 12.8 for max dims 1024 / 4096."""
+    import workloads as W
+    w = W.ae18_muon_bf16()
+    text = O.plan_dump(w.names, w.shapes, w.trainable)
+    lines = text.splitlines()
+    assert lines[0] == ("muon_adamw_plan v1 mode=0 entries=126 muon=126 adamw=0 none=0 "
+                        "buckets=3 adamw_numel=0")
+    assert lines[1] == "bucket 0 r=1024 c=1024 count=36"
+    assert lines[2] == "bucket 1 r=256 c=1024 count=36"
+    assert lines[3] == "bucket 2 r=1024 c=4096 count=54"
+    six4 = "%08x" % int(np.array([6.4], np.float32).view(np.uint32)[0])
+    t128 = "%08x" % int(np.array([12.8], np.float32).view(np.uint32)[0])
+    assert lines[4] == "0 MUON 0 1024 1024 1024 1024 0 %s 1048576 -1" % six4
+    assert lines[8] == "4 MUON 2 4096 1024 1024 4096 1 %s 4194304 -1" % t128
+
+
+# --------------------------------------------------------------------------
+# diagnostic bf16 emulation
+# --------------------------------------------------------------------------
+
+def test_bf16_round_matches_torch():
+    """Special case reducing to a library routine: torch's float32->bfloat16
+    conversion rounds to nearest even."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(13)
+    x = np.concatenate([rng.standard_normal(10000).astype(np.float32) * 10.0 ** rng.integers(-20, 20, 10000),
+                        np.array([0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 65504.0], np.float32)]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(O.bf16_round(x), want)
+
+
+def test_bf16_emulated_ns_close_to_exact():
+    """The bf16-emulating diagnostic stays within the bf16 tolerance of the
+    fp64 iteration on a C1-like matrix (a sanity bound, not a parity gate)."""
+    rng = np.random.default_rng(14)
+    g = rng.standard_normal((64, 256)) * np.exp(rng.uniform(np.log(0.1), np.log(10), 64))[:, None]
+    a = O.newton_schulz(g, 5)
+    b = O.newton_schulz_bf16_emulated(g, 5)
+    assert np.linalg.norm(a - b) / np.linalg.norm(a) < 2e-2

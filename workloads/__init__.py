@@ -1,0 +1,304 @@
+"""Synthetic workloads and seeded input generators.
+
+This module holds parameter tables (names, shapes, trainable flags), the
+hyperparameters each workload runs with, and seeded random inputs.  It holds
+none of the optimizer's arithmetic, so both the oracle side (tests, the CPU
+baseline) and the GPU side (tests, the benchmark) may draw from it.
+
+Names follow the layout of the model family on the OpenDM training-stack page
+(an action expert with `layers`, a VLM backbone whose token embedding is frozen);
+the page gives no concrete tables, so these are synthetic and sized by the
+workload definitions below.
+
+Two generator back ends produce the same *kind* of values from the same seeds:
+  * numpy: PCG64 streams `default_rng([seed, kind, step, index])`, float32;
+  * torch: one Philox generator on the target device per tensor, seeded by a
+    hash of the same tuple.  Used where host generation of billions of values
+    would dominate the run (the full-size hybrid workload).
+The two back ends do not produce equal values; a run uses one of them for
+both sides of a comparison (the oracle reads the device tensors' copies).
+"""
+
+from __future__ import annotations
+
+import hashlib
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+KIND_PARAM, KIND_GRAD, KIND_MOMENTUM = 0, 1, 2
+
+
+@dataclass(frozen=True)
+class ParamSpec:
+    name: str
+    shape: Tuple[int, ...]
+    trainable: bool = True
+
+    @property
+    def numel(self) -> int:
+        n = 1
+        for d in self.shape:
+            n *= d
+        return n
+
+
+@dataclass
+class Workload:
+    name: str
+    seed: int
+    steps: int
+    ns_precision: str                 # "bf16" or "fp32"
+    params: List[ParamSpec]
+    grad_std: float
+    weight_std: float = 0.02
+    grad_row_scale: Optional[Tuple[float, float]] = None   # log-uniform per stored row
+    spike: Optional[Tuple[int, float]] = None               # (rank, entry std)
+    momentum_init_std: float = 0.0
+    hparams: Dict[str, float] = field(default_factory=dict)
+    description: str = ""
+
+    @property
+    def names(self) -> List[str]:
+        return [p.name for p in self.params]
+
+    @property
+    def shapes(self) -> List[Tuple[int, ...]]:
+        return [p.shape for p in self.params]
+
+    @property
+    def trainable(self) -> List[bool]:
+        return [p.trainable for p in self.params]
+
+
+# --------------------------------------------------------------------------
+# parameter tables
+# --------------------------------------------------------------------------
+
+def _action_expert_layers(n_layers: int, hidden: int, kv: int, mlp: int) -> List[ParamSpec]:
+    out = []
+    for layer in range(n_layers):
+        pre = "action_expert.layers.%d." % layer
+        out += [
+            ParamSpec(pre + "self_attn.q_proj.weight", (hidden, hidden)),
+            ParamSpec(pre + "self_attn.k_proj.weight", (kv, hidden)),
+            ParamSpec(pre + "self_attn.v_proj.weight", (kv, hidden)),
+            ParamSpec(pre + "self_attn.o_proj.weight", (hidden, hidden)),
+            ParamSpec(pre + "mlp.gate_proj.weight", (mlp, hidden)),
+            ParamSpec(pre + "mlp.up_proj.weight", (mlp, hidden)),
+            ParamSpec(pre + "mlp.down_proj.weight", (hidden, mlp)),
+        ]
+    return out
+
+
+def tiny_hybrid_fp32() -> Workload:
+    """Two action-expert layers (q,k,v,o 256x256; gate,up 1024x256; down
+    256x1024: 14 matrices) plus an AdamW group of a 1000x256 embedding, eight
+    RMSNorm vectors and four biases of 256; fp32 Newton-Schulz; 3 steps."""
+    params = _action_expert_layers(2, 256, 256, 1024)
+    params.append(ParamSpec("action_expert.embed_tokens.weight", (1000, 256)))
+    for layer in range(2):
+        pre = "action_expert.layers.%d." % layer
+        for nm in ("input_layernorm", "post_attention_layernorm",
+                   "self_attn.q_norm", "self_attn.k_norm"):
+            params.append(ParamSpec(pre + nm + ".weight", (256,)))
+    for layer in range(2):
+        pre = "action_expert.layers.%d." % layer
+        for nm in ("q_proj", "k_proj"):
+            params.append(ParamSpec(pre + "self_attn." + nm + ".bias", (256,)))
+    return Workload("tiny_hybrid_fp32", seed=0, steps=3, ns_precision="fp32",
+                    params=params, grad_std=1e-3,
+                    description="14 Muon matrices (256-1024) + 259,072 AdamW "
+                                "elements, fp32 NS")
+
+
+def _action_expert_18() -> List[ParamSpec]:
+    return _action_expert_layers(18, 1024, 256, 4096)
+
+
+def ae18_muon_bf16() -> Workload:
+    """Muon group only: 18 action-expert layers x {q,o 1024x1024; k,v
+    256x1024; gate,up 4096x1024; down 1024x4096} = 126 matrices; bf16 NS;
+    gradients N(0,1e-3) times a log-uniform [0.1,10] scale per stored row;
+    10 steps."""
+    return Workload("ae18_muon_bf16", seed=1, steps=10, ns_precision="bf16",
+                    params=_action_expert_18(), grad_std=1e-3,
+                    grad_row_scale=(0.1, 10.0),
+                    description="126 Muon matrices, 273,678,336 params, bf16 NS")
+
+
+def _vlm_backbone(n_layers=28, hidden=2048, mlp=8192, vocab=151000) -> List[ParamSpec]:
+    out = [ParamSpec("vlm.model.embed_tokens.weight", (vocab, hidden), trainable=False)]
+    for layer in range(n_layers):
+        pre = "vlm.model.layers.%d." % layer
+        out += [
+            ParamSpec(pre + "self_attn.q_proj.weight", (hidden, hidden)),
+            ParamSpec(pre + "self_attn.k_proj.weight", (hidden, hidden)),
+            ParamSpec(pre + "self_attn.v_proj.weight", (hidden, hidden)),
+            ParamSpec(pre + "self_attn.o_proj.weight", (hidden, hidden)),
+            ParamSpec(pre + "mlp.gate_proj.weight", (mlp, hidden)),
+            ParamSpec(pre + "mlp.up_proj.weight", (mlp, hidden)),
+            ParamSpec(pre + "mlp.down_proj.weight", (hidden, mlp)),
+            ParamSpec(pre + "input_layernorm.weight", (hidden,)),
+            ParamSpec(pre + "post_attention_layernorm.weight", (hidden,)),
+        ]
+    out.append(ParamSpec("vlm.model.norm.weight", (hidden,)))
+    return out
+
+
+def vla_hybrid_bf16() -> Workload:
+    """The full hybrid step: the 126-matrix action-expert Muon group plus an
+    AdamW group shaped like a 1.9B VLM backbone (28 layers, hidden 2048, MLP
+    8192; 253 tensors, 1,879,164,928 elements) and a frozen 151000x2048 token
+    embedding; gradients N(0,1e-2) so the clip to 1.0 triggers; bf16 NS."""
+    return Workload("vla_hybrid_bf16", seed=2, steps=5, ns_precision="bf16",
+                    params=_vlm_backbone() + _action_expert_18(), grad_std=1e-2,
+                    description="126 Muon matrices + 253 AdamW tensors "
+                                "(2,152,843,264 trainable params), bf16 NS")
+
+
+def vla_hybrid_fp32ns() -> Workload:
+    """vla_hybrid_bf16's parameters and seeds with the NS products in full
+    fp32."""
+    w = vla_hybrid_bf16()
+    w.name = "vla_hybrid_fp32ns"
+    w.ns_precision = "fp32"
+    w.description = "vla_hybrid parameter set, fp32 NS"
+    return w
+
+
+def ragged_stress_bf16(clip: bool = True) -> Workload:
+    """Large and ragged Muon matrices in one call: 8192x8192, 4096x14336,
+    14336x4096, 128x8192 and 64 matrices of 64x256; gradients N(0,1) plus a
+    rank-8 spike whose entries have std 100; momentum buffers preloaded
+    N(0,1e-2); bf16 NS; 3 steps.  `clip=False` turns the global clip off."""
+    params = [
+        ParamSpec("action_expert.layers.0.stress_0.weight", (8192, 8192)),
+        ParamSpec("action_expert.layers.0.stress_1.weight", (4096, 14336)),
+        ParamSpec("action_expert.layers.0.stress_2.weight", (14336, 4096)),
+        ParamSpec("action_expert.layers.0.stress_3.weight", (128, 8192)),
+    ]
+    for j in range(64):
+        params.append(ParamSpec("action_expert.layers.1.stress_%d.weight" % j, (64, 256)))
+    hp = {} if clip else {"max_grad_norm": 0.0}
+    return Workload("ragged_stress_bf16" + ("" if clip else "_noclip"), seed=4,
+                    steps=3, ns_precision="bf16", params=params, grad_std=1.0,
+                    spike=(8, 100.0), momentum_init_std=1e-2, hparams=hp,
+                    description="68 Muon matrices (8192^2 ... 64x256), spiked "
+                                "gradients, preloaded momentum")
+
+
+WORKLOADS = {
+    "tiny_hybrid_fp32": tiny_hybrid_fp32,
+    "ae18_muon_bf16": ae18_muon_bf16,
+    "vla_hybrid_bf16": vla_hybrid_bf16,
+    "vla_hybrid_fp32ns": vla_hybrid_fp32ns,
+    "ragged_stress_bf16": ragged_stress_bf16,
+    "ragged_stress_bf16_noclip": lambda: ragged_stress_bf16(clip=False),
+}
+
+
+# --------------------------------------------------------------------------
+# numpy back end
+# --------------------------------------------------------------------------
+
+def _rng(seed: int, kind: int, step: int, index: int) -> np.random.Generator:
+    return np.random.default_rng([seed, kind, step, index])
+
+
+def np_param(w: Workload, index: int) -> np.ndarray:
+    spec = w.params[index]
+    r = _rng(w.seed, KIND_PARAM, 0, index)
+    return (r.standard_normal(spec.shape, dtype=np.float32) * np.float32(w.weight_std))
+
+
+def np_momentum(w: Workload, index: int) -> np.ndarray:
+    spec = w.params[index]
+    if w.momentum_init_std == 0.0:
+        return np.zeros(spec.shape, np.float32)
+    r = _rng(w.seed, KIND_MOMENTUM, 0, index)
+    return r.standard_normal(spec.shape, dtype=np.float32) * np.float32(w.momentum_init_std)
+
+
+def np_grad(w: Workload, step: int, index: int) -> np.ndarray:
+    spec = w.params[index]
+    r = _rng(w.seed, KIND_GRAD, step, index)
+    g = r.standard_normal(spec.shape, dtype=np.float32) * np.float32(w.grad_std)
+    if w.grad_row_scale is not None and len(spec.shape) >= 1:
+        lo, hi = w.grad_row_scale
+        s = np.exp(r.uniform(math.log(lo), math.log(hi), spec.shape[0])).astype(np.float32)
+        g *= s.reshape((-1,) + (1,) * (len(spec.shape) - 1))
+    if w.spike is not None and len(spec.shape) == 2:
+        rank, mag = w.spike
+        m, n = spec.shape
+        u = r.standard_normal((m, rank), dtype=np.float32)
+        v = r.standard_normal((n, rank), dtype=np.float32)
+        g += (np.float32(mag / math.sqrt(rank)) * (u @ v.T)).astype(np.float32)
+    return g
+
+
+# --------------------------------------------------------------------------
+# torch back end (device-side generation for the large workloads)
+# --------------------------------------------------------------------------
+
+def torch_seed(seed: int, kind: int, step: int, index: int) -> int:
+    h = hashlib.blake2b(("%d/%d/%d/%d" % (seed, kind, step, index)).encode(),
+                        digest_size=8).digest()
+    return int.from_bytes(h, "little") & ((1 << 63) - 1)
+
+
+def _torch_gen(device, seed: int, kind: int, step: int, index: int):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(torch_seed(seed, kind, step, index))
+    return g
+
+
+def torch_param(w: Workload, index: int, device, out=None):
+    import torch
+    spec = w.params[index]
+    gen = _torch_gen(device, w.seed, KIND_PARAM, 0, index)
+    t = out if out is not None else torch.empty(spec.shape, dtype=torch.float32, device=device)
+    t.normal_(0.0, w.weight_std, generator=gen)
+    return t
+
+
+def torch_momentum(w: Workload, index: int, device, out=None):
+    import torch
+    spec = w.params[index]
+    t = out if out is not None else torch.empty(spec.shape, dtype=torch.float32, device=device)
+    if w.momentum_init_std == 0.0:
+        t.zero_()
+        return t
+    gen = _torch_gen(device, w.seed, KIND_MOMENTUM, 0, index)
+    t.normal_(0.0, w.momentum_init_std, generator=gen)
+    return t
+
+
+def torch_grad(w: Workload, step: int, index: int, device, out=None):
+    import torch
+    spec = w.params[index]
+    gen = _torch_gen(device, w.seed, KIND_GRAD, step, index)
+    t = out if out is not None else torch.empty(spec.shape, dtype=torch.float32, device=device)
+    t.normal_(0.0, w.grad_std, generator=gen)
+    if w.grad_row_scale is not None and len(spec.shape) >= 1:
+        lo, hi = w.grad_row_scale
+        s = torch.empty(spec.shape[0], dtype=torch.float32, device=device)
+        s.uniform_(math.log(lo), math.log(hi), generator=gen).exp_()
+        t.mul_(s.reshape((-1,) + (1,) * (len(spec.shape) - 1)))
+    if w.spike is not None and len(spec.shape) == 2:
+        rank, mag = w.spike
+        m, n = spec.shape
+        u = torch.randn((m, rank), generator=gen, device=device, dtype=torch.float32)
+        v = torch.randn((rank, n), generator=gen, device=device, dtype=torch.float32)
+        t.add_(torch.mm(u, v), alpha=mag / math.sqrt(rank))
+    return t
+
+
+def hparams_for(w: Workload) -> Dict[str, float]:
+    """Hyperparameter overrides of a workload on top of the defaults
+    (lr 2.5e-5, momentum 0.95 Nesterov, 5 NS steps, moonlight 0.2, AdamW
+    betas (0.9, 0.999), eps 1e-8, decay 0.01, clip 1.0)."""
+    return dict(w.hparams)
