@@ -1,0 +1,262 @@
+"""Benchmark of the hybrid MuonAdamW optimizer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is the whole hot path over the full parameter table of the
+workload: clip norm over every trainable gradient, AdamW over the AdamW
+group, momentum/normalise and 5 bf16 Newton-Schulz steps with the fused
+update over the Muon group.  Inputs (parameters, gradients, states) are
+synthetic, seeded, and resident in HBM before timing starts.
+
+Prints one JSON line: whole-step params/s (the metric's headline value),
+step time, per-phase times taken with HIP events recorded by the library on
+its own stream, Newton-Schulz TFLOP/s and AdamW GB/s against the MI355X
+peaks, the roofline of the dominant kernel, and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import math
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0       # dense MFMA
+PEAK_FP32_TFLOPS = 157.3        # dense MFMA fp32
+METRIC = "hybrid MuonAdamW step: params/s; NS TFLOP/s (MFMA %); AdamW HBM GB/s"
+
+
+class HipEvents:
+    """Timing events from the HIP runtime, recorded by the library itself on
+    the stream its kernels run on."""
+
+    def __init__(self, n: int):
+        self.hip = C.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = C.c_void_p()
+            rc = self.hip.hipEventCreate(C.byref(e))
+            if rc != 0:
+                raise RuntimeError("hipEventCreate failed (%d)" % rc)
+            self.ev.append(e.value)
+
+    def elapsed(self, a: int, b: int) -> float:
+        ms = C.c_float()
+        self.hip.hipEventSynchronize(C.c_void_p(self.ev[b]))
+        rc = self.hip.hipEventElapsedTime(C.byref(ms), C.c_void_p(self.ev[a]), C.c_void_p(self.ev[b]))
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(C.c_void_p(e))
+
+
+def ns_flops(shapes, ns_steps: int) -> float:
+    """Dense algorithmic flops of NS: per step and matrix (r <= c) the Gram
+    X X^T (2 r^2 c), the square A A (2 r^3) and B X (2 r^2 c)."""
+    tot = 0.0
+    for m, n in shapes:
+        r, c = min(m, n), max(m, n)
+        tot += 4.0 * r * r * c + 2.0 * r ** 3
+    return tot * ns_steps
+
+
+def cpu_baseline(w, hp_overrides) -> dict:
+    """The oracle, as it stands, on a bounded sample of the workload: one of
+    the action-expert layers (7 Muon matrices) and one of the VLM layers (9
+    AdamW tensors) of the full hybrid table, each timed whole (clip norm of
+    the sampled gradients + updates) and scaled by the layer counts to the
+    whole table's params/s."""
+    import numpy as np
+    import oracle as O
+    import workloads as W
+
+    hp = O.HParams()
+    for k, v in hp_overrides.items():
+        setattr(hp, k, v)
+    names = w.names
+    ae = [i for i, n in enumerate(names) if n.startswith("action_expert.layers.0.")]
+    vlm = [i for i, n in enumerate(names) if n.startswith("vlm.model.layers.0.")]
+    n_ae_layers = len({n.split(".")[2] for n in names if n.startswith("action_expert.layers.")})
+    n_vlm_layers = len({n.split(".")[3] for n in names if n.startswith("vlm.model.layers.")})
+    train = [i for i, p in enumerate(w.params) if p.trainable]
+    total_params = sum(w.params[i].numel for i in train)
+
+    def timed(idx):
+        params = {i: W.np_param(w, i) for i in idx}
+        grads = {i: W.np_grad(w, 1, i) for i in idx}
+        bufs = {i: W.np_momentum(w, i) for i in idx}
+        t0 = time.perf_counter()
+        norm = O.global_grad_norm([grads[i] for i in idx])
+        coef = O.clip_coefficient(norm, hp.max_grad_norm)
+        for i in idx:
+            shape = w.params[i].shape
+            if O.route_one(names[i], shape, True) == O.MUON:
+                s = O.lr_shape_scale(shape[0], shape[1], hp.moonlight_coefficient)
+                O.muon_matrix_update(params[i], grads[i], bufs[i], coef, hp, s)
+            else:
+                z = np.zeros(shape, np.float32)
+                O.adamw_update(params[i], grads[i], z, z, 1, coef, hp)
+        return time.perf_counter() - t0
+
+    t_ae = timed(ae)
+    t_vlm = timed(vlm)
+    est = t_ae * n_ae_layers + t_vlm * n_vlm_layers
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    sample_params = sum(w.params[i].numel for i in ae + vlm)
+    return {
+        "value": total_params / est,
+        "unit": "params/s",
+        "cores": min(cores, threads),
+        "kind": "oracle",
+        "sample": ("action_expert.layers.0 (7 Muon matrices, %.1f s) + vlm.model.layers.0 "
+                   "(9 AdamW tensors, %.1f s), %d params, scaled x%d / x%d layers to the "
+                   "whole table; NumPy fp64, BLAS threads for matmuls, elementwise "
+                   "single-threaded" % (t_ae, t_vlm, sample_params, n_ae_layers, n_vlm_layers)),
+        "sample_seconds": t_ae + t_vlm,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="vla_hybrid_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(every matrix is held whole on one device); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import muon_newton_schulz_02_amd as M
+
+    M.load_library()  # fails loudly if the HIP library is not built
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    w = W.WORKLOADS[args.workload]()
+    hp_over = W.hparams_for(w)
+    hp = M.muon_adamw_default_hparams(ns_precision=w.ns_precision, **hp_over)
+    table = list(zip(w.names, w.shapes, w.trainable))
+    plan = M.muon_adamw_plan(table)
+    n = len(table)
+    groups = [M.muon_adamw_plan_entry(plan, i)["group"] for i in range(n)]
+    params, grads = [None] * n, [None] * n
+    state = M.State(n)
+    print("[bench] allocating %s" % w.name, file=sys.stderr, flush=True)
+    for i, spec in enumerate(w.params):
+        if groups[i] == M.MA_GROUP_NONE:
+            continue
+        params[i] = W.torch_param(w, i, dev)
+        grads[i] = W.torch_grad(w, 1, i, dev)
+        if groups[i] == M.MA_GROUP_MUON:
+            state.muon_momentum[i] = W.torch_momentum(w, i, dev)
+        else:
+            state.adam_m[i] = torch.zeros(spec.shape, dtype=torch.float32, device=dev)
+            state.adam_v[i] = torch.zeros(spec.shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(M.muon_adamw_workspace_size(plan, hp.ns_precision), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+
+    muon_shapes = [w.params[i].shape for i in range(n) if groups[i] == M.MA_GROUP_MUON]
+    n_muon = sum(w.params[i].numel for i in range(n) if groups[i] == M.MA_GROUP_MUON)
+    n_adam = sum(w.params[i].numel for i in range(n) if groups[i] == M.MA_GROUP_ADAMW)
+    n_train = n_muon + n_adam
+
+    stream = torch.cuda.current_stream()
+    K = 5  # MA_PROFILE_EVENTS
+    evs = HipEvents(K * max(args.steps, 1))
+    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        M.muon_adamw_step(plan, params, grads, state, hp, ws, stream=stream)
+    torch.cuda.synchronize()
+    print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        M.muon_adamw_step_profiled(plan, params, grads, state, hp, ws,
+                                   evs.ev[K * s:K * s + K], stream=stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    phases = {"clip_norm": [], "adamw": [], "muon_prep": [], "newton_schulz": [], "step": []}
+    for s in range(args.steps):
+        b = K * s
+        phases["clip_norm"].append(evs.elapsed(b, b + 1))
+        phases["adamw"].append(evs.elapsed(b + 1, b + 2))
+        phases["muon_prep"].append(evs.elapsed(b + 2, b + 3))
+        phases["newton_schulz"].append(evs.elapsed(b + 3, b + 4))
+        phases["step"].append(evs.elapsed(b, b + 4))
+    evs.close()
+    mean = {k: sum(v) / len(v) for k, v in phases.items()}
+    ms_per_step = wall * 1e3 / args.steps
+    flops = ns_flops(muon_shapes, hp.muon_ns_steps)
+    ns_peak = PEAK_BF16_TFLOPS if w.ns_precision == "bf16" else PEAK_FP32_TFLOPS
+    ns_tflops = flops / (mean["newton_schulz"] * 1e-3) / 1e12 if mean["newton_schulz"] > 0 else 0.0
+    adam_bytes = 28.0 * n_adam           # read p, g, m, v; write p, m, v (fp32)
+    norm_bytes = 4.0 * n_train           # read every gradient once
+    adam_gbps = adam_bytes / (mean["adamw"] * 1e-3) / 1e9 if mean["adamw"] > 0 else 0.0
+    norm_gbps = norm_bytes / (mean["clip_norm"] * 1e-3) / 1e9 if mean["clip_norm"] > 0 else 0.0
+    if n_adam > 0 and mean["adamw"] >= mean["newton_schulz"]:
+        roofline = {"kernel": "k_adamw", "bound": "hbm", "achieved": adam_gbps,
+                    "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": adam_gbps / PEAK_HBM_GBPS,
+                    "traffic": None}
+    else:
+        roofline = {"kernel": "k_ns_gemm (5 steps x 3 launches)", "bound": "mfma",
+                    "achieved": ns_tflops, "peak": ns_peak, "unit": "TFLOP/s",
+                    "frac": ns_tflops / ns_peak, "traffic": None}
+    out = {
+        "metric": METRIC,
+        "value": n_train / (ms_per_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+fp32" if w.ns_precision == "bf16" else "fp32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "muon_params": n_muon, "adamw_params": n_adam,
+                   "muon_matrices": len(muon_shapes), "ns_precision": w.ns_precision,
+                   "ns_steps": hp.muon_ns_steps, "parallelism": "single GPU"},
+        "phase_ms": mean,
+        "ns_tflops": ns_tflops,
+        "ns_mfma_frac": ns_tflops / ns_peak,
+        "adamw_gbps": adam_gbps,
+        "adamw_hbm_frac": adam_gbps / PEAK_HBM_GBPS,
+        "clip_norm_gbps": norm_gbps,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, hp_over) if w.name.startswith("vla_hybrid") else None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,240 @@
+/*
+ * muon_adamw.h -- C ABI of the MI355X (gfx950) hybrid MuonAdamW optimizer step.
+ *
+ * The method is the one described on the OpenDM training-stack page
+ * ("VLA训练栈深度揭秘：OpenDM的MuonAdamW优化器、FSDP分布式训练与混合精度策略"):
+ *   - its Muon/AdamW hybrid section, table on how parameters are split
+ *     (routing, reproduced by muon_adamw_plan);
+ *   - the Newton-Schulz paragraph of that section (a fixed number of quintic
+ *     Newton-Schulz steps stand in for the zeroth power of each whole matrix);
+ *   - the hyperparameter table of the optimizer config and the sentence after
+ *     it (momentum 0.95, Nesterov, 5 steps, moonlight coefficient 0.2, base
+ *     lr 2.5e-5, Muon lr = lr * muon_lr_scale * 0.2 * sqrt(max(shape)));
+ *   - the MuonShardPlan paragraph (the plan records full shapes before any
+ *     wrapping; NS acts on whole matrices -- on one GPU every matrix is whole);
+ *   - the defaults quick-reference table (max_grad_norm 1.0).
+ *
+ * Conventions shared by every entry point:
+ *   - Return 0 (MA_OK) on success, a negative MA_ERR_* code otherwise; the
+ *     thread-local muon_adamw_last_error() then holds a message.
+ *   - Arguments are validated before anything is launched: an error return
+ *     means no kernel ran and no buffer changed.
+ *   - No C++ exception crosses this boundary.
+ *   - Parameters, gradients and optimizer states are float32, contiguous,
+ *     row-major, in device memory owned by the caller.  The library never
+ *     allocates device memory; its scratch lives in a caller-provided
+ *     workspace.
+ *   - Device work is asynchronous on the caller's HIP stream; device faults
+ *     surface at the caller's next synchronisation (HIP semantics).
+ */
+#ifndef MUON_ADAMW_H_
+#define MUON_ADAMW_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define MA_OK                 0
+#define MA_ERR_INVALID_ARG   (-1)  /* null pointer, bad count, bad value   */
+#define MA_ERR_SHAPE         (-2)  /* non-positive or overflowing shape    */
+#define MA_ERR_UNSUPPORTED   (-3)  /* ndim > 8, ns_steps < 1, bad mode ... */
+#define MA_ERR_WORKSPACE     (-4)  /* workspace null, small or misaligned  */
+#define MA_ERR_HIP           (-5)  /* a HIP runtime call failed            */
+
+/* ---- groups, modes, precisions ------------------------------------------ */
+#define MA_GROUP_MUON   0
+#define MA_GROUP_ADAMW  1
+#define MA_GROUP_NONE   2      /* frozen: no update, not in the clip norm */
+
+#define MA_MODE_MUON_ADAMW 0   /* the hybrid (optim = muon_adamw)          */
+#define MA_MODE_ADAMW      1   /* every trainable tensor to AdamW          */
+
+#define MA_NS_BF16 0           /* bf16 MFMA operands, fp32 accumulation    */
+#define MA_NS_FP32 1           /* fp32 MFMA throughout                     */
+
+#define MA_MAX_NDIM 8
+
+/* One model parameter, in the caller's order.  `name` is the dotted module
+ * path (UTF-8, NUL-terminated), `shape` holds `ndim` positive sizes,
+ * `trainable` is 0 for frozen parameters.  Borrowed for the duration of the
+ * muon_adamw_plan call only. */
+typedef struct {
+    const char*    name;
+    int32_t        ndim;
+    const int64_t* shape;
+    int32_t        trainable;
+} ma_param_desc;
+
+typedef struct {
+    int32_t mode;                  /* MA_MODE_*                            */
+    double  moonlight_coefficient; /* 0.2 on the page                      */
+} ma_plan_opts;
+
+typedef struct ma_plan ma_plan;    /* opaque, immutable once built         */
+
+/* What the plan decided for one entry.  For a Muon matrix stored m x n,
+ * (r, c) = (min, max) is its canonical orientation (Gram matrix r x r),
+ * `transposed` is 1 when m > n, `bucket` numbers the distinct (r, c) in order
+ * of first appearance, `lr_shape_scale` is the float32 rounding of
+ * moonlight_coefficient * sqrt(max(m, n)) computed in double.  For an AdamW
+ * tensor, `adam_offset` is its start in the concatenation of all AdamW
+ * tensors in table order.  Unused fields are 0 (-1 for bucket, adam_offset). */
+typedef struct {
+    int32_t group;
+    int32_t bucket;
+    int64_t m, n, r, c;
+    int32_t transposed;
+    float   lr_shape_scale;
+    int64_t numel;
+    int64_t adam_offset;
+} ma_plan_entry;
+
+/* Caller-owned optimizer state, arrays indexed like the plan's entries.
+ * muon_momentum[i] (m x n) for Muon entries, adam_m[i] / adam_v[i] (numel)
+ * for AdamW entries; other slots are ignored and may be NULL.  `step` counts
+ * completed steps; muon_adamw_step uses step+1 for the bias correction and
+ * increments it on success.  All tensors start at zero for a fresh run. */
+typedef struct {
+    float* const* muon_momentum;
+    float* const* adam_m;
+    float* const* adam_v;
+    int64_t       step;
+} ma_state;
+
+/* Hyperparameters of one step.  muon_adamw_default_hparams fills the page's
+ * defaults (lr 2.5e-5, muon_lr_scale 1, momentum 0.95, Nesterov on, 5 NS
+ * steps, clip 1.0) and the readings where the page is silent: NS coefficients
+ * (3.2608, -3.6447, 1.3650), NS epsilon 1e-7, AdamW betas (0.9, 0.999), eps
+ * 1e-8, decay 0.01, Muon decay 0, bf16 NS.  max_grad_norm <= 0 turns the
+ * global clip off.  ns_coeffs (a, b, c) define X <- a X + (b A + c A^2) X.
+ * Scalars are double on the host: derived constants (1 - beta, bias
+ * corrections, lr * shape factor) are formed in double and rounded once to
+ * the float32 the kernels compute in. */
+typedef struct {
+    double  lr;
+    double  muon_lr_scale;
+    double  muon_momentum;
+    int32_t muon_nesterov;
+    int32_t muon_ns_steps;
+    double  ns_coeffs[3];
+    int32_t ns_precision;      /* MA_NS_BF16 or MA_NS_FP32 */
+    double  ns_eps;
+    double  beta1;
+    double  beta2;
+    double  eps;
+    double  weight_decay;
+    double  muon_weight_decay;
+    double  max_grad_norm;
+} ma_hparams;
+
+/* Fill *hp with the defaults listed above.  Errors: INVALID_ARG if hp is
+ * NULL. */
+int muon_adamw_default_hparams(ma_hparams* hp);
+
+/* Build the routing/shape plan of a parameter table (the page's routing
+ * rule: a trainable matrix whose name has a component containing
+ * 'action_expert', then a component 'layers', ends in '.weight' and contains
+ * none of 'embed', 'lm_head', 'norm' (case-insensitive) is Muon; any other
+ * trainable tensor is AdamW; frozen tensors are NONE).  Host only: touches no
+ * GPU.  On success *out owns a plan to be released with muon_adamw_plan_free.
+ * Errors: INVALID_ARG (null table/out/name, n < 1, bad mode, coefficient not
+ * finite and positive), UNSUPPORTED (ndim < 0 or > 8), SHAPE (a size < 1 or
+ * an element count above 2^62). */
+int muon_adamw_plan(const ma_param_desc* table, int32_t n,
+                    const ma_plan_opts* opts, ma_plan** out);
+
+/* Number of entries (equal to the table length).  Errors: INVALID_ARG. */
+int muon_adamw_plan_size(const ma_plan* plan, int32_t* n_entries);
+
+/* Decision for entry i.  Errors: INVALID_ARG (null, i out of range). */
+int muon_adamw_plan_entry(const ma_plan* plan, int32_t i, ma_plan_entry* e);
+
+/* Canonical text of the plan (header, one line per bucket, one line per
+ * entry; format documented with the oracle that produces the same bytes).
+ * Writes at most cap bytes (NUL-terminated when it fits) and sets *len to the
+ * full length without the NUL; call with buf = NULL, cap = 0 to size it.
+ * Errors: INVALID_ARG (null plan or len), WORKSPACE if cap is too small
+ * (buf untouched, *len set). */
+int muon_adamw_plan_dump(const ma_plan* plan, char* buf, size_t cap, size_t* len);
+
+/* Bytes of device workspace one muon_adamw_step call needs for this plan
+ * and NS precision.  The caller allocates it (256-byte aligned) and may
+ * reuse it across steps; contents between calls are scratch.
+ * Errors: INVALID_ARG (null, bad precision). */
+int muon_adamw_workspace_size(const ma_plan* plan, int32_t ns_precision, size_t* bytes);
+
+/* One optimizer step on `stream` (a hipStream_t; NULL = the null stream).
+ *
+ *   1. N = sqrt(sum of g^2 over every trainable gradient);
+ *      coef = max_grad_norm > 0 ? min(1, max_grad_norm / (N + 1e-6)) : 1
+ *      (gradients are read-only: coef is applied on the fly).
+ *   2. AdamW entries: g' = coef g; p *= 1 - lr wd; m = b1 m + (1-b1) g';
+ *      v = b2 v + (1-b2) g'^2; p -= lr/(1-b1^t) * m / (sqrt(v)/sqrt(1-b2^t) + eps).
+ *   3. Muon entries (m x n): buf = mu buf + coef g; u = coef g + mu buf
+ *      (Nesterov; u = buf otherwise); X = u (transposed if m > n) / (||u||_F
+ *      + ns_eps); ns_steps times { A = X X^T; B = b A + c A A; X = a X + B X };
+ *      delta = lr * muon_lr_scale * lr_shape_scale * X (back in m x n);
+ *      p = p (1 - lr muon_wd) - delta.
+ *
+ * params[i], grads[i]: entry i's tensors (NULL allowed for NONE entries).
+ * grad_norm_out: optional device float receiving N.
+ * muon_update_out: optional array (indexed like entries) of device m x n
+ *   float buffers receiving delta for Muon entries; the array itself or any
+ *   slot may be NULL.
+ * workspace / ws_bytes: device scratch of at least muon_adamw_workspace_size
+ *   bytes for hp->ns_precision, 256-byte aligned.
+ * Errors (nothing launched): INVALID_ARG (null plan/state/hp, a required
+ * pointer NULL, hp values out of range), UNSUPPORTED (ns_steps < 1 or > 64,
+ * unknown precision), WORKSPACE (null, too small, misaligned), HIP (a launch
+ * or copy failed; state->step is then not advanced). */
+int muon_adamw_step(const ma_plan* plan,
+                    float* const* params,
+                    const float* const* grads,
+                    ma_state* state,
+                    const ma_hparams* hp,
+                    void* workspace, size_t ws_bytes,
+                    void* stream,
+                    float* grad_norm_out,
+                    float* const* muon_update_out);
+
+/* Number of events muon_adamw_step_profiled records. */
+#define MA_PROFILE_EVENTS 5
+
+/* muon_adamw_step, plus measurement: phase_events (nullable) is an array of
+ * MA_PROFILE_EVENTS hipEvent_t created by the caller, recorded on `stream`
+ * at [0] the start of the step, [1] after the clip norm, [2] after the AdamW
+ * group, [3] after the Muon momentum/normalise pass, [4] after the last
+ * Newton-Schulz launch.  Elapsed times between them time each phase on the
+ * stream the kernels run on.  Same errors as muon_adamw_step. */
+int muon_adamw_step_profiled(const ma_plan* plan,
+                             float* const* params,
+                             const float* const* grads,
+                             ma_state* state,
+                             const ma_hparams* hp,
+                             void* workspace, size_t ws_bytes,
+                             void* stream,
+                             float* grad_norm_out,
+                             float* const* muon_update_out,
+                             void* const* phase_events);
+
+/* Release a plan (NULL is a no-op).  Must not race with a step using it;
+ * device work already queued does not reference plan memory after the step
+ * returns... except the library's pinned staging buffers, which are freed
+ * only after their last copy completed. */
+void muon_adamw_plan_free(ma_plan* plan);
+
+/* Message of the last error on this thread ("" if none). */
+const char* muon_adamw_last_error(void);
+
+/* Library version string. */
+const char* muon_adamw_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_ADAMW_H_ */

@@ -1,0 +1,104 @@
+"""ctypes mirror of include/muon_adamw.h.
+
+Argument marshalling only: every step of the optimizer runs in the HIP
+library.  Loading fails loudly when the library has not been built; there is
+no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmuon_adamw.so")
+
+MA_OK = 0
+MA_ERR_INVALID_ARG = -1
+MA_ERR_SHAPE = -2
+MA_ERR_UNSUPPORTED = -3
+MA_ERR_WORKSPACE = -4
+MA_ERR_HIP = -5
+
+MA_GROUP_MUON, MA_GROUP_ADAMW, MA_GROUP_NONE = 0, 1, 2
+MA_MODE_MUON_ADAMW, MA_MODE_ADAMW = 0, 1
+MA_NS_BF16, MA_NS_FP32 = 0, 1
+MA_MAX_NDIM = 8
+MA_PROFILE_EVENTS = 5
+
+
+class ma_param_desc(C.Structure):
+    _fields_ = [("name", C.c_char_p), ("ndim", C.c_int32),
+                ("shape", C.POINTER(C.c_int64)), ("trainable", C.c_int32)]
+
+
+class ma_plan_opts(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("moonlight_coefficient", C.c_double)]
+
+
+class ma_plan_entry(C.Structure):
+    _fields_ = [("group", C.c_int32), ("bucket", C.c_int32),
+                ("m", C.c_int64), ("n", C.c_int64), ("r", C.c_int64), ("c", C.c_int64),
+                ("transposed", C.c_int32), ("lr_shape_scale", C.c_float),
+                ("numel", C.c_int64), ("adam_offset", C.c_int64)]
+
+
+class ma_state(C.Structure):
+    _fields_ = [("muon_momentum", C.POINTER(C.c_void_p)),
+                ("adam_m", C.POINTER(C.c_void_p)),
+                ("adam_v", C.POINTER(C.c_void_p)),
+                ("step", C.c_int64)]
+
+
+class ma_hparams(C.Structure):
+    _fields_ = [("lr", C.c_double), ("muon_lr_scale", C.c_double), ("muon_momentum", C.c_double),
+                ("muon_nesterov", C.c_int32), ("muon_ns_steps", C.c_int32),
+                ("ns_coeffs", C.c_double * 3), ("ns_precision", C.c_int32),
+                ("ns_eps", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
+                ("eps", C.c_double), ("weight_decay", C.c_double),
+                ("muon_weight_decay", C.c_double), ("max_grad_norm", C.c_double)]
+
+
+# (name, restype, argtypes) of every exported symbol of the header
+SIGNATURES = [
+    ("muon_adamw_default_hparams", C.c_int, [C.POINTER(ma_hparams)]),
+    ("muon_adamw_plan", C.c_int, [C.POINTER(ma_param_desc), C.c_int32,
+                                  C.POINTER(ma_plan_opts), C.POINTER(C.c_void_p)]),
+    ("muon_adamw_plan_size", C.c_int, [C.c_void_p, C.POINTER(C.c_int32)]),
+    ("muon_adamw_plan_entry", C.c_int, [C.c_void_p, C.c_int32, C.POINTER(ma_plan_entry)]),
+    ("muon_adamw_plan_dump", C.c_int, [C.c_void_p, C.c_char_p, C.c_size_t,
+                                       C.POINTER(C.c_size_t)]),
+    ("muon_adamw_workspace_size", C.c_int, [C.c_void_p, C.c_int32, C.POINTER(C.c_size_t)]),
+    ("muon_adamw_step", C.c_int, [C.c_void_p, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p),
+                                  C.POINTER(ma_state), C.POINTER(ma_hparams),
+                                  C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p,
+                                  C.POINTER(C.c_void_p)]),
+    ("muon_adamw_step_profiled", C.c_int, [C.c_void_p, C.POINTER(C.c_void_p),
+                                           C.POINTER(C.c_void_p), C.POINTER(ma_state),
+                                           C.POINTER(ma_hparams), C.c_void_p, C.c_size_t,
+                                           C.c_void_p, C.c_void_p, C.POINTER(C.c_void_p),
+                                           C.POINTER(C.c_void_p)]),
+    ("muon_adamw_plan_free", None, [C.c_void_p]),
+    ("muon_adamw_last_error", C.c_char_p, []),
+    ("muon_adamw_version", C.c_char_p, []),
+]
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (once).  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "libmuon_adamw.so is not built (%s); run "
+            "`python -m muon_newton_schulz_02_amd.build` first" % path)
+    lib = C.CDLL(path)
+    for name, res, args in SIGNATURES:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib

@@ -1,0 +1,404 @@
+// HBM-bound kernels of the MuonAdamW step on gfx950:
+//   * clip norm: multi-tensor sum of squares, one deterministic partial per
+//     16 Ki-element chunk (wave shuffles + LDS tree), then one finalising
+//     workgroup in double precision -> clip factor in device memory;
+//   * AdamW: multi-tensor fused clip-scale + decoupled-decay Adam with
+//     128-bit loads and stores;
+//   * Muon momentum: clip-scale, momentum/Nesterov, buffer write-back and a
+//     per-chunk partial of ||u||_F^2; per-matrix finalisation in double;
+//   * normalise/orient: scale u to unit Frobenius norm and write the NS
+//     operands in canonical orientation (rows <= cols) and transposed,
+//     through an LDS tile, zero-filling the padding.
+//
+// Method: OpenDM training-stack page, Muon/AdamW hybrid section (routing,
+// hyperparameter table: momentum 0.95 with Nesterov) and the defaults table
+// (global clip to max_grad_norm 1.0).  The clip guard 1e-6 and the AdamW
+// algorithm follow the usual clip_grad_norm_ / torch.optim.AdamW
+// definitions, since the page names an HF-Trainer-based trainer.
+
+#include <hip/hip_runtime.h>
+
+#include "ma_internal.h"
+
+namespace ma {
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Block-wide sum in a fixed order (same result on every run).
+__device__ __forceinline__ float block_sum(float v, float* smem) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) smem[wave] = v;
+    __syncthreads();
+    float t = 0.f;
+    if (threadIdx.x == 0) {
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += smem[w];
+    }
+    return t;  // valid in thread 0 only
+}
+
+// Index of the table entry whose chunk range holds `chunk` (binary search
+// over ascending chunk_begin).
+template <typename Tab>
+__device__ __forceinline__ int find_tensor(const Tab* tab, int n, int64_t chunk) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tab[mid].chunk_begin <= chunk) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// ------------------------------------------------------------ clip norm --
+__global__ __launch_bounds__(kThreads) void k_norm_partials(const NormTensor* __restrict__ tab,
+                                                            int n_tab,
+                                                            float* __restrict__ partials) {
+    __shared__ float smem[kThreads / 64];
+    const int64_t chunk = blockIdx.x;
+    const int t = find_tensor(tab, n_tab, chunk);
+    const NormTensor d = tab[t];
+    const int64_t begin = (chunk - d.chunk_begin) * kChunk;
+    const int64_t len = min<int64_t>(kChunk, d.numel - begin);
+    const float* g = reinterpret_cast<const float*>(d.g) + begin;
+    float acc = 0.f;
+    if (d.vec_ok && len == kChunk) {
+        const f4* g4 = reinterpret_cast<const f4*>(g);
+#pragma unroll 4
+        for (int i = threadIdx.x; i < kChunk / 4; i += kThreads) {
+            const f4 v = __builtin_nontemporal_load(g4 + i);
+            acc = fmaf(v.x, v.x, acc);
+            acc = fmaf(v.y, v.y, acc);
+            acc = fmaf(v.z, v.z, acc);
+            acc = fmaf(v.w, v.w, acc);
+        }
+    } else {
+        for (int64_t i = threadIdx.x; i < len; i += kThreads) {
+            const float v = g[i];
+            acc = fmaf(v, v, acc);
+        }
+    }
+    const float s = block_sum(acc, smem);
+    if (threadIdx.x == 0) partials[chunk] = s;
+}
+
+__global__ __launch_bounds__(1024) void k_clip_finalize(const float* __restrict__ partials,
+                                                        int64_t n, float max_norm,
+                                                        float* __restrict__ coef_out,
+                                                        float* __restrict__ norm_out,
+                                                        float* __restrict__ user_norm_out) {
+    __shared__ double smem[1024 / 64];
+    double acc = 0.0;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) acc += (double)partials[i];
+    acc = wave_sum_d(acc);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) smem[wave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double tot = 0.0;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += smem[w];
+        const double norm = sqrt(tot);
+        double coef = 1.0;
+        if (max_norm > 0.f) {
+            coef = (double)max_norm / (norm + 1e-6);
+            if (!(coef < 1.0)) coef = (coef == coef) ? 1.0 : coef;  // NaN propagates
+        }
+        coef_out[0] = (float)coef;
+        norm_out[0] = (float)norm;
+        if (user_norm_out) user_norm_out[0] = (float)norm;
+    }
+}
+
+// ---------------------------------------------------------------- AdamW --
+struct AdamArgs {
+    float step_size, inv_sqrt_bc2, decay, beta1, beta2, one_m_beta1, one_m_beta2, eps;
+};
+
+__device__ __forceinline__ void adam_elem(float& p, float g, float& m, float& v, float coef,
+                                          const AdamArgs& a) {
+    g *= coef;
+    p *= a.decay;
+    m = fmaf(a.beta1, m, a.one_m_beta1 * g);
+    v = fmaf(a.beta2, v, a.one_m_beta2 * g * g);
+    const float denom = fmaf(sqrtf(v), a.inv_sqrt_bc2, a.eps);
+    p = fmaf(-a.step_size, m / denom, p);
+}
+
+__global__ __launch_bounds__(kThreads) void k_adamw(const AdamTensor* __restrict__ tab, int n_tab,
+                                                    const float* __restrict__ coef_ptr,
+                                                    AdamArgs a) {
+    const int64_t chunk = blockIdx.x;
+    const int t = find_tensor(tab, n_tab, chunk);
+    const AdamTensor d = tab[t];
+    const int64_t begin = (chunk - d.chunk_begin) * kChunk;
+    const int64_t len = min<int64_t>(kChunk, d.numel - begin);
+    float* p = reinterpret_cast<float*>(d.p) + begin;
+    const float* g = reinterpret_cast<const float*>(d.g) + begin;
+    float* m = reinterpret_cast<float*>(d.m) + begin;
+    float* v = reinterpret_cast<float*>(d.v) + begin;
+    const float coef = *coef_ptr;
+    if (d.vec_ok && len == kChunk) {
+        f4* p4 = reinterpret_cast<f4*>(p);
+        const f4* g4 = reinterpret_cast<const f4*>(g);
+        f4* m4 = reinterpret_cast<f4*>(m);
+        f4* v4 = reinterpret_cast<f4*>(v);
+#pragma unroll 2
+        for (int i = threadIdx.x; i < kChunk / 4; i += kThreads) {
+            f4 pp = __builtin_nontemporal_load(p4 + i);
+            const f4 gg = __builtin_nontemporal_load(g4 + i);
+            f4 mm = __builtin_nontemporal_load(m4 + i);
+            f4 vv = __builtin_nontemporal_load(v4 + i);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float pq = pp[q], mq = mm[q], vq = vv[q];
+                adam_elem(pq, gg[q], mq, vq, coef, a);
+                pp[q] = pq;
+                mm[q] = mq;
+                vv[q] = vq;
+            }
+            __builtin_nontemporal_store(pp, p4 + i);
+            __builtin_nontemporal_store(mm, m4 + i);
+            __builtin_nontemporal_store(vv, v4 + i);
+        }
+    } else {
+        for (int64_t i = threadIdx.x; i < len; i += kThreads) {
+            float pp = p[i], mm = m[i], vv = v[i];
+            adam_elem(pp, g[i], mm, vv, coef, a);
+            p[i] = pp;
+            m[i] = mm;
+            v[i] = vv;
+        }
+    }
+}
+
+// -------------------------------------------------------- Muon momentum --
+struct MomArgs {
+    float mu;
+    int nesterov;
+};
+
+__device__ __forceinline__ float momentum_elem(float g, float& buf, float coef, const MomArgs& a) {
+    const float gc = g * coef;
+    buf = fmaf(a.mu, buf, gc);
+    return a.nesterov ? fmaf(a.mu, buf, gc) : buf;
+}
+
+__global__ __launch_bounds__(kThreads) void k_muon_momentum(const MuonMat* __restrict__ tab,
+                                                            int n_tab,
+                                                            const float* __restrict__ coef_ptr,
+                                                            MomArgs a,
+                                                            float* __restrict__ partials) {
+    __shared__ float smem[kThreads / 64];
+    const int64_t chunk = blockIdx.x;
+    const int t = find_tensor(tab, n_tab, chunk);
+    const MuonMat& d = tab[t];
+    const int64_t begin = (chunk - d.chunk_begin) * kChunk;
+    const int64_t len = min<int64_t>(kChunk, d.numel - begin);
+    const float* g = reinterpret_cast<const float*>(d.g) + begin;
+    float* buf = reinterpret_cast<float*>(d.buf) + begin;
+    const float coef = *coef_ptr;
+    float acc = 0.f;
+    if (d.vec_ok && len == kChunk) {
+        const float4* g4 = reinterpret_cast<const float4*>(g);
+        float4* b4 = reinterpret_cast<float4*>(buf);
+#pragma unroll 2
+        for (int i = threadIdx.x; i < kChunk / 4; i += kThreads) {
+            const float4 gg = g4[i];
+            float4 bb = b4[i];
+            const float u0 = momentum_elem(gg.x, bb.x, coef, a);
+            const float u1 = momentum_elem(gg.y, bb.y, coef, a);
+            const float u2 = momentum_elem(gg.z, bb.z, coef, a);
+            const float u3 = momentum_elem(gg.w, bb.w, coef, a);
+            b4[i] = bb;
+            acc = fmaf(u0, u0, acc);
+            acc = fmaf(u1, u1, acc);
+            acc = fmaf(u2, u2, acc);
+            acc = fmaf(u3, u3, acc);
+        }
+    } else {
+        for (int64_t i = threadIdx.x; i < len; i += kThreads) {
+            float bb = buf[i];
+            const float u = momentum_elem(g[i], bb, coef, a);
+            buf[i] = bb;
+            acc = fmaf(u, u, acc);
+        }
+    }
+    const float s = block_sum(acc, smem);
+    if (threadIdx.x == 0) partials[chunk] = s;
+}
+
+// One workgroup per matrix: 1 / (||u||_F + eps) from its chunk partials.
+__global__ __launch_bounds__(256) void k_muon_scale(const MuonMat* __restrict__ tab,
+                                                    const float* __restrict__ partials,
+                                                    float ns_eps, float* __restrict__ scales) {
+    __shared__ double smem[256 / 64];
+    const MuonMat& d = tab[blockIdx.x];
+    double acc = 0.0;
+    for (int i = threadIdx.x; i < d.n_chunks; i += blockDim.x)
+        acc += (double)partials[d.chunk_begin + i];
+    acc = wave_sum_d(acc);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) smem[wave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double tot = 0.0;
+        for (int w = 0; w < 4; ++w) tot += smem[w];
+        scales[blockIdx.x] = (float)(1.0 / (sqrt(tot) + (double)ns_eps));
+    }
+}
+
+// ------------------------------------------------------ normalise/orient --
+// Tile (ti, tj) of the canonical padded R x C operand.  Canonical (i, j) is
+// stored (i, j), or stored (j, i) for a transposed matrix.  Values outside the
+// true r x c are zero.
+template <typename T>
+__device__ __forceinline__ T to_operand(float x);
+template <>
+__device__ __forceinline__ float to_operand<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ __bf16 to_operand<__bf16>(float x) { return (__bf16)x; }
+
+template <typename T>
+__device__ __forceinline__ void write_operands(const MuonMat& d, const float (*tile)[kOrientTile + 1],
+                                               int i0, int j0) {
+    constexpr int TS = kOrientTile;
+    float* x32 = reinterpret_cast<float*>(d.x32);
+    T* xb = reinterpret_cast<T*>(d.xb);
+    T* xt = reinterpret_cast<T*>(d.xt[0]);
+    const bool write_xb = d.xb != d.x32;
+    // canonical rows i0.., cols j0..
+    for (int idx = threadIdx.x; idx < TS * TS; idx += kThreads) {
+        const int a_ = idx / TS, b_ = idx % TS;
+        const float v = d.transposed ? tile[b_][a_] : tile[a_][b_];
+        const int64_t o = (int64_t)(i0 + a_) * d.C + (j0 + b_);
+        x32[o] = v;
+        if (write_xb) xb[o] = to_operand<T>(v);
+    }
+    // transposed operand: rows j0.., cols i0..
+    for (int idx = threadIdx.x; idx < TS * TS; idx += kThreads) {
+        const int a_ = idx / TS, b_ = idx % TS;  // a_ along canonical cols, b_ along rows
+        const float v = d.transposed ? tile[a_][b_] : tile[b_][a_];
+        xt[(int64_t)(j0 + a_) * d.R + (i0 + b_)] = to_operand<T>(v);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_orient(const MuonMat* __restrict__ tab, int n_tab,
+                                                     const float* __restrict__ coef_ptr,
+                                                     const float* __restrict__ scales, MomArgs a) {
+    constexpr int TS = kOrientTile;
+    __shared__ float tile[TS][TS + 1];
+    const int64_t blk = blockIdx.x;
+    // find the matrix by orient_begin
+    int lo = 0, hi = n_tab - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tab[mid].orient_begin <= blk) lo = mid;
+        else hi = mid - 1;
+    }
+    const MuonMat& d = tab[lo];
+    const int64_t local = blk - d.orient_begin;
+    const int tiles_c = d.C / TS;
+    const int ti = (int)(local / tiles_c), tj = (int)(local % tiles_c);
+    const int i0 = ti * TS, j0 = tj * TS;
+    const float coef = *coef_ptr;
+    const float s = scales[lo];
+    const float* g = reinterpret_cast<const float*>(d.g);
+    const float* buf = reinterpret_cast<const float*>(d.buf);
+    // stored tile origin: rows sr0.., cols sc0..
+    const int sr0 = d.transposed ? j0 : i0;
+    const int sc0 = d.transposed ? i0 : j0;
+    for (int idx = threadIdx.x; idx < TS * TS; idx += kThreads) {
+        const int lr = idx / TS, lc = idx % TS;
+        const int sr = sr0 + lr, sc = sc0 + lc;
+        float u = 0.f;
+        if (sr < d.m && sc < d.n) {
+            const int64_t o = (int64_t)sr * d.n + sc;
+            // recompute u from the updated buffer: identical fp32 operations
+            // to the momentum pass
+            const float gc = g[o] * coef;
+            const float bb = buf[o];
+            u = a.nesterov ? fmaf(a.mu, bb, gc) : bb;
+            u *= s;
+        }
+        tile[lr][lc] = u;
+    }
+    __syncthreads();
+    if (d.op_bf16) write_operands<__bf16>(d, tile, i0, j0);
+    else write_operands<float>(d, tile, i0, j0);
+}
+}  // namespace
+
+int launch_norm_partials(const NormTensor* tab, int32_t n_tab, int64_t n_chunks, float* partials,
+                         void* stream) {
+    if (n_chunks == 0) return (int)hipSuccess;
+    hipLaunchKernelGGL(k_norm_partials, dim3((unsigned)n_chunks), dim3(kThreads), 0,
+                       (hipStream_t)stream, tab, n_tab, partials);
+    return (int)hipGetLastError();
+}
+
+int launch_clip_finalize(const float* partials, int64_t n, float max_grad_norm, float* coef_out,
+                         float* norm_out, float* user_norm_out, void* stream) {
+    hipLaunchKernelGGL(k_clip_finalize, dim3(1), dim3(1024), 0, (hipStream_t)stream, partials, n,
+                       max_grad_norm, coef_out, norm_out, user_norm_out);
+    return (int)hipGetLastError();
+}
+
+int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, const float* coef,
+                 const StepScalars& s, void* stream) {
+    if (n_chunks == 0) return (int)hipSuccess;
+    AdamArgs a;
+    a.step_size = s.step_size;
+    a.inv_sqrt_bc2 = s.inv_sqrt_bc2;
+    a.decay = s.adam_decay;
+    a.beta1 = s.beta1;
+    a.beta2 = s.beta2;
+    a.one_m_beta1 = s.one_m_beta1;
+    a.one_m_beta2 = s.one_m_beta2;
+    a.eps = s.eps;
+    hipLaunchKernelGGL(k_adamw, dim3((unsigned)n_chunks), dim3(kThreads), 0, (hipStream_t)stream,
+                       tab, n_tab, coef, a);
+    return (int)hipGetLastError();
+}
+
+int launch_muon_momentum(const MuonMat* tab, int32_t n_tab, int64_t n_chunks, const float* coef,
+                         const StepScalars& s, float* partials, void* stream) {
+    if (n_chunks == 0) return (int)hipSuccess;
+    MomArgs a{s.mu, s.nesterov};
+    hipLaunchKernelGGL(k_muon_momentum, dim3((unsigned)n_chunks), dim3(kThreads), 0,
+                       (hipStream_t)stream, tab, n_tab, coef, a, partials);
+    return (int)hipGetLastError();
+}
+
+int launch_muon_scale(const MuonMat* tab, int32_t n_tab, const float* partials, float ns_eps,
+                      float* scales, void* stream) {
+    if (n_tab == 0) return (int)hipSuccess;
+    hipLaunchKernelGGL(k_muon_scale, dim3((unsigned)n_tab), dim3(256), 0, (hipStream_t)stream, tab,
+                       partials, ns_eps, scales);
+    return (int)hipGetLastError();
+}
+
+int launch_orient(const MuonMat* tab, int32_t n_tab, int64_t n_tiles, const float* coef,
+                  const float* scales, const StepScalars& s, void* stream) {
+    if (n_tiles == 0) return (int)hipSuccess;
+    MomArgs a{s.mu, s.nesterov};
+    hipLaunchKernelGGL(k_orient, dim3((unsigned)n_tiles), dim3(kThreads), 0, (hipStream_t)stream,
+                       tab, n_tab, coef, scales, a);
+    return (int)hipGetLastError();
+}
+
+}  // namespace ma

@@ -1,0 +1,183 @@
+// Internal declarations of the MuonAdamW library: the plan object, the
+// device-side descriptor tables uploaded at every step, the workspace layout
+// and the kernel launchers.  Not part of the C ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/muon_adamw.h"
+
+namespace ma {
+
+// Every Newton-Schulz operand is padded with zeros to a multiple of this in
+// both dimensions, so GEMM tiles (which divide it) never need bounds checks
+// and the zero padding contributes nothing to any product.
+constexpr int64_t kNsPad = 256;
+
+// Elements per chunk of the multi-tensor elementwise passes (clip norm,
+// AdamW, Muon momentum).  Each chunk is one workgroup's work and produces one
+// deterministic partial sum.
+constexpr int64_t kChunk = 16384;
+
+// Side of the square tiles of the normalise/orient pass.
+constexpr int kOrientTile = 64;
+
+// GEMM block tile (square) used for the work lists.  Must divide kNsPad.
+constexpr int kGemmTile = 128;
+
+// Under the bf16 policy, matrices whose smaller side is below this run their
+// Newton-Schulz in fp32: for such thin matrices the bf16 rounding error is
+// inherent and reaches the 2e-2 tolerance (rank-1 inputs give 2-3 %), while
+// their share of the work is negligible.
+constexpr int64_t kBf16MinRows = 16;
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
+
+// ---------------------------------------------------------------- tables --
+// One trainable tensor in the global-norm pass.
+struct NormTensor {
+    uint64_t g;            // const float*
+    int64_t  numel;
+    int64_t  chunk_begin;  // first chunk index of this tensor
+    int32_t  vec_ok;       // 16-byte aligned base: float4 path allowed
+    int32_t  pad_;
+};
+
+// One AdamW tensor.
+struct AdamTensor {
+    uint64_t p, g, m, v;   // float*
+    int64_t  numel;
+    int64_t  chunk_begin;
+    int32_t  vec_ok;
+    int32_t  pad_;
+};
+
+// One Muon matrix: the elementwise view (momentum pass) and the NS view.
+struct MuonMat {
+    uint64_t p, g, buf, delta;     // float* (delta may be 0)
+    uint64_t x32;                  // R x C float, master copy of X
+    uint64_t xb;                   // R x C, NS operand type (bf16 mode only)
+    uint64_t xt[2];                // C x R, NS operand type, ping-pong
+    uint64_t a, b;                 // R x R, NS operand type
+    int64_t  numel;                // m * n
+    int64_t  chunk_begin;          // momentum-pass chunks (one partial each)
+    int64_t  orient_begin;         // first orient tile
+    int32_t  n_chunks;
+    int32_t  m, n, r, c, R, C;
+    int32_t  transposed;
+    int32_t  vec_ok;               // p, g, buf (and delta) 16-byte aligned and n % 4 == 0
+    float    lr_eff;               // lr * muon_lr_scale * lr_shape_scale
+    float    decay;                // 1 - lr * muon_weight_decay
+    int32_t  op_bf16;              // NS operands are bf16 (else fp32)
+};
+
+// One GEMM tile of an NS phase: matrix index and tile coordinates.
+struct GemmTile {
+    int32_t mat, tm, tn, k;        // k = reduction length (padded), for ordering
+};
+
+// ------------------------------------------------------------ workspace --
+// Operand precision groups of the NS launches.
+enum { kGroupBf16 = 0, kGroupFp32 = 1 };
+
+struct Layout {
+    size_t tables_off = 0, tables_bytes = 0;
+    size_t norm_tab_off = 0, adam_tab_off = 0, muon_tab_off = 0;
+    std::vector<int32_t> op_group;                   // per Muon matrix: kGroupBf16 / kGroupFp32
+    std::vector<GemmTile> g1[2], g2[2], g3[2];       // cost-ordered tile lists per group
+    size_t g1_off[2] = {0, 0}, g2_off[2] = {0, 0}, g3_off[2] = {0, 0};
+    size_t scalars_off = 0;                          // coef (float), norm (float)
+    size_t norm_partials_off = 0;                    // float[n_norm_chunks]
+    size_t muon_partials_off = 0;                    // float[n_muon_chunks]
+    size_t muon_scale_off = 0;                       // float[n_muon]
+    size_t ns_off = 0;                               // start of per-matrix NS buffers
+    std::vector<size_t> x32, xb, xt0, xt1, a, b;     // per Muon matrix, offsets
+    size_t total = 0;
+};
+
+struct Entry {
+    int32_t group = MA_GROUP_NONE;
+    int32_t bucket = -1;
+    int64_t m = 0, n = 0, r = 0, c = 0;
+    int32_t transposed = 0;
+    float   lr_shape_scale = 0.f;
+    int64_t numel = 0;
+    int64_t adam_offset = -1;
+};
+
+struct Bucket {
+    int64_t r, c;
+    std::vector<int32_t> members;
+};
+
+}  // namespace ma
+
+struct ma_plan {
+    int32_t mode = MA_MODE_MUON_ADAMW;
+    double  moonlight = 0.2;
+    std::vector<ma::Entry> entries;
+    std::vector<ma::Bucket> buckets;
+    std::vector<int32_t> muon_ids, adam_ids, train_ids;   // entry indices
+    int64_t adam_numel = 0;
+    int64_t n_norm_chunks = 0, n_adam_chunks = 0, n_muon_chunks = 0, n_orient_tiles = 0;
+    std::vector<int64_t> norm_chunk_begin, adam_chunk_begin;     // per train / adam id
+    std::vector<int64_t> muon_chunk_begin, muon_orient_begin;    // per muon id
+    ma::Layout layout[2];                                        // per NS precision
+    std::string dump;
+
+    // step-time staging (pinned host ring); guarded by mu
+    mutable std::mutex mu;
+    mutable void* staging[2] = {nullptr, nullptr};
+    mutable size_t staging_bytes[2] = {0, 0};
+    mutable void* staging_event[2] = {nullptr, nullptr};
+    mutable int staging_next = 0;
+};
+
+namespace ma {
+
+void set_error(const char* fmt, ...);
+void clear_error();
+
+// Build the layout of one precision (called by the plan builder).
+void build_layout(ma_plan* plan, int32_t precision);
+
+// --------------------------------------------------------- launchers -----
+// Per-step constants, formed in double on the host from the double
+// hyperparameters and rounded once to the float32 the kernels use.
+struct StepScalars {
+    float lr, beta1, beta2, eps, weight_decay;
+    float one_m_beta1, one_m_beta2;
+    float step_size;        // lr / (1 - beta1^t)
+    float inv_sqrt_bc2;     // 1 / sqrt(1 - beta2^t)
+    float adam_decay;       // 1 - lr * weight_decay
+    float max_grad_norm;
+    float mu;
+    int32_t nesterov;
+    float ns_eps;
+    float ns_a, ns_b, ns_c;
+};
+
+// Each returns a hipError_t as int.
+int launch_norm_partials(const NormTensor* tab, int32_t n_tab, int64_t n_chunks,
+                         float* partials, void* stream);
+int launch_clip_finalize(const float* partials, int64_t n, float max_grad_norm,
+                         float* coef_out, float* norm_out, float* user_norm_out, void* stream);
+int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
+                 const float* coef, const StepScalars& s, void* stream);
+int launch_muon_momentum(const MuonMat* tab, int32_t n_tab, int64_t n_chunks,
+                         const float* coef, const StepScalars& s, float* partials, void* stream);
+int launch_muon_scale(const MuonMat* tab, int32_t n_tab, const float* partials,
+                      float ns_eps, float* scales, void* stream);
+int launch_orient(const MuonMat* tab, int32_t n_tab, int64_t n_tiles, const float* coef,
+                  const float* scales, const StepScalars& s, void* stream);
+// phase 1 = Gram, 2 = polynomial, 3 = X update (the parameter update when
+// `last`); group = kGroupBf16 / kGroupFp32 selects the operand type.
+int launch_ns_phase(int phase, int32_t group, const MuonMat* tab, const GemmTile* tiles,
+                    int64_t n_tiles, int iter, int last, const StepScalars& s, void* stream);
+
+}  // namespace ma

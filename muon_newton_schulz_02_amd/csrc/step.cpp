@@ -1,0 +1,333 @@
+// muon_adamw_step: argument validation, descriptor tables and the launch
+// sequence of one hybrid step on the caller's stream.
+//
+// Order of work (OpenDM training-stack page: clip from the defaults table,
+// then the two optimizer groups of the Muon/AdamW hybrid section):
+//   1. one async copy of this step's descriptor tables into the workspace
+//   2. clip norm partials over every trainable gradient, then the clip factor
+//   3. AdamW over the AdamW group
+//   4. Muon momentum + ||u||^2 partials, per-matrix scale, normalise/orient
+//   5. ns_steps x (GRAM, POLY, XUPD); the last XUPD writes the update.
+// Nothing is launched before every argument has been checked.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "ma_internal.h"
+
+using namespace ma;
+
+namespace {
+
+bool is_finite(double x) { return std::isfinite(x); }
+
+int hip_fail(const char* what, int err) {
+    set_error("%s: %s", what, hipGetErrorString((hipError_t)err));
+    return MA_ERR_HIP;
+}
+
+// A pinned host staging buffer of at least `bytes`, whose previous copy (if
+// any) has completed.  Two buffers alternate so consecutive steps do not
+// wait on each other's copies.
+int get_staging(const ma_plan* plan, size_t bytes, void** out, void** event) {
+    const int k = plan->staging_next;
+    plan->staging_next ^= 1;
+    if (plan->staging_event[k]) {
+        hipError_t e = hipEventSynchronize((hipEvent_t)plan->staging_event[k]);
+        if (e != hipSuccess) return hip_fail("staging event wait", e);
+    } else {
+        hipEvent_t ev;
+        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail("hipEventCreate", e);
+        plan->staging_event[k] = ev;
+    }
+    if (plan->staging_bytes[k] < bytes) {
+        if (plan->staging[k]) (void)hipHostFree(plan->staging[k]);
+        plan->staging[k] = nullptr;
+        plan->staging_bytes[k] = 0;
+        void* p = nullptr;
+        hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocPortable);
+        if (e != hipSuccess) return hip_fail("hipHostMalloc (staging)", e);
+        plan->staging[k] = p;
+        plan->staging_bytes[k] = bytes;
+    }
+    *out = plan->staging[k];
+    *event = plan->staging_event[k];
+    return MA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int muon_adamw_step(const ma_plan* plan, float* const* params, const float* const* grads,
+                    ma_state* state, const ma_hparams* hp, void* workspace, size_t ws_bytes,
+                    void* stream, float* grad_norm_out, float* const* muon_update_out) {
+    return muon_adamw_step_profiled(plan, params, grads, state, hp, workspace, ws_bytes, stream,
+                                    grad_norm_out, muon_update_out, nullptr);
+}
+
+int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const float* const* grads,
+                             ma_state* state, const ma_hparams* hp, void* workspace,
+                             size_t ws_bytes, void* stream, float* grad_norm_out,
+                             float* const* muon_update_out, void* const* phase_events) {
+    // ---------------------------------------------------------- validate --
+    if (!plan || !state || !hp) {
+        set_error("muon_adamw_step: plan, state and hp are required");
+        return MA_ERR_INVALID_ARG;
+    }
+    const int32_t prec = hp->ns_precision;
+    if (prec != MA_NS_BF16 && prec != MA_NS_FP32) {
+        set_error("muon_adamw_step: unknown ns_precision %d", prec);
+        return MA_ERR_UNSUPPORTED;
+    }
+    if (hp->muon_ns_steps < 1 || hp->muon_ns_steps > 64) {
+        set_error("muon_adamw_step: muon_ns_steps %d outside [1, 64]", hp->muon_ns_steps);
+        return MA_ERR_UNSUPPORTED;
+    }
+    const double fields[] = {hp->lr, hp->muon_lr_scale, hp->muon_momentum, hp->ns_coeffs[0],
+                             hp->ns_coeffs[1], hp->ns_coeffs[2], hp->ns_eps, hp->beta1,
+                             hp->beta2, hp->eps, hp->weight_decay, hp->muon_weight_decay,
+                             hp->max_grad_norm};
+    for (double f : fields) {
+        if (!is_finite(f)) {
+            set_error("muon_adamw_step: non-finite hyperparameter");
+            return MA_ERR_INVALID_ARG;
+        }
+    }
+    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0 && hp->beta2 >= 0.0 && hp->beta2 < 1.0)) {
+        set_error("muon_adamw_step: betas must lie in [0, 1)");
+        return MA_ERR_INVALID_ARG;
+    }
+    if (hp->eps < 0.0 || hp->ns_eps < 0.0 || hp->lr < 0.0) {
+        set_error("muon_adamw_step: lr, eps and ns_eps must be >= 0");
+        return MA_ERR_INVALID_ARG;
+    }
+    if (state->step < 0 || state->step > (int64_t(1) << 40)) {
+        set_error("muon_adamw_step: state->step %lld out of range", (long long)state->step);
+        return MA_ERR_INVALID_ARG;
+    }
+    const bool any_train = !plan->train_ids.empty();
+    if (any_train && (!params || !grads)) {
+        set_error("muon_adamw_step: params and grads arrays are required");
+        return MA_ERR_INVALID_ARG;
+    }
+    for (int32_t id : plan->train_ids) {
+        if (!params[id] || !grads[id]) {
+            set_error("muon_adamw_step: entry %d needs a param and a grad pointer", id);
+            return MA_ERR_INVALID_ARG;
+        }
+    }
+    if (!plan->muon_ids.empty() && !state->muon_momentum) {
+        set_error("muon_adamw_step: state->muon_momentum is required");
+        return MA_ERR_INVALID_ARG;
+    }
+    for (int32_t id : plan->muon_ids) {
+        if (!state->muon_momentum[id]) {
+            set_error("muon_adamw_step: entry %d needs a momentum buffer", id);
+            return MA_ERR_INVALID_ARG;
+        }
+    }
+    if (!plan->adam_ids.empty() && (!state->adam_m || !state->adam_v)) {
+        set_error("muon_adamw_step: state->adam_m and adam_v are required");
+        return MA_ERR_INVALID_ARG;
+    }
+    for (int32_t id : plan->adam_ids) {
+        if (!state->adam_m[id] || !state->adam_v[id]) {
+            set_error("muon_adamw_step: entry %d needs AdamW moment buffers", id);
+            return MA_ERR_INVALID_ARG;
+        }
+    }
+    const Layout& L = plan->layout[prec];
+    if (!workspace || ws_bytes < L.total) {
+        set_error("muon_adamw_step: workspace of %zu bytes, need %zu", ws_bytes, L.total);
+        return MA_ERR_WORKSPACE;
+    }
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) {
+        set_error("muon_adamw_step: workspace must be 256-byte aligned");
+        return MA_ERR_WORKSPACE;
+    }
+
+    // -------------------------------------------------------- scalars ----
+    const int64_t t = state->step + 1;
+    StepScalars sc;
+    sc.lr = (float)hp->lr;
+    sc.beta1 = (float)hp->beta1;
+    sc.beta2 = (float)hp->beta2;
+    sc.one_m_beta1 = (float)(1.0 - hp->beta1);
+    sc.one_m_beta2 = (float)(1.0 - hp->beta2);
+    sc.eps = (float)hp->eps;
+    sc.weight_decay = (float)hp->weight_decay;
+    const double bc1 = 1.0 - std::pow(hp->beta1, (double)t);
+    const double bc2 = 1.0 - std::pow(hp->beta2, (double)t);
+    sc.step_size = (float)(hp->lr / (bc1 > 0.0 ? bc1 : 1.0));
+    sc.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2 > 0.0 ? bc2 : 1.0));
+    sc.adam_decay = (float)(1.0 - hp->lr * hp->weight_decay);
+    sc.max_grad_norm = (float)hp->max_grad_norm;
+    sc.mu = (float)hp->muon_momentum;
+    sc.nesterov = hp->muon_nesterov ? 1 : 0;
+    sc.ns_eps = (float)hp->ns_eps;
+    sc.ns_a = (float)hp->ns_coeffs[0];
+    sc.ns_b = (float)hp->ns_coeffs[1];
+    sc.ns_c = (float)hp->ns_coeffs[2];
+    const float muon_decay = (float)(1.0 - hp->lr * hp->muon_weight_decay);
+
+    std::lock_guard<std::mutex> lock(plan->mu);
+    void* host = nullptr;
+    void* event = nullptr;
+    int rc = get_staging(plan, L.tables_bytes, &host, &event);
+    if (rc != MA_OK) return rc;
+
+    // ------------------------------------------------- descriptor tables --
+    char* base = reinterpret_cast<char*>(workspace);
+    char* hb = reinterpret_cast<char*>(host);
+    std::memset(hb, 0, L.tables_bytes);
+    auto* norm_tab = reinterpret_cast<NormTensor*>(hb + L.norm_tab_off);
+    for (size_t k = 0; k < plan->train_ids.size(); ++k) {
+        const int32_t id = plan->train_ids[k];
+        NormTensor& d = norm_tab[k];
+        d.g = reinterpret_cast<uint64_t>(grads[id]);
+        d.numel = plan->entries[id].numel;
+        d.chunk_begin = plan->norm_chunk_begin[k];
+        d.vec_ok = aligned16(grads[id]) ? 1 : 0;
+    }
+    auto* adam_tab = reinterpret_cast<AdamTensor*>(hb + L.adam_tab_off);
+    for (size_t k = 0; k < plan->adam_ids.size(); ++k) {
+        const int32_t id = plan->adam_ids[k];
+        AdamTensor& d = adam_tab[k];
+        d.p = reinterpret_cast<uint64_t>(params[id]);
+        d.g = reinterpret_cast<uint64_t>(grads[id]);
+        d.m = reinterpret_cast<uint64_t>(state->adam_m[id]);
+        d.v = reinterpret_cast<uint64_t>(state->adam_v[id]);
+        d.numel = plan->entries[id].numel;
+        d.chunk_begin = plan->adam_chunk_begin[k];
+        d.vec_ok = (aligned16(params[id]) && aligned16(grads[id]) && aligned16(state->adam_m[id]) &&
+                    aligned16(state->adam_v[id]))
+                       ? 1
+                       : 0;
+    }
+    auto* muon_tab = reinterpret_cast<MuonMat*>(hb + L.muon_tab_off);
+    for (size_t k = 0; k < plan->muon_ids.size(); ++k) {
+        const int32_t id = plan->muon_ids[k];
+        const Entry& e = plan->entries[id];
+        MuonMat& d = muon_tab[k];
+        float* delta = muon_update_out ? muon_update_out[id] : nullptr;
+        d.p = reinterpret_cast<uint64_t>(params[id]);
+        d.g = reinterpret_cast<uint64_t>(grads[id]);
+        d.buf = reinterpret_cast<uint64_t>(state->muon_momentum[id]);
+        d.delta = reinterpret_cast<uint64_t>(delta);
+        d.x32 = reinterpret_cast<uint64_t>(base + L.x32[k]);
+        d.xb = reinterpret_cast<uint64_t>(base + L.xb[k]);
+        d.xt[0] = reinterpret_cast<uint64_t>(base + L.xt0[k]);
+        d.xt[1] = reinterpret_cast<uint64_t>(base + L.xt1[k]);
+        d.a = reinterpret_cast<uint64_t>(base + L.a[k]);
+        d.b = reinterpret_cast<uint64_t>(base + L.b[k]);
+        d.numel = e.numel;
+        d.chunk_begin = plan->muon_chunk_begin[k];
+        d.orient_begin = plan->muon_orient_begin[k];
+        d.n_chunks = (int32_t)ceil_div(e.numel, kChunk);
+        d.m = (int32_t)e.m;
+        d.n = (int32_t)e.n;
+        d.r = (int32_t)e.r;
+        d.c = (int32_t)e.c;
+        d.R = (int32_t)round_up(e.r, kNsPad);
+        d.C = (int32_t)round_up(e.c, kNsPad);
+        d.transposed = e.transposed;
+        d.vec_ok = (aligned16(params[id]) && aligned16(grads[id]) &&
+                    aligned16(state->muon_momentum[id]) && (!delta || aligned16(delta)) &&
+                    (e.n % 4) == 0)
+                       ? 1
+                       : 0;
+        d.lr_eff = (float)(hp->lr * hp->muon_lr_scale * (double)e.lr_shape_scale);
+        d.decay = muon_decay;
+        d.op_bf16 = L.op_group[k] == kGroupBf16 ? 1 : 0;
+    }
+    for (int g = 0; g < 2; ++g) {
+        std::memcpy(hb + L.g1_off[g], L.g1[g].data(), sizeof(GemmTile) * L.g1[g].size());
+        std::memcpy(hb + L.g2_off[g], L.g2[g].data(), sizeof(GemmTile) * L.g2[g].size());
+        std::memcpy(hb + L.g3_off[g], L.g3[g].data(), sizeof(GemmTile) * L.g3[g].size());
+    }
+
+    hipStream_t st = (hipStream_t)stream;
+    auto mark = [&](int k) -> int {
+        if (!phase_events || !phase_events[k]) return 0;
+        return (int)hipEventRecord((hipEvent_t)phase_events[k], st);
+    };
+    if (int er = mark(0)) return hip_fail("phase event", er);
+    hipError_t e = hipMemcpyAsync(base + L.tables_off, hb, L.tables_bytes, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return hip_fail("hipMemcpyAsync (tables)", e);
+    e = hipEventRecord((hipEvent_t)event, st);
+    if (e != hipSuccess) return hip_fail("hipEventRecord", e);
+
+    // ------------------------------------------------------------ launch --
+    const auto* d_norm = reinterpret_cast<const NormTensor*>(base + L.norm_tab_off);
+    const auto* d_adam = reinterpret_cast<const AdamTensor*>(base + L.adam_tab_off);
+    const auto* d_muon = reinterpret_cast<const MuonMat*>(base + L.muon_tab_off);
+    float* scal = reinterpret_cast<float*>(base + L.scalars_off);
+    float* coef = scal + 0;
+    float* norm = scal + 1;
+    float* norm_partials = reinterpret_cast<float*>(base + L.norm_partials_off);
+    float* muon_partials = reinterpret_cast<float*>(base + L.muon_partials_off);
+    float* muon_scales = reinterpret_cast<float*>(base + L.muon_scale_off);
+    const int32_t n_train = (int32_t)plan->train_ids.size();
+    const int32_t n_adam = (int32_t)plan->adam_ids.size();
+    const int32_t n_muon = (int32_t)plan->muon_ids.size();
+
+    int err = launch_norm_partials(d_norm, n_train, plan->n_norm_chunks, norm_partials, stream);
+    if (err) return hip_fail("clip norm partials", err);
+    err = launch_clip_finalize(norm_partials, plan->n_norm_chunks, sc.max_grad_norm, coef, norm,
+                               grad_norm_out, stream);
+    if (err) return hip_fail("clip finalize", err);
+    if ((err = mark(1))) return hip_fail("phase event", err);
+    err = launch_adamw(d_adam, n_adam, plan->n_adam_chunks, coef, sc, stream);
+    if (err) return hip_fail("adamw", err);
+    if ((err = mark(2))) return hip_fail("phase event", err);
+    if (n_muon > 0) {
+        err = launch_muon_momentum(d_muon, n_muon, plan->n_muon_chunks, coef, sc, muon_partials,
+                                   stream);
+        if (err) return hip_fail("muon momentum", err);
+        err = launch_muon_scale(d_muon, n_muon, muon_partials, sc.ns_eps, muon_scales, stream);
+        if (err) return hip_fail("muon scale", err);
+        err = launch_orient(d_muon, n_muon, plan->n_orient_tiles, coef, muon_scales, sc, stream);
+        if (err) return hip_fail("muon orient", err);
+        if ((err = mark(3))) return hip_fail("phase event", err);
+        for (int it = 0; it < hp->muon_ns_steps; ++it) {
+            const int last = it == hp->muon_ns_steps - 1;
+            for (int phase = 1; phase <= 3; ++phase) {
+                for (int g = 0; g < 2; ++g) {
+                    const std::vector<GemmTile>& tl =
+                        phase == 1 ? L.g1[g] : phase == 2 ? L.g2[g] : L.g3[g];
+                    const size_t off = phase == 1 ? L.g1_off[g] : phase == 2 ? L.g2_off[g] : L.g3_off[g];
+                    err = launch_ns_phase(phase, g, d_muon, reinterpret_cast<const GemmTile*>(base + off),
+                                          (int64_t)tl.size(), it, last, sc, stream);
+                    if (err) return hip_fail("newton-schulz", err);
+                }
+            }
+        }
+    } else if ((err = mark(3))) {
+        return hip_fail("phase event", err);
+    }
+    if ((err = mark(4))) return hip_fail("phase event", err);
+    state->step = t;
+    clear_error();
+    return MA_OK;
+}
+
+void muon_adamw_plan_free(ma_plan* plan) {
+    if (!plan) return;
+    for (int k = 0; k < 2; ++k) {
+        if (plan->staging_event[k]) {
+            (void)hipEventSynchronize((hipEvent_t)plan->staging_event[k]);
+            (void)hipEventDestroy((hipEvent_t)plan->staging_event[k]);
+        }
+        if (plan->staging[k]) (void)hipHostFree(plan->staging[k]);
+    }
+    delete plan;
+}
+
+}  // extern "C"

@@ -109,9 +109,10 @@ def route_one(name: str, shape: Sequence[int], trainable: bool,
     to plain AdamW every trainable tensor is AdamW.  Otherwise a tensor is
     Muon when it is a matrix (two dimensions) whose dotted name contains
     'action_expert' in one component, has a component exactly 'layers' after
-    that one, ends with '.weight', and whose lower-cased name contains none of
-    'embed', 'lm_head', 'norm' (the page's exclusion of embeddings and of
-    every norm layer).  Anything else trainable is AdamW.
+    that one, ends with '.weight', and whose name, with ASCII letters folded
+    to lower case, contains none of 'embed', 'lm_head', 'norm' (the page's
+    exclusion of embeddings and of every norm layer).  Anything else
+    trainable is AdamW.
     """
     if not trainable:
         return NONE
@@ -131,9 +132,9 @@ def route_one(name: str, shape: Sequence[int], trainable: bool,
         return ADAMW
     if "layers" not in parts[ae + 1:]:
         return ADAMW
-    lowered = name.lower()
+    lowered = name.encode("utf-8").lower()      # ASCII case folding only
     for bad in _EXCLUDED_SUBSTRINGS:
-        if bad in lowered:
+        if bad.encode() in lowered:
             return ADAMW
     return MUON
 
@@ -217,10 +218,14 @@ def global_grad_norm(grads: Sequence[np.ndarray]) -> float:
 
 def clip_coefficient(norm: float, max_grad_norm: float) -> float:
     """Factor applied to every gradient before the update: 1 when clipping is
-    off (max_grad_norm <= 0), else min(1, max_grad_norm / (norm + 1e-6))."""
+    off (max_grad_norm <= 0), else min(1, max_grad_norm / (norm + 1e-6)),
+    clamped like a tensor clamp: a NaN norm gives a NaN factor."""
     if max_grad_norm <= 0.0:
         return 1.0
-    return min(1.0, max_grad_norm / (norm + 1e-6))
+    coef = max_grad_norm / (norm + 1e-6)
+    if math.isnan(coef):
+        return coef                     # a NaN norm poisons every update
+    return min(1.0, coef)
 
 
 # --------------------------------------------------------------------------

@@ -1,0 +1,193 @@
+"""Host-side tests of the C-ABI library (no GPU needed).
+
+* the built library loads and exports every function include/muon_adamw.h
+  declares;
+* the plan (routing, canonical shapes, buckets, shape factors, AdamW offsets)
+  matches the oracle's plan dump byte for byte on every synthetic workload and
+  on the adversarial routing table;
+* every argument error is reported before anything is launched (pointers
+  passed here are never dereferenced: validation fails first).
+"""
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon_adamw.h")
+
+M = pytest.importorskip("muon_newton_schulz_02_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    try:
+        return M.load_library()
+    except RuntimeError as e:
+        pytest.fail("library not built: %s" % e)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_adamw_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert len(names) == 11, names
+    for n in names:
+        assert hasattr(lib, n), n
+    from muon_newton_schulz_02_amd import _abi
+    assert sorted(s[0] for s in _abi.SIGNATURES) == names
+
+
+def test_version_and_defaults(lib):
+    assert "gfx950" in M.muon_adamw_version()
+    hp = M.muon_adamw_default_hparams()
+    assert hp.lr == 2.5e-5
+    assert hp.muon_momentum == 0.95 and hp.muon_nesterov == 1
+    assert hp.muon_ns_steps == 5 and hp.max_grad_norm == 1.0
+    assert tuple(hp.ns_coeffs) == O.DEFAULT_NS_COEFFS
+    assert hp.ns_precision == M.MA_NS_BF16
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_plan_dump_matches_oracle(lib, name):
+    w = W.WORKLOADS[name]()
+    plan = M.muon_adamw_plan(list(zip(w.names, w.shapes, w.trainable)))
+    assert M.muon_adamw_plan_dump(plan) == O.plan_dump(w.names, w.shapes, w.trainable)
+    assert M.muon_adamw_plan_size(plan) == len(w.names)
+
+
+def _golden_routing():
+    rows = []
+    for line in open(os.path.join(ROOT, "tests", "golden", "routing_table.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        grp, tr, shape, name = line.rstrip("\n").split("\t")
+        rows.append((name, tuple(int(s) for s in shape.split(",")), tr == "1"))
+    return rows
+
+
+@pytest.mark.parametrize("mode", [O.MODE_MUON_ADAMW, O.MODE_ADAMW])
+@pytest.mark.parametrize("moon", [0.2, 0.37])
+def test_plan_dump_adversarial(lib, mode, moon):
+    rows = _golden_routing()
+    names, shapes, tr = zip(*rows)
+    plan = M.muon_adamw_plan(rows, mode=mode, moonlight_coefficient=moon)
+    assert M.muon_adamw_plan_dump(plan) == O.plan_dump(names, shapes, tr, mode, moon)
+
+
+def test_plan_entries_and_shape_scale_bits(lib):
+    rng = np.random.default_rng(0)
+    table = []
+    for i in range(200):
+        m, n = (int(x) for x in rng.integers(1, 20000, 2))
+        table.append(("action_expert.layers.%d.w.weight" % i, (m, n), True))
+    plan = M.muon_adamw_plan(table)
+    for i, (_, (m, n), _) in enumerate(table):
+        e = M.muon_adamw_plan_entry(plan, i)
+        assert e["group"] == M.MA_GROUP_MUON
+        assert (e["m"], e["n"], e["r"], e["c"]) == (m, n, min(m, n), max(m, n))
+        assert e["transposed"] == (1 if m > n else 0)
+        assert np.float32(e["lr_shape_scale"]) == O.lr_shape_scale(m, n)
+    names, shapes, tr = zip(*table)
+    assert M.muon_adamw_plan_dump(plan) == O.plan_dump(names, shapes, tr)
+
+
+def test_plan_errors(lib):
+    with pytest.raises(M.MuonAdamWError) as e:
+        M.muon_adamw_plan([])
+    assert e.value.code == M.MA_ERR_INVALID_ARG
+    with pytest.raises(M.MuonAdamWError) as e:
+        M.muon_adamw_plan([("a.weight", (3, 0), True)])
+    assert e.value.code == M.MA_ERR_SHAPE
+    with pytest.raises(M.MuonAdamWError) as e:
+        M.muon_adamw_plan([("a.weight", (1,) * 9, True)])
+    assert e.value.code == M.MA_ERR_UNSUPPORTED
+    with pytest.raises(M.MuonAdamWError) as e:
+        M.muon_adamw_plan([("a.weight", (4, 4), True)], mode=7)
+    assert e.value.code == M.MA_ERR_INVALID_ARG
+    with pytest.raises(M.MuonAdamWError) as e:
+        M.muon_adamw_plan([("a.weight", (4, 4), True)], moonlight_coefficient=-1.0)
+    assert e.value.code == M.MA_ERR_INVALID_ARG
+    with pytest.raises(M.MuonAdamWError) as e:
+        M.muon_adamw_plan([("a.weight", (1 << 40, 1 << 40), True)])
+    assert e.value.code == M.MA_ERR_SHAPE
+    plan = M.muon_adamw_plan([("a.weight", (4, 4), True)])
+    with pytest.raises(M.MuonAdamWError):
+        M.muon_adamw_plan_entry(plan, 5)
+    with pytest.raises(M.MuonAdamWError):
+        M.muon_adamw_workspace_size(plan, 9)
+    assert "range" in M.muon_adamw_last_error() or "precision" in M.muon_adamw_last_error()
+
+
+def test_plan_dump_small_buffer(lib):
+    from muon_newton_schulz_02_amd import _abi
+    plan = M.muon_adamw_plan([("action_expert.layers.0.q.weight", (8, 4), True)])
+    n = C.c_size_t()
+    buf = C.create_string_buffer(4)
+    rc = _abi.load().muon_adamw_plan_dump(plan.handle, buf, 4, C.byref(n))
+    assert rc == M.MA_ERR_WORKSPACE and n.value > 4
+
+
+def _table_small():
+    return [("action_expert.layers.0.q.weight", (8, 4), True),
+            ("vlm.model.norm.weight", (16,), True),
+            ("vlm.model.embed_tokens.weight", (10, 4), False)]
+
+
+def test_step_argument_errors_launch_nothing(lib):
+    """Validation fails before any HIP call, so fake addresses are safe."""
+    plan = M.muon_adamw_plan(_table_small())
+    ws_need = M.muon_adamw_workspace_size(plan, M.MA_NS_BF16)
+    fake = 1 << 40
+    st = M.State(3)
+    st.muon_momentum[0] = fake
+    st.adam_m[1] = fake
+    st.adam_v[1] = fake
+    params = [fake, fake, None]
+    grads = [fake, fake, None]
+
+    def run(hp=None, ws=(fake, ws_need), params=params, grads=grads, state=st):
+        hp = hp or M.muon_adamw_default_hparams()
+        with pytest.raises(M.MuonAdamWError) as e:
+            M.muon_adamw_step(plan, params, grads, state, hp, ws, stream=0)
+        return e.value.code
+
+    assert run(ws=(fake, ws_need - 1)) == M.MA_ERR_WORKSPACE
+    assert run(ws=(fake + 4, ws_need)) == M.MA_ERR_WORKSPACE
+    assert run(ws=(0, ws_need)) == M.MA_ERR_WORKSPACE
+    assert run(hp=M.muon_adamw_default_hparams(muon_ns_steps=0)) == M.MA_ERR_UNSUPPORTED
+    assert run(hp=M.muon_adamw_default_hparams(ns_precision=3)) == M.MA_ERR_UNSUPPORTED
+    assert run(hp=M.muon_adamw_default_hparams(lr=float("nan"))) == M.MA_ERR_INVALID_ARG
+    assert run(hp=M.muon_adamw_default_hparams(beta1=1.0)) == M.MA_ERR_INVALID_ARG
+    assert run(params=[fake, None, None]) == M.MA_ERR_INVALID_ARG
+    assert run(grads=[None, fake, None]) == M.MA_ERR_INVALID_ARG
+    st2 = M.State(3)
+    st2.adam_m[1] = fake
+    st2.adam_v[1] = fake
+    assert run(state=st2) == M.MA_ERR_INVALID_ARG
+    st3 = M.State(3)
+    st3.muon_momentum[0] = fake
+    st3.adam_m[1] = fake
+    assert run(state=st3) == M.MA_ERR_INVALID_ARG
+    assert st.step == 0
+
+
+def test_workspace_size_grows_with_precision(lib):
+    w = W.ae18_muon_bf16()
+    plan = M.muon_adamw_plan(list(zip(w.names, w.shapes, w.trainable)))
+    b = M.muon_adamw_workspace_size(plan, M.MA_NS_BF16)
+    f = M.muon_adamw_workspace_size(plan, M.MA_NS_FP32)
+    # x32 + xb + 2 xt (bf16) + A + B  vs  x32 + 2 xt (fp32) + A + B (fp32)
+    rc = sum(min(s) * max(s) for s in w.shapes)
+    assert b >= rc * (4 + 2 + 4) and f >= rc * (4 + 8)
+    assert f > b

@@ -1,0 +1,243 @@
+"""GPU parity of the HIP MuonAdamW step against the CPU oracle.
+
+Each test seeds the same inputs for both sides (workloads module), runs the
+GPU path through the C ABI and the oracle independently for several steps,
+and compares after every step (tolerances in tests/_harness.py).  Sizes span
+several GEMM tiles with ragged tails; the full-size workloads run in the
+launch configuration the benchmark times and are compared on sampled
+tensors, since the oracle cannot afford every matrix.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from tests import _harness as H
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+M = pytest.importorskip("muon_newton_schulz_02_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    M.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _run_parity(w, ns_precision, steps, hp=None, sampled=None, backend="numpy",
+                check_params=True, say_every=1):
+    """Run `steps` steps on both sides; compare the whole table (or only the
+    entries in `sampled`)."""
+    hp = hp or H.oracle_hparams(w)
+    tol = H.BF16_TOL if ns_precision == "bf16" else H.FP32_TOL
+    deltas = "all" if sampled is None else set(sampled)
+    run = H.setup_gpu(M, torch, w, hp, ns_precision, backend, deltas=deltas)
+    idx = range(len(w.params)) if sampled is None else sorted(sampled)
+    # oracle-side state of the compared entries, from the same seeded inputs
+    op, obuf, om, ov, omabs = {}, {}, {}, {}, {}
+    for i in idx:
+        if run.groups[i] == O.NONE:
+            continue
+        op[i] = H.host(run.params[i]).copy()
+        if run.groups[i] == O.MUON:
+            obuf[i] = H.host(run.state.muon_momentum[i]).copy()
+        else:
+            om[i] = np.zeros(w.params[i].shape, np.float32)
+            ov[i] = np.zeros(w.params[i].shape, np.float32)
+            omabs[i] = np.zeros(w.params[i].shape, np.float64)
+    worst = 0.0
+    for t in range(1, steps + 1):
+        H.say("%s ns=%s step %d: inputs" % (w.name, ns_precision, t))
+        H.fill_grads(run, torch, t, backend)
+        torch.cuda.synchronize()
+        H.say("%s step %d: oracle norm" % (w.name, t))
+        norm = H.oracle_norm_of_device_grads(run)
+        coef = O.clip_coefficient(norm, hp.max_grad_norm)
+        H.say("%s step %d: gpu step" % (w.name, t))
+        H.gpu_step(M, torch, run)
+        gnorm = float(H.host(run.norm_out)[0])
+        assert abs(gnorm - norm) <= 1e-5 * norm, (gnorm, norm)
+        assert run.state.step == t
+        H.say("%s step %d: oracle updates (norm %.6g)" % (w.name, t, norm))
+        for i in idx:
+            g = run.groups[i]
+            if g == O.NONE:
+                continue
+            grad = H.host(run.grads[i])
+            if g == O.ADAMW:
+                p, m, v = O.adamw_update(op[i], grad, om[i], ov[i], t, coef, hp)
+                omabs[i] = hp.beta1 * omabs[i] + (1 - hp.beta1) * np.abs(coef * grad.astype(np.float64))
+                H.check_adamw(H.host(run.params[i]), H.host(run.state.adam_m[i]),
+                              H.host(run.state.adam_v[i]), p, m, v, "%s[%d] step %d" % (w.name, i, t),
+                              m_terms=omabs[i])
+                op[i], om[i], ov[i] = p, m, v
+            else:
+                m_, n_ = w.params[i].shape
+                scale = O.lr_shape_scale(m_, n_, hp.moonlight_coefficient)
+                p, buf, delta = O.muon_matrix_update(op[i], grad, obuf[i], coef, hp, scale)
+                gbuf = H.host(run.state.muon_momentum[i])
+                np.testing.assert_allclose(gbuf, buf, rtol=1e-5, atol=1e-7 * (np.abs(buf).max() + 1e-30))
+                err = H.rel_fro(H.host(run.deltas[i]), delta)
+                worst = max(worst, err)
+                assert err <= tol, "%s[%d] %s step %d: delta rel err %.3g > %.1g" % (
+                    w.name, i, w.params[i].shape, t, err, tol)
+                if check_params:
+                    gp = H.host(run.params[i]).astype(np.float64)
+                    # parameter error = update error + one fp32 rounding per step
+                    slack = t * (tol * np.linalg.norm(delta) + 6e-8 * np.linalg.norm(p)) + 1e-30
+                    assert np.linalg.norm(gp - p.astype(np.float64)) <= 2 * slack
+                op[i], obuf[i] = p, buf
+        H.say("%s step %d ok (worst muon rel err %.3g)" % (w.name, t, worst))
+    return worst
+
+
+def test_tiny_hybrid_fp32_all_entries():
+    """14 Muon matrices (256..1024, both orientations) + 13 AdamW tensors,
+    fp32 NS, 3 steps, every entry compared."""
+    _run_parity(W.tiny_hybrid_fp32(), "fp32", 3)
+
+
+def _ragged_workload():
+    shapes = [(1, 7), (7, 1), (33, 65), (65, 33), (130, 300), (300, 130), (256, 256),
+              (257, 513), (513, 257), (64, 256), (3, 1000), (129, 129)]
+    params = [W.ParamSpec("action_expert.layers.%d.r.weight" % i, s) for i, s in enumerate(shapes)]
+    params += [W.ParamSpec("vlm.bias", (3,)), W.ParamSpec("vlm.w", (5, 7)),
+               W.ParamSpec("vlm.big", (16385,)), W.ParamSpec("vlm.cube", (4, 4, 4)),
+               W.ParamSpec("vlm.frozen", (9, 9), trainable=False),
+               W.ParamSpec("action_expert.layers.0.norm.weight", (40, 40))]
+    return W.Workload("ragged_small", seed=7, steps=2, ns_precision="bf16", params=params,
+                      grad_std=1e-3)
+
+
+@pytest.mark.parametrize("prec,steps", [("bf16", 5), ("fp32", 5), ("bf16", 1), ("fp32", 2)])
+def test_ragged_shapes(prec, steps):
+    """Ragged Muon shapes (1xn, nx1, odd sizes around tile edges, both
+    orientations) and odd AdamW sizes (tails of a chunk, non-multiples of 4),
+    with 1, 2 and 5 NS steps."""
+    w = _ragged_workload()
+    hp = H.oracle_hparams(w, ns_steps=steps)
+    _run_parity(w, prec, 2, hp=hp)
+
+
+def test_ragged_published_coefficients_no_nesterov_with_decay():
+    w = _ragged_workload()
+    hp = H.oracle_hparams(w, ns_coeffs=O.PUBLISHED_NS_COEFFS, muon_nesterov=False,
+                          muon_weight_decay=0.1, lr=1e-3, max_grad_norm=0.0)
+    _run_parity(w, "fp32", 2, hp=hp)
+
+
+def test_adamw_mode_and_misaligned_views():
+    """Plain-AdamW mode sends every trainable tensor through the AdamW kernel;
+    a view starting one float into its storage takes the scalar path."""
+    dev = torch.device("cuda", 0)
+    table = [("action_expert.layers.0.q.weight", (64, 48), True),
+             ("vlm.x", (1000,), True), ("vlm.y", (20001,), True)]
+    plan = M.muon_adamw_plan(table, mode=M.MA_MODE_ADAMW)
+    assert all(M.muon_adamw_plan_entry(plan, i)["group"] == M.MA_GROUP_ADAMW for i in range(3))
+    rng = np.random.default_rng(3)
+    store = torch.zeros(20002, device=dev)
+    p_host = [rng.standard_normal(s).astype(np.float32) * np.float32(0.02) for _, s, _ in table]
+    params = [torch.from_numpy(p_host[0]).to(dev), torch.from_numpy(p_host[1]).to(dev), store[1:]]
+    params[2].copy_(torch.from_numpy(p_host[2]))
+    assert params[2].data_ptr() % 16 == 4
+    st = M.State(3)
+    for i, (_, s, _) in enumerate(table):
+        st.adam_m[i] = torch.zeros(s, device=dev)
+        st.adam_v[i] = torch.zeros(s, device=dev)
+    hp = O.HParams()
+    lhp = H.lib_hparams(M, hp, "bf16")
+    ws = torch.empty(M.muon_adamw_workspace_size(plan, 0), dtype=torch.uint8, device=dev)
+    om = [np.zeros(s, np.float32) for _, s, _ in table]
+    ov = [np.zeros(s, np.float32) for _, s, _ in table]
+    op = [p.copy() for p in p_host]
+    mabs = [np.zeros(s, np.float64) for _, s, _ in table]
+    for t in (1, 2, 3):
+        g_host = [rng.standard_normal(s).astype(np.float32) * np.float32(0.05) for _, s, _ in table]
+        grads = [torch.from_numpy(g).to(dev) for g in g_host]
+        H.say("adamw mode step", t)
+        M.muon_adamw_step(plan, params, grads, st, lhp, ws)
+        torch.cuda.synchronize()
+        coef = O.clip_coefficient(O.global_grad_norm(g_host), hp.max_grad_norm)
+        for i in range(3):
+            mabs[i] = hp.beta1 * mabs[i] + (1 - hp.beta1) * np.abs(coef * g_host[i].astype(np.float64))
+            op[i], om[i], ov[i] = O.adamw_update(op[i], g_host[i], om[i], ov[i], t, coef, hp)
+            H.check_adamw(H.host(params[i]), H.host(st.adam_m[i]), H.host(st.adam_v[i]),
+                          op[i], om[i], ov[i], "adamw-mode[%d] step %d" % (i, t), m_terms=mabs[i])
+    assert float(store[0]) == 0.0
+
+
+def test_bitwise_deterministic_reruns():
+    """Two runs from identical inputs give bit-identical parameters, states,
+    deltas and norms (fixed reduction trees, no float atomics)."""
+    w = _ragged_workload()
+    hp = H.oracle_hparams(w)
+    outs = []
+    for rep in range(2):
+        run = H.setup_gpu(M, torch, w, hp, "bf16")
+        for t in (1, 2):
+            H.fill_grads(run, torch, t)
+            H.say("determinism rep %d step %d" % (rep, t))
+            H.gpu_step(M, torch, run)
+        outs.append([H.host(x) for x in run.params + run.deltas + run.state.muon_momentum +
+                     run.state.adam_m + run.state.adam_v + [run.norm_out] if x is not None])
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_zero_gradients():
+    """Degenerate input: all-zero gradients.  Norm 0, no clipping, Muon deltas
+    exactly 0 (NS of the zero matrix), AdamW is pure decay."""
+    w = _ragged_workload()
+    hp = H.oracle_hparams(w)
+    run = H.setup_gpu(M, torch, w, hp, "bf16")
+    p0 = [None if p is None else H.host(p).copy() for p in run.params]
+    for g in run.grads:
+        if g is not None:
+            g.zero_()
+    H.say("zero gradients")
+    H.gpu_step(M, torch, run)
+    assert float(H.host(run.norm_out)[0]) == 0.0
+    for i, grp in enumerate(run.groups):
+        if grp == O.MUON:
+            assert np.all(H.host(run.deltas[i]) == 0.0)
+            np.testing.assert_array_equal(H.host(run.params[i]), p0[i])
+        elif grp == O.ADAMW:
+            np.testing.assert_allclose(H.host(run.params[i]), p0[i] * np.float32(1 - 2.5e-7),
+                                       rtol=1e-7, atol=0)
+
+
+def test_ae18_full_size_sampled():
+    """The 18-layer action-expert Muon group at full size (126 matrices),
+    bf16 NS, per-row-scaled gradients, 10 steps; the oracle follows one
+    matrix of every shape (q 1024^2, k 256x1024, gate 4096x1024 transposed,
+    down 1024x4096) and the global norm over all gradients."""
+    w = W.ae18_muon_bf16()
+    sampled = {0, 1, 4, 6 + 7 * 17}
+    _run_parity(w, "bf16", w.steps, sampled=sampled, backend="torch")
+
+
+def test_vla_hybrid_full_size_sampled():
+    """The full hybrid step in the benchmark's configuration: 126 Muon
+    matrices (bf16 NS) + 253 AdamW tensors (1.88e9 elements) + a frozen
+    embedding; clip triggers.  The oracle follows the global norm over all
+    2.15e9 gradients, eight AdamW tensors of every shape and four Muon
+    matrices, for two steps."""
+    w = W.vla_hybrid_bf16()
+    names = w.names
+    pick = ["vlm.model.layers.0.self_attn.q_proj.weight", "vlm.model.layers.3.mlp.gate_proj.weight",
+            "vlm.model.layers.27.mlp.down_proj.weight", "vlm.model.layers.13.input_layernorm.weight",
+            "vlm.model.norm.weight", "vlm.model.layers.27.post_attention_layernorm.weight",
+            "action_expert.layers.0.self_attn.q_proj.weight",
+            "action_expert.layers.5.self_attn.k_proj.weight",
+            "action_expert.layers.17.mlp.gate_proj.weight",
+            "action_expert.layers.9.mlp.down_proj.weight"]
+    sampled = {names.index(n) for n in pick}
+    _run_parity(w, "bf16", 2, sampled=sampled, backend="torch")

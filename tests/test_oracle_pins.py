@@ -281,7 +281,8 @@ def test_clip_coefficient_closed_forms():
     n = 464.0
     assert O.clip_coefficient(n, 1.0) * n == pytest.approx(n / (n + 1e-6), rel=1e-15)
     assert O.clip_coefficient(1e9, 0.0) == 1.0
-    assert math.isnan(O.clip_coefficient(float("nan"), 1.0)) or O.clip_coefficient(float("nan"), 1.0) == 1.0
+    assert math.isnan(O.clip_coefficient(float("nan"), 1.0))
+    assert O.clip_coefficient(float("inf"), 1.0) == 0.0
     assert O.HParams().max_grad_norm == 1.0
 
 
