@@ -27,7 +27,7 @@ constexpr int64_t kChunk = 16384;
 constexpr int kOrientTile = 64;
 
 // GEMM block tile (square) used for the work lists.  Must divide kNsPad.
-constexpr int kGemmTile = 128;
+constexpr int kGemmTile = 256;
 
 // Under the bf16 policy, matrices whose smaller side is below this run their
 // Newton-Schulz in fp32: for such thin matrices the bf16 rounding error is

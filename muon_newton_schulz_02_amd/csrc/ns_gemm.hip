@@ -134,12 +134,46 @@ __device__ __forceinline__ void update_run(const MuonMat& d, int row, int col, c
         if (dl) store16(dl, dv);
     } else {
         const int cnt = min(16, d.n - col);
-        for (int e = 0; e < cnt; ++e) {
-            const float dv = d.lr_eff * x[e];
-            p[e] = fmaf(p[e], d.decay, -dv);
-            if (dl) dl[e] = dv;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            if (e < cnt) {
+                const float dv = d.lr_eff * x[e];
+                p[e] = fmaf(p[e], d.decay, -dv);
+                if (dl) dl[e] = dv;
+            }
         }
     }
+}
+
+// Buffer resource of one operand: base address, extent in bytes (reads past
+// it return zero) and the raw 32-bit-element format word of gfx9 parts.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+    const int32_t n = bytes > 0x7fffffffLL ? 0x7fffffff : (int32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(Rsrc r, uint32_t voff, uint32_t soff) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return __builtin_bit_cast(uint4, v);
+}
+
+template <int VPT, int VP, int RPI>
+__device__ __forceinline__ void stage_load(uint4 (&st)[VPT], Rsrc rp, Rsrc rq, uint32_t voff_p,
+                                           uint32_t voff_q, uint32_t ldp, uint32_t ldq,
+                                           uint32_t koff) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        if (i < VP) st[i] = buf_load16(rp, voff_p, koff + (uint32_t)(i * RPI) * ldp);
+        else st[i] = buf_load16(rq, voff_q, koff + (uint32_t)((i - VP) * RPI) * ldq);
+    }
+}
+
+template <int VPT, int RPI, int ROWB>
+__device__ __forceinline__ void stage_store(const uint4 (&st)[VPT], char* lds, uint32_t lds_off) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) *reinterpret_cast<uint4*>(lds + i * RPI * ROWB + lds_off) = st[i];
 }
 
 template <typename T, int BM, int BN, int WM, int WN, int EPI>
@@ -164,24 +198,26 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_ns_gemm(
     const char* P;
     const char* Q;
     int64_t ldp, ldq;  // bytes
-    int K;
+    int K, K_rows_p, K_rows_q;
     if (EPI == EPI_GRAM) {
         P = Q = reinterpret_cast<const char*>(d.xb);
         ldp = ldq = (int64_t)d.C * sizeof(T);
         K = d.C;
+        K_rows_p = K_rows_q = d.R;
     } else if (EPI == EPI_POLY) {
         P = Q = reinterpret_cast<const char*>(d.a);
         ldp = ldq = (int64_t)d.R * sizeof(T);
         K = d.R;
+        K_rows_p = K_rows_q = d.R;
     } else {
         P = reinterpret_cast<const char*>(d.b);
         Q = reinterpret_cast<const char*>(d.xt[args.iter & 1]);
         ldp = ldq = (int64_t)d.R * sizeof(T);
         K = d.R;
+        K_rows_p = d.R;
+        K_rows_q = d.C;
     }
     const int m0 = tile.tm * BM, n0 = tile.tn * BN;
-    P += (int64_t)m0 * ldp;
-    Q += (int64_t)n0 * ldq;
     const int nk = K / KELEM;
 
     f32x16 acc[MI][NI];
@@ -192,49 +228,43 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_ns_gemm(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    uint4 stage_regs[VPT];
-    auto gload = [&](int s) {
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int v = tid + i * NT;
-            const int row = v >> 3, seg = v & 7;
-            const char* src = (i < VP) ? P + (int64_t)row * ldp : Q + (int64_t)(row - BM) * ldq;
-            stage_regs[i] = *reinterpret_cast<const uint4*>(src + (int64_t)s * 128 + seg * 16);
-        }
-    };
-    auto lstore = [&](int buf) {
-        char* base = smem + buf * STAGE;
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int v = tid + i * NT;
-            const int row = v >> 3, seg = v & 7;
-            *reinterpret_cast<uint4*>(base + row * ROWB + seg * 16) = stage_regs[i];
-        }
-    };
+    // Global -> register -> LDS staging, double-buffered in LDS.  Thread t
+    // moves 16-byte segment (t % 8) of rows t / 8 + RPI i (i < VPT) of the
+    // stacked [P rows; Q rows] stage: one buffer load per row block, with the
+    // per-thread offset in a VGPR and the row-block/stage offset in an SGPR.
+    constexpr int RPI = NT / 8;  // rows covered per i
+    const Rsrc rp = make_rsrc(P, (int64_t)(K_rows_p) * ldp);
+    const Rsrc rq = make_rsrc(Q, (int64_t)(K_rows_q) * ldq);
+    const uint32_t voff_p = (uint32_t)((m0 + (tid >> 3)) * ldp + (tid & 7) * 16);
+    const uint32_t voff_q = (uint32_t)((n0 + (tid >> 3)) * ldq + (tid & 7) * 16);
+    const uint32_t lds_off = (uint32_t)((tid >> 3) * ROWB + (tid & 7) * 16);
+    uint4 stage[VPT];
 
-    gload(0);
-    lstore(0);
+    stage_load<VPT, VP, RPI>(stage, rp, rq, voff_p, voff_q, (uint32_t)ldp, (uint32_t)ldq, 0);
+    stage_store<VPT, RPI, ROWB>(stage, smem, lds_off);
     __syncthreads();
+    const int arow = (wm * WM + (lane & 31)) * ROWB + (lane >> 5) * 16;
+    const int brow = (BM + wn * WN + (lane & 31)) * ROWB + (lane >> 5) * 16;
     for (int s = 0; s < nk; ++s) {
-        if (s + 1 < nk) gload(s + 1);
-        const char* As = smem + (s & 1) * STAGE;
-        const char* Bs = As + BM * ROWB;
+        if (s + 1 < nk)
+            stage_load<VPT, VP, RPI>(stage, rp, rq, voff_p, voff_q, (uint32_t)ldp, (uint32_t)ldq,
+                                     (uint32_t)(s + 1) * 128u);
+        const char* base = smem + (s & 1) * STAGE;
 #pragma unroll
         for (int kg = 0; kg < 4; ++kg) {
             uint4 af[MI], bfr[NI];
-            const int koff = kg * 32 + (lane >> 5) * 16;
 #pragma unroll
             for (int i = 0; i < MI; ++i)
-                af[i] = *reinterpret_cast<const uint4*>(As + (wm * WM + i * 32 + (lane & 31)) * ROWB + koff);
+                af[i] = *reinterpret_cast<const uint4*>(base + arow + i * 32 * ROWB + kg * 32);
 #pragma unroll
             for (int j = 0; j < NI; ++j)
-                bfr[j] = *reinterpret_cast<const uint4*>(Bs + (wn * WN + j * 32 + (lane & 31)) * ROWB + koff);
+                bfr[j] = *reinterpret_cast<const uint4*>(base + brow + j * 32 * ROWB + kg * 32);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < NI; ++j) acc[i][j] = Mma<T>::run(af[i], bfr[j], acc[i][j]);
         }
-        if (s + 1 < nk) lstore((s + 1) & 1);
+        if (s + 1 < nk) stage_store<VPT, RPI, ROWB>(stage, smem + ((s + 1) & 1) * STAGE, lds_off);
         __syncthreads();
     }
 
@@ -320,7 +350,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_ns_gemm(
 
 template <typename T, int EPI>
 int launch_t(const MuonMat* tab, const GemmTile* tiles, int64_t n, const NsArgs& a, hipStream_t st) {
-    constexpr int BM = 128, BN = 128, WM = 64, WN = 64;
+    constexpr int BM = 256, BN = 256, WM = 128, WN = 128;
     static_assert(BM == kGemmTile && BN == kGemmTile, "tile lists are built for kGemmTile");
     hipLaunchKernelGGL((k_ns_gemm<T, BM, BN, WM, WN, EPI>), dim3((unsigned)n),
                        dim3((BM / WM) * (BN / WN) * 64), 0, st, tab, tiles, a);
