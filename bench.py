@@ -90,8 +90,11 @@ def cpu_baseline(w, hp_overrides) -> dict:
     for k, v in hp_overrides.items():
         setattr(hp, k, v)
     names = w.names
-    ae = [i for i, n in enumerate(names) if n.startswith("action_expert.layers.0.")]
-    vlm = [i for i, n in enumerate(names) if n.startswith("vlm.model.layers.0.")]
+    k_ae, k_vlm = 4, 6   # sampled layers of each kind
+    ae = [i for i, n in enumerate(names)
+          if n.startswith("action_expert.layers.") and int(n.split(".")[2]) < k_ae]
+    vlm = [i for i, n in enumerate(names)
+           if n.startswith("vlm.model.layers.") and int(n.split(".")[3]) < k_vlm]
     n_ae_layers = len({n.split(".")[2] for n in names if n.startswith("action_expert.layers.")})
     n_vlm_layers = len({n.split(".")[3] for n in names if n.startswith("vlm.model.layers.")})
     train = [i for i, p in enumerate(w.params) if p.trainable]
@@ -116,7 +119,7 @@ def cpu_baseline(w, hp_overrides) -> dict:
 
     t_ae = timed(ae)
     t_vlm = timed(vlm)
-    est = t_ae * n_ae_layers + t_vlm * n_vlm_layers
+    est = t_ae * n_ae_layers / k_ae + t_vlm * n_vlm_layers / k_vlm
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -128,10 +131,12 @@ def cpu_baseline(w, hp_overrides) -> dict:
         "unit": "params/s",
         "cores": min(cores, threads),
         "kind": "oracle",
-        "sample": ("action_expert.layers.0 (7 Muon matrices, %.1f s) + vlm.model.layers.0 "
-                   "(9 AdamW tensors, %.1f s), %d params, scaled x%d / x%d layers to the "
-                   "whole table; NumPy fp64, BLAS threads for matmuls, elementwise "
-                   "single-threaded" % (t_ae, t_vlm, sample_params, n_ae_layers, n_vlm_layers)),
+        "sample": ("action_expert.layers.0-%d (%d Muon matrices, %.1f s) + "
+                   "vlm.model.layers.0-%d (%d AdamW tensors, %.1f s), %d params, scaled by "
+                   "layer count (%d and %d layers) to the whole table; NumPy fp64, BLAS "
+                   "threads for matmuls, elementwise single-threaded"
+                   % (k_ae - 1, len(ae), t_ae, k_vlm - 1, len(vlm), t_vlm, sample_params,
+                      n_ae_layers, n_vlm_layers)),
         "sample_seconds": t_ae + t_vlm,
     }
 
@@ -143,7 +148,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="vla_hybrid_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 times), to calibrate "
+                         "the FETCH_SIZE / WRITE_SIZE counters against known bytes")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(every matrix is held whole on one device); run with --gpus 1",
