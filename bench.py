@@ -148,6 +148,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="vla_hybrid_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--serial", action="store_true",
+                    help="run every kernel on one stream (no AdamW / Muon overlap)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes")
@@ -181,7 +183,7 @@ def main():
     hp_over = W.hparams_for(w)
     hp = M.muon_adamw_default_hparams(ns_precision=w.ns_precision, **hp_over)
     table = list(zip(w.names, w.shapes, w.trainable))
-    plan = M.muon_adamw_plan(table)
+    plan = M.muon_adamw_plan(table, overlap_groups=not args.serial)
     n = len(table)
     groups = [M.muon_adamw_plan_entry(plan, i)["group"] for i in range(n)]
     params, grads = [None] * n, [None] * n
@@ -261,7 +263,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "muon_params": n_muon, "adamw_params": n_adam,
                    "muon_matrices": len(muon_shapes), "ns_precision": w.ns_precision,
-                   "ns_steps": hp.muon_ns_steps, "parallelism": "single GPU"},
+                   "ns_steps": hp.muon_ns_steps, "parallelism": "single GPU",
+                   "streams": "serial" if args.serial else "adamw overlapped with muon"},
         "phase_ms": mean,
         "ns_tflops": ns_tflops,
         "ns_mfma_frac": ns_tflops / ns_peak,

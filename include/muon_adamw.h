@@ -69,9 +69,16 @@ typedef struct {
     int32_t        trainable;
 } ma_param_desc;
 
+/* `overlap_groups` = 1 lets muon_adamw_step run the AdamW group on a
+ * library-owned second stream of the same device (default priority), joined
+ * back into the caller's stream before the step's work ends, so the
+ * HBM-bound AdamW kernel overlaps the MFMA-bound Muon work; 0 runs every
+ * kernel on the caller's stream in order.  A NULL opts means mode
+ * MA_MODE_MUON_ADAMW, moonlight 0.2, overlap 1. */
 typedef struct {
     int32_t mode;                  /* MA_MODE_*                            */
     double  moonlight_coefficient; /* 0.2 on the page                      */
+    int32_t overlap_groups;        /* 1: AdamW concurrent with Muon        */
 } ma_plan_opts;
 
 typedef struct ma_plan ma_plan;    /* opaque, immutable once built         */
@@ -207,9 +214,11 @@ int muon_adamw_step(const ma_plan* plan,
 /* muon_adamw_step, plus measurement: phase_events (nullable) is an array of
  * MA_PROFILE_EVENTS hipEvent_t created by the caller, recorded on `stream`
  * at [0] the start of the step, [1] after the clip norm, [2] after the AdamW
- * group, [3] after the Muon momentum/normalise pass, [4] after the last
- * Newton-Schulz launch.  Elapsed times between them time each phase on the
- * stream the kernels run on.  Same errors as muon_adamw_step. */
+ * group, [3] after the Muon momentum/normalise pass, [4] at the end of the
+ * step.  Each event is recorded on the stream its phase's kernels run on (with
+ * overlap_groups, [2] is on the side stream, so [1]->[2] is the AdamW kernel
+ * and [3]->[4] covers Newton-Schulz plus any wait for AdamW).  Same errors as
+ * muon_adamw_step. */
 int muon_adamw_step_profiled(const ma_plan* plan,
                              float* const* params,
                              const float* const* grads,

@@ -92,8 +92,9 @@ class Plan:
 
 def muon_adamw_plan(table: Sequence[Tuple[str, Sequence[int], bool]],
                     mode: int = MA_MODE_MUON_ADAMW,
-                    moonlight_coefficient: float = 0.2) -> Plan:
-    """Route a parameter table [(name, shape, trainable), ...] (host only)."""
+                    moonlight_coefficient: float = 0.2, overlap_groups: bool = True) -> Plan:
+    """Route a parameter table [(name, shape, trainable), ...] (host only).
+    overlap_groups: run the AdamW group concurrently with the Muon group."""
     n = len(table)
     descs = (_abi.ma_param_desc * max(n, 1))()
     keep = []
@@ -105,7 +106,7 @@ def muon_adamw_plan(table: Sequence[Tuple[str, Sequence[int], bool]],
         descs[i].ndim = len(shape)
         descs[i].shape = C.cast(sh, C.POINTER(C.c_int64))
         descs[i].trainable = 1 if trainable else 0
-    opts = _abi.ma_plan_opts(int(mode), float(moonlight_coefficient))
+    opts = _abi.ma_plan_opts(int(mode), float(moonlight_coefficient), 1 if overlap_groups else 0)
     out = C.c_void_p()
     _check(_abi.load().muon_adamw_plan(descs, n, C.byref(opts), C.byref(out)), "muon_adamw_plan")
     return Plan(out.value, [t[0] for t in table], [tuple(t[1]) for t in table])

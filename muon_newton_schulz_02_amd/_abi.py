@@ -33,7 +33,8 @@ class ma_param_desc(C.Structure):
 
 
 class ma_plan_opts(C.Structure):
-    _fields_ = [("mode", C.c_int32), ("moonlight_coefficient", C.c_double)]
+    _fields_ = [("mode", C.c_int32), ("moonlight_coefficient", C.c_double),
+                ("overlap_groups", C.c_int32)]
 
 
 class ma_plan_entry(C.Structure):

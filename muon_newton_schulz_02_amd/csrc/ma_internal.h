@@ -35,6 +35,10 @@ constexpr int kGemmTile = 256;
 // their share of the work is negligible.
 constexpr int64_t kBf16MinRows = 16;
 
+// XCDs of an MI355X: consecutive workgroups of a launch are dispatched to
+// XCDs round-robin, and each XCD has its own L2.
+constexpr int kXcds = 8;
+
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
 
@@ -130,7 +134,17 @@ struct ma_plan {
     ma::Layout layout[2];                                        // per NS precision
     std::string dump;
 
-    // step-time staging (pinned host ring); guarded by mu
+    int32_t overlap = 1;    // AdamW on a second stream, concurrent with Muon
+
+    // step-time staging (pinned host ring) and the per-device side stream of
+    // the overlapped AdamW group; guarded by mu
+    struct Side {
+        int device;
+        void* stream;
+        void* ev_fork;
+        void* ev_join;
+    };
+    mutable std::vector<Side> side;
     mutable std::mutex mu;
     mutable void* staging[2] = {nullptr, nullptr};
     mutable size_t staging_bytes[2] = {0, 0};

@@ -115,6 +115,31 @@ __device__ __forceinline__ void load16(const __bf16* src, float* v) {
     }
 }
 
+// Make this wave's LDS writes visible to its other lanes before they read.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void lds_read16(const float* src, float* v) {
+    const float4* s4 = reinterpret_cast<const float4*>(src);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float4 t = s4[q];
+        v[4 * q] = t.x;
+        v[4 * q + 1] = t.y;
+        v[4 * q + 2] = t.z;
+        v[4 * q + 3] = t.w;
+    }
+}
+
+__device__ __forceinline__ void lds_write16(float* dst, const float* v) {
+    float4* d4 = reinterpret_cast<float4*>(dst);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d4[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+}
+
 // Stored-orientation update of 16 consecutive elements of parameter row
 // `row`, starting at column `col`: p = p * decay - lr_eff * x (and the
 // optional delta = lr_eff * x).
@@ -176,6 +201,16 @@ __device__ __forceinline__ void stage_store(const uint4 (&st)[VPT], char* lds, u
     for (int i = 0; i < VPT; ++i) *reinterpret_cast<uint4*>(lds + i * RPI * ROWB + lds_off) = st[i];
 }
 
+// One k-group's operand fragments of a wave: MI rows-of-32 of P, NI of Q.
+template <int MI, int NI, int ROWB>
+__device__ __forceinline__ void lds_frags(uint4 (&af)[MI], uint4 (&bf)[NI], const char* a,
+                                          const char* b, int koff) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) af[i] = *reinterpret_cast<const uint4*>(a + i * 32 * ROWB + koff);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) bf[j] = *reinterpret_cast<const uint4*>(b + j * 32 * ROWB + koff);
+}
+
 template <typename T, int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_ns_gemm(
     const MuonMat* __restrict__ tab, const GemmTile* __restrict__ tiles, NsArgs args) {
@@ -191,6 +226,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_ns_gemm(
     __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
     const GemmTile tile = tiles[blockIdx.x];
+    if (tile.mat < 0) return;  // padding of a shorter per-XCD list
     const MuonMat& d = tab[tile.mat];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -250,26 +286,35 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_ns_gemm(
             stage_load<VPT, VP, RPI>(stage, rp, rq, voff_p, voff_q, (uint32_t)ldp, (uint32_t)ldq,
                                      (uint32_t)(s + 1) * 128u);
         const char* base = smem + (s & 1) * STAGE;
+        // fragments of k-group kg+1 are read from LDS while the MFMAs of
+        // k-group kg run (two register sets), so LDS latency stays hidden
+        uint4 af[2][MI], bfr[2][NI];
+        lds_frags<MI, NI, ROWB>(af[0], bfr[0], base + arow, base + brow, 0);
 #pragma unroll
         for (int kg = 0; kg < 4; ++kg) {
-            uint4 af[MI], bfr[NI];
+            if (kg + 1 < 4)
+                lds_frags<MI, NI, ROWB>(af[(kg + 1) & 1], bfr[(kg + 1) & 1], base + arow,
+                                        base + brow, (kg + 1) * 32);
+            // keep the prefetch above this k-group's MFMAs (the scheduler
+            // would otherwise sink the reads next to their uses)
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
-                af[i] = *reinterpret_cast<const uint4*>(base + arow + i * 32 * ROWB + kg * 32);
 #pragma unroll
-            for (int j = 0; j < NI; ++j)
-                bfr[j] = *reinterpret_cast<const uint4*>(base + brow + j * 32 * ROWB + kg * 32);
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j) acc[i][j] = Mma<T>::run(af[i], bfr[j], acc[i][j]);
+                for (int j = 0; j < NI; ++j)
+                    acc[i][j] = Mma<T>::run(af[kg & 1][i], bfr[kg & 1][j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (s + 1 < nk) stage_store<VPT, RPI, ROWB>(stage, smem + ((s + 1) & 1) * STAGE, lds_off);
         __syncthreads();
     }
 
-    // ---- epilogue: each wave stages one 32x32 block at a time in LDS ----
-    float* S = reinterpret_cast<float*>(smem) + wave * (32 * 33);
+    // ---- epilogue: each wave stages its 32x32 accumulator blocks in its own
+    // LDS region (wave-level synchronisation only, no block barriers) and
+    // moves them as 16-element runs: row runs for row-major outputs, column
+    // runs for the transposed outputs ----
+    constexpr int SLD = 36;  // staging row stride (floats): 16-byte aligned runs
+    float* S = reinterpret_cast<float*>(smem) + wave * (32 * SLD);
     const bool mirror = (EPI == EPI_GRAM || EPI == EPI_POLY) && tile.tm != tile.tn;
     const bool need_cols = mirror || EPI == EPI_XUPD || (EPI == EPI_FINAL && d.transposed);
     T* out_direct = nullptr;
@@ -281,6 +326,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_ns_gemm(
         out_direct = reinterpret_cast<T*>(d.b);
         ld_direct = d.R;
     }
+    const int rrow = lane >> 1, rc0 = (lane & 1) * 16;   // row run of this lane
+    const int ccol = lane & 31, cr0 = (lane >> 5) * 16;  // column run of this lane
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -290,17 +337,15 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_ns_gemm(
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                S[row * 33 + (lane & 31)] = acc[i][j][r];
+                S[row * SLD + (lane & 31)] = acc[i][j][r];
             }
-            __syncthreads();
+            wave_lds_sync();
             const int bi = m0 + wm * WM + i * 32;  // block origin in the output
             const int bj = n0 + wn * WN + j * 32;
             {
-                const int row = lane >> 1, c0 = (lane & 1) * 16;
                 float v[16];
-#pragma unroll
-                for (int e = 0; e < 16; ++e) v[e] = S[row * 33 + c0 + e];
-                const int gi = bi + row, gj = bj + c0;
+                lds_read16(S + rrow * SLD + rc0, v);
+                const int gi = bi + rrow, gj = bj + rc0;
                 if (EPI == EPI_GRAM) {
                     store16(out_direct + (int64_t)gi * ld_direct + gj, v);
                 } else if (EPI == EPI_POLY) {
@@ -322,18 +367,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_ns_gemm(
                         update_run(d, gi, gj, v);
                     }
                 }
-                if (need_cols) {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) S[row * 33 + c0 + e] = v[e];
-                }
+                if (need_cols) lds_write16(S + rrow * SLD + rc0, v);
             }
-            __syncthreads();
+            wave_lds_sync();
             if (need_cols) {
-                const int col = lane >> 1, r0 = (lane & 1) * 16;
                 float v[16];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) v[e] = S[(r0 + e) * 33 + col];
-                const int tr = bj + col, tc = bi + r0;  // row / first column in the transposed view
+                for (int e = 0; e < 16; ++e) v[e] = S[(cr0 + e) * SLD + ccol];
+                const int tr = bj + ccol, tc = bi + cr0;  // row / first column in the transposed view
                 if (EPI == EPI_GRAM || EPI == EPI_POLY) {
                     store16(out_direct + (int64_t)tr * ld_direct + tc, v);
                 } else if (EPI == EPI_XUPD) {
@@ -342,7 +383,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_ns_gemm(
                 } else {
                     update_run(d, tr, tc, v);
                 }
-                __syncthreads();
+                wave_lds_sync();
             }
         }
     }

@@ -124,12 +124,56 @@ std::string make_dump(const ma_plan& p) {
     return out;
 }
 
-// Tiles of one NS phase, ordered so the longest reductions start first
-// (largest K first; ties keep matrix order), which keeps the tail of a
-// grouped launch short.
-void sort_tiles(std::vector<GemmTile>& t) {
-    std::stable_sort(t.begin(), t.end(),
-                     [](const GemmTile& x, const GemmTile& y) { return x.k > y.k; });
+// Order the tiles of one grouped NS launch for the chip's XCDs.  Workgroup b
+// is dispatched to XCD b % kXcds, and every XCD has its own L2.  Tiles that
+// share operand blocks form a unit -- a whole matrix, or, for a matrix
+// heavier than a sixteenth of the launch, one row block of it.  Units are
+// placed longest first onto the least-loaded XCD; each XCD's list keeps its
+// units contiguous, so the tiles an XCD runs together share operands in its
+// L2; the lists are interleaved so that b % kXcds selects the list.  Shorter
+// lists are padded with empty tiles (mat = -1) that exit at once.
+void schedule_tiles(std::vector<GemmTile>& t) {
+    if (t.empty()) return;
+    double total = 0.0;
+    for (const auto& x : t) total += x.k;
+    std::map<int32_t, std::vector<GemmTile>> by_mat;
+    for (const auto& x : t) by_mat[x.mat].push_back(x);
+    struct Unit {
+        double cost = 0.0;
+        std::vector<GemmTile> tiles;
+    };
+    std::vector<Unit> units;
+    for (auto& kv : by_mat) {
+        double c = 0.0;
+        for (const auto& x : kv.second) c += x.k;
+        if (c * 16.0 <= total) {
+            units.push_back(Unit{c, kv.second});
+        } else {
+            std::map<int32_t, Unit> rows;
+            for (const auto& x : kv.second) {
+                rows[x.tm].cost += x.k;
+                rows[x.tm].tiles.push_back(x);
+            }
+            for (auto& r : rows) units.push_back(std::move(r.second));
+        }
+    }
+    std::stable_sort(units.begin(), units.end(),
+                     [](const Unit& a, const Unit& b) { return a.cost > b.cost; });
+    std::vector<std::vector<GemmTile>> lists(kXcds);
+    double load[kXcds] = {};
+    for (const auto& u : units) {
+        int best = 0;
+        for (int x = 1; x < kXcds; ++x)
+            if (load[x] < load[best]) best = x;
+        lists[best].insert(lists[best].end(), u.tiles.begin(), u.tiles.end());
+        load[best] += u.cost;
+    }
+    size_t longest = 0;
+    for (const auto& l : lists) longest = std::max(longest, l.size());
+    t.clear();
+    for (size_t j = 0; j < longest; ++j)
+        for (int x = 0; x < kXcds; ++x)
+            t.push_back(j < lists[x].size() ? lists[x][j] : GemmTile{-1, 0, 0, 0});
 }
 
 void build_tables(ma_plan* p) {
@@ -186,9 +230,9 @@ void build_layout(ma_plan* p, int32_t precision) {
             for (int32_t j = 0; j < TC; ++j) L.g3[grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R});
     }
     for (int g = 0; g < 2; ++g) {
-        sort_tiles(L.g1[g]);
-        sort_tiles(L.g2[g]);
-        sort_tiles(L.g3[g]);
+        schedule_tiles(L.g1[g]);
+        schedule_tiles(L.g2[g]);
+        schedule_tiles(L.g3[g]);
     }
     size_t off = 0;
     L.tables_off = off;
@@ -284,6 +328,11 @@ int muon_adamw_plan(const ma_param_desc* table, int32_t n, const ma_plan_opts* o
     }
     int32_t mode = opts ? opts->mode : MA_MODE_MUON_ADAMW;
     double moon = opts ? opts->moonlight_coefficient : 0.2;
+    int32_t overlap = opts ? opts->overlap_groups : 1;
+    if (overlap != 0 && overlap != 1) {
+        set_error("muon_adamw_plan: overlap_groups must be 0 or 1");
+        return MA_ERR_INVALID_ARG;
+    }
     if (mode != MA_MODE_MUON_ADAMW && mode != MA_MODE_ADAMW) {
         set_error("muon_adamw_plan: unknown mode %d", mode);
         return MA_ERR_INVALID_ARG;
@@ -336,6 +385,7 @@ int muon_adamw_plan(const ma_param_desc* table, int32_t n, const ma_plan_opts* o
     }
     p->mode = mode;
     p->moonlight = moon;
+    p->overlap = overlap;
     p->entries.resize(n);
     std::map<std::pair<int64_t, int64_t>, int32_t> bucket_of;
     for (int32_t i = 0; i < n; ++i) {

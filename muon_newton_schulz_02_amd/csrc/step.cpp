@@ -61,6 +61,35 @@ int get_staging(const ma_plan* plan, size_t bytes, void** out, void** event) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// The side stream and fork/join events of the current device (created on
+// first use; default priority, non-blocking with respect to the null stream).
+int get_side(const ma_plan* plan, ma_plan::Side** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    for (auto& s : plan->side) {
+        if (s.device == dev) {
+            *out = &s;
+            return MA_OK;
+        }
+    }
+    ma_plan::Side s{dev, nullptr, nullptr, nullptr};
+    hipStream_t st;
+    e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail("hipStreamCreate (side)", e);
+    s.stream = st;
+    hipEvent_t a, b;
+    e = hipEventCreateWithFlags(&a, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail("hipEventCreate (fork)", e);
+    s.ev_fork = a;
+    e = hipEventCreateWithFlags(&b, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail("hipEventCreate (join)", e);
+    s.ev_join = b;
+    plan->side.push_back(s);
+    *out = &plan->side.back();
+    return MA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -284,9 +313,29 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
                                grad_norm_out, stream);
     if (err) return hip_fail("clip finalize", err);
     if ((err = mark(1))) return hip_fail("phase event", err);
-    err = launch_adamw(d_adam, n_adam, plan->n_adam_chunks, coef, sc, stream);
-    if (err) return hip_fail("adamw", err);
-    if ((err = mark(2))) return hip_fail("phase event", err);
+    // AdamW: on the caller's stream, or forked to the side stream so it runs
+    // concurrently with the Muon group and joined back at the end
+    ma_plan::Side* side = nullptr;
+    if (plan->overlap && n_adam > 0 && n_muon > 0) {
+        int rs = get_side(plan, &side);
+        if (rs != MA_OK) return rs;
+        hipStream_t ss = (hipStream_t)side->stream;
+        if ((e = hipEventRecord((hipEvent_t)side->ev_fork, st)) != hipSuccess)
+            return hip_fail("hipEventRecord (fork)", e);
+        if ((e = hipStreamWaitEvent(ss, (hipEvent_t)side->ev_fork, 0)) != hipSuccess)
+            return hip_fail("hipStreamWaitEvent (fork)", e);
+        err = launch_adamw(d_adam, n_adam, plan->n_adam_chunks, coef, sc, ss);
+        if (err) return hip_fail("adamw", err);
+        if (phase_events && phase_events[2] &&
+            (e = hipEventRecord((hipEvent_t)phase_events[2], ss)) != hipSuccess)
+            return hip_fail("phase event", e);
+        if ((e = hipEventRecord((hipEvent_t)side->ev_join, ss)) != hipSuccess)
+            return hip_fail("hipEventRecord (join)", e);
+    } else {
+        err = launch_adamw(d_adam, n_adam, plan->n_adam_chunks, coef, sc, stream);
+        if (err) return hip_fail("adamw", err);
+        if ((err = mark(2))) return hip_fail("phase event", err);
+    }
     if (n_muon > 0) {
         err = launch_muon_momentum(d_muon, n_muon, plan->n_muon_chunks, coef, sc, muon_partials,
                                    stream);
@@ -312,6 +361,8 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     } else if ((err = mark(3))) {
         return hip_fail("phase event", err);
     }
+    if (side && (e = hipStreamWaitEvent(st, (hipEvent_t)side->ev_join, 0)) != hipSuccess)
+        return hip_fail("hipStreamWaitEvent (join)", e);
     if ((err = mark(4))) return hip_fail("phase event", err);
     state->step = t;
     clear_error();
@@ -320,6 +371,12 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
 
 void muon_adamw_plan_free(ma_plan* plan) {
     if (!plan) return;
+    for (auto& sd : plan->side) {
+        (void)hipStreamSynchronize((hipStream_t)sd.stream);
+        (void)hipEventDestroy((hipEvent_t)sd.ev_fork);
+        (void)hipEventDestroy((hipEvent_t)sd.ev_join);
+        (void)hipStreamDestroy((hipStream_t)sd.stream);
+    }
     for (int k = 0; k < 2; ++k) {
         if (plan->staging_event[k]) {
             (void)hipEventSynchronize((hipEvent_t)plan->staging_event[k]);

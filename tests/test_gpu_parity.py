@@ -241,3 +241,24 @@ def test_vla_hybrid_full_size_sampled():
             "action_expert.layers.9.mlp.down_proj.weight"]
     sampled = {names.index(n) for n in pick}
     _run_parity(w, "bf16", 2, sampled=sampled, backend="torch")
+
+
+def test_overlapped_groups_match_serial_bitwise():
+    """AdamW on the side stream (concurrent with the Muon group) gives the
+    same bits as the serial order on one stream, over two steps."""
+    w = _ragged_workload()
+    w.params.append(W.ParamSpec("vlm.model.layers.0.mlp.up_proj.weight", (512, 300)))
+    hp = H.oracle_hparams(w)
+    outs = []
+    for overlap in (False, True):
+        run = H.setup_gpu(M, torch, w, hp, "bf16")
+        run.plan = M.muon_adamw_plan(list(zip(w.names, w.shapes, w.trainable)),
+                                     overlap_groups=overlap)
+        for t in (1, 2):
+            H.fill_grads(run, torch, t)
+            H.say("overlap=%s step %d" % (overlap, t))
+            H.gpu_step(M, torch, run)
+        outs.append([H.host(x) for x in run.params + run.deltas + run.state.muon_momentum +
+                     run.state.adam_m + run.state.adam_v + [run.norm_out] if x is not None])
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
