@@ -81,6 +81,8 @@ def _run_parity(w, ns_precision, steps, hp=None, sampled=None, backend="numpy",
                 op[i], om[i], ov[i] = p, m, v
             else:
                 m_, n_ = w.params[i].shape
+                if m_ * n_ >= (1 << 24):
+                    H.say("  oracle NS of %s %dx%d" % (w.names[i], m_, n_))
                 scale = O.lr_shape_scale(m_, n_, hp.moonlight_coefficient)
                 p, buf, delta = O.muon_matrix_update(op[i], grad, obuf[i], coef, hp, scale)
                 gbuf = H.host(run.state.muon_momentum[i])
@@ -262,3 +264,36 @@ def test_overlapped_groups_match_serial_bitwise():
                      run.state.adam_m + run.state.adam_v + [run.norm_out] if x is not None])
     for a, b in zip(*outs):
         np.testing.assert_array_equal(a, b)
+
+
+def test_vla_hybrid_fp32ns_full_size_sampled():
+    """The full hybrid parameter set with the Newton-Schulz products in fp32
+    (true fp32 MFMA): delta relative error <= 1e-4 per matrix and step, on
+    four Muon matrices of every shape and four AdamW tensors, two steps."""
+    w = W.vla_hybrid_fp32ns()
+    names = w.names
+    pick = ["vlm.model.layers.1.mlp.down_proj.weight", "vlm.model.layers.20.input_layernorm.weight",
+            "vlm.model.norm.weight", "vlm.model.layers.7.self_attn.o_proj.weight",
+            "action_expert.layers.2.self_attn.o_proj.weight",
+            "action_expert.layers.11.self_attn.v_proj.weight",
+            "action_expert.layers.4.mlp.up_proj.weight",
+            "action_expert.layers.16.mlp.down_proj.weight"]
+    sampled = {names.index(n) for n in pick}
+    _run_parity(w, "fp32", 2, sampled=sampled, backend="torch")
+
+
+def test_ragged_stress_noclip_full_size():
+    """Large and ragged matrices in one grouped call, clip off so the rank-8
+    spike (entry std 100) reaches Newton-Schulz ill-conditioned: every one of
+    the 68 matrices (8192^2, 4096x14336, 14336x4096, 128x8192, 64 x 64x256)
+    compared with the oracle after the first step, over preloaded momentum."""
+    w = W.ragged_stress_bf16(clip=False)
+    _run_parity(w, "bf16", 1, backend="torch")
+
+
+def test_ragged_stress_clip_full_size_sampled():
+    """The same workload with the clip on (it triggers: the spike makes the
+    norm ~1e5), three steps, on the tall and wide 4096/14336 pair, the
+    128x8192 matrix and four of the 64x256 ones."""
+    w = W.ragged_stress_bf16(clip=True)
+    _run_parity(w, "bf16", w.steps, sampled={1, 2, 3, 4, 30, 50, 67}, backend="torch")
