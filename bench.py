@@ -66,6 +66,30 @@ class HipEvents:
             self.hip.hipEventDestroy(C.c_void_p(e))
 
 
+KERNEL_SOURCES = {
+    "k_adamw": os.path.join(HERE, "muon_newton_schulz_02_amd", "csrc", "elementwise.hip"),
+    "k_ns_gemm": os.path.join(HERE, "muon_newton_schulz_02_amd", "csrc", "ns_gemm.hip"),
+}
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None when
+    there is none or the kernel's source changed since it was taken."""
+    import hashlib
+    path = os.path.join(HERE, "profiles", "%s.md" % workload)
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(KERNEL_SOURCES[kernel], "rb").read()).hexdigest()[:16]
+    for line in open(path):
+        if not line.startswith("traffic:"):
+            continue
+        f = dict(kv.split("=", 1) for kv in line.split()[1:])
+        if f.get("kernel") == kernel and f.get("workload") == workload:
+            return float(f["bytes_per_launch"]) if f.get("source_sha256") == sha else None
+    return None
+
+
 def ns_flops(shapes, ns_steps: int) -> float:
     """Dense algorithmic flops of NS: per step and matrix (r <= c) the Gram
     X X^T (2 r^2 c), the square A A (2 r^3) and B X (2 r^2 c)."""
@@ -148,8 +172,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="vla_hybrid_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--serial", action="store_true",
-                    help="run every kernel on one stream (no AdamW / Muon overlap)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="run the AdamW group on a second stream, concurrent with the Muon group")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes")
@@ -183,7 +207,7 @@ def main():
     hp_over = W.hparams_for(w)
     hp = M.muon_adamw_default_hparams(ns_precision=w.ns_precision, **hp_over)
     table = list(zip(w.names, w.shapes, w.trainable))
-    plan = M.muon_adamw_plan(table, overlap_groups=not args.serial)
+    plan = M.muon_adamw_plan(table, overlap_groups=args.overlap)
     n = len(table)
     groups = [M.muon_adamw_plan_entry(plan, i)["group"] for i in range(n)]
     params, grads = [None] * n, [None] * n
@@ -243,7 +267,8 @@ def main():
     if n_adam > 0 and mean["adamw"] >= mean["newton_schulz"]:
         roofline = {"kernel": "k_adamw", "bound": "hbm", "achieved": adam_gbps,
                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": adam_gbps / PEAK_HBM_GBPS,
-                    "traffic": None}
+                    "traffic": measured_traffic("k_adamw", w.name),
+                    "algorithmic_bytes": adam_bytes}
     else:
         roofline = {"kernel": "k_ns_gemm (5 steps x 3 launches)", "bound": "mfma",
                     "achieved": ns_tflops, "peak": ns_peak, "unit": "TFLOP/s",
@@ -264,7 +289,7 @@ def main():
         "config": {"workload": w.name, "muon_params": n_muon, "adamw_params": n_adam,
                    "muon_matrices": len(muon_shapes), "ns_precision": w.ns_precision,
                    "ns_steps": hp.muon_ns_steps, "parallelism": "single GPU",
-                   "streams": "serial" if args.serial else "adamw overlapped with muon"},
+                   "streams": "adamw overlapped with muon" if args.overlap else "one stream"},
         "phase_ms": mean,
         "ns_tflops": ns_tflops,
         "ns_mfma_frac": ns_tflops / ns_peak,

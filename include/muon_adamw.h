@@ -73,8 +73,10 @@ typedef struct {
  * library-owned second stream of the same device (default priority), joined
  * back into the caller's stream before the step's work ends, so the
  * HBM-bound AdamW kernel overlaps the MFMA-bound Muon work; 0 runs every
- * kernel on the caller's stream in order.  A NULL opts means mode
- * MA_MODE_MUON_ADAMW, moonlight 0.2, overlap 1. */
+ * kernel on the caller's stream in order (the default: on MI355X both
+ * groups are bound by HBM bandwidth, and running them concurrently measured
+ * no faster).  A NULL opts means mode MA_MODE_MUON_ADAMW, moonlight 0.2,
+ * overlap 0. */
 typedef struct {
     int32_t mode;                  /* MA_MODE_*                            */
     double  moonlight_coefficient; /* 0.2 on the page                      */

@@ -92,7 +92,7 @@ class Plan:
 
 def muon_adamw_plan(table: Sequence[Tuple[str, Sequence[int], bool]],
                     mode: int = MA_MODE_MUON_ADAMW,
-                    moonlight_coefficient: float = 0.2, overlap_groups: bool = True) -> Plan:
+                    moonlight_coefficient: float = 0.2, overlap_groups: bool = False) -> Plan:
     """Route a parameter table [(name, shape, trainable), ...] (host only).
     overlap_groups: run the AdamW group concurrently with the Muon group."""
     n = len(table)

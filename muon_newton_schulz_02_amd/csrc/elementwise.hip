@@ -157,23 +157,38 @@ __global__ __launch_bounds__(kThreads) void k_adamw(const AdamTensor* __restrict
         const f4* g4 = reinterpret_cast<const f4*>(g);
         f4* m4 = reinterpret_cast<f4*>(m);
         f4* v4 = reinterpret_cast<f4*>(v);
-#pragma unroll 2
-        for (int i = threadIdx.x; i < kChunk / 4; i += kThreads) {
-            f4 pp = __builtin_nontemporal_load(p4 + i);
-            const f4 gg = __builtin_nontemporal_load(g4 + i);
-            f4 mm = __builtin_nontemporal_load(m4 + i);
-            f4 vv = __builtin_nontemporal_load(v4 + i);
+        // four 16-byte vectors of each of the four streams in flight per
+        // thread before any arithmetic (the chunk is 16 of them per thread)
+        constexpr int U = 4;
+        static_assert(kChunk / 4 % (kThreads * U) == 0, "chunk split");
+        for (int i0 = threadIdx.x; i0 < kChunk / 4; i0 += kThreads * U) {
+            f4 pp[U], gg[U], mm[U], vv[U];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float pq = pp[q], mq = mm[q], vq = vv[q];
-                adam_elem(pq, gg[q], mq, vq, coef, a);
-                pp[q] = pq;
-                mm[q] = mq;
-                vv[q] = vq;
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + u * kThreads;
+                pp[u] = __builtin_nontemporal_load(p4 + i);
+                gg[u] = __builtin_nontemporal_load(g4 + i);
+                mm[u] = __builtin_nontemporal_load(m4 + i);
+                vv[u] = __builtin_nontemporal_load(v4 + i);
             }
-            __builtin_nontemporal_store(pp, p4 + i);
-            __builtin_nontemporal_store(mm, m4 + i);
-            __builtin_nontemporal_store(vv, v4 + i);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float pq = pp[u][q], mq = mm[u][q], vq = vv[u][q];
+                    adam_elem(pq, gg[u][q], mq, vq, coef, a);
+                    pp[u][q] = pq;
+                    mm[u][q] = mq;
+                    vv[u][q] = vq;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + u * kThreads;
+                __builtin_nontemporal_store(pp[u], p4 + i);
+                __builtin_nontemporal_store(mm[u], m4 + i);
+                __builtin_nontemporal_store(vv[u], v4 + i);
+            }
         }
     } else {
         for (int64_t i = threadIdx.x; i < len; i += kThreads) {

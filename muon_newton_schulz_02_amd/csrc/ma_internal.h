@@ -134,7 +134,7 @@ struct ma_plan {
     ma::Layout layout[2];                                        // per NS precision
     std::string dump;
 
-    int32_t overlap = 1;    // AdamW on a second stream, concurrent with Muon
+    int32_t overlap = 0;    // 1: AdamW on a second stream, concurrent with Muon
 
     // step-time staging (pinned host ring) and the per-device side stream of
     // the overlapped AdamW group; guarded by mu

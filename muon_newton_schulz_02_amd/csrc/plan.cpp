@@ -328,7 +328,7 @@ int muon_adamw_plan(const ma_param_desc* table, int32_t n, const ma_plan_opts* o
     }
     int32_t mode = opts ? opts->mode : MA_MODE_MUON_ADAMW;
     double moon = opts ? opts->moonlight_coefficient : 0.2;
-    int32_t overlap = opts ? opts->overlap_groups : 1;
+    int32_t overlap = opts ? opts->overlap_groups : 0;
     if (overlap != 0 && overlap != 1) {
         set_error("muon_adamw_plan: overlap_groups must be 0 or 1");
         return MA_ERR_INVALID_ARG;
