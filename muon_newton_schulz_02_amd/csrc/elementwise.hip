@@ -139,6 +139,7 @@ __device__ __forceinline__ void adam_elem(float& p, float g, float& m, float& v,
     p = fmaf(-a.step_size, m / denom, p);
 }
 
+template <int U>
 __global__ __launch_bounds__(kThreads) void k_adamw(const AdamTensor* __restrict__ tab, int n_tab,
                                                     const float* __restrict__ coef_ptr,
                                                     AdamArgs a) {
@@ -157,9 +158,8 @@ __global__ __launch_bounds__(kThreads) void k_adamw(const AdamTensor* __restrict
         const f4* g4 = reinterpret_cast<const f4*>(g);
         f4* m4 = reinterpret_cast<f4*>(m);
         f4* v4 = reinterpret_cast<f4*>(v);
-        // four 16-byte vectors of each of the four streams in flight per
-        // thread before any arithmetic (the chunk is 16 of them per thread)
-        constexpr int U = 4;
+        // U 16-byte vectors of each of the four streams in flight per thread
+        // before any arithmetic (the chunk is 16 of them per thread)
         static_assert(kChunk / 4 % (kThreads * U) == 0, "chunk split");
         for (int i0 = threadIdx.x; i0 < kChunk / 4; i0 += kThreads * U) {
             f4 pp[U], gg[U], mm[U], vv[U];
@@ -281,34 +281,40 @@ __global__ __launch_bounds__(256) void k_muon_scale(const MuonMat* __restrict__ 
 // Tile (ti, tj) of the canonical padded R x C operand.  Canonical (i, j) is
 // stored (i, j), or stored (j, i) for a transposed matrix.  Values outside the
 // true r x c are zero.
-template <typename T>
-__device__ __forceinline__ T to_operand(float x);
-template <>
-__device__ __forceinline__ float to_operand<float>(float x) { return x; }
-template <>
-__device__ __forceinline__ __bf16 to_operand<__bf16>(float x) { return (__bf16)x; }
-
-template <typename T>
-__device__ __forceinline__ void write_operands(const MuonMat& d, const float (*tile)[kOrientTile + 1],
-                                               int i0, int j0) {
+// bf16 operands: X as a hi / lo pair of row-major bf16 matrices (step-0
+// buffers), hi = RNE(x), lo = RNE(x - hi).
+__device__ __forceinline__ void write_operands_bf16(const MuonMat& d,
+                                                    const float (*tile)[kOrientTile + 1], int i0,
+                                                    int j0) {
     constexpr int TS = kOrientTile;
-    float* x32 = reinterpret_cast<float*>(d.x32);
-    T* xb = reinterpret_cast<T*>(d.xb);
-    T* xt = reinterpret_cast<T*>(d.xt[0]);
-    const bool write_xb = d.xb != d.x32;
-    // canonical rows i0.., cols j0..
+    __bf16* hi = reinterpret_cast<__bf16*>(d.x[0]);
+    __bf16* lo = reinterpret_cast<__bf16*>(d.xlo[0]);
     for (int idx = threadIdx.x; idx < TS * TS; idx += kThreads) {
         const int a_ = idx / TS, b_ = idx % TS;
         const float v = d.transposed ? tile[b_][a_] : tile[a_][b_];
         const int64_t o = (int64_t)(i0 + a_) * d.C + (j0 + b_);
-        x32[o] = v;
-        if (write_xb) xb[o] = to_operand<T>(v);
+        const __bf16 h = (__bf16)v;
+        hi[o] = h;
+        lo[o] = (__bf16)(v - (float)h);
+    }
+}
+
+// fp32 operands: X row-major (the master) and X^T (step-0 buffer).
+__device__ __forceinline__ void write_operands_fp32(const MuonMat& d,
+                                                    const float (*tile)[kOrientTile + 1], int i0,
+                                                    int j0) {
+    constexpr int TS = kOrientTile;
+    float* x = reinterpret_cast<float*>(d.x[0]);
+    float* xt = reinterpret_cast<float*>(d.xt[0]);
+    // canonical rows i0.., cols j0..
+    for (int idx = threadIdx.x; idx < TS * TS; idx += kThreads) {
+        const int a_ = idx / TS, b_ = idx % TS;
+        x[(int64_t)(i0 + a_) * d.C + (j0 + b_)] = d.transposed ? tile[b_][a_] : tile[a_][b_];
     }
     // transposed operand: rows j0.., cols i0..
     for (int idx = threadIdx.x; idx < TS * TS; idx += kThreads) {
         const int a_ = idx / TS, b_ = idx % TS;  // a_ along canonical cols, b_ along rows
-        const float v = d.transposed ? tile[a_][b_] : tile[b_][a_];
-        xt[(int64_t)(j0 + a_) * d.R + (i0 + b_)] = to_operand<T>(v);
+        xt[(int64_t)(j0 + a_) * d.R + (i0 + b_)] = d.transposed ? tile[a_][b_] : tile[b_][a_];
     }
 }
 
@@ -353,8 +359,8 @@ __global__ __launch_bounds__(kThreads) void k_orient(const MuonMat* __restrict__
         tile[lr][lc] = u;
     }
     __syncthreads();
-    if (d.op_bf16) write_operands<__bf16>(d, tile, i0, j0);
-    else write_operands<float>(d, tile, i0, j0);
+    if (d.op_bf16) write_operands_bf16(d, tile, i0, j0);
+    else write_operands_fp32(d, tile, i0, j0);
 }
 }  // namespace
 
@@ -374,7 +380,7 @@ int launch_clip_finalize(const float* partials, int64_t n, float max_grad_norm, 
 }
 
 int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, const float* coef,
-                 const StepScalars& s, void* stream) {
+                 const StepScalars& s, bool concurrent, void* stream) {
     if (n_chunks == 0) return (int)hipSuccess;
     AdamArgs a;
     a.step_size = s.step_size;
@@ -385,8 +391,15 @@ int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, const f
     a.one_m_beta1 = s.one_m_beta1;
     a.one_m_beta2 = s.one_m_beta2;
     a.eps = s.eps;
-    hipLaunchKernelGGL(k_adamw, dim3((unsigned)n_chunks), dim3(kThreads), 0, (hipStream_t)stream,
-                       tab, n_tab, coef, a);
+    // Serial: four vectors per stream in flight (108 VGPRs) for the full
+    // HBM rate.  Concurrent with the Newton-Schulz GEMMs: two (fewer VGPRs),
+    // so an AdamW wave fits on a SIMD beside a GEMM wave.
+    if (concurrent)
+        hipLaunchKernelGGL(k_adamw<2>, dim3((unsigned)n_chunks), dim3(kThreads), 0,
+                           (hipStream_t)stream, tab, n_tab, coef, a);
+    else
+        hipLaunchKernelGGL(k_adamw<4>, dim3((unsigned)n_chunks), dim3(kThreads), 0,
+                           (hipStream_t)stream, tab, n_tab, coef, a);
     return (int)hipGetLastError();
 }
 

@@ -64,10 +64,12 @@ struct AdamTensor {
 // One Muon matrix: the elementwise view (momentum pass) and the NS view.
 struct MuonMat {
     uint64_t p, g, buf, delta;     // float* (delta may be 0)
-    uint64_t x32;                  // R x C float, master copy of X
-    uint64_t xb;                   // R x C, NS operand type (bf16 mode only)
-    uint64_t xt[2];                // C x R, NS operand type, ping-pong
-    uint64_t a, b;                 // R x R, NS operand type
+    // NS operands, zero-padded to R x C (X), C x R (X^T), R x R (A, B):
+    //   bf16: x[k] = hi part of X (row-major; the MFMA operand) and xlo[k] =
+    //         its lo part, ping-pong buffers k = step parity; xt unused
+    //   fp32: x[0] = X (row-major master and operand), xt[k] = X^T ping-pong
+    uint64_t x[2], xlo[2], xt[2];
+    uint64_t a, b;                 // R x R, operand type
     int64_t  numel;                // m * n
     int64_t  chunk_begin;          // momentum-pass chunks (one partial each)
     int64_t  orient_begin;         // first orient tile
@@ -100,7 +102,7 @@ struct Layout {
     size_t muon_partials_off = 0;                    // float[n_muon_chunks]
     size_t muon_scale_off = 0;                       // float[n_muon]
     size_t ns_off = 0;                               // start of per-matrix NS buffers
-    std::vector<size_t> x32, xb, xt0, xt1, a, b;     // per Muon matrix, offsets
+    std::vector<size_t> x0, x1, lo0, lo1, xt0, xt1, a, b;  // per Muon matrix (0: unused)
     size_t total = 0;
 };
 
@@ -181,8 +183,9 @@ int launch_norm_partials(const NormTensor* tab, int32_t n_tab, int64_t n_chunks,
                          float* partials, void* stream);
 int launch_clip_finalize(const float* partials, int64_t n, float max_grad_norm,
                          float* coef_out, float* norm_out, float* user_norm_out, void* stream);
+// `concurrent`: the launch shares the GPU with the Newton-Schulz GEMMs.
 int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
-                 const float* coef, const StepScalars& s, void* stream);
+                 const float* coef, const StepScalars& s, bool concurrent, void* stream);
 int launch_muon_momentum(const MuonMat* tab, int32_t n_tab, int64_t n_chunks,
                          const float* coef, const StepScalars& s, float* partials, void* stream);
 int launch_muon_scale(const MuonMat* tab, int32_t n_tab, const float* partials,

@@ -1,19 +1,22 @@
 // Newton-Schulz as grouped MFMA GEMMs on gfx950 (CDNA4).
 //
 // One NS step of every Muon matrix is three grouped launches, each covering
-// all matrices of all shape buckets through a cost-ordered tile list:
+// all matrices of all shape buckets through an XCD-aware tile list:
 //   GRAM  A = X X^T                      (r x r, K = c; upper tiles, mirrored)
 //   POLY  B = b A + c (A A^T)            (r x r, K = r; A symmetric, mirrored)
-//   XUPD  X = a X + B X                  (r x c, K = r; the right operand is
-//                                          read from the transposed copy of X)
+//   XUPD  X = a X + B X                  (r x c, K = r)
 // and on the last step XUPD is replaced by FINAL, whose epilogue writes the
 // parameter update p = p * decay - lr_eff * X back in the stored orientation.
 //
-// Every product is in "NT" form: both operands are read as rows whose
-// reduction index is contiguous in memory, which is what the MFMA operand
-// layout wants from LDS.  This is why the step keeps both X (row-major) and
-// X^T as NS operands.  Operands are zero-padded to multiples of 256 in both
-// dimensions, so no tile needs bounds checks.
+// MFMA operands are read from LDS as rows whose reduction index is
+// contiguous.  For GRAM and POLY both operands are such rows of a row-major
+// matrix.  For B X the right operand is X with the reduction index along its
+// rows:
+//   * bf16: X is kept row-major only and the loader transposes 8x8 bf16
+//     blocks in registers on their way to LDS;
+//   * fp32: a transposed copy X^T is kept and read directly.
+// Operands are zero-padded to multiples of 256 in both dimensions, so no
+// tile needs bounds checks.
 //
 // Method: OpenDM training-stack page, Muon/AdamW hybrid section, the
 // Newton-Schulz paragraph (a few quintic Newton-Schulz steps on the whole
@@ -21,9 +24,11 @@
 // (5 steps; update scaled by lr * muon_lr_scale * 0.2 * sqrt(max(shape))).
 //
 // bf16 mode: operands bf16 (round to nearest even), v_mfma_f32_32x32x16_bf16
-// with fp32 accumulation; a float32 master X carries the linear a*X term.
+// with fp32 accumulation.  The linear a*X term uses a master copy of X held
+// as a pair of bf16 values (hi = bf16(x), lo = bf16(x - hi): a 16-bit
+// mantissa), and hi is itself the MFMA operand.
 // fp32 mode: v_mfma_f32_32x32x2_f32 on fp32 operands (no reduced-precision
-// fp32 mode).
+// fp32 mode), master X in fp32.
 
 #include <hip/hip_runtime.h>
 
@@ -70,14 +75,25 @@ struct Mma<float> {
 struct NsArgs {
     float a, b, c;
     int iter;
-    int write_xb;
 };
+
+// Global-memory accesses through address-space-1 pointers, so they are
+// counted on vmcnt only (flat accesses also count on lgkmcnt, which would
+// make every LDS wait of the epilogue wait for them too).
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) v4u32 g_v4u32;
+typedef __attribute__((address_space(1))) float g_float;
+
+__device__ __forceinline__ uint4 gld(const void* p) {
+    return __builtin_bit_cast(uint4, *(const g_v4u32*)p);
+}
+__device__ __forceinline__ void gst(void* p, uint4 v) { *(g_v4u32*)p = __builtin_bit_cast(v4u32, v); }
 
 // 16 consecutive values of a row, to / from global memory.
 __device__ __forceinline__ void store16(float* dst, const float* v) {
-    float4* d4 = reinterpret_cast<float4*>(dst);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) d4[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    for (int q = 0; q < 4; ++q)
+        gst(dst + 4 * q, __builtin_bit_cast(uint4, make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3])));
 }
 
 __device__ __forceinline__ void store16(__bf16* dst, const float* v) {
@@ -87,16 +103,14 @@ __device__ __forceinline__ void store16(__bf16* dst, const float* v) {
         lo[e] = (__bf16)v[e];
         hi[e] = (__bf16)v[8 + e];
     }
-    uint4* d4 = reinterpret_cast<uint4*>(dst);
-    d4[0] = __builtin_bit_cast(uint4, lo);
-    d4[1] = __builtin_bit_cast(uint4, hi);
+    gst(dst, __builtin_bit_cast(uint4, lo));
+    gst(dst + 8, __builtin_bit_cast(uint4, hi));
 }
 
 __device__ __forceinline__ void load16(const float* src, float* v) {
-    const float4* s4 = reinterpret_cast<const float4*>(src);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const float4 t = s4[q];
+        const float4 t = __builtin_bit_cast(float4, gld(src + 4 * q));
         v[4 * q] = t.x;
         v[4 * q + 1] = t.y;
         v[4 * q + 2] = t.z;
@@ -104,15 +118,13 @@ __device__ __forceinline__ void load16(const float* src, float* v) {
     }
 }
 
-__device__ __forceinline__ void load16(const __bf16* src, float* v) {
-    const uint4* s4 = reinterpret_cast<const uint4*>(src);
-    const bf16x8 lo = __builtin_bit_cast(bf16x8, s4[0]);
-    const bf16x8 hi = __builtin_bit_cast(bf16x8, s4[1]);
+// Split 16 fp32 values into bf16 hi = RNE(x) and lo = RNE(x - hi).
+__device__ __forceinline__ void store16_hilo(__bf16* dhi, __bf16* dlo, const float* v) {
+    float lo[16];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        v[e] = (float)lo[e];
-        v[8 + e] = (float)hi[e];
-    }
+    for (int e = 0; e < 16; ++e) lo[e] = v[e] - (float)(__bf16)v[e];
+    store16(dhi, v);
+    store16(dlo, lo);
 }
 
 // Make this wave's LDS writes visible to its other lanes before they read.
@@ -159,164 +171,529 @@ __device__ __forceinline__ void update_run(const MuonMat& d, int row, int col, c
         if (dl) store16(dl, dv);
     } else {
         const int cnt = min(16, d.n - col);
+        g_float* gp = (g_float*)p;
+        g_float* gd = (g_float*)dl;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             if (e < cnt) {
                 const float dv = d.lr_eff * x[e];
-                p[e] = fmaf(p[e], d.decay, -dv);
-                if (dl) dl[e] = dv;
+                gp[e] = fmaf(gp[e], d.decay, -dv);
+                if (dl) gd[e] = dv;
             }
         }
     }
 }
 
-// Buffer resource of one operand: base address, extent in bytes (reads past
-// it return zero) and the raw 32-bit-element format word of gfx9 parts.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
+// Buffer resource of one operand (gfx9 layout): base address, stride 0,
+// extent in bytes (reads past it return zero) and the raw 32-bit-element
+// format word.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
-    const int32_t n = bytes > 0x7fffffffLL ? 0x7fffffff : (int32_t)bytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, int64_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    const uint32_t n = bytes > 0x7fffffffLL ? 0x7fffffffu : (uint32_t)bytes;
+    u32x4 r;
+    r.x = (uint32_t)a;
+    r.y = (uint32_t)(a >> 32) & 0xffffu;
+    r.z = n;
+    r.w = 0x00020000u;
+    return r;
 }
 
-__device__ __forceinline__ uint4 buf_load16(Rsrc r, uint32_t voff, uint32_t soff) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-    return __builtin_bit_cast(uint4, v);
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-template <int VPT, int VP, int RPI>
-__device__ __forceinline__ void stage_load(uint4 (&st)[VPT], Rsrc rp, Rsrc rq, uint32_t voff_p,
-                                           uint32_t voff_q, uint32_t ldp, uint32_t ldq,
-                                           uint32_t koff) {
+// 16 bytes per lane from global memory straight into LDS: lane t of the wave
+// writes bytes [lds + 16 t, lds + 16 t + 16).  Issued as inline assembly so
+// the compiler's own wait-count insertion does not treat every later LDS
+// read as dependent on it (it cannot tell the stage buffers apart); the
+// kernel orders these copies itself with explicit vmcnt waits and barriers.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+// ---------------------------------------------------------------------------
+// Shared-memory staging of the operands.
+//
+// A stage holds 64 bytes of the reduction index for the 256 rows of each
+// operand: P (rows of the left operand) in the first 16 KB, Q in the second.
+// Four stage buffers form a ring; global memory is copied straight into them
+// with buffer loads that write LDS (no register staging), three stages
+// ahead of the multiply.
+//
+// Row-operand layout (rows whose reduction index is contiguous): row r of a
+// region at r * 64 bytes, its 16-byte chunk c at slot c ^ ((r >> 2) & 3), so
+// the 16 rows read by each quarter of a wave's 128-bit fragment loads fall
+// in distinct banks.
+//
+// Transposed-operand layout (bf16 X of B X, reduction index along X's rows):
+// the region holds 32 rows of X (the stage's reduction range) by the tile's
+// 256 columns, row k at k * 512 bytes and chunk c at slot c ^ ((k & 3) << 2).
+// Fragments are read with the gfx950 transposing LDS load (ds_read_b64_tr_b16):
+// within each 16-lane group, lane i receives element i % 4 of the 8-byte
+// pieces addressed by lanes i / 4 + 4 e, e = 0..3, so pointing the 16 lanes
+// at four consecutive rows by four 4-column pieces hands every lane one
+// column of four consecutive rows.
+// ---------------------------------------------------------------------------
+constexpr int kStageBytes = 32768;
+constexpr int kRegionBytes = 16384;
+constexpr int kRowBytes = 64;   // reduction bytes per row per stage
+constexpr int kStages = 4;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint2 lds_tr8(const char* p) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
+__device__ __forceinline__ void wait_vm(int n) {
+    // s_waitcnt with only the vector-memory counter constrained (expcnt and
+    // lgkmcnt at their maxima); n is 0 or 8 here.
+    if (n == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+    else __builtin_amdgcn_s_waitcnt(0x0F78);
+}
+
+// Workgroup barrier that orders this wave's LDS accesses around it without
+// waiting for outstanding LDS copies (a release fence would drain them all).
+__device__ __forceinline__ void stage_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Global inputs of one epilogue block's row run, loaded ahead of time: the
+// polynomial step's A values (fp32, or bf16 with c = 0), the lo half of the
+// bf16 master X, or the fp32 master X.  At most 64 bytes per lane.
+struct EpiIn {
+    uint4 q[4];
+};
+
+template <typename T, int EPI>
+__device__ __forceinline__ void epi_load(EpiIn& in, const MuonMat& d, int lane, int bi, int bj,
+                                         int cur, bool poly_direct) {
+    constexpr bool BF = sizeof(T) == 2;
+    const int gi = bi + (lane >> 1), gj = bj + (lane & 1) * 16;
+    if (EPI == EPI_POLY) {
+        if (!poly_direct) {
+            const uint4* a = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(d.a) +
+                                                            (int64_t)gi * d.R + gj);
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        if (i < VP) st[i] = buf_load16(rp, voff_p, koff + (uint32_t)(i * RPI) * ldp);
-        else st[i] = buf_load16(rq, voff_q, koff + (uint32_t)((i - VP) * RPI) * ldq);
+            for (int q = 0; q < (BF ? 2 : 4); ++q) in.q[q] = gld(a + q);
+        }
+    } else if (EPI == EPI_XUPD || EPI == EPI_FINAL) {
+        const int64_t o = (int64_t)gi * d.C + gj;
+        if (BF) {
+            const uint4* lo = reinterpret_cast<const uint4*>(reinterpret_cast<const __bf16*>(d.xlo[cur]) + o);
+            in.q[0] = gld(lo);
+            in.q[1] = gld(lo + 1);
+        } else {
+            const uint4* x = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(d.x[0]) + o);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) in.q[q] = gld(x + q);
+        }
     }
 }
 
-template <int VPT, int RPI, int ROWB>
-__device__ __forceinline__ void stage_store(const uint4 (&st)[VPT], char* lds, uint32_t lds_off) {
+__device__ __forceinline__ void unpack16(const uint4* q, float* v, bool bf) {
+    if (bf) {
+        const bf16x8 lo = __builtin_bit_cast(bf16x8, q[0]);
+        const bf16x8 hi = __builtin_bit_cast(bf16x8, q[1]);
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) *reinterpret_cast<uint4*>(lds + i * RPI * ROWB + lds_off) = st[i];
+        for (int e = 0; e < 8; ++e) {
+            v[e] = (float)lo[e];
+            v[8 + e] = (float)hi[e];
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float4 t = __builtin_bit_cast(float4, q[k]);
+            v[4 * k] = t.x;
+            v[4 * k + 1] = t.y;
+            v[4 * k + 2] = t.z;
+            v[4 * k + 3] = t.w;
+        }
+    }
 }
 
-// One k-group's operand fragments of a wave: MI rows-of-32 of P, NI of Q.
-template <int MI, int NI, int ROWB>
-__device__ __forceinline__ void lds_frags(uint4 (&af)[MI], uint4 (&bf)[NI], const char* a,
-                                          const char* b, int koff) {
+// Epilogue of one 32x32 accumulator block at output rows bi.., columns
+// bj..: stage it in the wave's LDS region, then move 16-element row runs
+// (row-major outputs) and, where needed, column runs (transposed outputs).
+// In bf16 the linear terms a X (update steps) and b A (polynomial step,
+// c != 0) are already in the accumulators, except the lo half of the master
+// X, which arrives in `in`; in fp32 they are added here from `in`.  Called with literal block indices so the accumulators
+// stay in registers.
+template <typename T, int EPI, int SLD>
+__device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, const MuonMat& d,
+                                          float* S, const NsArgs& args, int lane, int bi, int bj,
+                                          int cur, bool need_cols, bool poly_direct, T* out_direct,
+                                          int64_t ld_direct) {
+    constexpr bool BF = sizeof(T) == 2;
+    const int rrow = lane >> 1, rc0 = (lane & 1) * 16;   // row run of this lane
+    const int ccol = lane & 31, cr0 = (lane >> 5) * 16;  // column run of this lane
+    // accumulator layout of a 32x32 MFMA block: register r of lane l holds
+    // row 8*(r/4) + 4*(l/32) + r%4, column l%32
 #pragma unroll
-    for (int i = 0; i < MI; ++i) af[i] = *reinterpret_cast<const uint4*>(a + i * 32 * ROWB + koff);
+    for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        S[row * SLD + (lane & 31)] = blk[r];
+    }
+    wave_lds_sync();
+    {
+        float v[16];
+        lds_read16(S + rrow * SLD + rc0, v);
+        const int gi = bi + rrow, gj = bj + rc0;
+        const int64_t o = (int64_t)gi * d.C + gj;
+        if (EPI == EPI_GRAM) {
+            store16(out_direct + (int64_t)gi * ld_direct + gj, v);
+        } else if (EPI == EPI_POLY) {
+            if (poly_direct) {
 #pragma unroll
-    for (int j = 0; j < NI; ++j) bf[j] = *reinterpret_cast<const uint4*>(b + j * 32 * ROWB + koff);
+                for (int e = 0; e < 16; ++e) v[e] = args.c * v[e];
+            } else {
+                float av[16];
+                unpack16(in.q, av, BF);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) v[e] = fmaf(args.b, av[e], args.c * v[e]);
+            }
+            store16(out_direct + (int64_t)gi * ld_direct + gj, v);
+        } else if (BF) {
+            // a * lo of the master X; a * hi was added in the main loop
+            float lv[16];
+            unpack16(in.q, lv, true);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v[e] = fmaf(args.a, lv[e], v[e]);
+            if (EPI == EPI_XUPD) {
+                store16_hilo(reinterpret_cast<__bf16*>(d.x[cur ^ 1]) + o,
+                             reinterpret_cast<__bf16*>(d.xlo[cur ^ 1]) + o, v);
+            } else if (!d.transposed) {
+                update_run(d, gi, gj, v);
+            }
+        } else {
+            float xv[16];
+            unpack16(in.q, xv, false);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v[e] = fmaf(args.a, xv[e], v[e]);
+            if (EPI == EPI_XUPD) {
+                store16(reinterpret_cast<float*>(d.x[0]) + o, v);
+            } else if (!d.transposed) {
+                update_run(d, gi, gj, v);
+            }
+        }
+        if (need_cols) lds_write16(S + rrow * SLD + rc0, v);
+    }
+    wave_lds_sync();
+    if (need_cols) {
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = S[(cr0 + e) * SLD + ccol];
+        const int tr = bj + ccol, tc = bi + cr0;  // row / first column in the transposed view
+        if (EPI == EPI_GRAM || EPI == EPI_POLY) {
+            store16(out_direct + (int64_t)tr * ld_direct + tc, v);
+        } else if (EPI == EPI_XUPD) {
+            T* xt = reinterpret_cast<T*>(d.xt[cur ^ 1]);
+            store16(xt + (int64_t)tr * d.R + tc, v);
+        } else {
+            update_run(d, tr, tc, v);
+        }
+        wave_lds_sync();
+    }
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_ns_gemm(
-    const MuonMat* __restrict__ tab, const GemmTile* __restrict__ tiles, NsArgs args) {
-    constexpr int WAVES_N = BN / WN;
-    constexpr int NT = (BM / WM) * WAVES_N * 64;
-    constexpr int MI = WM / 32, NI = WN / 32;
-    constexpr int ROWB = 128 + 16;                 // LDS row: 128 B of K + 16 B pad
-    constexpr int STAGE = (BM + BN) * ROWB;
-    constexpr int VPT = (BM + BN) * 8 / NT;        // 16-byte vectors per thread per stage
-    constexpr int VP = BM * 8 / NT;                // of which from P
-    static_assert((BM + BN) * 8 % NT == 0 && BM * 8 % NT == 0, "loader split");
-    constexpr int KELEM = 128 / (int)sizeof(T);    // K elements per stage
-    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+// Per-lane addressing of one tile's operands: LDS copy offsets (voffset of
+// the buffer loads; the stage and row-block parts go in soffset) and the
+// fragment offsets inside a stage buffer.
+struct Addr {
+    uint32_t dma_p;          // P copy: this lane's row and chunk
+    uint32_t dma_q[2];       // Q copy (row operand: [0]; transposed: even / odd loads)
+    uint32_t frag_a[2];      // A fragment of row block 0, per k-group
+    uint32_t frag_b[2];      // B fragment (row operand) of column block 0, per k-group
+    uint32_t frag_t[4];      // B fragment (transposed), per column block, k-group 0
+    uint32_t lin_t[4];       // linear-term reads (transposed), per column block
+    uint32_t lin_r[4];       // linear-term reads (row operand) of column block 0, per quarter
+};
+
+template <typename T, bool QT>
+__device__ __forceinline__ void stage_copy(uint32_t buf, u32x4 rp, u32x4 rq, const Addr& ad,
+                                           uint32_t wbase, int s, uint32_t ldp, uint32_t ldq) {
+    constexpr int KE = kRowBytes / (int)sizeof(T);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        dma16(rp, buf + wbase + i * 1024, ad.dma_p, (uint32_t)s * kRowBytes + (uint32_t)(i * 16) * ldp);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (QT)
+            dma16(rq, buf + kRegionBytes + wbase + i * 1024, ad.dma_q[i & 1],
+                  ((uint32_t)s * KE + (uint32_t)(2 * i)) * ldq);
+        else
+            dma16(rq, buf + kRegionBytes + wbase + i * 1024, ad.dma_q[0],
+                  (uint32_t)s * kRowBytes + (uint32_t)(i * 16) * ldq);
+    }
+}
+
+// One k-group's fragments of a wave: four row blocks of P, four column
+// blocks of Q.
+template <bool QT>
+__device__ __forceinline__ void stage_frags(uint4 (&fa)[4], uint4 (&fb)[4], const char* buf,
+                                            const Addr& ad, int kg) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        fa[i] = *reinterpret_cast<const uint4*>(buf + ad.frag_a[kg] + i * 2048);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (QT) {
+            const char* p = buf + ad.frag_t[j] + kg * 16 * 512;
+            const uint2 lo = lds_tr8(p), hi = lds_tr8(p + 4 * 512);
+            fb[j] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+            fb[j] = *reinterpret_cast<const uint4*>(buf + ad.frag_b[kg] + j * 2048);
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void stage_mma(f32x16 (&acc)[4][4], const uint4 (&fa)[4],
+                                          const uint4 (&fb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = Mma<T>::run(fa[i], fb[j], acc[i][j]);
+}
+
+// Linear term of the update and polynomial steps, added while its values sit
+// in the stage buffer: the output row of accumulator block row IB equals the
+// reduction index of the stage (update: X[i][j] is Q's row i; polynomial:
+// A[i][j] = A[j][i] is Q's row j at reduction index i).  A bf16 stage covers
+// one 32-row block (quarters Q = 0..3 of the block's registers), an fp32
+// stage half of one (quarters 2 H, 2 H + 1).
+template <typename T, bool QT, int IB, int H>
+__device__ __forceinline__ void stage_linear(f32x16 (&acc)[4][4], const char* buf, const Addr& ad,
+                                             float scale) {
+    constexpr bool BF = sizeof(T) == 2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int q = 0; q < (BF ? 4 : 2); ++q) {
+            float v[4];
+            if (QT) {
+                const uint2 w = lds_tr8(buf + ad.lin_t[j] + q * 8 * 512);
+                const bf16x8 b = __builtin_bit_cast(bf16x8, make_uint4(w.x, w.y, 0u, 0u));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (float)b[e];
+            } else if (BF) {
+                const uint2 w = *reinterpret_cast<const uint2*>(buf + ad.lin_r[q] + j * 2048);
+                const bf16x8 b = __builtin_bit_cast(bf16x8, make_uint4(w.x, w.y, 0u, 0u));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (float)b[e];
+            } else {
+                const float4 w = *reinterpret_cast<const float4*>(buf + ad.lin_r[q] + j * 2048);
+                v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+            }
+            const int qq = BF ? q : 2 * H + q;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[IB][j][4 * qq + e] = fmaf(scale, v[e], acc[IB][j][4 * qq + e]);
+        }
+    }
+}
+
+template <typename T, bool QT, int IB>
+__device__ __forceinline__ void stage_linear_h(f32x16 (&acc)[4][4], const char* buf, const Addr& ad,
+                                               float scale, int h) {
+    if (sizeof(T) == 2 || h == 0) stage_linear<T, QT, IB, 0>(acc, buf, ad, scale);
+    else stage_linear<T, QT, IB, 1>(acc, buf, ad, scale);
+}
+
+template <typename T, bool QT>
+__device__ __forceinline__ void stage_linear_at(f32x16 (&acc)[4][4], const char* buf, const Addr& ad,
+                                                float scale, int rel) {
+    // rel = first reduction index of the stage minus the wave's first output
+    // row; the stage contributes when 0 <= rel < 128
+    if (rel < 0 || rel >= 128) return;
+    const int h = (rel >> 4) & 1;
+    switch (rel >> 5) {
+        case 0: stage_linear_h<T, QT, 0>(acc, buf, ad, scale, h); break;
+        case 1: stage_linear_h<T, QT, 1>(acc, buf, ad, scale, h); break;
+        case 2: stage_linear_h<T, QT, 2>(acc, buf, ad, scale, h); break;
+        default: stage_linear_h<T, QT, 3>(acc, buf, ad, scale, h); break;
+    }
+}
+
+// One stage of the main loop: k-group 0 (fragments already in fa/fb), the
+// barrier that publishes stage s + 1 and recycles the buffer of stage s - 1,
+// the copy of stage s + 3, the k-group-0 fragments of stage s + 1, the linear
+// term, and k-group 1.
+template <typename T, bool QT, bool LIN>
+__device__ __forceinline__ void stage_step(f32x16 (&acc)[4][4], uint4 (&fa)[4], uint4 (&fb)[4],
+                                           const char* cur, const char* nxt, uint32_t tgt, u32x4 rp,
+                                           u32x4 rq, const Addr& ad, uint32_t wbase, int s, int nk,
+                                           uint32_t ldp, uint32_t ldq, float scale, int rel0) {
+    constexpr int KE = kRowBytes / (int)sizeof(T);
+    uint4 ga[4], gb[4];
+    stage_frags<QT>(ga, gb, cur, ad, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_mma<T>(acc, fa, fb);
+    __builtin_amdgcn_sched_barrier(0);
+    // every stage takes the barrier and reads the next k-group-0 fragments
+    // (after the last stage they are unused reads of a stale buffer), so the
+    // code has no join point that would blur the LDS wait counts
+    wait_vm(s + 2 < nk ? 8 : 0);
+    stage_barrier();
+    if (s + 3 < nk) stage_copy<T, QT>(tgt, rp, rq, ad, wbase, s + 3, ldp, ldq);
+    stage_frags<QT>(fa, fb, nxt, ad, 0);
+    if (LIN) stage_linear_at<T, QT>(acc, cur, ad, scale, rel0 + s * KE);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_mma<T>(acc, ga, gb);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) void k_ns_gemm(const MuonMat* __restrict__ tab,
+                                                 const GemmTile* __restrict__ tiles, NsArgs args) {
+    constexpr bool BF = sizeof(T) == 2;
+    // B X in bf16 reads X row-major through the transposing LDS loads
+    constexpr bool QT = BF && (EPI == EPI_XUPD || EPI == EPI_FINAL);
+    constexpr bool XT = EPI == EPI_XUPD || EPI == EPI_FINAL;
+    constexpr int KE = kRowBytes / (int)sizeof(T);
+    constexpr int SLD = 36;  // epilogue staging row stride (floats): 16-byte aligned runs
+    __shared__ __attribute__((aligned(1024))) char sb0[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char sb1[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char sb2[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char sb3[kStageBytes];
+    __shared__ __attribute__((aligned(16))) float stg[4 * 32 * SLD];
 
     const GemmTile tile = tiles[blockIdx.x];
     if (tile.mat < 0) return;  // padding of a shorter per-XCD list
     const MuonMat& d = tab[tile.mat];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    // the wave index is uniform across the wave: keep it (and what derives
+    // from it) in scalar registers so per-wave branches are scalar branches
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int cur = args.iter & 1;
 
     const char* P;
     const char* Q;
     int64_t ldp, ldq;  // bytes
-    int K, K_rows_p, K_rows_q;
+    int K, rows_p, rows_q;
     if (EPI == EPI_GRAM) {
-        P = Q = reinterpret_cast<const char*>(d.xb);
+        P = Q = reinterpret_cast<const char*>(BF ? d.x[cur] : d.x[0]);
         ldp = ldq = (int64_t)d.C * sizeof(T);
         K = d.C;
-        K_rows_p = K_rows_q = d.R;
+        rows_p = rows_q = d.R;
     } else if (EPI == EPI_POLY) {
         P = Q = reinterpret_cast<const char*>(d.a);
         ldp = ldq = (int64_t)d.R * sizeof(T);
         K = d.R;
-        K_rows_p = K_rows_q = d.R;
+        rows_p = rows_q = d.R;
     } else {
         P = reinterpret_cast<const char*>(d.b);
-        Q = reinterpret_cast<const char*>(d.xt[args.iter & 1]);
-        ldp = ldq = (int64_t)d.R * sizeof(T);
+        ldp = (int64_t)d.R * sizeof(T);
+        rows_p = d.R;
         K = d.R;
-        K_rows_p = d.R;
-        K_rows_q = d.C;
+        if (QT) {  // X row-major: R rows (the reduction index) of C columns
+            Q = reinterpret_cast<const char*>(d.x[cur]);
+            ldq = (int64_t)d.C * sizeof(T);
+            rows_q = d.R;
+        } else {   // X^T: C rows of R
+            Q = reinterpret_cast<const char*>(d.xt[cur]);
+            ldq = (int64_t)d.R * sizeof(T);
+            rows_q = d.C;
+        }
     }
-    const int m0 = tile.tm * BM, n0 = tile.tn * BN;
-    const int nk = K / KELEM;
+    const int m0 = tile.tm * 256, n0 = tile.tn * 256;
+    const int nk = K / KE;  // a multiple of 8: K is padded to 256
 
-    f32x16 acc[MI][NI];
+    const u32x4 rp = make_rsrc(P, (int64_t)rows_p * ldp);
+    const u32x4 rq = make_rsrc(Q, (int64_t)rows_q * ldq);
+    Addr ad;
+    {
+        const uint32_t c = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+        ad.dma_p = (uint32_t)((m0 + wave * 64 + (lane >> 2)) * ldp) + c * 16;
+        if (QT) {
+            const uint32_t r = (uint32_t)(8 * wave + (lane >> 5));
+            const uint32_t ce = (uint32_t)((lane & 31) ^ (((lane >> 5) & 3) << 2));
+            const uint32_t co = (uint32_t)((lane & 31) ^ (((2 + (lane >> 5)) & 3) << 2));
+            ad.dma_q[0] = r * (uint32_t)ldq + (uint32_t)n0 * 2 + ce * 16;
+            ad.dma_q[1] = r * (uint32_t)ldq + (uint32_t)n0 * 2 + co * 16;
+        } else {
+            ad.dma_q[0] = (uint32_t)((n0 + wave * 64 + (lane >> 2)) * ldq) + c * 16;
+            ad.dma_q[1] = ad.dma_q[0];
+        }
+        const int r32 = lane & 31, sw = (r32 >> 2) & 3, half = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+        for (int kg = 0; kg < 2; ++kg) {
+            const int slot = (2 * kg + half) ^ sw;
+            ad.frag_a[kg] = (uint32_t)((wm * 128 + r32) * kRowBytes + (slot << 4));
+            ad.frag_b[kg] = (uint32_t)(kRegionBytes + (wn * 128 + r32) * kRowBytes + (slot << 4));
+        }
+        // linear term from a row-operand Q: bf16 quarter q is the 8 bytes at
+        // chunk q, half `half`; fp32 quarter q is chunk 2 q + half
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
+        for (int q = 0; q < 4; ++q) {
+            const int rowb = kRegionBytes + (wn * 128 + r32) * kRowBytes;
+            ad.lin_r[q] = BF ? (uint32_t)(rowb + ((q ^ sw) << 4) + 8 * half)
+                             : (uint32_t)(rowb + ((((2 * q + half) & 3) ^ sw) << 4));
+        }
+        const int g = lane >> 4, jj = lane & 15;
+        const int tsw = (jj >> 2) & 3;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int chunk = wn * 16 + ((j ^ tsw) << 2) + 2 * (g & 1) + ((jj & 3) >> 1);
+            const int row_f = 8 * (g >> 1) + (jj >> 2);
+            const int row_l = 4 * (g >> 1) + (jj >> 2);
+            ad.frag_t[j] = (uint32_t)(kRegionBytes + row_f * 512 + (chunk << 4) + 8 * (jj & 1));
+            ad.lin_t[j] = (uint32_t)(kRegionBytes + row_l * 512 + (chunk << 4) + 8 * (jj & 1));
+        }
+    }
+    const uint32_t uldp = (uint32_t)ldp, uldq = (uint32_t)ldq;
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // Global -> register -> LDS staging, double-buffered in LDS.  Thread t
-    // moves 16-byte segment (t % 8) of rows t / 8 + RPI i (i < VPT) of the
-    // stacked [P rows; Q rows] stage: one buffer load per row block, with the
-    // per-thread offset in a VGPR and the row-block/stage offset in an SGPR.
-    constexpr int RPI = NT / 8;  // rows covered per i
-    const Rsrc rp = make_rsrc(P, (int64_t)(K_rows_p) * ldp);
-    const Rsrc rq = make_rsrc(Q, (int64_t)(K_rows_q) * ldq);
-    const uint32_t voff_p = (uint32_t)((m0 + (tid >> 3)) * ldp + (tid & 7) * 16);
-    const uint32_t voff_q = (uint32_t)((n0 + (tid >> 3)) * ldq + (tid & 7) * 16);
-    const uint32_t lds_off = (uint32_t)((tid >> 3) * ROWB + (tid & 7) * 16);
-    uint4 stage[VPT];
+    // bf16 linear terms taken from the stage buffers: a X_hi (update steps)
+    // and (b / c) A (polynomial step with c != 0; the epilogue scales by c)
+    const bool poly_direct = BF && EPI == EPI_POLY && args.c != 0.f;
+    constexpr bool LIN = BF && (XT || EPI == EPI_POLY);
+    const float scale = XT ? args.a : (poly_direct ? args.b / args.c : 0.f);
+    const int rel0 = LIN && (XT || poly_direct) ? -(m0 + wm * 128) : -(1 << 30);
 
-    stage_load<VPT, VP, RPI>(stage, rp, rq, voff_p, voff_q, (uint32_t)ldp, (uint32_t)ldq, 0);
-    stage_store<VPT, RPI, ROWB>(stage, smem, lds_off);
-    __syncthreads();
-    const int arow = (wm * WM + (lane & 31)) * ROWB + (lane >> 5) * 16;
-    const int brow = (BM + wn * WN + (lane & 31)) * ROWB + (lane >> 5) * 16;
-    for (int s = 0; s < nk; ++s) {
-        if (s + 1 < nk)
-            stage_load<VPT, VP, RPI>(stage, rp, rq, voff_p, voff_q, (uint32_t)ldp, (uint32_t)ldq,
-                                     (uint32_t)(s + 1) * 128u);
-        const char* base = smem + (s & 1) * STAGE;
-        // fragments of k-group kg+1 are read from LDS while the MFMAs of
-        // k-group kg run (two register sets), so LDS latency stays hidden
-        uint4 af[2][MI], bfr[2][NI];
-        lds_frags<MI, NI, ROWB>(af[0], bfr[0], base + arow, base + brow, 0);
-#pragma unroll
-        for (int kg = 0; kg < 4; ++kg) {
-            if (kg + 1 < 4)
-                lds_frags<MI, NI, ROWB>(af[(kg + 1) & 1], bfr[(kg + 1) & 1], base + arow,
-                                        base + brow, (kg + 1) * 32);
-            // keep the prefetch above this k-group's MFMAs (the scheduler
-            // would otherwise sink the reads next to their uses)
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    acc[i][j] = Mma<T>::run(af[kg & 1][i], bfr[kg & 1][j], acc[i][j]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (s + 1 < nk) stage_store<VPT, RPI, ROWB>(stage, smem + ((s + 1) & 1) * STAGE, lds_off);
-        __syncthreads();
+    const uint32_t wbase = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 4 * 1024);
+    const uint32_t l0 = lds_addr(sb0), l1 = lds_addr(sb1), l2 = lds_addr(sb2), l3 = lds_addr(sb3);
+    stage_copy<T, QT>(l0, rp, rq, ad, wbase, 0, uldp, uldq);
+    stage_copy<T, QT>(l1, rp, rq, ad, wbase, 1, uldp, uldq);
+    stage_copy<T, QT>(l2, rp, rq, ad, wbase, 2, uldp, uldq);
+    // stage 0 has landed once at most the 16 copies of stages 1 and 2 are
+    // outstanding (vmcnt(16): low bits 0, high bits 1)
+    __builtin_amdgcn_s_waitcnt(0x4F70);
+    stage_barrier();
+    uint4 fa[4], fb[4];
+    stage_frags<QT>(fa, fb, sb0, ad, 0);
+    for (int s = 0; s < nk; s += 4) {
+        stage_step<T, QT, LIN>(acc, fa, fb, sb0, sb1, l3, rp, rq, ad, wbase, s, nk, uldp, uldq, scale, rel0);
+        stage_step<T, QT, LIN>(acc, fa, fb, sb1, sb2, l0, rp, rq, ad, wbase, s + 1, nk, uldp, uldq, scale, rel0);
+        stage_step<T, QT, LIN>(acc, fa, fb, sb2, sb3, l1, rp, rq, ad, wbase, s + 2, nk, uldp, uldq, scale, rel0);
+        stage_step<T, QT, LIN>(acc, fa, fb, sb3, sb0, l2, rp, rq, ad, wbase, s + 3, nk, uldp, uldq, scale, rel0);
     }
 
     // ---- epilogue: each wave stages its 32x32 accumulator blocks in its own
     // LDS region (wave-level synchronisation only, no block barriers) and
     // moves them as 16-element runs: row runs for row-major outputs, column
     // runs for the transposed outputs ----
-    constexpr int SLD = 36;  // staging row stride (floats): 16-byte aligned runs
-    float* S = reinterpret_cast<float*>(smem) + wave * (32 * SLD);
+    float* S = stg + wave * (32 * SLD);
     const bool mirror = (EPI == EPI_GRAM || EPI == EPI_POLY) && tile.tm != tile.tn;
-    const bool need_cols = mirror || EPI == EPI_XUPD || (EPI == EPI_FINAL && d.transposed);
+    const bool need_cols =
+        mirror || (EPI == EPI_XUPD && !BF) || (EPI == EPI_FINAL && d.transposed);
     T* out_direct = nullptr;
     int64_t ld_direct = 0;
     if (EPI == EPI_GRAM) {
@@ -326,75 +703,41 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_ns_gemm(
         out_direct = reinterpret_cast<T*>(d.b);
         ld_direct = d.R;
     }
-    const int rrow = lane >> 1, rc0 = (lane & 1) * 16;   // row run of this lane
-    const int ccol = lane & 31, cr0 = (lane >> 5) * 16;  // column run of this lane
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            // accumulator layout of a 32x32 MFMA block: register r of lane l
-            // holds row 8*(r/4) + 4*(l/32) + r%4, column l%32
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                S[row * SLD + (lane & 31)] = acc[i][j][r];
-            }
-            wave_lds_sync();
-            const int bi = m0 + wm * WM + i * 32;  // block origin in the output
-            const int bj = n0 + wn * WN + j * 32;
-            {
-                float v[16];
-                lds_read16(S + rrow * SLD + rc0, v);
-                const int gi = bi + rrow, gj = bj + rc0;
-                if (EPI == EPI_GRAM) {
-                    store16(out_direct + (int64_t)gi * ld_direct + gj, v);
-                } else if (EPI == EPI_POLY) {
-                    float av[16];
-                    load16(reinterpret_cast<const T*>(d.a) + (int64_t)gi * d.R + gj, av);
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) v[e] = fmaf(args.b, av[e], args.c * v[e]);
-                    store16(out_direct + (int64_t)gi * ld_direct + gj, v);
-                } else {
-                    float* x32 = reinterpret_cast<float*>(d.x32) + (int64_t)gi * d.C + gj;
-                    float xv[16];
-                    load16(x32, xv);
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) v[e] = fmaf(args.a, xv[e], v[e]);
-                    if (EPI == EPI_XUPD) {
-                        store16(x32, v);
-                        if (args.write_xb) store16(reinterpret_cast<T*>(d.xb) + (int64_t)gi * d.C + gj, v);
-                    } else if (!d.transposed) {
-                        update_run(d, gi, gj, v);
-                    }
-                }
-                if (need_cols) lds_write16(S + rrow * SLD + rc0, v);
-            }
-            wave_lds_sync();
-            if (need_cols) {
-                float v[16];
-#pragma unroll
-                for (int e = 0; e < 16; ++e) v[e] = S[(cr0 + e) * SLD + ccol];
-                const int tr = bj + ccol, tc = bi + cr0;  // row / first column in the transposed view
-                if (EPI == EPI_GRAM || EPI == EPI_POLY) {
-                    store16(out_direct + (int64_t)tr * ld_direct + tc, v);
-                } else if (EPI == EPI_XUPD) {
-                    T* xt = reinterpret_cast<T*>(d.xt[(args.iter + 1) & 1]);
-                    store16(xt + (int64_t)tr * d.R + tc, v);
-                } else {
-                    update_run(d, tr, tc, v);
-                }
-                wave_lds_sync();
-            }
-        }
-    }
+    const int bi0 = m0 + wm * 128, bj0 = n0 + wn * 128;
+    // The 16 blocks go in row order; each block's global inputs are loaded
+    // four blocks ahead (slots in0..in3), so their latency overlaps the
+    // work on the blocks in between instead of stalling every block.
+    EpiIn in0, in1, in2, in3;
+#define NS_LOAD(SLOT, I, J) \
+    epi_load<T, EPI>(SLOT, d, lane, bi0 + (I) * 32, bj0 + (J) * 32, cur, poly_direct)
+#define NS_EPI(I, J, SLOT)                                                                   \
+    epi_block<T, EPI, SLD>(acc[I][J], SLOT, d, S, args, lane, bi0 + (I) * 32, bj0 + (J) * 32, \
+                           cur, need_cols, poly_direct, out_direct, ld_direct)
+    NS_LOAD(in0, 0, 0); NS_LOAD(in1, 0, 1); NS_LOAD(in2, 0, 2); NS_LOAD(in3, 0, 3);
+    NS_EPI(0, 0, in0); NS_LOAD(in0, 1, 0);
+    NS_EPI(0, 1, in1); NS_LOAD(in1, 1, 1);
+    NS_EPI(0, 2, in2); NS_LOAD(in2, 1, 2);
+    NS_EPI(0, 3, in3); NS_LOAD(in3, 1, 3);
+    NS_EPI(1, 0, in0); NS_LOAD(in0, 2, 0);
+    NS_EPI(1, 1, in1); NS_LOAD(in1, 2, 1);
+    NS_EPI(1, 2, in2); NS_LOAD(in2, 2, 2);
+    NS_EPI(1, 3, in3); NS_LOAD(in3, 2, 3);
+    NS_EPI(2, 0, in0); NS_LOAD(in0, 3, 0);
+    NS_EPI(2, 1, in1); NS_LOAD(in1, 3, 1);
+    NS_EPI(2, 2, in2); NS_LOAD(in2, 3, 2);
+    NS_EPI(2, 3, in3); NS_LOAD(in3, 3, 3);
+    NS_EPI(3, 0, in0);
+    NS_EPI(3, 1, in1);
+    NS_EPI(3, 2, in2);
+    NS_EPI(3, 3, in3);
+#undef NS_LOAD
+#undef NS_EPI
 }
 
 template <typename T, int EPI>
 int launch_t(const MuonMat* tab, const GemmTile* tiles, int64_t n, const NsArgs& a, hipStream_t st) {
-    constexpr int BM = 256, BN = 256, WM = 128, WN = 128;
-    static_assert(BM == kGemmTile && BN == kGemmTile, "tile lists are built for kGemmTile");
-    hipLaunchKernelGGL((k_ns_gemm<T, BM, BN, WM, WN, EPI>), dim3((unsigned)n),
-                       dim3((BM / WM) * (BN / WN) * 64), 0, st, tab, tiles, a);
+    static_assert(kGemmTile == 256, "tile lists are built for 256x256 tiles");
+    hipLaunchKernelGGL((k_ns_gemm<T, EPI>), dim3((unsigned)n), dim3(256), 0, st, tab, tiles, a);
     return (int)hipGetLastError();
 }
 
@@ -403,7 +746,7 @@ int launch_t(const MuonMat* tab, const GemmTile* tiles, int64_t n, const NsArgs&
 int launch_ns_phase(int phase, int32_t group, const MuonMat* tab, const GemmTile* tiles,
                     int64_t n_tiles, int iter, int last, const StepScalars& s, void* stream) {
     if (n_tiles == 0) return (int)hipSuccess;
-    NsArgs a{s.ns_a, s.ns_b, s.ns_c, iter, group == kGroupBf16 ? 1 : 0};
+    NsArgs a{s.ns_a, s.ns_b, s.ns_c, iter};
     hipStream_t st = (hipStream_t)stream;
     const int epi = phase == 1 ? EPI_GRAM : phase == 2 ? EPI_POLY : (last ? EPI_FINAL : EPI_XUPD);
     if (group == kGroupBf16) {

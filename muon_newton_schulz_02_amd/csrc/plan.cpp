@@ -264,18 +264,28 @@ void build_layout(ma_plan* p, int32_t precision) {
         const auto& e = p->entries[p->muon_ids[k]];
         const size_t R = (size_t)round_up(e.r, kNsPad), C = (size_t)round_up(e.c, kNsPad);
         const size_t esz = L.op_group[k] == kGroupBf16 ? 2 : 4;
-        L.x32.push_back(off);
-        off = align256(off + R * C * 4);
+        auto take = [&](size_t bytes) {
+            const size_t at = off;
+            off = align256(off + bytes);
+            return at;
+        };
         if (L.op_group[k] == kGroupBf16) {
-            L.xb.push_back(off);
-            off = align256(off + R * C * esz);
+            // X as bf16 hi / lo pairs, ping-pong; B X reads hi transposed on load
+            L.x0.push_back(take(R * C * 2));
+            L.x1.push_back(take(R * C * 2));
+            L.lo0.push_back(take(R * C * 2));
+            L.lo1.push_back(take(R * C * 2));
+            L.xt0.push_back(0);
+            L.xt1.push_back(0);
         } else {
-            L.xb.push_back(L.x32.back());  // fp32 mode: X itself is the operand
+            // fp32 master X (updated in place) and X^T ping-pong
+            L.x0.push_back(take(R * C * 4));
+            L.x1.push_back(0);
+            L.lo0.push_back(0);
+            L.lo1.push_back(0);
+            L.xt0.push_back(take(R * C * 4));
+            L.xt1.push_back(take(R * C * 4));
         }
-        L.xt0.push_back(off);
-        off = align256(off + R * C * esz);
-        L.xt1.push_back(off);
-        off = align256(off + R * C * esz);
         L.a.push_back(off);
         off = align256(off + R * R * esz);
         L.b.push_back(off);

@@ -250,10 +250,13 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         d.g = reinterpret_cast<uint64_t>(grads[id]);
         d.buf = reinterpret_cast<uint64_t>(state->muon_momentum[id]);
         d.delta = reinterpret_cast<uint64_t>(delta);
-        d.x32 = reinterpret_cast<uint64_t>(base + L.x32[k]);
-        d.xb = reinterpret_cast<uint64_t>(base + L.xb[k]);
-        d.xt[0] = reinterpret_cast<uint64_t>(base + L.xt0[k]);
-        d.xt[1] = reinterpret_cast<uint64_t>(base + L.xt1[k]);
+        auto ws = [&](size_t off) { return off ? reinterpret_cast<uint64_t>(base + off) : 0; };
+        d.x[0] = ws(L.x0[k]);
+        d.x[1] = ws(L.x1[k]);
+        d.xlo[0] = ws(L.lo0[k]);
+        d.xlo[1] = ws(L.lo1[k]);
+        d.xt[0] = ws(L.xt0[k]);
+        d.xt[1] = ws(L.xt1[k]);
         d.a = reinterpret_cast<uint64_t>(base + L.a[k]);
         d.b = reinterpret_cast<uint64_t>(base + L.b[k]);
         d.numel = e.numel;
@@ -324,7 +327,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
             return hip_fail("hipEventRecord (fork)", e);
         if ((e = hipStreamWaitEvent(ss, (hipEvent_t)side->ev_fork, 0)) != hipSuccess)
             return hip_fail("hipStreamWaitEvent (fork)", e);
-        err = launch_adamw(d_adam, n_adam, plan->n_adam_chunks, coef, sc, ss);
+        err = launch_adamw(d_adam, n_adam, plan->n_adam_chunks, coef, sc, true, ss);
         if (err) return hip_fail("adamw", err);
         if (phase_events && phase_events[2] &&
             (e = hipEventRecord((hipEvent_t)phase_events[2], ss)) != hipSuccess)
@@ -332,7 +335,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         if ((e = hipEventRecord((hipEvent_t)side->ev_join, ss)) != hipSuccess)
             return hip_fail("hipEventRecord (join)", e);
     } else {
-        err = launch_adamw(d_adam, n_adam, plan->n_adam_chunks, coef, sc, stream);
+        err = launch_adamw(d_adam, n_adam, plan->n_adam_chunks, coef, sc, false, stream);
         if (err) return hip_fail("adamw", err);
         if ((err = mark(2))) return hip_fail("phase event", err);
     }

@@ -136,6 +136,16 @@ def test_ragged_published_coefficients_no_nesterov_with_decay():
     _run_parity(w, "fp32", 2, hp=hp)
 
 
+@pytest.mark.parametrize("prec", ["bf16", "fp32"])
+def test_ragged_cubic_coefficients(prec):
+    """c = 0 (the classic cubic iteration 1.5 X - 0.5 X X^T X): the polynomial
+    step reduces to B = b A, which the bf16 kernels cannot fold into the
+    product's accumulators and take from the A operand in the epilogue."""
+    w = _ragged_workload()
+    hp = H.oracle_hparams(w, ns_coeffs=(1.5, -0.5, 0.0))
+    _run_parity(w, prec, 2, hp=hp)
+
+
 def test_adamw_mode_and_misaligned_views():
     """Plain-AdamW mode sends every trainable tensor through the AdamW kernel;
     a view starting one float into its storage takes the scalar path."""
