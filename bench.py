@@ -68,7 +68,7 @@ class HipEvents:
 
 KERNEL_SOURCES = {
     "k_adamw": os.path.join(HERE, "muon_newton_schulz_02_amd", "csrc", "elementwise.hip"),
-    "k_ns_gemm": os.path.join(HERE, "muon_newton_schulz_02_amd", "csrc", "ns_gemm.hip"),
+    "k_ns_xupd_bf16": os.path.join(HERE, "muon_newton_schulz_02_amd", "csrc", "ns_gemm.hip"),
 }
 
 
@@ -270,7 +270,7 @@ def main():
                     "traffic": measured_traffic("k_adamw", w.name),
                     "algorithmic_bytes": adam_bytes}
     else:
-        roofline = {"kernel": "k_ns_gemm (5 steps x 3 launches)", "bound": "mfma",
+        roofline = {"kernel": "k_ns_* GEMMs (5 steps x 3 launches)", "bound": "mfma",
                     "achieved": ns_tflops, "peak": ns_peak, "unit": "TFLOP/s",
                     "frac": ns_tflops / ns_peak, "traffic": None}
     out = {

@@ -32,6 +32,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <utility>
+
 #include "ma_internal.h"
 
 namespace ma {
@@ -222,9 +224,9 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds, uint32_t voff, u
 //
 // A stage holds 64 bytes of the reduction index for the 256 rows of each
 // operand: P (rows of the left operand) in the first 16 KB, Q in the second.
-// Four stage buffers form a ring; global memory is copied straight into them
-// with buffer loads that write LDS (no register staging), three stages
-// ahead of the multiply.
+// Four stage buffers (128 KB of LDS) form a ring; global memory is
+// copied straight into them with buffer loads that write LDS (no register
+// staging), three stages ahead of the multiply.
 //
 // Row-operand layout (rows whose reduction index is contiguous): row r of a
 // region at r * 64 bytes, its 16-byte chunk c at slot c ^ ((r >> 2) & 3), so
@@ -243,7 +245,7 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds, uint32_t voff, u
 constexpr int kStageBytes = 32768;
 constexpr int kRegionBytes = 16384;
 constexpr int kRowBytes = 64;   // reduction bytes per row per stage
-constexpr int kStages = 4;
+constexpr int kStages = 4;      // ring depth: copies run kStages - 1 stages ahead
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -252,11 +254,14 @@ __device__ __forceinline__ uint2 lds_tr8(const char* p) {
     return __builtin_bit_cast(uint2, v);
 }
 
+// s_waitcnt with only the vector-memory counter constrained (expcnt and
+// lgkmcnt at their maxima): vmcnt(n) for n in {0, 8, 16, 24}.  The 6-bit
+// count is split into bits [3:0] and [15:14] of the immediate.
 __device__ __forceinline__ void wait_vm(int n) {
-    // s_waitcnt with only the vector-memory counter constrained (expcnt and
-    // lgkmcnt at their maxima); n is 0 or 8 here.
-    if (n == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
-    else __builtin_amdgcn_s_waitcnt(0x0F78);
+    if (n <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+    else if (n == 8) __builtin_amdgcn_s_waitcnt(0x0F78);
+    else if (n == 16) __builtin_amdgcn_s_waitcnt(0x4F70);
+    else __builtin_amdgcn_s_waitcnt(0x4F78);
 }
 
 // Workgroup barrier that orders this wave's LDS accesses around it without
@@ -526,8 +531,8 @@ __device__ __forceinline__ void stage_linear_at(f32x16 (&acc)[4][4], const char*
 
 // One stage of the main loop: k-group 0 (fragments already in fa/fb), the
 // barrier that publishes stage s + 1 and recycles the buffer of stage s - 1,
-// the copy of stage s + 3, the k-group-0 fragments of stage s + 1, the linear
-// term, and k-group 1.
+// the copy of stage s + kStages - 1 into it, the k-group-0 fragments of stage
+// s + 1, the linear term, and k-group 1.
 template <typename T, bool QT, bool LIN>
 __device__ __forceinline__ void stage_step(f32x16 (&acc)[4][4], uint4 (&fa)[4], uint4 (&fb)[4],
                                            const char* cur, const char* nxt, uint32_t tgt, u32x4 rp,
@@ -539,12 +544,14 @@ __device__ __forceinline__ void stage_step(f32x16 (&acc)[4][4], uint4 (&fa)[4], 
     __builtin_amdgcn_sched_barrier(0);
     stage_mma<T>(acc, fa, fb);
     __builtin_amdgcn_sched_barrier(0);
-    // every stage takes the barrier and reads the next k-group-0 fragments
-    // (after the last stage they are unused reads of a stale buffer), so the
-    // code has no join point that would blur the LDS wait counts
-    wait_vm(s + 2 < nk ? 8 : 0);
+    // stage s + 1 has landed once only the copies of the stages after it
+    // (at most kStages - 3 of them, 8 loads each) are outstanding.  Every
+    // stage takes the barrier and reads the next k-group-0 fragments (after
+    // the last stage they are unused reads of a stale buffer), so the code
+    // has no join point that would blur the LDS wait counts.
+    wait_vm(8 * min(nk - 2 - s, kStages - 3));
     stage_barrier();
-    if (s + 3 < nk) stage_copy<T, QT>(tgt, rp, rq, ad, wbase, s + 3, ldp, ldq);
+    if (s + kStages - 1 < nk) stage_copy<T, QT>(tgt, rp, rq, ad, wbase, s + kStages - 1, ldp, ldq);
     stage_frags<QT>(fa, fb, nxt, ad, 0);
     if (LIN) stage_linear_at<T, QT>(acc, cur, ad, scale, rel0 + s * KE);
     __builtin_amdgcn_sched_barrier(0);
@@ -552,20 +559,35 @@ __device__ __forceinline__ void stage_step(f32x16 (&acc)[4][4], uint4 (&fa)[4], 
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Stages s .. s + kStages - 1 of the main loop, stage s + B in ring slot B.
+template <typename T, bool QT, bool LIN, int... B>
+__device__ __forceinline__ void ring_round(std::integer_sequence<int, B...>, f32x16 (&acc)[4][4],
+                                           uint4 (&fa)[4], uint4 (&fb)[4], const char* ring,
+                                           uint32_t lring, u32x4 rp, u32x4 rq, const Addr& ad,
+                                           uint32_t wbase, int s, int nk, uint32_t ldp,
+                                           uint32_t ldq, float scale, int rel0) {
+    // nk is a multiple of 8, so a ring depth dividing 8 needs no guard
+    (((8 % kStages == 0 || s + B < nk)
+          ? stage_step<T, QT, LIN>(acc, fa, fb, ring + B * kStageBytes,
+                                   ring + ((B + 1) % kStages) * kStageBytes,
+                                   lring + ((B + kStages - 1) % kStages) * kStageBytes, rp, rq,
+                                   ad, wbase, s + B, nk, ldp, ldq, scale, rel0)
+          : void()),
+     ...);
+}
+
 template <typename T, int EPI>
-__global__ __launch_bounds__(256) void k_ns_gemm(const MuonMat* __restrict__ tab,
-                                                 const GemmTile* __restrict__ tiles, NsArgs args) {
+__device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
+                                             const GemmTile* __restrict__ tiles, const NsArgs& args) {
     constexpr bool BF = sizeof(T) == 2;
     // B X in bf16 reads X row-major through the transposing LDS loads
     constexpr bool QT = BF && (EPI == EPI_XUPD || EPI == EPI_FINAL);
     constexpr bool XT = EPI == EPI_XUPD || EPI == EPI_FINAL;
     constexpr int KE = kRowBytes / (int)sizeof(T);
     constexpr int SLD = 36;  // epilogue staging row stride (floats): 16-byte aligned runs
-    __shared__ __attribute__((aligned(1024))) char sb0[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) char sb1[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) char sb2[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) char sb3[kStageBytes];
-    __shared__ __attribute__((aligned(16))) float stg[4 * 32 * SLD];
+    // the stage ring; after the main loop its start is the epilogue staging
+    __shared__ __attribute__((aligned(1024))) char ring[kStages * kStageBytes];
+    static_assert(4 * 32 * SLD * 4 <= kStageBytes, "epilogue staging fits in one stage buffer");
 
     const GemmTile tile = tiles[blockIdx.x];
     if (tile.mat < 0) return;  // padding of a shorter per-XCD list
@@ -669,28 +691,30 @@ __global__ __launch_bounds__(256) void k_ns_gemm(const MuonMat* __restrict__ tab
     const int rel0 = LIN && (XT || poly_direct) ? -(m0 + wm * 128) : -(1 << 30);
 
     const uint32_t wbase = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 4 * 1024);
-    const uint32_t l0 = lds_addr(sb0), l1 = lds_addr(sb1), l2 = lds_addr(sb2), l3 = lds_addr(sb3);
-    stage_copy<T, QT>(l0, rp, rq, ad, wbase, 0, uldp, uldq);
-    stage_copy<T, QT>(l1, rp, rq, ad, wbase, 1, uldp, uldq);
-    stage_copy<T, QT>(l2, rp, rq, ad, wbase, 2, uldp, uldq);
-    // stage 0 has landed once at most the 16 copies of stages 1 and 2 are
-    // outstanding (vmcnt(16): low bits 0, high bits 1)
-    __builtin_amdgcn_s_waitcnt(0x4F70);
+    const uint32_t lring = lds_addr(ring);
+#pragma unroll
+    for (int st = 0; st < kStages - 1; ++st)
+        stage_copy<T, QT>(lring + st * kStageBytes, rp, rq, ad, wbase, st, uldp, uldq);
+    // stage 0 has landed once only the copies of stages 1 .. kStages - 2 are
+    // outstanding
+    wait_vm(8 * (kStages - 2));
     stage_barrier();
     uint4 fa[4], fb[4];
-    stage_frags<QT>(fa, fb, sb0, ad, 0);
-    for (int s = 0; s < nk; s += 4) {
-        stage_step<T, QT, LIN>(acc, fa, fb, sb0, sb1, l3, rp, rq, ad, wbase, s, nk, uldp, uldq, scale, rel0);
-        stage_step<T, QT, LIN>(acc, fa, fb, sb1, sb2, l0, rp, rq, ad, wbase, s + 1, nk, uldp, uldq, scale, rel0);
-        stage_step<T, QT, LIN>(acc, fa, fb, sb2, sb3, l1, rp, rq, ad, wbase, s + 2, nk, uldp, uldq, scale, rel0);
-        stage_step<T, QT, LIN>(acc, fa, fb, sb3, sb0, l2, rp, rq, ad, wbase, s + 3, nk, uldp, uldq, scale, rel0);
-    }
+    stage_frags<QT>(fa, fb, ring, ad, 0);
+    // the loop is unrolled by the ring depth so every stage buffer address
+    // is a compile-time offset
+    for (int s = 0; s < nk; s += kStages)
+        ring_round<T, QT, LIN>(std::make_integer_sequence<int, kStages>(), acc, fa, fb, ring, lring,
+                               rp, rq, ad, wbase, s, nk, uldp, uldq, scale, rel0);
+    // every wave is done with the ring (all copies landed at the last
+    // stage's wait) before it becomes the epilogue staging area
+    stage_barrier();
 
     // ---- epilogue: each wave stages its 32x32 accumulator blocks in its own
     // LDS region (wave-level synchronisation only, no block barriers) and
     // moves them as 16-element runs: row runs for row-major outputs, column
     // runs for the transposed outputs ----
-    float* S = stg + wave * (32 * SLD);
+    float* S = reinterpret_cast<float*>(ring) + wave * (32 * SLD);
     const bool mirror = (EPI == EPI_GRAM || EPI == EPI_POLY) && tile.tm != tile.tn;
     const bool need_cols =
         mirror || (EPI == EPI_XUPD && !BF) || (EPI == EPI_FINAL && d.transposed);
@@ -734,10 +758,30 @@ __global__ __launch_bounds__(256) void k_ns_gemm(const MuonMat* __restrict__ tab
 #undef NS_EPI
 }
 
-template <typename T, int EPI>
-int launch_t(const MuonMat* tab, const GemmTile* tiles, int64_t n, const NsArgs& a, hipStream_t st) {
+// One kernel per phase and operand type, named for what it computes so that
+// traces and counters read directly.
+#define NS_KERNEL(NAME, T, EPI)                                                           \
+    __global__ __launch_bounds__(256) void NAME(const MuonMat* __restrict__ tab,          \
+                                                const GemmTile* __restrict__ tiles,       \
+                                                NsArgs args) {                            \
+        ns_gemm_tile<T, EPI>(tab, tiles, args);                                          \
+    }
+NS_KERNEL(k_ns_gram_bf16, __bf16, EPI_GRAM)
+NS_KERNEL(k_ns_poly_bf16, __bf16, EPI_POLY)
+NS_KERNEL(k_ns_xupd_bf16, __bf16, EPI_XUPD)
+NS_KERNEL(k_ns_final_bf16, __bf16, EPI_FINAL)
+NS_KERNEL(k_ns_gram_f32, float, EPI_GRAM)
+NS_KERNEL(k_ns_poly_f32, float, EPI_POLY)
+NS_KERNEL(k_ns_xupd_f32, float, EPI_XUPD)
+NS_KERNEL(k_ns_final_f32, float, EPI_FINAL)
+#undef NS_KERNEL
+
+typedef void (*NsKernel)(const MuonMat*, const GemmTile*, NsArgs);
+
+int launch_k(NsKernel k, const MuonMat* tab, const GemmTile* tiles, int64_t n, const NsArgs& a,
+             hipStream_t st) {
     static_assert(kGemmTile == 256, "tile lists are built for 256x256 tiles");
-    hipLaunchKernelGGL((k_ns_gemm<T, EPI>), dim3((unsigned)n), dim3(256), 0, st, tab, tiles, a);
+    hipLaunchKernelGGL(k, dim3((unsigned)n), dim3(256), 0, st, tab, tiles, a);
     return (int)hipGetLastError();
 }
 
@@ -749,20 +793,9 @@ int launch_ns_phase(int phase, int32_t group, const MuonMat* tab, const GemmTile
     NsArgs a{s.ns_a, s.ns_b, s.ns_c, iter};
     hipStream_t st = (hipStream_t)stream;
     const int epi = phase == 1 ? EPI_GRAM : phase == 2 ? EPI_POLY : (last ? EPI_FINAL : EPI_XUPD);
-    if (group == kGroupBf16) {
-        switch (epi) {
-            case EPI_GRAM: return launch_t<__bf16, EPI_GRAM>(tab, tiles, n_tiles, a, st);
-            case EPI_POLY: return launch_t<__bf16, EPI_POLY>(tab, tiles, n_tiles, a, st);
-            case EPI_XUPD: return launch_t<__bf16, EPI_XUPD>(tab, tiles, n_tiles, a, st);
-            default: return launch_t<__bf16, EPI_FINAL>(tab, tiles, n_tiles, a, st);
-        }
-    }
-    switch (epi) {
-        case EPI_GRAM: return launch_t<float, EPI_GRAM>(tab, tiles, n_tiles, a, st);
-        case EPI_POLY: return launch_t<float, EPI_POLY>(tab, tiles, n_tiles, a, st);
-        case EPI_XUPD: return launch_t<float, EPI_XUPD>(tab, tiles, n_tiles, a, st);
-        default: return launch_t<float, EPI_FINAL>(tab, tiles, n_tiles, a, st);
-    }
+    static const NsKernel bf[4] = {k_ns_gram_bf16, k_ns_poly_bf16, k_ns_xupd_bf16, k_ns_final_bf16};
+    static const NsKernel f32[4] = {k_ns_gram_f32, k_ns_poly_f32, k_ns_xupd_f32, k_ns_final_f32};
+    return launch_k((group == kGroupBf16 ? bf : f32)[epi - 1], tab, tiles, n_tiles, a, st);
 }
 
 }  // namespace ma
