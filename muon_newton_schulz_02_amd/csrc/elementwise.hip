@@ -101,7 +101,8 @@ __global__ __launch_bounds__(1024) void k_clip_finalize(const float* __restrict_
                                                         int64_t n, float max_norm,
                                                         float* __restrict__ coef_out,
                                                         float* __restrict__ norm_out,
-                                                        float* __restrict__ user_norm_out) {
+                                                        float* __restrict__ user_norm_out,
+                                                        int* __restrict__ claim_counter) {
     __shared__ double smem[1024 / 64];
     double acc = 0.0;
     for (int64_t i = threadIdx.x; i < n; i += blockDim.x) acc += (double)partials[i];
@@ -120,6 +121,7 @@ __global__ __launch_bounds__(1024) void k_clip_finalize(const float* __restrict_
         }
         coef_out[0] = (float)coef;
         norm_out[0] = (float)norm;
+        if (claim_counter) claim_counter[0] = 0;
         if (user_norm_out) user_norm_out[0] = (float)norm;
     }
 }
@@ -198,6 +200,84 @@ __global__ __launch_bounds__(kThreads) void k_adamw(const AdamTensor* __restrict
             m[i] = mm;
             v[i] = vv;
         }
+    }
+}
+
+// One 16 Ki-element chunk of AdamW done by a single wave (64 lanes), U
+// 16-byte vectors of each of the four streams in flight per lane.
+template <int U>
+__device__ __forceinline__ void adamw_chunk_wave(const AdamTensor* __restrict__ tab, int n_tab,
+                                                 int64_t chunk, float coef, const AdamArgs& a,
+                                                 int lane) {
+    const int t = find_tensor(tab, n_tab, chunk);
+    const AdamTensor d = tab[t];
+    const int64_t begin = (chunk - d.chunk_begin) * kChunk;
+    const int64_t len = min<int64_t>(kChunk, d.numel - begin);
+    float* p = reinterpret_cast<float*>(d.p) + begin;
+    const float* g = reinterpret_cast<const float*>(d.g) + begin;
+    float* m = reinterpret_cast<float*>(d.m) + begin;
+    float* v = reinterpret_cast<float*>(d.v) + begin;
+    if (d.vec_ok && len == kChunk) {
+        f4* p4 = reinterpret_cast<f4*>(p);
+        const f4* g4 = reinterpret_cast<const f4*>(g);
+        f4* m4 = reinterpret_cast<f4*>(m);
+        f4* v4 = reinterpret_cast<f4*>(v);
+        static_assert(kChunk / 4 % (64 * U) == 0, "chunk split");
+        for (int i0 = lane; i0 < kChunk / 4; i0 += 64 * U) {
+            f4 pp[U], gg[U], mm[U], vv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + u * 64;
+                pp[u] = __builtin_nontemporal_load(p4 + i);
+                gg[u] = __builtin_nontemporal_load(g4 + i);
+                mm[u] = __builtin_nontemporal_load(m4 + i);
+                vv[u] = __builtin_nontemporal_load(v4 + i);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float pq = pp[u][q], mq = mm[u][q], vq = vv[u][q];
+                    adam_elem(pq, gg[u][q], mq, vq, coef, a);
+                    pp[u][q] = pq;
+                    mm[u][q] = mq;
+                    vv[u][q] = vq;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + u * 64;
+                __builtin_nontemporal_store(pp[u], p4 + i);
+                __builtin_nontemporal_store(mm[u], m4 + i);
+                __builtin_nontemporal_store(vv[u], v4 + i);
+            }
+        }
+    } else {
+        for (int64_t i = lane; i < len; i += 64) {
+            float pp = p[i], mm = m[i], vv = v[i];
+            adam_elem(pp, g[i], mm, vv, coef, a);
+            p[i] = pp;
+            m[i] = mm;
+            v[i] = vv;
+        }
+    }
+}
+
+// AdamW with chunks claimed per wave from a shared counter; every wave runs
+// until the counter passes n_chunks.
+template <int U>
+__global__ __launch_bounds__(kThreads) void k_adamw_claim(const AdamTensor* __restrict__ tab,
+                                                          int n_tab, int64_t n_chunks,
+                                                          const float* __restrict__ coef_ptr,
+                                                          AdamArgs a, int* __restrict__ counter) {
+    const int lane = threadIdx.x & 63;
+    const float coef = *coef_ptr;
+    for (;;) {
+        int c = 0;
+        if (lane == 0) c = atomicAdd(counter, 1);
+        c = __builtin_amdgcn_readfirstlane(c);
+        if ((int64_t)c >= n_chunks) break;
+        adamw_chunk_wave<U>(tab, n_tab, c, coef, a, lane);
     }
 }
 
@@ -373,9 +453,9 @@ int launch_norm_partials(const NormTensor* tab, int32_t n_tab, int64_t n_chunks,
 }
 
 int launch_clip_finalize(const float* partials, int64_t n, float max_grad_norm, float* coef_out,
-                         float* norm_out, float* user_norm_out, void* stream) {
+                         float* norm_out, float* user_norm_out, int* claim_counter, void* stream) {
     hipLaunchKernelGGL(k_clip_finalize, dim3(1), dim3(1024), 0, (hipStream_t)stream, partials, n,
-                       max_grad_norm, coef_out, norm_out, user_norm_out);
+                       max_grad_norm, coef_out, norm_out, user_norm_out, claim_counter);
     return (int)hipGetLastError();
 }
 
@@ -400,6 +480,25 @@ int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, const f
     else
         hipLaunchKernelGGL(k_adamw<4>, dim3((unsigned)n_chunks), dim3(kThreads), 0,
                            (hipStream_t)stream, tab, n_tab, coef, a);
+    return (int)hipGetLastError();
+}
+
+int launch_adamw_claim(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, const float* coef,
+                       const StepScalars& s, int* counter, int64_t grid, void* stream) {
+    if (n_chunks == 0 || grid <= 0) return (int)hipSuccess;
+    AdamArgs a;
+    a.step_size = s.step_size;
+    a.inv_sqrt_bc2 = s.inv_sqrt_bc2;
+    a.decay = s.adam_decay;
+    a.beta1 = s.beta1;
+    a.beta2 = s.beta2;
+    a.one_m_beta1 = s.one_m_beta1;
+    a.one_m_beta2 = s.one_m_beta2;
+    a.eps = s.eps;
+    // four vectors per stream in flight: 88 VGPRs, which with a Newton-Schulz
+    // GEMM wave's 168 VGPRs + 256 AGPRs fills a SIMD's 512 exactly
+    hipLaunchKernelGGL(k_adamw_claim<4>, dim3((unsigned)grid), dim3(kThreads), 0,
+                       (hipStream_t)stream, tab, n_tab, n_chunks, coef, a, counter);
     return (int)hipGetLastError();
 }
 

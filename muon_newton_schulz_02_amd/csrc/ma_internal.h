@@ -97,7 +97,7 @@ struct Layout {
     std::vector<int32_t> op_group;                   // per Muon matrix: kGroupBf16 / kGroupFp32
     std::vector<GemmTile> g1[2], g2[2], g3[2];       // cost-ordered tile lists per group
     size_t g1_off[2] = {0, 0}, g2_off[2] = {0, 0}, g3_off[2] = {0, 0};
-    size_t scalars_off = 0;                          // coef (float), norm (float)
+    size_t scalars_off = 0;                          // coef (float), norm (float), AdamW chunk counter (int)
     size_t norm_partials_off = 0;                    // float[n_norm_chunks]
     size_t muon_partials_off = 0;                    // float[n_muon_chunks]
     size_t muon_scale_off = 0;                       // float[n_muon]
@@ -181,11 +181,23 @@ struct StepScalars {
 // Each returns a hipError_t as int.
 int launch_norm_partials(const NormTensor* tab, int32_t n_tab, int64_t n_chunks,
                          float* partials, void* stream);
+// Also zeroes `claim_counter` (nullable), the chunk counter of
+// launch_adamw_claim, so every step starts claiming at chunk 0.
 int launch_clip_finalize(const float* partials, int64_t n, float max_grad_norm,
-                         float* coef_out, float* norm_out, float* user_norm_out, void* stream);
+                         float* coef_out, float* norm_out, float* user_norm_out,
+                         int* claim_counter, void* stream);
 // `concurrent`: the launch shares the GPU with the Newton-Schulz GEMMs.
 int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
                  const float* coef, const StepScalars& s, bool concurrent, void* stream);
+// AdamW whose 16 Ki-element chunks are claimed one at a time by single waves
+// from `counter` until all n_chunks are taken.  Several such launches, on
+// different streams, may share one counter: each chunk is processed exactly
+// once, and since AdamW is elementwise the result does not depend on which
+// launch takes it.  Its waves are lean enough (88 VGPRs) to share a SIMD with
+// a Newton-Schulz GEMM wave.
+int launch_adamw_claim(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
+                       const float* coef, const StepScalars& s, int* counter, int64_t grid,
+                       void* stream);
 int launch_muon_momentum(const MuonMat* tab, int32_t n_tab, int64_t n_chunks,
                          const float* coef, const StepScalars& s, float* partials, void* stream);
 int launch_muon_scale(const MuonMat* tab, int32_t n_tab, const float* partials,

@@ -213,7 +213,7 @@ void build_layout(ma_plan* p, int32_t precision) {
     L = Layout();
     // operand group and GEMM tiles of every matrix: Gram and polynomial
     // phases cover the upper triangle of the r x r result (mirrored on
-    // write), the X update the whole r x c result
+    // write), the X update the whole r x c result in column-major order
     for (size_t k = 0; k < p->muon_ids.size(); ++k) {
         const auto& e = p->entries[p->muon_ids[k]];
         const int32_t grp =
@@ -226,8 +226,11 @@ void build_layout(ma_plan* p, int32_t precision) {
                 L.g1[grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)C});
                 L.g2[grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R});
             }
-        for (int32_t i = 0; i < TR; ++i)
-            for (int32_t j = 0; j < TC; ++j) L.g3[grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R});
+        // column-major: the tiles of one column block (all readers of that
+        // X panel) are consecutive, so the tiles an XCD runs together read
+        // each panel once from HBM while the r x r B stays in its L2
+        for (int32_t j = 0; j < TC; ++j)
+            for (int32_t i = 0; i < TR; ++i) L.g3[grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R});
     }
     for (int g = 0; g < 2; ++g) {
         schedule_tiles(L.g1[g]);

@@ -61,6 +61,11 @@ int get_staging(const ma_plan* plan, size_t bytes, void** out, void** event) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Workgroups of the AdamW launch that runs beside the Muon group (one per CU
+// of the MI355X), and of the launch that finishes the remaining chunks.
+constexpr int64_t kSideAdamGroups = 256;
+constexpr int64_t kFinishAdamGroups = 2048;
+
 // The side stream and fork/join events of the current device (created on
 // first use; default priority, non-blocking with respect to the null stream).
 int get_side(const ma_plan* plan, ma_plan::Side** out) {
@@ -312,14 +317,16 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
 
     int err = launch_norm_partials(d_norm, n_train, plan->n_norm_chunks, norm_partials, stream);
     if (err) return hip_fail("clip norm partials", err);
+    int* claim = reinterpret_cast<int*>(scal + 2);
     err = launch_clip_finalize(norm_partials, plan->n_norm_chunks, sc.max_grad_norm, coef, norm,
-                               grad_norm_out, stream);
+                               grad_norm_out, claim, stream);
     if (err) return hip_fail("clip finalize", err);
     if ((err = mark(1))) return hip_fail("phase event", err);
     // AdamW: on the caller's stream, or forked to the side stream so it runs
     // concurrently with the Muon group and joined back at the end
     ma_plan::Side* side = nullptr;
-    if (plan->overlap && n_adam > 0 && n_muon > 0) {
+    // (the chunk counter is an int: beyond 2^30 chunks run serially)
+    if (plan->overlap && n_adam > 0 && n_muon > 0 && plan->n_adam_chunks < (int64_t(1) << 30)) {
         int rs = get_side(plan, &side);
         if (rs != MA_OK) return rs;
         hipStream_t ss = (hipStream_t)side->stream;
@@ -327,7 +334,11 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
             return hip_fail("hipEventRecord (fork)", e);
         if ((e = hipStreamWaitEvent(ss, (hipEvent_t)side->ev_fork, 0)) != hipSuccess)
             return hip_fail("hipStreamWaitEvent (fork)", e);
-        err = launch_adamw(d_adam, n_adam, plan->n_adam_chunks, coef, sc, true, ss);
+        // one workgroup per CU: each of its waves shares a SIMD with a
+        // Newton-Schulz GEMM wave (whose LDS and registers leave room for
+        // exactly that) and streams AdamW chunks while the GEMMs run
+        err = launch_adamw_claim(d_adam, n_adam, plan->n_adam_chunks, coef, sc, claim,
+                                 kSideAdamGroups, ss);
         if (err) return hip_fail("adamw", err);
         if (phase_events && phase_events[2] &&
             (e = hipEventRecord((hipEvent_t)phase_events[2], ss)) != hipSuccess)
@@ -363,6 +374,12 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         }
     } else if ((err = mark(3))) {
         return hip_fail("phase event", err);
+    }
+    if (side) {
+        // the chunks the side kernel has not claimed yet, at full occupancy
+        err = launch_adamw_claim(d_adam, n_adam, plan->n_adam_chunks, coef, sc, claim,
+                                 kFinishAdamGroups, stream);
+        if (err) return hip_fail("adamw", err);
     }
     if (side && (e = hipStreamWaitEvent(st, (hipEvent_t)side->ev_join, 0)) != hipSuccess)
         return hip_fail("hipStreamWaitEvent (join)", e);
