@@ -4,11 +4,11 @@
 //     workgroup in double precision -> clip factor in device memory;
 //   * AdamW: multi-tensor fused clip-scale + decoupled-decay Adam with
 //     128-bit loads and stores;
-//   * Muon momentum: clip-scale, momentum/Nesterov, buffer write-back and a
-//     per-chunk partial of ||u||_F^2; per-matrix finalisation in double;
-//   * normalise/orient: scale u to unit Frobenius norm and write the NS
-//     operands in canonical orientation (rows <= cols) and transposed,
-//     through an LDS tile, zero-filling the padding.
+//   * Muon prep: per 64 x 64 tile, clip-scale, momentum/Nesterov, buffer
+//     write-back, the Newton-Schulz input operands in canonical orientation
+//     (rows <= cols, transposed through LDS, zero padding) and a partial of
+//     ||u||_F^2; per-matrix finalisation in double gives the normalising
+//     factor that the first Newton-Schulz launches apply.
 //
 // Method: OpenDM training-stack page, Muon/AdamW hybrid section (routing,
 // hyperparameter table: momentum 0.95 with Nesterov) and the defaults table
@@ -281,86 +281,35 @@ __global__ __launch_bounds__(kThreads) void k_adamw_claim(const AdamTensor* __re
     }
 }
 
-// -------------------------------------------------------- Muon momentum --
+// ------------------------------------------------- Muon momentum + operands --
 struct MomArgs {
     float mu;
     int nesterov;
 };
 
+// Clip-scaled gradient, momentum buffer update and the Nesterov (or plain)
+// momentum direction u of one element.
 __device__ __forceinline__ float momentum_elem(float g, float& buf, float coef, const MomArgs& a) {
     const float gc = g * coef;
     buf = fmaf(a.mu, buf, gc);
     return a.nesterov ? fmaf(a.mu, buf, gc) : buf;
 }
 
-__global__ __launch_bounds__(kThreads) void k_muon_momentum(const MuonMat* __restrict__ tab,
-                                                            int n_tab,
-                                                            const float* __restrict__ coef_ptr,
-                                                            MomArgs a,
-                                                            float* __restrict__ partials) {
-    __shared__ float smem[kThreads / 64];
-    const int64_t chunk = blockIdx.x;
-    const int t = find_tensor(tab, n_tab, chunk);
-    const MuonMat& d = tab[t];
-    const int64_t begin = (chunk - d.chunk_begin) * kChunk;
-    const int64_t len = min<int64_t>(kChunk, d.numel - begin);
-    const float* g = reinterpret_cast<const float*>(d.g) + begin;
-    float* buf = reinterpret_cast<float*>(d.buf) + begin;
-    const float coef = *coef_ptr;
-    float acc = 0.f;
-    if (d.vec_ok && len == kChunk) {
-        const float4* g4 = reinterpret_cast<const float4*>(g);
-        float4* b4 = reinterpret_cast<float4*>(buf);
-#pragma unroll 2
-        for (int i = threadIdx.x; i < kChunk / 4; i += kThreads) {
-            const float4 gg = g4[i];
-            float4 bb = b4[i];
-            const float u0 = momentum_elem(gg.x, bb.x, coef, a);
-            const float u1 = momentum_elem(gg.y, bb.y, coef, a);
-            const float u2 = momentum_elem(gg.z, bb.z, coef, a);
-            const float u3 = momentum_elem(gg.w, bb.w, coef, a);
-            b4[i] = bb;
-            acc = fmaf(u0, u0, acc);
-            acc = fmaf(u1, u1, acc);
-            acc = fmaf(u2, u2, acc);
-            acc = fmaf(u3, u3, acc);
-        }
-    } else {
-        for (int64_t i = threadIdx.x; i < len; i += kThreads) {
-            float bb = buf[i];
-            const float u = momentum_elem(g[i], bb, coef, a);
-            buf[i] = bb;
-            acc = fmaf(u, u, acc);
-        }
+// Index of the Muon matrix whose operand-tile range holds `blk`.
+__device__ __forceinline__ int find_matrix(const MuonMat* tab, int n, int64_t blk) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tab[mid].orient_begin <= blk) lo = mid;
+        else hi = mid - 1;
     }
-    const float s = block_sum(acc, smem);
-    if (threadIdx.x == 0) partials[chunk] = s;
+    return lo;
 }
 
-// One workgroup per matrix: 1 / (||u||_F + eps) from its chunk partials.
-__global__ __launch_bounds__(256) void k_muon_scale(const MuonMat* __restrict__ tab,
-                                                    const float* __restrict__ partials,
-                                                    float ns_eps, float* __restrict__ scales) {
-    __shared__ double smem[256 / 64];
-    const MuonMat& d = tab[blockIdx.x];
-    double acc = 0.0;
-    for (int i = threadIdx.x; i < d.n_chunks; i += blockDim.x)
-        acc += (double)partials[d.chunk_begin + i];
-    acc = wave_sum_d(acc);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) smem[wave] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        double tot = 0.0;
-        for (int w = 0; w < 4; ++w) tot += smem[w];
-        scales[blockIdx.x] = (float)(1.0 / (sqrt(tot) + (double)ns_eps));
-    }
-}
-
-// ------------------------------------------------------ normalise/orient --
-// Tile (ti, tj) of the canonical padded R x C operand.  Canonical (i, j) is
-// stored (i, j), or stored (j, i) for a transposed matrix.  Values outside the
-// true r x c are zero.
+// The Newton-Schulz input operand of canonical tile (i0, j0), from the LDS
+// tile of u in stored orientation: canonical (i, j) is stored (i, j), or
+// stored (j, i) for a transposed matrix.  Values outside the true r x c are
+// zero.
 // bf16 operands: X as a hi / lo pair of row-major bf16 matrices (step-0
 // buffers), hi = RNE(x), lo = RNE(x - hi).
 __device__ __forceinline__ void write_operands_bf16(const MuonMat& d,
@@ -386,61 +335,148 @@ __device__ __forceinline__ void write_operands_fp32(const MuonMat& d,
     constexpr int TS = kOrientTile;
     float* x = reinterpret_cast<float*>(d.x[0]);
     float* xt = reinterpret_cast<float*>(d.xt[0]);
-    // canonical rows i0.., cols j0..
     for (int idx = threadIdx.x; idx < TS * TS; idx += kThreads) {
         const int a_ = idx / TS, b_ = idx % TS;
         x[(int64_t)(i0 + a_) * d.C + (j0 + b_)] = d.transposed ? tile[b_][a_] : tile[a_][b_];
     }
-    // transposed operand: rows j0.., cols i0..
     for (int idx = threadIdx.x; idx < TS * TS; idx += kThreads) {
         const int a_ = idx / TS, b_ = idx % TS;  // a_ along canonical cols, b_ along rows
         xt[(int64_t)(j0 + a_) * d.R + (i0 + b_)] = d.transposed ? tile[a_][b_] : tile[b_][a_];
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_orient(const MuonMat* __restrict__ tab, int n_tab,
-                                                     const float* __restrict__ coef_ptr,
-                                                     const float* __restrict__ scales, MomArgs a) {
+// One 64 x 64 tile of the padded canonical R x C operand of a Muon matrix:
+// read the clip-scaled gradient and the momentum buffer of the stored tile,
+// write the updated buffer back, and write u -- not yet normalised -- as the
+// Newton-Schulz input operand in canonical orientation, zero padding
+// included; plus this tile's partial of ||u||_F^2.  The normalising factor
+// is applied by the first Newton-Schulz launches (Gram: its square; X
+// update: itself), which is exact up to rounding since every product is
+// homogeneous in X.
+__global__ __launch_bounds__(kThreads) void k_muon_prep(const MuonMat* __restrict__ tab, int n_tab,
+                                                        const float* __restrict__ coef_ptr,
+                                                        MomArgs a, float* __restrict__ partials) {
     constexpr int TS = kOrientTile;
     __shared__ float tile[TS][TS + 1];
+    __shared__ float smem[kThreads / 64];
     const int64_t blk = blockIdx.x;
-    // find the matrix by orient_begin
-    int lo = 0, hi = n_tab - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (tab[mid].orient_begin <= blk) lo = mid;
-        else hi = mid - 1;
-    }
-    const MuonMat& d = tab[lo];
+    const MuonMat& d = tab[find_matrix(tab, n_tab, blk)];
     const int64_t local = blk - d.orient_begin;
     const int tiles_c = d.C / TS;
-    const int ti = (int)(local / tiles_c), tj = (int)(local % tiles_c);
-    const int i0 = ti * TS, j0 = tj * TS;
+    const int i0 = (int)(local / tiles_c) * TS, j0 = (int)(local % tiles_c) * TS;
     const float coef = *coef_ptr;
-    const float s = scales[lo];
     const float* g = reinterpret_cast<const float*>(d.g);
-    const float* buf = reinterpret_cast<const float*>(d.buf);
+    float* buf = reinterpret_cast<float*>(d.buf);
     // stored tile origin: rows sr0.., cols sc0..
     const int sr0 = d.transposed ? j0 : i0;
     const int sc0 = d.transposed ? i0 : j0;
-    for (int idx = threadIdx.x; idx < TS * TS; idx += kThreads) {
-        const int lr = idx / TS, lc = idx % TS;
-        const int sr = sr0 + lr, sc = sc0 + lc;
-        float u = 0.f;
-        if (sr < d.m && sc < d.n) {
-            const int64_t o = (int64_t)sr * d.n + sc;
-            // recompute u from the updated buffer: identical fp32 operations
-            // to the momentum pass
-            const float gc = g[o] * coef;
-            const float bb = buf[o];
-            u = a.nesterov ? fmaf(a.mu, bb, gc) : bb;
-            u *= s;
+    float acc = 0.f;
+    if (d.vec_ok && sr0 + TS <= d.m && sc0 + TS <= d.n) {
+        // whole tile inside the matrix: 16-byte accesses, 4 per thread
+        for (int q = threadIdx.x; q < TS * TS / 4; q += kThreads) {
+            const int lr = q / (TS / 4), lc = (q % (TS / 4)) * 4;
+            const int64_t o = (int64_t)(sr0 + lr) * d.n + (sc0 + lc);
+            const float4 gg = *reinterpret_cast<const float4*>(g + o);
+            float4 bb = *reinterpret_cast<const float4*>(buf + o);
+            const float u0 = momentum_elem(gg.x, bb.x, coef, a);
+            const float u1 = momentum_elem(gg.y, bb.y, coef, a);
+            const float u2 = momentum_elem(gg.z, bb.z, coef, a);
+            const float u3 = momentum_elem(gg.w, bb.w, coef, a);
+            *reinterpret_cast<float4*>(buf + o) = bb;
+            tile[lr][lc] = u0;
+            tile[lr][lc + 1] = u1;
+            tile[lr][lc + 2] = u2;
+            tile[lr][lc + 3] = u3;
+            acc = fmaf(u0, u0, acc);
+            acc = fmaf(u1, u1, acc);
+            acc = fmaf(u2, u2, acc);
+            acc = fmaf(u3, u3, acc);
         }
-        tile[lr][lc] = u;
+    } else {
+        for (int idx = threadIdx.x; idx < TS * TS; idx += kThreads) {
+            const int lr = idx / TS, lc = idx % TS;
+            const int sr = sr0 + lr, sc = sc0 + lc;
+            float u = 0.f;
+            if (sr < d.m && sc < d.n) {
+                const int64_t o = (int64_t)sr * d.n + sc;
+                float bb = buf[o];
+                u = momentum_elem(g[o], bb, coef, a);
+                buf[o] = bb;
+            }
+            tile[lr][lc] = u;
+            acc = fmaf(u, u, acc);
+        }
     }
-    __syncthreads();
+    const float part = block_sum(acc, smem);  // its barrier also completes the tile
+    if (threadIdx.x == 0) partials[blk] = part;
     if (d.op_bf16) write_operands_bf16(d, tile, i0, j0);
     else write_operands_fp32(d, tile, i0, j0);
+}
+
+// Below 2^-40 or above 2^40 for ||u||_F, products of unnormalised operand
+// values could leave the fp32 range inside the Gram product; such matrices
+// get their operands scaled in place instead (k_operand_rescale).
+constexpr double kNormLo = 0x1p-40, kNormHi = 0x1p40;
+
+// One workgroup per matrix: s = 1 / (||u||_F + eps) from its tile partials,
+// summed in double in a fixed order.  ns_scale[k] is the factor the first
+// Newton-Schulz launches apply; pre_scale[k] != 0 asks k_operand_rescale to
+// scale the operands themselves (and ns_scale[k] is then 1).
+__global__ __launch_bounds__(256) void k_muon_scale(const MuonMat* __restrict__ tab,
+                                                    const float* __restrict__ partials,
+                                                    float ns_eps, float* __restrict__ ns_scale,
+                                                    float* __restrict__ pre_scale) {
+    __shared__ double smem[256 / 64];
+    const MuonMat& d = tab[blockIdx.x];
+    const int64_t n_tiles = (int64_t)(d.R / kOrientTile) * (d.C / kOrientTile);
+    double acc = 0.0;
+    for (int64_t i = threadIdx.x; i < n_tiles; i += blockDim.x)
+        acc += (double)partials[d.orient_begin + i];
+    acc = wave_sum_d(acc);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) smem[wave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double tot = 0.0;
+        for (int w = 0; w < 4; ++w) tot += smem[w];
+        const double nrm = sqrt(tot);
+        const float s = (float)(1.0 / (nrm + (double)ns_eps));
+        const bool in_range = nrm >= kNormLo && nrm <= kNormHi;  // false for NaN
+        ns_scale[blockIdx.x] = in_range ? s : 1.f;
+        pre_scale[blockIdx.x] = in_range ? 0.f : s;
+    }
+}
+
+// Scale the Newton-Schulz input operands of the matrices whose pre_scale is
+// non-zero (a norm outside [2^-40, 2^40]); kRescaleSplit workgroups per
+// matrix, the others return at once.
+constexpr int kRescaleSplit = 16;
+
+__global__ __launch_bounds__(kThreads) void k_operand_rescale(const MuonMat* __restrict__ tab,
+                                                              const float* __restrict__ pre_scale) {
+    const int k = blockIdx.x / kRescaleSplit, part = blockIdx.x % kRescaleSplit;
+    const float f = pre_scale[k];
+    if (f == 0.f) return;
+    const MuonMat& d = tab[k];
+    const int64_t n = (int64_t)d.R * d.C;
+    const int64_t stride = (int64_t)kRescaleSplit * kThreads;
+    if (d.op_bf16) {
+        __bf16* hi = reinterpret_cast<__bf16*>(d.x[0]);
+        __bf16* lo = reinterpret_cast<__bf16*>(d.xlo[0]);
+        for (int64_t i = (int64_t)part * kThreads + threadIdx.x; i < n; i += stride) {
+            const float v = f * ((float)hi[i] + (float)lo[i]);
+            const __bf16 h = (__bf16)v;
+            hi[i] = h;
+            lo[i] = (__bf16)(v - (float)h);
+        }
+    } else {
+        float* x = reinterpret_cast<float*>(d.x[0]);
+        float* xt = reinterpret_cast<float*>(d.xt[0]);
+        for (int64_t i = (int64_t)part * kThreads + threadIdx.x; i < n; i += stride) {
+            x[i] *= f;
+            xt[i] *= f;
+        }
+    }
 }
 }  // namespace
 
@@ -460,7 +496,7 @@ int launch_clip_finalize(const float* partials, int64_t n, float max_grad_norm, 
 }
 
 int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, const float* coef,
-                 const StepScalars& s, bool concurrent, void* stream) {
+                 const StepScalars& s, void* stream) {
     if (n_chunks == 0) return (int)hipSuccess;
     AdamArgs a;
     a.step_size = s.step_size;
@@ -471,15 +507,9 @@ int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, const f
     a.one_m_beta1 = s.one_m_beta1;
     a.one_m_beta2 = s.one_m_beta2;
     a.eps = s.eps;
-    // Serial: four vectors per stream in flight (108 VGPRs) for the full
-    // HBM rate.  Concurrent with the Newton-Schulz GEMMs: two (fewer VGPRs),
-    // so an AdamW wave fits on a SIMD beside a GEMM wave.
-    if (concurrent)
-        hipLaunchKernelGGL(k_adamw<2>, dim3((unsigned)n_chunks), dim3(kThreads), 0,
-                           (hipStream_t)stream, tab, n_tab, coef, a);
-    else
-        hipLaunchKernelGGL(k_adamw<4>, dim3((unsigned)n_chunks), dim3(kThreads), 0,
-                           (hipStream_t)stream, tab, n_tab, coef, a);
+    // four vectors per stream in flight (108 VGPRs) for the full HBM rate
+    hipLaunchKernelGGL(k_adamw<4>, dim3((unsigned)n_chunks), dim3(kThreads), 0, (hipStream_t)stream,
+                       tab, n_tab, coef, a);
     return (int)hipGetLastError();
 }
 
@@ -502,29 +532,24 @@ int launch_adamw_claim(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, c
     return (int)hipGetLastError();
 }
 
-int launch_muon_momentum(const MuonMat* tab, int32_t n_tab, int64_t n_chunks, const float* coef,
-                         const StepScalars& s, float* partials, void* stream) {
-    if (n_chunks == 0) return (int)hipSuccess;
+int launch_muon_prep(const MuonMat* tab, int32_t n_tab, int64_t n_tiles, const float* coef,
+                     const StepScalars& s, float* partials, void* stream) {
+    if (n_tiles == 0) return (int)hipSuccess;
     MomArgs a{s.mu, s.nesterov};
-    hipLaunchKernelGGL(k_muon_momentum, dim3((unsigned)n_chunks), dim3(kThreads), 0,
-                       (hipStream_t)stream, tab, n_tab, coef, a, partials);
+    hipLaunchKernelGGL(k_muon_prep, dim3((unsigned)n_tiles), dim3(kThreads), 0, (hipStream_t)stream,
+                       tab, n_tab, coef, a, partials);
     return (int)hipGetLastError();
 }
 
 int launch_muon_scale(const MuonMat* tab, int32_t n_tab, const float* partials, float ns_eps,
-                      float* scales, void* stream) {
+                      float* ns_scale, float* pre_scale, void* stream) {
     if (n_tab == 0) return (int)hipSuccess;
     hipLaunchKernelGGL(k_muon_scale, dim3((unsigned)n_tab), dim3(256), 0, (hipStream_t)stream, tab,
-                       partials, ns_eps, scales);
-    return (int)hipGetLastError();
-}
-
-int launch_orient(const MuonMat* tab, int32_t n_tab, int64_t n_tiles, const float* coef,
-                  const float* scales, const StepScalars& s, void* stream) {
-    if (n_tiles == 0) return (int)hipSuccess;
-    MomArgs a{s.mu, s.nesterov};
-    hipLaunchKernelGGL(k_orient, dim3((unsigned)n_tiles), dim3(kThreads), 0, (hipStream_t)stream,
-                       tab, n_tab, coef, scales, a);
+                       partials, ns_eps, ns_scale, pre_scale);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    hipLaunchKernelGGL(k_operand_rescale, dim3((unsigned)n_tab * kRescaleSplit), dim3(kThreads), 0,
+                       (hipStream_t)stream, tab, pre_scale);
     return (int)hipGetLastError();
 }
 

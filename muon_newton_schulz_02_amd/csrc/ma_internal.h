@@ -71,9 +71,7 @@ struct MuonMat {
     uint64_t x[2], xlo[2], xt[2];
     uint64_t a, b;                 // R x R, operand type
     int64_t  numel;                // m * n
-    int64_t  chunk_begin;          // momentum-pass chunks (one partial each)
-    int64_t  orient_begin;         // first orient tile
-    int32_t  n_chunks;
+    int64_t  orient_begin;         // first 64 x 64 operand tile of the prep pass
     int32_t  m, n, r, c, R, C;
     int32_t  transposed;
     int32_t  vec_ok;               // p, g, buf (and delta) 16-byte aligned and n % 4 == 0
@@ -99,8 +97,9 @@ struct Layout {
     size_t g1_off[2] = {0, 0}, g2_off[2] = {0, 0}, g3_off[2] = {0, 0};
     size_t scalars_off = 0;                          // coef (float), norm (float), AdamW chunk counter (int)
     size_t norm_partials_off = 0;                    // float[n_norm_chunks]
-    size_t muon_partials_off = 0;                    // float[n_muon_chunks]
-    size_t muon_scale_off = 0;                       // float[n_muon]
+    size_t muon_partials_off = 0;                    // float[n_orient_tiles]
+    size_t muon_scale_off = 0;                       // float[n_muon]: factor applied in NS
+    size_t muon_prescale_off = 0;                    // float[n_muon]: operand rescale (0: none)
     size_t ns_off = 0;                               // start of per-matrix NS buffers
     std::vector<size_t> x0, x1, lo0, lo1, xt0, xt1, a, b;  // per Muon matrix (0: unused)
     size_t total = 0;
@@ -130,9 +129,9 @@ struct ma_plan {
     std::vector<ma::Bucket> buckets;
     std::vector<int32_t> muon_ids, adam_ids, train_ids;   // entry indices
     int64_t adam_numel = 0;
-    int64_t n_norm_chunks = 0, n_adam_chunks = 0, n_muon_chunks = 0, n_orient_tiles = 0;
+    int64_t n_norm_chunks = 0, n_adam_chunks = 0, n_orient_tiles = 0;
     std::vector<int64_t> norm_chunk_begin, adam_chunk_begin;     // per train / adam id
-    std::vector<int64_t> muon_chunk_begin, muon_orient_begin;    // per muon id
+    std::vector<int64_t> muon_orient_begin;                      // per muon id
     ma::Layout layout[2];                                        // per NS precision
     std::string dump;
 
@@ -186,9 +185,8 @@ int launch_norm_partials(const NormTensor* tab, int32_t n_tab, int64_t n_chunks,
 int launch_clip_finalize(const float* partials, int64_t n, float max_grad_norm,
                          float* coef_out, float* norm_out, float* user_norm_out,
                          int* claim_counter, void* stream);
-// `concurrent`: the launch shares the GPU with the Newton-Schulz GEMMs.
 int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
-                 const float* coef, const StepScalars& s, bool concurrent, void* stream);
+                 const float* coef, const StepScalars& s, void* stream);
 // AdamW whose 16 Ki-element chunks are claimed one at a time by single waves
 // from `counter` until all n_chunks are taken.  Several such launches, on
 // different streams, may share one counter: each chunk is processed exactly
@@ -198,15 +196,20 @@ int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
 int launch_adamw_claim(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
                        const float* coef, const StepScalars& s, int* counter, int64_t grid,
                        void* stream);
-int launch_muon_momentum(const MuonMat* tab, int32_t n_tab, int64_t n_chunks,
-                         const float* coef, const StepScalars& s, float* partials, void* stream);
-int launch_muon_scale(const MuonMat* tab, int32_t n_tab, const float* partials,
-                      float ns_eps, float* scales, void* stream);
-int launch_orient(const MuonMat* tab, int32_t n_tab, int64_t n_tiles, const float* coef,
-                  const float* scales, const StepScalars& s, void* stream);
+// Momentum/Nesterov and the unnormalised Newton-Schulz input operands, one
+// workgroup per 64 x 64 operand tile, with per-tile partials of ||u||_F^2.
+int launch_muon_prep(const MuonMat* tab, int32_t n_tab, int64_t n_tiles, const float* coef,
+                     const StepScalars& s, float* partials, void* stream);
+// Per matrix, the normalising factor 1 / (||u||_F + eps): into ns_scale
+// (applied by the first Newton-Schulz launches), or, for a norm outside
+// [2^-40, 2^40], applied to the operands in place (ns_scale = 1).
+int launch_muon_scale(const MuonMat* tab, int32_t n_tab, const float* partials, float ns_eps,
+                      float* ns_scale, float* pre_scale, void* stream);
 // phase 1 = Gram, 2 = polynomial, 3 = X update (the parameter update when
 // `last`); group = kGroupBf16 / kGroupFp32 selects the operand type.
+// `ns_scale`: the per-matrix normalising factor, applied on iteration 0.
 int launch_ns_phase(int phase, int32_t group, const MuonMat* tab, const GemmTile* tiles,
-                    int64_t n_tiles, int iter, int last, const StepScalars& s, void* stream);
+                    int64_t n_tiles, int iter, int last, const StepScalars& s,
+                    const float* ns_scale, void* stream);
 
 }  // namespace ma

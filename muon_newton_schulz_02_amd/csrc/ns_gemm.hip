@@ -77,6 +77,9 @@ struct Mma<float> {
 struct NsArgs {
     float a, b, c;
     int iter;
+    // per matrix 1 / (||u||_F + eps): the input operand is u itself, so the
+    // first Gram scales by its square and the first X update by it
+    const float* scales;
 };
 
 // Global-memory accesses through address-space-1 pointers, so they are
@@ -336,9 +339,9 @@ __device__ __forceinline__ void unpack16(const uint4* q, float* v, bool bf) {
 // stay in registers.
 template <typename T, int EPI, int SLD>
 __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, const MuonMat& d,
-                                          float* S, const NsArgs& args, int lane, int bi, int bj,
-                                          int cur, bool need_cols, bool poly_direct, T* out_direct,
-                                          int64_t ld_direct) {
+                                          float* S, const NsArgs& args, float escale, int lane,
+                                          int bi, int bj, int cur, bool need_cols,
+                                          bool poly_direct, T* out_direct, int64_t ld_direct) {
     constexpr bool BF = sizeof(T) == 2;
     const int rrow = lane >> 1, rc0 = (lane & 1) * 16;   // row run of this lane
     const int ccol = lane & 31, cr0 = (lane >> 5) * 16;  // column run of this lane
@@ -356,6 +359,8 @@ __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, co
         const int gi = bi + rrow, gj = bj + rc0;
         const int64_t o = (int64_t)gi * d.C + gj;
         if (EPI == EPI_GRAM) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v[e] *= escale;
             store16(out_direct + (int64_t)gi * ld_direct + gj, v);
         } else if (EPI == EPI_POLY) {
             if (poly_direct) {
@@ -373,7 +378,7 @@ __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, co
             float lv[16];
             unpack16(in.q, lv, true);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) v[e] = fmaf(args.a, lv[e], v[e]);
+            for (int e = 0; e < 16; ++e) v[e] = escale * fmaf(args.a, lv[e], v[e]);
             if (EPI == EPI_XUPD) {
                 store16_hilo(reinterpret_cast<__bf16*>(d.x[cur ^ 1]) + o,
                              reinterpret_cast<__bf16*>(d.xlo[cur ^ 1]) + o, v);
@@ -384,7 +389,7 @@ __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, co
             float xv[16];
             unpack16(in.q, xv, false);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) v[e] = fmaf(args.a, xv[e], v[e]);
+            for (int e = 0; e < 16; ++e) v[e] = escale * fmaf(args.a, xv[e], v[e]);
             if (EPI == EPI_XUPD) {
                 store16(reinterpret_cast<float*>(d.x[0]) + o, v);
             } else if (!d.transposed) {
@@ -728,6 +733,8 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
         ld_direct = d.R;
     }
     const int bi0 = m0 + wm * 128, bj0 = n0 + wn * 128;
+    const float s0 = args.iter == 0 ? args.scales[tile.mat] : 1.f;
+    const float escale = EPI == EPI_GRAM ? s0 * s0 : (XT ? s0 : 1.f);
     // The 16 blocks go in row order; each block's global inputs are loaded
     // four blocks ahead (slots in0..in3), so their latency overlaps the
     // work on the blocks in between instead of stalling every block.
@@ -735,8 +742,8 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
 #define NS_LOAD(SLOT, I, J) \
     epi_load<T, EPI>(SLOT, d, lane, bi0 + (I) * 32, bj0 + (J) * 32, cur, poly_direct)
 #define NS_EPI(I, J, SLOT)                                                                   \
-    epi_block<T, EPI, SLD>(acc[I][J], SLOT, d, S, args, lane, bi0 + (I) * 32, bj0 + (J) * 32, \
-                           cur, need_cols, poly_direct, out_direct, ld_direct)
+    epi_block<T, EPI, SLD>(acc[I][J], SLOT, d, S, args, escale, lane, bi0 + (I) * 32,         \
+                           bj0 + (J) * 32, cur, need_cols, poly_direct, out_direct, ld_direct)
     NS_LOAD(in0, 0, 0); NS_LOAD(in1, 0, 1); NS_LOAD(in2, 0, 2); NS_LOAD(in3, 0, 3);
     NS_EPI(0, 0, in0); NS_LOAD(in0, 1, 0);
     NS_EPI(0, 1, in1); NS_LOAD(in1, 1, 1);
@@ -788,9 +795,10 @@ int launch_k(NsKernel k, const MuonMat* tab, const GemmTile* tiles, int64_t n, c
 }  // namespace
 
 int launch_ns_phase(int phase, int32_t group, const MuonMat* tab, const GemmTile* tiles,
-                    int64_t n_tiles, int iter, int last, const StepScalars& s, void* stream) {
+                    int64_t n_tiles, int iter, int last, const StepScalars& s,
+                    const float* ns_scale, void* stream) {
     if (n_tiles == 0) return (int)hipSuccess;
-    NsArgs a{s.ns_a, s.ns_b, s.ns_c, iter};
+    NsArgs a{s.ns_a, s.ns_b, s.ns_c, iter, ns_scale};
     hipStream_t st = (hipStream_t)stream;
     const int epi = phase == 1 ? EPI_GRAM : phase == 2 ? EPI_POLY : (last ? EPI_FINAL : EPI_XUPD);
     static const NsKernel bf[4] = {k_ns_gram_bf16, k_ns_poly_bf16, k_ns_xupd_bf16, k_ns_final_bf16};

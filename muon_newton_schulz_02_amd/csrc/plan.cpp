@@ -190,17 +190,13 @@ void build_tables(ma_plan* p) {
         ch += ceil_div(p->entries[id].numel, kChunk);
     }
     p->n_adam_chunks = ch;
-    ch = 0;
     int64_t ot = 0;
     for (size_t k = 0; k < p->muon_ids.size(); ++k) {
         const auto& e = p->entries[p->muon_ids[k]];
-        p->muon_chunk_begin.push_back(ch);
-        ch += ceil_div(e.numel, kChunk);
         p->muon_orient_begin.push_back(ot);
         const int64_t R = round_up(e.r, kNsPad), C = round_up(e.c, kNsPad);
         ot += (R / kOrientTile) * (C / kOrientTile);
     }
-    p->n_muon_chunks = ch;
     p->n_orient_tiles = ot;
 }
 
@@ -259,8 +255,10 @@ void build_layout(ma_plan* p, int32_t precision) {
     L.norm_partials_off = off;
     off = align256(off + sizeof(float) * (size_t)std::max<int64_t>(p->n_norm_chunks, 1));
     L.muon_partials_off = off;
-    off = align256(off + sizeof(float) * (size_t)std::max<int64_t>(p->n_muon_chunks, 1));
+    off = align256(off + sizeof(float) * (size_t)std::max<int64_t>(p->n_orient_tiles, 1));
     L.muon_scale_off = off;
+    off = align256(off + sizeof(float) * std::max<size_t>(p->muon_ids.size(), 1));
+    L.muon_prescale_off = off;
     off = align256(off + sizeof(float) * std::max<size_t>(p->muon_ids.size(), 1));
     L.ns_off = off;
     for (size_t k = 0; k < p->muon_ids.size(); ++k) {

@@ -6,8 +6,10 @@
 //   1. one async copy of this step's descriptor tables into the workspace
 //   2. clip norm partials over every trainable gradient, then the clip factor
 //   3. AdamW over the AdamW group
-//   4. Muon momentum + ||u||^2 partials, per-matrix scale, normalise/orient
-//   5. ns_steps x (GRAM, POLY, XUPD); the last XUPD writes the update.
+//   4. Muon momentum + unnormalised operands + ||u||^2 partials, then the
+//      per-matrix normalising factor
+//   5. ns_steps x (GRAM, POLY, XUPD), the first GRAM and XUPD applying the
+//      normalising factor; the last XUPD writes the update.
 // Nothing is launched before every argument has been checked.
 
 #include <hip/hip_runtime.h>
@@ -265,9 +267,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         d.a = reinterpret_cast<uint64_t>(base + L.a[k]);
         d.b = reinterpret_cast<uint64_t>(base + L.b[k]);
         d.numel = e.numel;
-        d.chunk_begin = plan->muon_chunk_begin[k];
         d.orient_begin = plan->muon_orient_begin[k];
-        d.n_chunks = (int32_t)ceil_div(e.numel, kChunk);
         d.m = (int32_t)e.m;
         d.n = (int32_t)e.n;
         d.r = (int32_t)e.r;
@@ -311,6 +311,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     float* norm_partials = reinterpret_cast<float*>(base + L.norm_partials_off);
     float* muon_partials = reinterpret_cast<float*>(base + L.muon_partials_off);
     float* muon_scales = reinterpret_cast<float*>(base + L.muon_scale_off);
+    float* muon_prescales = reinterpret_cast<float*>(base + L.muon_prescale_off);
     const int32_t n_train = (int32_t)plan->train_ids.size();
     const int32_t n_adam = (int32_t)plan->adam_ids.size();
     const int32_t n_muon = (int32_t)plan->muon_ids.size();
@@ -346,18 +347,17 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         if ((e = hipEventRecord((hipEvent_t)side->ev_join, ss)) != hipSuccess)
             return hip_fail("hipEventRecord (join)", e);
     } else {
-        err = launch_adamw(d_adam, n_adam, plan->n_adam_chunks, coef, sc, false, stream);
+        err = launch_adamw(d_adam, n_adam, plan->n_adam_chunks, coef, sc, stream);
         if (err) return hip_fail("adamw", err);
         if ((err = mark(2))) return hip_fail("phase event", err);
     }
     if (n_muon > 0) {
-        err = launch_muon_momentum(d_muon, n_muon, plan->n_muon_chunks, coef, sc, muon_partials,
-                                   stream);
-        if (err) return hip_fail("muon momentum", err);
-        err = launch_muon_scale(d_muon, n_muon, muon_partials, sc.ns_eps, muon_scales, stream);
+        err = launch_muon_prep(d_muon, n_muon, plan->n_orient_tiles, coef, sc, muon_partials,
+                               stream);
+        if (err) return hip_fail("muon prep", err);
+        err = launch_muon_scale(d_muon, n_muon, muon_partials, sc.ns_eps, muon_scales,
+                                muon_prescales, stream);
         if (err) return hip_fail("muon scale", err);
-        err = launch_orient(d_muon, n_muon, plan->n_orient_tiles, coef, muon_scales, sc, stream);
-        if (err) return hip_fail("muon orient", err);
         if ((err = mark(3))) return hip_fail("phase event", err);
         for (int it = 0; it < hp->muon_ns_steps; ++it) {
             const int last = it == hp->muon_ns_steps - 1;
@@ -367,7 +367,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
                         phase == 1 ? L.g1[g] : phase == 2 ? L.g2[g] : L.g3[g];
                     const size_t off = phase == 1 ? L.g1_off[g] : phase == 2 ? L.g2_off[g] : L.g3_off[g];
                     err = launch_ns_phase(phase, g, d_muon, reinterpret_cast<const GemmTile*>(base + off),
-                                          (int64_t)tl.size(), it, last, sc, stream);
+                                          (int64_t)tl.size(), it, last, sc, muon_scales, stream);
                     if (err) return hip_fail("newton-schulz", err);
                 }
             }

@@ -146,6 +146,24 @@ def test_ragged_cubic_coefficients(prec):
     _run_parity(w, prec, 2, hp=hp)
 
 
+@pytest.mark.parametrize("std,clip,prec", [(1e-20, 1.0, "bf16"), (1e-20, 1.0, "fp32"),
+                                           (1e-9, 1.0, "bf16"), (1e15, 0.0, "bf16"),
+                                           (1e15, 0.0, "fp32")])
+def test_extreme_gradient_scales(std, clip, prec):
+    """Muon matrices whose momentum direction u has a Frobenius norm far from
+    1.  The GPU path writes u unnormalised as the Newton-Schulz input and
+    applies 1 / (||u|| + eps) in the first Gram and X-update epilogues; for a
+    norm outside [2^-40, 2^40] (here ~1e-17 and ~1e18) it scales the operands
+    themselves first, so products stay inside the fp32 range.  Both paths
+    must match the oracle, which normalises before iterating."""
+    shapes = [(1, 7), (33, 65), (65, 33), (300, 130), (257, 513), (3, 1000), (129, 129)]
+    params = [W.ParamSpec("action_expert.layers.%d.x.weight" % i, s) for i, s in enumerate(shapes)]
+    w = W.Workload("extreme_%g" % std, seed=11, steps=2, ns_precision=prec, params=params,
+                   grad_std=std)
+    hp = H.oracle_hparams(w, max_grad_norm=clip)
+    _run_parity(w, prec, 2, hp=hp)
+
+
 def test_adamw_mode_and_misaligned_views():
     """Plain-AdamW mode sends every trainable tensor through the AdamW kernel;
     a view starting one float into its storage takes the scalar path."""
