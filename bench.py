@@ -1,6 +1,6 @@
 """Benchmark of the hybrid MuonAdamW optimizer step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--serial]
 
 One step is the whole hot path over the full parameter table of the
 workload: clip norm over every trainable gradient, AdamW over the AdamW
@@ -8,11 +8,17 @@ group, momentum/normalise and 5 bf16 Newton-Schulz steps with the fused
 update over the Muon group.  Inputs (parameters, gradients, states) are
 synthetic, seeded, and resident in HBM before timing starts.
 
+The headline steps run the AdamW group beside the Muon group (the library's
+overlap_groups plan option; --serial turns it off).  After them, a roofline
+pass times serial steps with HIP events that the library records on its own
+stream at the phase boundaries, so the AdamW phase is exactly one k_adamw
+launch and the Newton-Schulz phase its GEMM launches; a plain device copy
+is timed as the HBM rate reachable on this GPU.
+
 Prints one JSON line: whole-step params/s (the metric's headline value),
-step time, per-phase times taken with HIP events recorded by the library on
-its own stream, Newton-Schulz TFLOP/s and AdamW GB/s against the MI355X
-peaks, the roofline of the dominant kernel, and the CPU oracle timed on a
-bounded sample of the same workload.
+step time, the serial pass's per-phase times, Newton-Schulz TFLOP/s and
+AdamW GB/s against the MI355X peaks, the roofline of the dominant kernel,
+and the CPU oracle timed on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -77,7 +83,7 @@ def measured_traffic(kernel: str, workload: str):
     (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None when
     there is none or the kernel's source changed since it was taken."""
     import hashlib
-    path = os.path.join(HERE, "profiles", "%s.md" % workload)
+    path = os.path.join(HERE, "profiles", "kernels_%s.md" % workload)
     if not os.path.exists(path):
         return None
     sha = hashlib.sha256(open(KERNEL_SOURCES[kernel], "rb").read()).hexdigest()[:16]
@@ -98,6 +104,25 @@ def ns_flops(shapes, ns_steps: int) -> float:
         r, c = min(m, n), max(m, n)
         tot += 4.0 * r * r * c + 2.0 * r ** 3
     return tot * ns_steps
+
+
+def copy_bandwidth(torch, mib: int = 2048, reps: int = 5) -> float:
+    """Bytes moved per second (read + write) by a plain device-to-device copy
+    of `mib` MiB, timed with events: the HBM rate this GPU reaches for a
+    read/write mix, next to the datasheet peak."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2.0 * n * 4 / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(w, hp_overrides) -> dict:
@@ -172,8 +197,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="vla_hybrid_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--overlap", action="store_true",
-                    help="run the AdamW group on a second stream, concurrent with the Muon group")
+    ap.add_argument("--serial", action="store_true",
+                    help="time the groups one after the other on one stream (default: the AdamW "
+                         "group runs beside the Muon group)")
+    ap.add_argument("--roofline-steps", type=int, default=10,
+                    help="serial steps timed after the headline ones, for per-kernel rooflines")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes")
@@ -207,7 +235,8 @@ def main():
     hp_over = W.hparams_for(w)
     hp = M.muon_adamw_default_hparams(ns_precision=w.ns_precision, **hp_over)
     table = list(zip(w.names, w.shapes, w.trainable))
-    plan = M.muon_adamw_plan(table, overlap_groups=args.overlap)
+    plan = M.muon_adamw_plan(table, overlap_groups=not args.serial)
+    serial_plan = M.muon_adamw_plan(table, overlap_groups=False)
     n = len(table)
     groups = [M.muon_adamw_plan_entry(plan, i)["group"] for i in range(n)]
     params, grads = [None] * n, [None] * n
@@ -234,7 +263,8 @@ def main():
 
     stream = torch.cuda.current_stream()
     K = 5  # MA_PROFILE_EVENTS
-    evs = HipEvents(K * max(args.steps, 1))
+    R = max(args.roofline_steps, 1)
+    evs = HipEvents(K * R)
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         M.muon_adamw_step(plan, params, grads, state, hp, ws, stream=stream)
@@ -242,12 +272,24 @@ def main():
     print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for s in range(args.steps):
-        M.muon_adamw_step_profiled(plan, params, grads, state, hp, ws,
-                                   evs.ev[K * s:K * s + K], stream=stream)
+        M.muon_adamw_step(plan, params, grads, state, hp, ws, stream=stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # Per-kernel rooflines come from serial steps, where the library's phase
+    # events bracket single kernels: [1] -> [2] is the one AdamW launch.
+    print("[bench] roofline pass: %d serial steps" % R, file=sys.stderr, flush=True)
+    M.muon_adamw_step(serial_plan, params, grads, state, hp, ws, stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for s in range(R):
+        M.muon_adamw_step_profiled(serial_plan, params, grads, state, hp, ws,
+                                   evs.ev[K * s:K * s + K], stream=stream)
+    torch.cuda.synchronize()
+    serial_ms = (time.perf_counter() - t1) * 1e3 / R
     phases = {"clip_norm": [], "adamw": [], "muon_prep": [], "newton_schulz": [], "step": []}
-    for s in range(args.steps):
+    for s in range(R):
         b = K * s
         phases["clip_norm"].append(evs.elapsed(b, b + 1))
         phases["adamw"].append(evs.elapsed(b + 1, b + 2))
@@ -256,7 +298,7 @@ def main():
         phases["step"].append(evs.elapsed(b, b + 4))
     evs.close()
     mean = {k: sum(v) / len(v) for k, v in phases.items()}
-    ms_per_step = wall * 1e3 / args.steps
+    copy_gbps = copy_bandwidth(torch)
     flops = ns_flops(muon_shapes, hp.muon_ns_steps)
     ns_peak = PEAK_BF16_TFLOPS if w.ns_precision == "bf16" else PEAK_FP32_TFLOPS
     ns_tflops = flops / (mean["newton_schulz"] * 1e-3) / 1e12 if mean["newton_schulz"] > 0 else 0.0
@@ -268,7 +310,7 @@ def main():
         roofline = {"kernel": "k_adamw", "bound": "hbm", "achieved": adam_gbps,
                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": adam_gbps / PEAK_HBM_GBPS,
                     "traffic": measured_traffic("k_adamw", w.name),
-                    "algorithmic_bytes": adam_bytes}
+                    "algorithmic_bytes": adam_bytes, "frac_of_copy": adam_gbps / copy_gbps}
     else:
         roofline = {"kernel": "k_ns_* GEMMs (5 steps x 3 launches)", "bound": "mfma",
                     "achieved": ns_tflops, "peak": ns_peak, "unit": "TFLOP/s",
@@ -289,13 +331,16 @@ def main():
         "config": {"workload": w.name, "muon_params": n_muon, "adamw_params": n_adam,
                    "muon_matrices": len(muon_shapes), "ns_precision": w.ns_precision,
                    "ns_steps": hp.muon_ns_steps, "parallelism": "single GPU",
-                   "streams": "adamw overlapped with muon" if args.overlap else "one stream"},
+                   "streams": "one stream" if args.serial else
+                   "adamw beside the muon group (second stream)"},
+        "serial_ms_per_step": serial_ms,
         "phase_ms": mean,
         "ns_tflops": ns_tflops,
         "ns_mfma_frac": ns_tflops / ns_peak,
         "adamw_gbps": adam_gbps,
         "adamw_hbm_frac": adam_gbps / PEAK_HBM_GBPS,
         "clip_norm_gbps": norm_gbps,
+        "hbm_copy_gbps": copy_gbps,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
