@@ -69,18 +69,21 @@ typedef struct {
     int32_t        trainable;
 } ma_param_desc;
 
-/* `overlap_groups` = 1 lets muon_adamw_step run the AdamW group on a
- * library-owned second stream of the same device (default priority), joined
- * back into the caller's stream before the step's work ends, so the
- * HBM-bound AdamW kernel overlaps the MFMA-bound Muon work; 0 runs every
- * kernel on the caller's stream in order (the default: on MI355X both
- * groups are bound by HBM bandwidth, and running them concurrently measured
- * no faster).  A NULL opts means mode MA_MODE_MUON_ADAMW, moonlight 0.2,
- * overlap 0. */
+/* `overlap_groups` = 1 runs the AdamW group beside the Muon group: one
+ * workgroup per CU on a library-owned second stream of the same device
+ * (default priority) streams AdamW chunks while the Muon kernels run on the
+ * caller's stream -- its waves are small enough to share each SIMD with a
+ * Newton-Schulz GEMM wave -- and after the Newton-Schulz launches a second
+ * AdamW launch on the caller's stream finishes whatever chunks are left.
+ * Chunks are claimed from a counter in the workspace; AdamW is elementwise,
+ * so the results are bitwise those of overlap 0.  The side stream is joined
+ * back into the caller's stream before the step's work ends.  0 runs every
+ * kernel on the caller's stream in order.  A NULL opts means mode
+ * MA_MODE_MUON_ADAMW, moonlight 0.2, overlap 0. */
 typedef struct {
     int32_t mode;                  /* MA_MODE_*                            */
     double  moonlight_coefficient; /* 0.2 on the page                      */
-    int32_t overlap_groups;        /* 1: AdamW concurrent with Muon        */
+    int32_t overlap_groups;        /* 1: AdamW beside the Muon group       */
 } ma_plan_opts;
 
 typedef struct ma_plan ma_plan;    /* opaque, immutable once built         */
@@ -217,10 +220,11 @@ int muon_adamw_step(const ma_plan* plan,
  * MA_PROFILE_EVENTS hipEvent_t created by the caller, recorded on `stream`
  * at [0] the start of the step, [1] after the clip norm, [2] after the AdamW
  * group, [3] after the Muon momentum/normalise pass, [4] at the end of the
- * step.  Each event is recorded on the stream its phase's kernels run on (with
- * overlap_groups, [2] is on the side stream, so [1]->[2] is the AdamW kernel
- * and [3]->[4] covers Newton-Schulz plus any wait for AdamW).  Same errors as
- * muon_adamw_step. */
+ * step.  Without overlap_groups each interval is exactly its phase's
+ * kernels ([1] -> [2] is the one AdamW launch).  With overlap_groups, [2] is
+ * recorded on the side stream after its AdamW launch and the remaining
+ * AdamW chunks run between [3] and [4], so only [0] -> [4] is meaningful.
+ * Same errors as muon_adamw_step. */
 int muon_adamw_step_profiled(const ma_plan* plan,
                              float* const* params,
                              const float* const* grads,
