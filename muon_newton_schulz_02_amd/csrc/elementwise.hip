@@ -265,11 +265,13 @@ __device__ __forceinline__ void adamw_chunk_wave(const AdamTensor* __restrict__ 
 
 // AdamW with chunks claimed per wave from a shared counter; every wave runs
 // until the counter passes n_chunks.
+// At most 80 VGPRs (six waves per SIMD), so a wave fits on a SIMD beside a
+// Newton-Schulz GEMM wave (at most 432 registers once rounded to the
+// allocation granule).
 template <int U>
-__global__ __launch_bounds__(kThreads) void k_adamw_claim(const AdamTensor* __restrict__ tab,
-                                                          int n_tab, int64_t n_chunks,
-                                                          const float* __restrict__ coef_ptr,
-                                                          AdamArgs a, int* __restrict__ counter) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) void k_adamw_claim(
+    const AdamTensor* __restrict__ tab, int n_tab, int64_t n_chunks,
+    const float* __restrict__ coef_ptr, AdamArgs a, int* __restrict__ counter) {
     const int lane = threadIdx.x & 63;
     const float coef = *coef_ptr;
     for (;;) {
@@ -525,8 +527,8 @@ int launch_adamw_claim(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, c
     a.one_m_beta1 = s.one_m_beta1;
     a.one_m_beta2 = s.one_m_beta2;
     a.eps = s.eps;
-    // four vectors per stream in flight: 88 VGPRs, which with a Newton-Schulz
-    // GEMM wave's 168 VGPRs + 256 AGPRs fills a SIMD's 512 exactly
+    // four vectors per stream in flight in 80 VGPRs, which with a
+    // Newton-Schulz GEMM wave's at most 432 registers fills a SIMD's 512
     hipLaunchKernelGGL(k_adamw_claim<4>, dim3((unsigned)grid), dim3(kThreads), 0,
                        (hipStream_t)stream, tab, n_tab, n_chunks, coef, a, counter);
     return (int)hipGetLastError();

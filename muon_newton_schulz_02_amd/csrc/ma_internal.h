@@ -191,7 +191,7 @@ int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
 // from `counter` until all n_chunks are taken.  Several such launches, on
 // different streams, may share one counter: each chunk is processed exactly
 // once, and since AdamW is elementwise the result does not depend on which
-// launch takes it.  Its waves are lean enough (88 VGPRs) to share a SIMD with
+// launch takes it.  Its waves are lean enough (80 VGPRs) to share a SIMD with
 // a Newton-Schulz GEMM wave.
 int launch_adamw_claim(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
                        const float* coef, const StepScalars& s, int* counter, int64_t grid,
