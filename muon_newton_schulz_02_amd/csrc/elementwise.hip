@@ -312,8 +312,10 @@ __device__ __forceinline__ int find_matrix(const MuonMat* tab, int n, int64_t bl
 // tile of u in stored orientation: canonical (i, j) is stored (i, j), or
 // stored (j, i) for a transposed matrix.  Values outside the true r x c are
 // zero.
-// bf16 operands: X as a hi / lo pair of row-major bf16 matrices (step-0
-// buffers), hi = RNE(x), lo = RNE(x - hi).
+// bf16 operands: X as a hi / lo pair of bf16 matrices (step-0 buffers),
+// hi = RNE(x), lo = RNE(x - hi), each stored in 32x32 blocks of 2 KB
+// (row-major inside a block, block-row-major outside), the layout the
+// Newton-Schulz launches read and write.
 __device__ __forceinline__ void write_operands_bf16(const MuonMat& d,
                                                     const float (*tile)[kOrientTile + 1], int i0,
                                                     int j0) {
@@ -323,7 +325,8 @@ __device__ __forceinline__ void write_operands_bf16(const MuonMat& d,
     for (int idx = threadIdx.x; idx < TS * TS; idx += kThreads) {
         const int a_ = idx / TS, b_ = idx % TS;
         const float v = d.transposed ? tile[b_][a_] : tile[a_][b_];
-        const int64_t o = (int64_t)(i0 + a_) * d.C + (j0 + b_);
+        const int i = i0 + a_, j = j0 + b_;
+        const int64_t o = ((int64_t)(i >> 5) * (d.C >> 5) + (j >> 5)) * 1024 + (i & 31) * 32 + (j & 31);
         const __bf16 h = (__bf16)v;
         hi[o] = h;
         lo[o] = (__bf16)(v - (float)h);

@@ -45,6 +45,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 enum { EPI_GRAM = 1, EPI_POLY = 2, EPI_XUPD = 3, EPI_FINAL = 4 };
 
+// Element offset of (i, j) in an X operand stored in bf16 (hi and lo): 32x32
+// blocks of 2 KB, row-major inside a block and block-row-major outside, so
+// the epilogue's 32-byte row runs of a block form one contiguous 2 KB write
+// and every 64-byte stage row the loaders copy stays contiguous.
+__device__ __forceinline__ int64_t xblk(int i, int j, int C) {
+    return ((int64_t)(i >> 5) * (C >> 5) + (j >> 5)) * 1024 + (i & 31) * 32 + (j & 31);
+}
+
 // A lane contributes 16 bytes of one operand row per "k-group": 8 bf16 for
 // one 32x32x16 MFMA, or 4 fp32 for four 32x32x2 MFMAs.  Inside a k-group the
 // lane half h = lane / 32 holds k-offsets [16h, 16h + 16) bytes; A and B
@@ -296,12 +304,13 @@ __device__ __forceinline__ void epi_load(EpiIn& in, const MuonMat& d, int lane, 
             for (int q = 0; q < (BF ? 2 : 4); ++q) in.q[q] = gld(a + q);
         }
     } else if (EPI == EPI_XUPD || EPI == EPI_FINAL) {
-        const int64_t o = (int64_t)gi * d.C + gj;
         if (BF) {
-            const uint4* lo = reinterpret_cast<const uint4*>(reinterpret_cast<const __bf16*>(d.xlo[cur]) + o);
+            const uint4* lo =
+                reinterpret_cast<const uint4*>(reinterpret_cast<const __bf16*>(d.xlo[cur]) + xblk(gi, gj, d.C));
             in.q[0] = gld(lo);
             in.q[1] = gld(lo + 1);
         } else {
+            const int64_t o = (int64_t)gi * d.C + gj;
             const uint4* x = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(d.x[0]) + o);
 #pragma unroll
             for (int q = 0; q < 4; ++q) in.q[q] = gld(x + q);
@@ -380,8 +389,9 @@ __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, co
 #pragma unroll
             for (int e = 0; e < 16; ++e) v[e] = escale * fmaf(args.a, lv[e], v[e]);
             if (EPI == EPI_XUPD) {
-                store16_hilo(reinterpret_cast<__bf16*>(d.x[cur ^ 1]) + o,
-                             reinterpret_cast<__bf16*>(d.xlo[cur ^ 1]) + o, v);
+                const int64_t ob = xblk(gi, gj, d.C);
+                store16_hilo(reinterpret_cast<__bf16*>(d.x[cur ^ 1]) + ob,
+                             reinterpret_cast<__bf16*>(d.xlo[cur ^ 1]) + ob, v);
             } else if (!d.transposed) {
                 update_run(d, gi, gj, v);
             }
@@ -429,21 +439,28 @@ struct Addr {
     uint32_t lin_r[4];       // linear-term reads (row operand) of column block 0, per quarter
 };
 
-template <typename T, bool QT>
+// PB / QB: that operand is a bf16 X in 32x32 blocks (xblk), whose row
+// pitch ld covers one row of a block row: a block row spans 32 ld, a stage
+// (32 columns) one 2 KB block, and rows 16..31 of a block start 1 KB in.
+template <typename T, bool QT, bool PB, bool QB>
 __device__ __forceinline__ void stage_copy(uint32_t buf, u32x4 rp, u32x4 rq, const Addr& ad,
                                            uint32_t wbase, int s, uint32_t ldp, uint32_t ldq) {
     constexpr int KE = kRowBytes / (int)sizeof(T);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        dma16(rp, buf + wbase + i * 1024, ad.dma_p, (uint32_t)s * kRowBytes + (uint32_t)(i * 16) * ldp);
+        dma16(rp, buf + wbase + i * 1024, ad.dma_p,
+              PB ? (uint32_t)s * 2048 + (uint32_t)(i >> 1) * 32 * ldp + (uint32_t)(i & 1) * 1024
+                 : (uint32_t)s * kRowBytes + (uint32_t)(i * 16) * ldp);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if (QT)
             dma16(rq, buf + kRegionBytes + wbase + i * 1024, ad.dma_q[i & 1],
-                  ((uint32_t)s * KE + (uint32_t)(2 * i)) * ldq);
+                  QB ? (uint32_t)s * 32 * ldq + (uint32_t)(2 * i) * 64
+                     : ((uint32_t)s * KE + (uint32_t)(2 * i)) * ldq);
         else
             dma16(rq, buf + kRegionBytes + wbase + i * 1024, ad.dma_q[0],
-                  (uint32_t)s * kRowBytes + (uint32_t)(i * 16) * ldq);
+                  QB ? (uint32_t)s * 2048 + (uint32_t)(i >> 1) * 32 * ldq + (uint32_t)(i & 1) * 1024
+                     : (uint32_t)s * kRowBytes + (uint32_t)(i * 16) * ldq);
     }
 }
 
@@ -538,7 +555,7 @@ __device__ __forceinline__ void stage_linear_at(f32x16 (&acc)[4][4], const char*
 // barrier that publishes stage s + 1 and recycles the buffer of stage s - 1,
 // the copy of stage s + kStages - 1 into it, the k-group-0 fragments of stage
 // s + 1, the linear term, and k-group 1.
-template <typename T, bool QT, bool LIN>
+template <typename T, bool QT, bool LIN, bool PB, bool QB>
 __device__ __forceinline__ void stage_step(f32x16 (&acc)[4][4], uint4 (&fa)[4], uint4 (&fb)[4],
                                            const char* cur, const char* nxt, uint32_t tgt, u32x4 rp,
                                            u32x4 rq, const Addr& ad, uint32_t wbase, int s, int nk,
@@ -556,7 +573,7 @@ __device__ __forceinline__ void stage_step(f32x16 (&acc)[4][4], uint4 (&fa)[4], 
     // has no join point that would blur the LDS wait counts.
     wait_vm(8 * min(nk - 2 - s, kStages - 3));
     stage_barrier();
-    if (s + kStages - 1 < nk) stage_copy<T, QT>(tgt, rp, rq, ad, wbase, s + kStages - 1, ldp, ldq);
+    if (s + kStages - 1 < nk) stage_copy<T, QT, PB, QB>(tgt, rp, rq, ad, wbase, s + kStages - 1, ldp, ldq);
     stage_frags<QT>(fa, fb, nxt, ad, 0);
     if (LIN) stage_linear_at<T, QT>(acc, cur, ad, scale, rel0 + s * KE);
     __builtin_amdgcn_sched_barrier(0);
@@ -565,7 +582,7 @@ __device__ __forceinline__ void stage_step(f32x16 (&acc)[4][4], uint4 (&fa)[4], 
 }
 
 // Stages s .. s + kStages - 1 of the main loop, stage s + B in ring slot B.
-template <typename T, bool QT, bool LIN, int... B>
+template <typename T, bool QT, bool LIN, bool PB, bool QB, int... B>
 __device__ __forceinline__ void ring_round(std::integer_sequence<int, B...>, f32x16 (&acc)[4][4],
                                            uint4 (&fa)[4], uint4 (&fb)[4], const char* ring,
                                            uint32_t lring, u32x4 rp, u32x4 rq, const Addr& ad,
@@ -573,7 +590,7 @@ __device__ __forceinline__ void ring_round(std::integer_sequence<int, B...>, f32
                                            uint32_t ldq, float scale, int rel0) {
     // nk is a multiple of 8, so a ring depth dividing 8 needs no guard
     (((8 % kStages == 0 || s + B < nk)
-          ? stage_step<T, QT, LIN>(acc, fa, fb, ring + B * kStageBytes,
+          ? stage_step<T, QT, LIN, PB, QB>(acc, fa, fb, ring + B * kStageBytes,
                                    ring + ((B + 1) % kStages) * kStageBytes,
                                    lring + ((B + kStages - 1) % kStages) * kStageBytes, rp, rq,
                                    ad, wbase, s + B, nk, ldp, ldq, scale, rel0)
@@ -588,6 +605,10 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
     // B X in bf16 reads X row-major through the transposing LDS loads
     constexpr bool QT = BF && (EPI == EPI_XUPD || EPI == EPI_FINAL);
     constexpr bool XT = EPI == EPI_XUPD || EPI == EPI_FINAL;
+    // bf16 X operands are stored in 32x32 blocks: both Gram operands and the
+    // update's right operand
+    constexpr bool PB = BF && EPI == EPI_GRAM;
+    constexpr bool QB = BF && (EPI == EPI_GRAM || XT);
     constexpr int KE = kRowBytes / (int)sizeof(T);
     constexpr int SLD = 36;  // epilogue staging row stride (floats): 16-byte aligned runs
     // the stage ring; after the main loop its start is the epilogue staging
@@ -641,15 +662,22 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
     Addr ad;
     {
         const uint32_t c = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-        ad.dma_p = (uint32_t)((m0 + wave * 64 + (lane >> 2)) * ldp) + c * 16;
+        ad.dma_p = PB ? (uint32_t)((m0 + wave * 64) * ldp) + (uint32_t)(lane >> 2) * 64 + c * 16
+                      : (uint32_t)((m0 + wave * 64 + (lane >> 2)) * ldp) + c * 16;
         if (QT) {
             const uint32_t r = (uint32_t)(8 * wave + (lane >> 5));
             const uint32_t ce = (uint32_t)((lane & 31) ^ (((lane >> 5) & 3) << 2));
             const uint32_t co = (uint32_t)((lane & 31) ^ (((2 + (lane >> 5)) & 3) << 2));
-            ad.dma_q[0] = r * (uint32_t)ldq + (uint32_t)n0 * 2 + ce * 16;
-            ad.dma_q[1] = r * (uint32_t)ldq + (uint32_t)n0 * 2 + co * 16;
+            if (QB) {
+                ad.dma_q[0] = ((uint32_t)n0 / 32 + (ce >> 2)) * 2048 + r * 64 + (ce & 3) * 16;
+                ad.dma_q[1] = ((uint32_t)n0 / 32 + (co >> 2)) * 2048 + r * 64 + (co & 3) * 16;
+            } else {
+                ad.dma_q[0] = r * (uint32_t)ldq + (uint32_t)n0 * 2 + ce * 16;
+                ad.dma_q[1] = r * (uint32_t)ldq + (uint32_t)n0 * 2 + co * 16;
+            }
         } else {
-            ad.dma_q[0] = (uint32_t)((n0 + wave * 64 + (lane >> 2)) * ldq) + c * 16;
+            ad.dma_q[0] = QB ? (uint32_t)((n0 + wave * 64) * ldq) + (uint32_t)(lane >> 2) * 64 + c * 16
+                             : (uint32_t)((n0 + wave * 64 + (lane >> 2)) * ldq) + c * 16;
             ad.dma_q[1] = ad.dma_q[0];
         }
         const int r32 = lane & 31, sw = (r32 >> 2) & 3, half = lane >> 5;
@@ -699,7 +727,7 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
     const uint32_t lring = lds_addr(ring);
 #pragma unroll
     for (int st = 0; st < kStages - 1; ++st)
-        stage_copy<T, QT>(lring + st * kStageBytes, rp, rq, ad, wbase, st, uldp, uldq);
+        stage_copy<T, QT, PB, QB>(lring + st * kStageBytes, rp, rq, ad, wbase, st, uldp, uldq);
     // stage 0 has landed once only the copies of stages 1 .. kStages - 2 are
     // outstanding
     wait_vm(8 * (kStages - 2));
@@ -709,8 +737,8 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
     // the loop is unrolled by the ring depth so every stage buffer address
     // is a compile-time offset
     for (int s = 0; s < nk; s += kStages)
-        ring_round<T, QT, LIN>(std::make_integer_sequence<int, kStages>(), acc, fa, fb, ring, lring,
-                               rp, rq, ad, wbase, s, nk, uldp, uldq, scale, rel0);
+        ring_round<T, QT, LIN, PB, QB>(std::make_integer_sequence<int, kStages>(), acc, fa, fb, ring,
+                                       lring, rp, rq, ad, wbase, s, nk, uldp, uldq, scale, rel0);
     // every wave is done with the ring (all copies landed at the last
     // stage's wait) before it becomes the epilogue staging area
     stage_barrier();
