@@ -45,12 +45,20 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 enum { EPI_GRAM = 1, EPI_POLY = 2, EPI_XUPD = 3, EPI_FINAL = 4 };
 
-// Element offset of (i, j) in an X operand stored in bf16 (hi and lo): 32x32
-// blocks of 2 KB, row-major inside a block and block-row-major outside, so
-// the epilogue's 32-byte row runs of a block form one contiguous 2 KB write
-// and every 64-byte stage row the loaders copy stays contiguous.
+// Element offset of (i, j) in a bf16 operand (X hi and lo, A, B) with C
+// columns: 32x32 blocks of 2 KB, row-major inside a block and
+// block-row-major outside, so the epilogue's 32-byte row (or column) runs of
+// a block form one contiguous 2 KB write and every 64-byte stage row the
+// loaders copy stays contiguous.
 __device__ __forceinline__ int64_t xblk(int i, int j, int C) {
     return ((int64_t)(i >> 5) * (C >> 5) + (j >> 5)) * 1024 + (i & 31) * 32 + (j & 31);
+}
+
+// Offset of (i, j) in an epilogue output or input of operand type T with
+// leading dimension ld: blocked for bf16, row-major for fp32.
+template <typename T>
+__device__ __forceinline__ int64_t op_off(int i, int j, int64_t ld) {
+    return sizeof(T) == 2 ? xblk(i, j, (int)ld) : (int64_t)i * ld + j;
 }
 
 // A lane contributes 16 bytes of one operand row per "k-group": 8 bf16 for
@@ -299,7 +307,7 @@ __device__ __forceinline__ void epi_load(EpiIn& in, const MuonMat& d, int lane, 
     if (EPI == EPI_POLY) {
         if (!poly_direct) {
             const uint4* a = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(d.a) +
-                                                            (int64_t)gi * d.R + gj);
+                                                            op_off<T>(gi, gj, d.R));
 #pragma unroll
             for (int q = 0; q < (BF ? 2 : 4); ++q) in.q[q] = gld(a + q);
         }
@@ -370,7 +378,7 @@ __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, co
         if (EPI == EPI_GRAM) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) v[e] *= escale;
-            store16(out_direct + (int64_t)gi * ld_direct + gj, v);
+            store16(out_direct + op_off<T>(gi, gj, ld_direct), v);
         } else if (EPI == EPI_POLY) {
             if (poly_direct) {
 #pragma unroll
@@ -381,7 +389,7 @@ __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, co
 #pragma unroll
                 for (int e = 0; e < 16; ++e) v[e] = fmaf(args.b, av[e], args.c * v[e]);
             }
-            store16(out_direct + (int64_t)gi * ld_direct + gj, v);
+            store16(out_direct + op_off<T>(gi, gj, ld_direct), v);
         } else if (BF) {
             // a * lo of the master X; a * hi was added in the main loop
             float lv[16];
@@ -415,7 +423,7 @@ __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, co
         for (int e = 0; e < 16; ++e) v[e] = S[(cr0 + e) * SLD + ccol];
         const int tr = bj + ccol, tc = bi + cr0;  // row / first column in the transposed view
         if (EPI == EPI_GRAM || EPI == EPI_POLY) {
-            store16(out_direct + (int64_t)tr * ld_direct + tc, v);
+            store16(out_direct + op_off<T>(tr, tc, ld_direct), v);
         } else if (EPI == EPI_XUPD) {
             T* xt = reinterpret_cast<T*>(d.xt[cur ^ 1]);
             store16(xt + (int64_t)tr * d.R + tc, v);
@@ -605,10 +613,8 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
     // B X in bf16 reads X row-major through the transposing LDS loads
     constexpr bool QT = BF && (EPI == EPI_XUPD || EPI == EPI_FINAL);
     constexpr bool XT = EPI == EPI_XUPD || EPI == EPI_FINAL;
-    // bf16 X operands are stored in 32x32 blocks: both Gram operands and the
-    // update's right operand
-    constexpr bool PB = BF && EPI == EPI_GRAM;
-    constexpr bool QB = BF && (EPI == EPI_GRAM || XT);
+    // every bf16 operand (X, A, B) is stored in 32x32 blocks
+    constexpr bool PB = BF, QB = BF;
     constexpr int KE = kRowBytes / (int)sizeof(T);
     constexpr int SLD = 36;  // epilogue staging row stride (floats): 16-byte aligned runs
     // the stage ring; after the main loop its start is the epilogue staging
