@@ -381,10 +381,17 @@ int muon_adamw_plan(const ma_param_desc* table, int32_t n, const ma_plan_opts* o
             }
             numel *= s;
         }
-        if (d.ndim == 2 && (d.shape[0] > (int64_t(1) << 30) || d.shape[1] > (int64_t(1) << 30))) {
-            // Muon dimensions are kept in 32-bit fields on the device.
-            if (route(d.name, d.ndim, d.trainable != 0, mode) == MA_GROUP_MUON) {
-                set_error("muon_adamw_plan: entry %d (%s): matrix side above 2^30", i, d.name);
+        if (d.ndim == 2 && route(d.name, d.ndim, d.trainable != 0, mode) == MA_GROUP_MUON) {
+            // The Newton-Schulz operands are addressed with 32-bit buffer
+            // offsets inside resources of at most 2^31 - 1 bytes: every padded
+            // operand, up to fp32 R x C, must fit.
+            const int64_t R = round_up(std::min(d.shape[0], d.shape[1]), kNsPad);
+            const int64_t C = round_up(std::max(d.shape[0], d.shape[1]), kNsPad);
+            if (d.shape[0] > (int64_t(1) << 30) || d.shape[1] > (int64_t(1) << 30) ||
+                R * C > ((int64_t(1) << 31) - 1) / 4) {
+                set_error("muon_adamw_plan: entry %d (%s): Muon matrix %lld x %lld too large "
+                          "(its padded fp32 operand must stay below 2 GiB)",
+                          i, d.name, (long long)d.shape[0], (long long)d.shape[1]);
                 return MA_ERR_SHAPE;
             }
         }

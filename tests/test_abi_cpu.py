@@ -121,6 +121,15 @@ def test_plan_errors(lib):
     with pytest.raises(M.MuonAdamWError) as e:
         M.muon_adamw_plan([("a.weight", (1 << 40, 1 << 40), True)])
     assert e.value.code == M.MA_ERR_SHAPE
+    # a Muon matrix whose padded fp32 operand would pass 2 GiB (the 32-bit
+    # buffer offsets of the GEMM loaders) is refused; the same shape routed to
+    # AdamW, and the largest Muon matrix that fits, are accepted
+    big = "action_expert.layers.0.q.weight"
+    with pytest.raises(M.MuonAdamWError) as e:
+        M.muon_adamw_plan([(big, (16384, 32768 + 1), True)])
+    assert e.value.code == M.MA_ERR_SHAPE and "too large" in M.muon_adamw_last_error()
+    M.muon_adamw_plan([("vlm.big.weight", (16384, 32769), True)])
+    M.muon_adamw_plan([(big, (16384, 32768 - 256), True)])
     plan = M.muon_adamw_plan([("a.weight", (4, 4), True)])
     with pytest.raises(M.MuonAdamWError):
         M.muon_adamw_plan_entry(plan, 5)
