@@ -154,8 +154,10 @@ int muon_adamw_default_hparams(ma_hparams* hp);
  * trainable tensor is AdamW; frozen tensors are NONE).  Host only: touches no
  * GPU.  On success *out owns a plan to be released with muon_adamw_plan_free.
  * Errors: INVALID_ARG (null table/out/name, n < 1, bad mode, coefficient not
- * finite and positive), UNSUPPORTED (ndim < 0 or > 8), SHAPE (a size < 1 or
- * an element count above 2^62). */
+ * finite and positive), UNSUPPORTED (ndim < 0 or > 8), SHAPE (a size < 1,
+ * an element count above 2^62, or a Muon matrix whose canonical r x c,
+ * each side rounded up to a multiple of 256, exceeds (2^31 - 1) / 4
+ * elements: its fp32 Newton-Schulz operand must stay below 2 GiB). */
 int muon_adamw_plan(const ma_param_desc* table, int32_t n,
                     const ma_plan_opts* opts, ma_plan** out);
 
