@@ -23,7 +23,8 @@ Citations name the page and the part of it a function follows:
                  matrix, never on a shard
   [frozen]       FSDP section: the VLM token embedding and its tied lm_head are
                  frozen by default
-  [defaults]     defaults quick-reference table (max_grad_norm 1.0)
+  [defaults]     defaults quick-reference table (max_grad_norm 1.0; learning
+                 rate schedule cosine_with_min_lr with min_lr_rate 0.1)
 
 Readings where the page is silent (each also listed in the design notes):
   * NS quintic coefficients: the page gives none.  Default (3.2608, -3.6447,
@@ -43,12 +44,17 @@ Readings where the page is silent (each also listed in the design notes):
   * Clipping is global over every trainable gradient of both groups, with the
     1e-6 guard of the usual clip_grad_norm_, and is applied before both
     updates; max_grad_norm <= 0 disables it; non-finite norms propagate.
+  * The schedule cosine_with_min_lr is the usual half-cosine from the base
+    lr down to min_lr_rate * lr over total_steps scheduler steps after a
+    linear warmup from 0 (0 warmup steps unless given); the scheduler step of
+    optimizer step t (counted from 1) is t - 1; past total_steps the rate
+    stays at its minimum.  The schedule scales the lr of both groups.
 """
 
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -57,7 +63,7 @@ __all__ = [
     "MUON", "ADAMW", "NONE", "GROUP_NAMES",
     "MODE_MUON_ADAMW", "MODE_ADAMW",
     "DEFAULT_NS_COEFFS", "PUBLISHED_NS_COEFFS",
-    "HParams",
+    "HParams", "schedule_factor", "scheduled_lr",
     "route_one", "route", "lr_shape_scale", "plan_dump",
     "global_grad_norm", "clip_coefficient",
     "adamw_update", "nesterov_momentum", "frobenius_normalise",
@@ -91,6 +97,34 @@ class HParams:
     muon_weight_decay: float = 0.0
     max_grad_norm: float = 1.0
     moonlight_coefficient: float = 0.2
+    lr_schedule: str = "constant"        # or "cosine_with_min_lr"  [defaults]
+    warmup_steps: int = 0
+    total_steps: int = 0
+    min_lr_rate: float = 0.1
+
+
+def schedule_factor(hp: HParams, k: int) -> float:
+    """Multiplier of the base lr at scheduler step k (0, 1, ...).  [defaults]
+
+    constant: 1.  cosine_with_min_lr: k / warmup during the linear warmup;
+    then, with progress p = (k - warmup) / (total - warmup) held at 1 past the
+    end, min_lr_rate + (1 - min_lr_rate) * (1 + cos(pi p)) / 2, which runs
+    from 1 down to min_lr_rate along half a cosine period."""
+    if hp.lr_schedule == "constant":
+        return 1.0
+    if hp.lr_schedule != "cosine_with_min_lr":
+        raise ValueError("unknown lr schedule %r" % (hp.lr_schedule,))
+    warm, total = int(hp.warmup_steps), int(hp.total_steps)
+    if k < warm:
+        return k / max(1, warm)
+    progress = min(1.0, (k - warm) / max(1, total - warm))
+    half_cosine = 0.5 * (1.0 + math.cos(math.pi * progress))
+    return hp.min_lr_rate + (1.0 - hp.min_lr_rate) * half_cosine
+
+
+def scheduled_lr(hp: HParams, t: int) -> float:
+    """Learning rate of optimizer step t (counted from 1)."""
+    return hp.lr * schedule_factor(hp, t - 1)
 
 
 # --------------------------------------------------------------------------
@@ -381,6 +415,8 @@ def optimizer_step(names, params, grads, trainable, muon_momentum, adam_m,
     shapes = [np.shape(p) if p is not None else np.shape(g) for p, g in zip(params, grads)]
     if groups is None:
         groups = route(names, shapes, trainable, mode)
+    # the schedule sets this step's lr for both groups
+    hp = replace(hp, lr=scheduled_lr(hp, t))
     live = [g for g, grp in zip(grads, groups) if grp != NONE]
     norm = global_grad_norm(live)
     coef = clip_coefficient(norm, hp.max_grad_norm)

@@ -413,3 +413,63 @@ def test_bf16_emulated_ns_close_to_exact():
     a = O.newton_schulz(g, 5)
     b = O.newton_schulz_bf16_emulated(g, 5)
     assert np.linalg.norm(a - b) / np.linalg.norm(a) < 2e-2
+
+
+# ---------------------------------------------------------------------------
+# Learning-rate schedule cosine_with_min_lr (defaults table: min_lr_rate 0.1)
+# ---------------------------------------------------------------------------
+
+def test_schedule_special_points():
+    """What the schedule's definition fixes: the base rate at the first
+    scheduler step, min_lr_rate times it at total_steps and after, the mean
+    of the two halfway (cos(pi/2) = 0), 0.5 (1 + 1/sqrt 2) of the way down at
+    a quarter, and a linear warmup from 0."""
+    hp = O.HParams(lr_schedule="cosine_with_min_lr", total_steps=100, min_lr_rate=0.1)
+    assert O.schedule_factor(hp, 0) == 1.0
+    assert O.schedule_factor(hp, 50) == pytest.approx(0.55, abs=1e-15)
+    assert O.schedule_factor(hp, 25) == pytest.approx(0.1 + 0.9 * 0.8535533905932737, abs=1e-15)
+    assert O.schedule_factor(hp, 100) == pytest.approx(0.1, abs=1e-15)
+    assert O.schedule_factor(hp, 1000) == pytest.approx(0.1, abs=1e-15)
+    warm = O.HParams(lr_schedule="cosine_with_min_lr", total_steps=30, warmup_steps=10)
+    assert [O.schedule_factor(warm, k) for k in (0, 1, 5, 9)] == [0.0, 0.1, 0.5, 0.9]
+    assert O.schedule_factor(warm, 10) == 1.0
+    assert O.schedule_factor(warm, 20) == pytest.approx(0.55, abs=1e-15)
+    const = O.HParams()
+    assert all(O.schedule_factor(const, k) == 1.0 for k in (0, 7, 10 ** 6))
+    with pytest.raises(ValueError):
+        O.schedule_factor(O.HParams(lr_schedule="linear"), 0)
+
+
+def test_schedule_monotone_and_bounded():
+    hp = O.HParams(lr_schedule="cosine_with_min_lr", total_steps=37, warmup_steps=5,
+                   min_lr_rate=0.25)
+    f = [O.schedule_factor(hp, k) for k in range(60)]
+    assert all(a <= b for a, b in zip(f[:5], f[1:6]))          # warmup rises
+    assert all(a >= b for a, b in zip(f[5:], f[6:]))           # then falls
+    assert min(f[5:]) == pytest.approx(0.25) and max(f) == 1.0
+
+
+def test_schedule_scales_the_whole_step():
+    """One AdamW step from zero moments at optimizer step t = 51 of a
+    100-step schedule (factor 0.55): closed form with lr 0.55 * 2.5e-5 and
+    the bias corrections of t = 51; and a Muon update scaled by exactly the
+    same factor as with a constant rate."""
+    hp = O.HParams(lr_schedule="cosine_with_min_lr", total_steps=100)
+    g = np.array([1e-3, -2e-6, 0.4], np.float32)
+    p0 = np.array([0.02, -0.01, 0.3], np.float32)
+    z = np.zeros(3, np.float32)
+    names = ["vlm.x", "action_expert.layers.0.q.weight"]
+    gm = np.random.default_rng(5).standard_normal((6, 9)).astype(np.float32) * np.float32(1e-3)
+    pm = np.random.default_rng(6).standard_normal((6, 9)).astype(np.float32) * np.float32(0.02)
+    res = O.optimizer_step(names, [p0, pm], [g, gm], [True, True], [None, np.zeros_like(gm)],
+                           [z, None], [z, None], 51, hp)
+    lr = 0.55 * 2.5e-5
+    coef = res.clip_coef
+    gc = coef * g.astype(np.float64)
+    m_hat = 0.1 * gc / (1 - 0.9 ** 51)
+    v_hat = 0.001 * gc * gc / (1 - 0.999 ** 51)
+    want = p0.astype(np.float64) * (1 - lr * 0.01) - lr * m_hat / (np.sqrt(v_hat) + 1e-8)
+    np.testing.assert_allclose(res.params[0], want, rtol=3e-7, atol=1e-12)
+    flat = O.optimizer_step(names, [p0, pm], [g, gm], [True, True], [None, np.zeros_like(gm)],
+                            [z, None], [z, None], 51, O.HParams())
+    np.testing.assert_allclose(res.deltas[1], 0.55 * flat.deltas[1], rtol=1e-12, atol=0)
