@@ -158,7 +158,7 @@ def cpu_baseline(w, hp_overrides) -> dict:
         coef = O.clip_coefficient(norm, hp.max_grad_norm)
         for i in idx:
             shape = w.params[i].shape
-            if O.route_one(names[i], shape, True) == O.MUON:
+            if O.route_one(names[i], shape, True, W.mode_id(w)) == O.MUON:
                 s = O.lr_shape_scale(shape[0], shape[1], hp.moonlight_coefficient)
                 O.muon_matrix_update(params[i], grads[i], bufs[i], coef, hp, s)
             else:
@@ -235,8 +235,8 @@ def main():
     hp_over = W.hparams_for(w)
     hp = M.muon_adamw_default_hparams(ns_precision=w.ns_precision, **hp_over)
     table = list(zip(w.names, w.shapes, w.trainable))
-    plan = M.muon_adamw_plan(table, overlap_groups=not args.serial)
-    serial_plan = M.muon_adamw_plan(table, overlap_groups=False)
+    plan = M.muon_adamw_plan(table, mode=W.mode_id(w), overlap_groups=not args.serial)
+    serial_plan = M.muon_adamw_plan(table, mode=W.mode_id(w), overlap_groups=False)
     n = len(table)
     groups = [M.muon_adamw_plan_entry(plan, i)["group"] for i in range(n)]
     params, grads = [None] * n, [None] * n
@@ -326,12 +326,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16+fp32" if w.ns_precision == "bf16" else "fp32",
+        "dtype": "bf16+fp32" if (n_muon > 0 and w.ns_precision == "bf16") else "fp32",
         "data": "synthetic",
         "config": {"workload": w.name, "muon_params": n_muon, "adamw_params": n_adam,
                    "muon_matrices": len(muon_shapes), "ns_precision": w.ns_precision,
                    "ns_steps": hp.muon_ns_steps, "parallelism": "single GPU",
-                   "streams": "one stream" if args.serial else
+                   "optimizer": w.mode, "lr_schedule": hp_over.get("lr_schedule", "constant"),
+                   "streams": "one stream" if (args.serial or n_muon == 0 or n_adam == 0) else
                    "adamw beside the muon group (second stream)"},
         "serial_ms_per_step": serial_ms,
         "phase_ms": mean,

@@ -56,6 +56,10 @@ extern "C" {
 #define MA_NS_BF16 0           /* bf16 MFMA operands, fp32 accumulation    */
 #define MA_NS_FP32 1           /* fp32 MFMA throughout                     */
 
+/* ---- learning-rate schedules (defaults table of the page) ---------------- */
+#define MA_LR_CONSTANT   0     /* lr every step                            */
+#define MA_LR_COSINE_MIN 1     /* cosine_with_min_lr                       */
+
 #define MA_MAX_NDIM 8
 
 /* One model parameter, in the caller's order.  `name` is the dotted module
@@ -125,7 +129,16 @@ typedef struct {
  * global clip off.  ns_coeffs (a, b, c) define X <- a X + (b A + c A^2) X.
  * Scalars are double on the host: derived constants (1 - beta, bias
  * corrections, lr * shape factor) are formed in double and rounded once to
- * the float32 the kernels compute in. */
+ * the float32 the kernels compute in.
+ *
+ * lr_schedule (the page's defaults table: cosine_with_min_lr, min_lr_rate
+ * 0.1; default MA_LR_CONSTANT) sets the rate of optimizer step t = step + 1
+ * for both groups to lr * f(t - 1): MA_LR_CONSTANT f = 1; MA_LR_COSINE_MIN
+ * f(k) = k / warmup_steps for k < warmup_steps, else min_lr_rate +
+ * (1 - min_lr_rate) (1 + cos(pi p)) / 2 with p = (k - warmup_steps) /
+ * max(1, total_steps - warmup_steps) held at 1 past the end.  It needs
+ * total_steps >= 1, 0 <= warmup_steps <= total_steps and min_lr_rate in
+ * [0, 1]. */
 typedef struct {
     double  lr;
     double  muon_lr_scale;
@@ -141,6 +154,10 @@ typedef struct {
     double  weight_decay;
     double  muon_weight_decay;
     double  max_grad_norm;
+    int32_t lr_schedule;       /* MA_LR_CONSTANT or MA_LR_COSINE_MIN */
+    int64_t warmup_steps;
+    int64_t total_steps;
+    double  min_lr_rate;
 } ma_hparams;
 
 /* Fill *hp with the defaults listed above.  Errors: INVALID_ARG if hp is

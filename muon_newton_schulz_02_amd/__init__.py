@@ -17,7 +17,8 @@ from typing import Dict, List, Optional, Sequence, Tuple
 from . import _abi
 from ._abi import (MA_ERR_HIP, MA_ERR_INVALID_ARG, MA_ERR_SHAPE, MA_ERR_UNSUPPORTED,  # noqa: F401
                    MA_ERR_WORKSPACE, MA_GROUP_ADAMW, MA_GROUP_MUON, MA_GROUP_NONE,
-                   MA_MODE_ADAMW, MA_MODE_MUON_ADAMW, MA_NS_BF16, MA_NS_FP32, MA_OK)
+                   MA_LR_CONSTANT, MA_LR_COSINE_MIN, MA_MODE_ADAMW, MA_MODE_MUON_ADAMW,
+                   MA_NS_BF16, MA_NS_FP32, MA_OK)
 
 __all__ = [
     "MuonAdamWError", "Plan", "State",
@@ -55,7 +56,7 @@ def muon_adamw_version() -> str:
 def muon_adamw_default_hparams(**overrides) -> _abi.ma_hparams:
     """The library's defaults, with keyword overrides (field names of
     ma_hparams; `ns_coeffs` takes a 3-sequence, `ns_precision` also accepts
-    'bf16' / 'fp32')."""
+    'bf16' / 'fp32', `lr_schedule` 'constant' / 'cosine_with_min_lr')."""
     hp = _abi.ma_hparams()
     _check(_abi.load().muon_adamw_default_hparams(C.byref(hp)), "muon_adamw_default_hparams")
     for k, v in overrides.items():
@@ -64,7 +65,10 @@ def muon_adamw_default_hparams(**overrides) -> _abi.ma_hparams:
                 hp.ns_coeffs[i] = float(v[i])
         elif k == "ns_precision" and isinstance(v, str):
             hp.ns_precision = {"bf16": MA_NS_BF16, "fp32": MA_NS_FP32}[v]
-        elif k in ("muon_nesterov", "muon_ns_steps", "ns_precision"):
+        elif k == "lr_schedule" and isinstance(v, str):
+            hp.lr_schedule = {"constant": MA_LR_CONSTANT, "cosine_with_min_lr": MA_LR_COSINE_MIN}[v]
+        elif k in ("muon_nesterov", "muon_ns_steps", "ns_precision", "lr_schedule",
+                   "warmup_steps", "total_steps"):
             setattr(hp, k, int(v))
         else:
             if not hasattr(hp, k):

@@ -23,6 +23,7 @@ MA_ERR_HIP = -5
 MA_GROUP_MUON, MA_GROUP_ADAMW, MA_GROUP_NONE = 0, 1, 2
 MA_MODE_MUON_ADAMW, MA_MODE_ADAMW = 0, 1
 MA_NS_BF16, MA_NS_FP32 = 0, 1
+MA_LR_CONSTANT, MA_LR_COSINE_MIN = 0, 1
 MA_MAX_NDIM = 8
 MA_PROFILE_EVENTS = 5
 
@@ -57,7 +58,9 @@ class ma_hparams(C.Structure):
                 ("ns_coeffs", C.c_double * 3), ("ns_precision", C.c_int32),
                 ("ns_eps", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
                 ("eps", C.c_double), ("weight_decay", C.c_double),
-                ("muon_weight_decay", C.c_double), ("max_grad_norm", C.c_double)]
+                ("muon_weight_decay", C.c_double), ("max_grad_norm", C.c_double),
+                ("lr_schedule", C.c_int32), ("warmup_steps", C.c_int64),
+                ("total_steps", C.c_int64), ("min_lr_rate", C.c_double)]
 
 
 # (name, restype, argtypes) of every exported symbol of the header

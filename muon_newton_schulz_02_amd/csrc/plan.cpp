@@ -322,6 +322,10 @@ int muon_adamw_default_hparams(ma_hparams* hp) {
     hp->weight_decay = 0.01;
     hp->muon_weight_decay = 0.0;
     hp->max_grad_norm = 1.0;
+    hp->lr_schedule = MA_LR_CONSTANT;
+    hp->warmup_steps = 0;
+    hp->total_steps = 0;
+    hp->min_lr_rate = 0.1;
     clear_error();
     return MA_OK;
 }

@@ -14,6 +14,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -62,6 +63,20 @@ int get_staging(const ma_plan* plan, size_t bytes, void** out, void** event) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Learning rate of optimizer step t (counted from 1): the base rate times
+// the schedule's factor at scheduler step t - 1 (cosine_with_min_lr of the
+// page's defaults table: linear warmup from 0, then half a cosine from 1 down
+// to min_lr_rate, held there past total_steps).
+double scheduled_lr(const ma_hparams& hp, int64_t t) {
+    if (hp.lr_schedule != MA_LR_COSINE_MIN) return hp.lr;
+    const int64_t k = t - 1;
+    if (k < hp.warmup_steps) return hp.lr * (double)k / (double)std::max<int64_t>(1, hp.warmup_steps);
+    const double span = (double)std::max<int64_t>(1, hp.total_steps - hp.warmup_steps);
+    const double progress = std::min(1.0, (double)(k - hp.warmup_steps) / span);
+    const double half_cosine = 0.5 * (1.0 + std::cos(M_PI * progress));
+    return hp.lr * (hp.min_lr_rate + (1.0 - hp.min_lr_rate) * half_cosine);
+}
 
 // Workgroups of the AdamW launch that runs beside the Muon group (one per CU
 // of the MI355X), and of the launch that finishes the remaining chunks.
@@ -144,6 +159,17 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         set_error("muon_adamw_step: lr, eps and ns_eps must be >= 0");
         return MA_ERR_INVALID_ARG;
     }
+    if (hp->lr_schedule != MA_LR_CONSTANT && hp->lr_schedule != MA_LR_COSINE_MIN) {
+        set_error("muon_adamw_step: unknown lr_schedule %d", hp->lr_schedule);
+        return MA_ERR_INVALID_ARG;
+    }
+    if (hp->lr_schedule == MA_LR_COSINE_MIN &&
+        !(hp->total_steps >= 1 && hp->warmup_steps >= 0 && hp->warmup_steps <= hp->total_steps &&
+          hp->min_lr_rate >= 0.0 && hp->min_lr_rate <= 1.0)) {
+        set_error("muon_adamw_step: cosine_with_min_lr needs total_steps >= 1, "
+                  "0 <= warmup_steps <= total_steps and min_lr_rate in [0, 1]");
+        return MA_ERR_INVALID_ARG;
+    }
     if (state->step < 0 || state->step > (int64_t(1) << 40)) {
         set_error("muon_adamw_step: state->step %lld out of range", (long long)state->step);
         return MA_ERR_INVALID_ARG;
@@ -191,8 +217,9 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
 
     // -------------------------------------------------------- scalars ----
     const int64_t t = state->step + 1;
+    const double lr = scheduled_lr(*hp, t);
     StepScalars sc;
-    sc.lr = (float)hp->lr;
+    sc.lr = (float)lr;
     sc.beta1 = (float)hp->beta1;
     sc.beta2 = (float)hp->beta2;
     sc.one_m_beta1 = (float)(1.0 - hp->beta1);
@@ -201,9 +228,9 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     sc.weight_decay = (float)hp->weight_decay;
     const double bc1 = 1.0 - std::pow(hp->beta1, (double)t);
     const double bc2 = 1.0 - std::pow(hp->beta2, (double)t);
-    sc.step_size = (float)(hp->lr / (bc1 > 0.0 ? bc1 : 1.0));
+    sc.step_size = (float)(lr / (bc1 > 0.0 ? bc1 : 1.0));
     sc.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2 > 0.0 ? bc2 : 1.0));
-    sc.adam_decay = (float)(1.0 - hp->lr * hp->weight_decay);
+    sc.adam_decay = (float)(1.0 - lr * hp->weight_decay);
     sc.max_grad_norm = (float)hp->max_grad_norm;
     sc.mu = (float)hp->muon_momentum;
     sc.nesterov = hp->muon_nesterov ? 1 : 0;
@@ -211,7 +238,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     sc.ns_a = (float)hp->ns_coeffs[0];
     sc.ns_b = (float)hp->ns_coeffs[1];
     sc.ns_c = (float)hp->ns_coeffs[2];
-    const float muon_decay = (float)(1.0 - hp->lr * hp->muon_weight_decay);
+    const float muon_decay = (float)(1.0 - lr * hp->muon_weight_decay);
 
     std::lock_guard<std::mutex> lock(plan->mu);
     void* host = nullptr;
@@ -280,7 +307,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
                     (e.n % 4) == 0)
                        ? 1
                        : 0;
-        d.lr_eff = (float)(hp->lr * hp->muon_lr_scale * (double)e.lr_shape_scale);
+        d.lr_eff = (float)(lr * hp->muon_lr_scale * (double)e.lr_shape_scale);
         d.decay = muon_decay;
         d.op_bf16 = L.op_group[k] == kGroupBf16 ? 1 : 0;
     }

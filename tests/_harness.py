@@ -49,7 +49,9 @@ def lib_hparams(M, hp: O.HParams, ns_precision: str):
         muon_nesterov=1 if hp.muon_nesterov else 0, muon_ns_steps=hp.muon_ns_steps,
         ns_coeffs=hp.ns_coeffs, ns_precision=ns_precision, ns_eps=hp.ns_eps,
         beta1=hp.beta1, beta2=hp.beta2, eps=hp.eps, weight_decay=hp.weight_decay,
-        muon_weight_decay=hp.muon_weight_decay, max_grad_norm=hp.max_grad_norm)
+        muon_weight_decay=hp.muon_weight_decay, max_grad_norm=hp.max_grad_norm,
+        lr_schedule=hp.lr_schedule, warmup_steps=hp.warmup_steps, total_steps=hp.total_steps,
+        min_lr_rate=hp.min_lr_rate)
 
 
 def rel_fro(a, b) -> float:
@@ -108,7 +110,7 @@ def setup_gpu(M, torch, w: W.Workload, hp: O.HParams, ns_precision: str, backend
     of entry indices that get a delta output buffer."""
     dev = torch.device("cuda", 0)
     table = list(zip(w.names, w.shapes, w.trainable))
-    plan = M.muon_adamw_plan(table)
+    plan = M.muon_adamw_plan(table, mode=W.mode_id(w))
     n = len(w.params)
     groups = [M.muon_adamw_plan_entry(plan, i)["group"] for i in range(n)]
     params, grads, dl = [None] * n, [None] * n, [None] * n

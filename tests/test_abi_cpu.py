@@ -56,13 +56,16 @@ def test_version_and_defaults(lib):
     assert hp.muon_ns_steps == 5 and hp.max_grad_norm == 1.0
     assert tuple(hp.ns_coeffs) == O.DEFAULT_NS_COEFFS
     assert hp.ns_precision == M.MA_NS_BF16
+    assert hp.lr_schedule == M.MA_LR_CONSTANT and hp.min_lr_rate == 0.1
+    assert hp.warmup_steps == 0 and hp.total_steps == 0
 
 
 @pytest.mark.parametrize("name", list(W.WORKLOADS))
 def test_plan_dump_matches_oracle(lib, name):
     w = W.WORKLOADS[name]()
-    plan = M.muon_adamw_plan(list(zip(w.names, w.shapes, w.trainable)))
-    assert M.muon_adamw_plan_dump(plan) == O.plan_dump(w.names, w.shapes, w.trainable)
+    plan = M.muon_adamw_plan(list(zip(w.names, w.shapes, w.trainable)), mode=W.mode_id(w))
+    assert M.muon_adamw_plan_dump(plan) == O.plan_dump(w.names, w.shapes, w.trainable,
+                                                       mode=W.mode_id(w))
     assert M.muon_adamw_plan_size(plan) == len(w.names)
 
 
@@ -178,6 +181,15 @@ def test_step_argument_errors_launch_nothing(lib):
     assert run(hp=M.muon_adamw_default_hparams(ns_precision=3)) == M.MA_ERR_UNSUPPORTED
     assert run(hp=M.muon_adamw_default_hparams(lr=float("nan"))) == M.MA_ERR_INVALID_ARG
     assert run(hp=M.muon_adamw_default_hparams(beta1=1.0)) == M.MA_ERR_INVALID_ARG
+    cos = dict(lr_schedule="cosine_with_min_lr")
+    assert run(hp=M.muon_adamw_default_hparams(lr_schedule=7)) == M.MA_ERR_INVALID_ARG
+    assert run(hp=M.muon_adamw_default_hparams(total_steps=0, **cos)) == M.MA_ERR_INVALID_ARG
+    assert run(hp=M.muon_adamw_default_hparams(total_steps=5, warmup_steps=6, **cos)) == \
+        M.MA_ERR_INVALID_ARG
+    assert run(hp=M.muon_adamw_default_hparams(total_steps=5, warmup_steps=-1, **cos)) == \
+        M.MA_ERR_INVALID_ARG
+    assert run(hp=M.muon_adamw_default_hparams(total_steps=5, min_lr_rate=1.5, **cos)) == \
+        M.MA_ERR_INVALID_ARG
     assert run(params=[fake, None, None]) == M.MA_ERR_INVALID_ARG
     assert run(grads=[None, fake, None]) == M.MA_ERR_INVALID_ARG
     st2 = M.State(3)

@@ -9,6 +9,7 @@ tensors, since the oracle cannot afford every matrix.
 """
 
 import math
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -67,13 +68,14 @@ def _run_parity(w, ns_precision, steps, hp=None, sampled=None, backend="numpy",
         assert abs(gnorm - norm) <= 1e-5 * norm, (gnorm, norm)
         assert run.state.step == t
         H.say("%s step %d: oracle updates (norm %.6g)" % (w.name, t, norm))
+        hp_t = replace(hp, lr=O.scheduled_lr(hp, t))  # this step's scheduled rate
         for i in idx:
             g = run.groups[i]
             if g == O.NONE:
                 continue
             grad = H.host(run.grads[i])
             if g == O.ADAMW:
-                p, m, v = O.adamw_update(op[i], grad, om[i], ov[i], t, coef, hp)
+                p, m, v = O.adamw_update(op[i], grad, om[i], ov[i], t, coef, hp_t)
                 omabs[i] = hp.beta1 * omabs[i] + (1 - hp.beta1) * np.abs(coef * grad.astype(np.float64))
                 H.check_adamw(H.host(run.params[i]), H.host(run.state.adam_m[i]),
                               H.host(run.state.adam_v[i]), p, m, v, "%s[%d] step %d" % (w.name, i, t),
@@ -84,7 +86,7 @@ def _run_parity(w, ns_precision, steps, hp=None, sampled=None, backend="numpy",
                 if m_ * n_ >= (1 << 24):
                     H.say("  oracle NS of %s %dx%d" % (w.names[i], m_, n_))
                 scale = O.lr_shape_scale(m_, n_, hp.moonlight_coefficient)
-                p, buf, delta = O.muon_matrix_update(op[i], grad, obuf[i], coef, hp, scale)
+                p, buf, delta = O.muon_matrix_update(op[i], grad, obuf[i], coef, hp_t, scale)
                 gbuf = H.host(run.state.muon_momentum[i])
                 np.testing.assert_allclose(gbuf, buf, rtol=1e-5, atol=1e-7 * (np.abs(buf).max() + 1e-30))
                 err = H.rel_fro(H.host(run.deltas[i]), delta)
@@ -162,6 +164,20 @@ def test_extreme_gradient_scales(std, clip, prec):
                    grad_std=std)
     hp = H.oracle_hparams(w, max_grad_norm=clip)
     _run_parity(w, prec, 2, hp=hp)
+
+
+@pytest.mark.parametrize("prec", ["bf16", "fp32"])
+def test_cosine_schedule(prec):
+    """The defaults table's cosine_with_min_lr (min_lr_rate 0.1) over five
+    steps of a 4-step schedule with one warmup step: the rates are 0 (warmup
+    start), the base rate, two points down the cosine and the minimum held
+    past the end, for both groups."""
+    w = _ragged_workload()
+    hp = H.oracle_hparams(w, lr_schedule="cosine_with_min_lr", warmup_steps=1, total_steps=4,
+                          lr=1e-3)
+    assert [O.schedule_factor(hp, k) for k in range(5)] == pytest.approx(
+        [0.0, 1.0, 0.775, 0.325, 0.1])
+    _run_parity(w, prec, 5, hp=hp)
 
 
 def test_adamw_mode_and_misaligned_views():
@@ -269,6 +285,24 @@ def test_vla_hybrid_full_size_sampled():
             "action_expert.layers.5.self_attn.k_proj.weight",
             "action_expert.layers.17.mlp.gate_proj.weight",
             "action_expert.layers.9.mlp.down_proj.weight"]
+    sampled = {names.index(n) for n in pick}
+    _run_parity(w, "bf16", 2, sampled=sampled, backend="torch")
+
+
+def test_vla_adamw_full_size_sampled():
+    """The page's default optimizer (optim = adamw) over the full hybrid
+    table: all 2.15e9 trainable elements through the clip and AdamW (the
+    action-expert matrices included), under cosine_with_min_lr over 1000
+    steps; the oracle follows the global norm and eight tensors of every
+    kind for two steps."""
+    w = W.vla_hybrid_adamw()
+    names = w.names
+    pick = ["vlm.model.layers.0.self_attn.q_proj.weight", "vlm.model.layers.9.mlp.up_proj.weight",
+            "vlm.model.norm.weight", "vlm.model.layers.27.input_layernorm.weight",
+            "action_expert.layers.0.self_attn.q_proj.weight",
+            "action_expert.layers.3.self_attn.v_proj.weight",
+            "action_expert.layers.17.mlp.gate_proj.weight",
+            "action_expert.layers.8.mlp.down_proj.weight"]
     sampled = {names.index(n) for n in pick}
     _run_parity(w, "bf16", 2, sampled=sampled, backend="torch")
 

@@ -352,17 +352,19 @@ def test_routing_adamw_mode():
 def test_workload_group_counts():
     """Group sizes of the synthetic workloads follow from the routing rule:
     tiny 14 Muon / 13 AdamW; 18-layer 126 / 0; full hybrid 126 / 253 / 1
-    frozen; stress 68 / 0; and the element totals of the workload text."""
+    frozen; stress 68 / 0; the full table in plain-AdamW mode 0 / 379 / 1;
+    and the element totals of the workload text."""
     import workloads as W
     expect = {
         "tiny_hybrid_fp32": (14, 13, 0, 2_097_152, 259_072),
         "ae18_muon_bf16": (126, 0, 0, 273_678_336, 0),
         "vla_hybrid_bf16": (126, 253, 1, 273_678_336, 1_879_164_928),
         "ragged_stress_bf16": (68, 0, 0, 186_646_528, 0),
+        "vla_hybrid_adamw": (0, 379, 1, 0, 2_152_843_264),
     }
     for name, (nm, na, nn, em, ea) in expect.items():
         w = W.WORKLOADS[name]()
-        groups = O.route(w.names, w.shapes, w.trainable)
+        groups = O.route(w.names, w.shapes, w.trainable, W.mode_id(w))
         assert groups.count(O.MUON) == nm
         assert groups.count(O.ADAMW) == na
         assert groups.count(O.NONE) == nn

@@ -57,8 +57,9 @@ class Workload:
     grad_row_scale: Optional[Tuple[float, float]] = None   # log-uniform per stored row
     spike: Optional[Tuple[int, float]] = None               # (rank, entry std)
     momentum_init_std: float = 0.0
-    hparams: Dict[str, float] = field(default_factory=dict)
+    hparams: Dict[str, object] = field(default_factory=dict)
     description: str = ""
+    mode: str = "muon_adamw"          # or "adamw": every trainable tensor to AdamW
 
     @property
     def names(self) -> List[str]:
@@ -169,6 +170,19 @@ def vla_hybrid_fp32ns() -> Workload:
     return w
 
 
+def vla_hybrid_adamw() -> Workload:
+    """The page's default optimizer (optim = adamw) over vla_hybrid_bf16's
+    parameters and seeds: all 2,152,843,264 trainable elements through the
+    clip and AdamW, under the defaults table's cosine_with_min_lr schedule
+    (min_lr_rate 0.1) over 1000 steps."""
+    w = vla_hybrid_bf16()
+    w.name = "vla_hybrid_adamw"
+    w.mode = "adamw"
+    w.hparams = {"lr_schedule": "cosine_with_min_lr", "total_steps": 1000, "min_lr_rate": 0.1}
+    w.description = "vla_hybrid parameter set, pure AdamW (2,152,843,264 params), cosine schedule"
+    return w
+
+
 def ragged_stress_bf16(clip: bool = True) -> Workload:
     """Large and ragged Muon matrices in one call: 8192x8192, 4096x14336,
     14336x4096, 128x8192 and 64 matrices of 64x256; gradients N(0,1) plus a
@@ -195,6 +209,7 @@ WORKLOADS = {
     "ae18_muon_bf16": ae18_muon_bf16,
     "vla_hybrid_bf16": vla_hybrid_bf16,
     "vla_hybrid_fp32ns": vla_hybrid_fp32ns,
+    "vla_hybrid_adamw": vla_hybrid_adamw,
     "ragged_stress_bf16": ragged_stress_bf16,
     "ragged_stress_bf16_noclip": lambda: ragged_stress_bf16(clip=False),
 }
@@ -297,7 +312,14 @@ def torch_grad(w: Workload, step: int, index: int, device, out=None):
     return t
 
 
-def hparams_for(w: Workload) -> Dict[str, float]:
+MODE_IDS = {"muon_adamw": 0, "adamw": 1}   # the plan's optimizer modes
+
+
+def mode_id(w: Workload) -> int:
+    return MODE_IDS[w.mode]
+
+
+def hparams_for(w: Workload) -> Dict[str, object]:
     """Hyperparameter overrides of a workload on top of the defaults
     (lr 2.5e-5, momentum 0.95 Nesterov, 5 NS steps, moonlight 0.2, AdamW
     betas (0.9, 0.999), eps 1e-8, decay 0.01, clip 1.0)."""
