@@ -44,6 +44,7 @@ extern "C" {
 #define MA_ERR_UNSUPPORTED   (-3)  /* ndim > 8, ns_steps < 1, bad mode ... */
 #define MA_ERR_WORKSPACE     (-4)  /* workspace null, small or misaligned  */
 #define MA_ERR_HIP           (-5)  /* a HIP runtime call failed            */
+#define MA_ERR_CAPTURE       (-6)  /* upload needed under stream capture   */
 
 /* ---- groups, modes, precisions ------------------------------------------ */
 #define MA_GROUP_MUON   0
@@ -112,13 +113,25 @@ typedef struct {
 /* Caller-owned optimizer state, arrays indexed like the plan's entries.
  * muon_momentum[i] (m x n) for Muon entries, adam_m[i] / adam_v[i] (numel)
  * for AdamW entries; other slots are ignored and may be NULL.  `step` counts
- * completed steps; muon_adamw_step uses step+1 for the bias correction and
- * increments it on success.  All tensors start at zero for a fresh run. */
+ * completed steps; muon_adamw_step uses t = step+1 for the schedule and the
+ * bias corrections and increments it on success.  All tensors start at zero
+ * for a fresh run.
+ *
+ * device_step (nullable): a device int64 that counts completed steps
+ * instead of `step`, which is then neither read nor changed.  Each step
+ * reads it on the device, uses t = *device_step + 1 and stores t back, in
+ * stream order.  Every launch of such a step takes the same arguments for
+ * any t, and the step skips re-uploading descriptor tables identical to the
+ * ones it last put in the same workspace; so after one eager step, a step
+ * with the same pointers and workspace can be captured in a HIP graph and
+ * replayed, each replay advancing *device_step.  In this mode nothing but
+ * this plan's steps may write the workspace between calls. */
 typedef struct {
     float* const* muon_momentum;
     float* const* adam_m;
     float* const* adam_v;
     int64_t       step;
+    int64_t*      device_step;
 } ma_state;
 
 /* Hyperparameters of one step.  muon_adamw_default_hparams fills the page's
@@ -220,8 +233,11 @@ int muon_adamw_workspace_size(const ma_plan* plan, int32_t ns_precision, size_t*
  *   bytes for hp->ns_precision, 256-byte aligned.
  * Errors (nothing launched): INVALID_ARG (null plan/state/hp, a required
  * pointer NULL, hp values out of range), UNSUPPORTED (ns_steps < 1 or > 64,
- * unknown precision), WORKSPACE (null, too small, misaligned), HIP (a launch
- * or copy failed; state->step is then not advanced). */
+ * unknown precision), WORKSPACE (null, too small, misaligned), CAPTURE (the
+ * stream is capturing and the descriptor tables would have to be uploaded:
+ * run one eager step with the same pointers and workspace first, with
+ * state->device_step set), HIP (a launch or copy failed; state->step is then
+ * not advanced). */
 int muon_adamw_step(const ma_plan* plan,
                     float* const* params,
                     const float* const* grads,

@@ -15,7 +15,7 @@ import ctypes as C
 from typing import Dict, List, Optional, Sequence, Tuple
 
 from . import _abi
-from ._abi import (MA_ERR_HIP, MA_ERR_INVALID_ARG, MA_ERR_SHAPE, MA_ERR_UNSUPPORTED,  # noqa: F401
+from ._abi import (MA_ERR_CAPTURE, MA_ERR_HIP, MA_ERR_INVALID_ARG, MA_ERR_SHAPE, MA_ERR_UNSUPPORTED,  # noqa: F401
                    MA_ERR_WORKSPACE, MA_GROUP_ADAMW, MA_GROUP_MUON, MA_GROUP_NONE,
                    MA_LR_CONSTANT, MA_LR_COSINE_MIN, MA_MODE_ADAMW, MA_MODE_MUON_ADAMW,
                    MA_NS_BF16, MA_NS_FP32, MA_OK)
@@ -178,13 +178,27 @@ def _ptr_array(xs, n: int):
 
 class State:
     """Caller-owned optimizer state: per-entry momentum (Muon) and moments
-    (AdamW) tensors, plus the step counter."""
+    (AdamW) tensors, plus the step counter: the host int `step`, or, when
+    `device_step` is set (a one-element int64 CUDA tensor or an address),
+    that device counter, which each step reads and advances on the GPU."""
 
     def __init__(self, n: int):
         self.muon_momentum: List = [None] * n
         self.adam_m: List = [None] * n
         self.adam_v: List = [None] * n
         self.step = 0
+        self.device_step = None
+
+
+def _step_ptr(x) -> int:
+    if x is None or isinstance(x, int):
+        return int(x or 0)
+    import torch
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.int64 or x.numel() != 1:
+        raise TypeError("device_step must be a one-element int64 tensor or an address")
+    if x.device.type != "cuda":
+        raise ValueError("device_step must live on the GPU")
+    return x.data_ptr()
 
 
 def muon_adamw_step(plan: Plan, params, grads, state: State, hp: _abi.ma_hparams,
@@ -214,6 +228,7 @@ def _step(plan, params, grads, state, hp, workspace, stream, grad_norm_out, muon
     st.adam_m = C.cast(am, C.POINTER(C.c_void_p))
     st.adam_v = C.cast(av, C.POINTER(C.c_void_p))
     st.step = int(state.step)
+    st.device_step = _step_ptr(getattr(state, "device_step", None)) or None
     pa = _ptr_array(params, n)
     ga = _ptr_array(grads, n)
     ua = _ptr_array(muon_update_out, n) if muon_update_out is not None else None

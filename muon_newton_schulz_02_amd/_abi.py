@@ -19,6 +19,7 @@ MA_ERR_SHAPE = -2
 MA_ERR_UNSUPPORTED = -3
 MA_ERR_WORKSPACE = -4
 MA_ERR_HIP = -5
+MA_ERR_CAPTURE = -6
 
 MA_GROUP_MUON, MA_GROUP_ADAMW, MA_GROUP_NONE = 0, 1, 2
 MA_MODE_MUON_ADAMW, MA_MODE_ADAMW = 0, 1
@@ -49,7 +50,7 @@ class ma_state(C.Structure):
     _fields_ = [("muon_momentum", C.POINTER(C.c_void_p)),
                 ("adam_m", C.POINTER(C.c_void_p)),
                 ("adam_v", C.POINTER(C.c_void_p)),
-                ("step", C.c_int64)]
+                ("step", C.c_int64), ("device_step", C.c_void_p)]
 
 
 class ma_hparams(C.Structure):

@@ -97,12 +97,24 @@ __global__ __launch_bounds__(kThreads) void k_norm_partials(const NormTensor* __
     if (threadIdx.x == 0) partials[chunk] = s;
 }
 
+// Learning rate of optimizer step t (counted from 1): the base rate times the
+// schedule's factor at scheduler step t - 1.  cosine_with_min_lr (the page's
+// defaults table): a linear warmup from 0, then half a cosine from 1 down to
+// min_lr_rate over total_steps - warmup_steps steps, held there after.
+__device__ double scheduled_lr(const StepIn& in, int64_t t) {
+    if (in.schedule != MA_LR_COSINE_MIN) return in.lr;
+    const int64_t k = t - 1;
+    if (k < in.warmup_steps) return in.lr * (double)k / (double)max(int64_t(1), in.warmup_steps);
+    const double span = (double)max(int64_t(1), in.total_steps - in.warmup_steps);
+    const double progress = fmin(1.0, (double)(k - in.warmup_steps) / span);
+    const double half_cosine = 0.5 * (1.0 + cos(M_PI * progress));
+    return in.lr * (in.min_lr_rate + (1.0 - in.min_lr_rate) * half_cosine);
+}
+
 __global__ __launch_bounds__(1024) void k_clip_finalize(const float* __restrict__ partials,
-                                                        int64_t n, float max_norm,
-                                                        float* __restrict__ coef_out,
-                                                        float* __restrict__ norm_out,
-                                                        float* __restrict__ user_norm_out,
-                                                        int* __restrict__ claim_counter) {
+                                                        int64_t n, float max_norm, StepIn in,
+                                                        StepDev* __restrict__ sd,
+                                                        float* __restrict__ user_norm_out) {
     __shared__ double smem[1024 / 64];
     double acc = 0.0;
     for (int64_t i = threadIdx.x; i < n; i += blockDim.x) acc += (double)partials[i];
@@ -119,10 +131,26 @@ __global__ __launch_bounds__(1024) void k_clip_finalize(const float* __restrict_
             coef = (double)max_norm / (norm + 1e-6);
             if (!(coef < 1.0)) coef = (coef == coef) ? 1.0 : coef;  // NaN propagates
         }
-        coef_out[0] = (float)coef;
-        norm_out[0] = (float)norm;
-        if (claim_counter) claim_counter[0] = 0;
+        sd->coef = (float)coef;
+        sd->norm = (float)norm;
+        sd->claim = 0;
         if (user_norm_out) user_norm_out[0] = (float)norm;
+        // the step number and everything that depends on it (formed in
+        // double, rounded once): the scheduled rate, AdamW's bias
+        // corrections and decay, the Muon rate and decay
+        int64_t t = in.t_host;
+        if (in.device_step) {
+            t = *in.device_step + 1;
+            *in.device_step = t;
+        }
+        const double lr = scheduled_lr(in, t);
+        const double bc1 = 1.0 - pow(in.beta1, (double)t);
+        const double bc2 = 1.0 - pow(in.beta2, (double)t);
+        sd->step_size = (float)(lr / (bc1 > 0.0 ? bc1 : 1.0));
+        sd->inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2 > 0.0 ? bc2 : 1.0));
+        sd->adam_decay = (float)(1.0 - lr * in.weight_decay);
+        sd->muon_lr = lr * in.muon_lr_scale;
+        sd->muon_decay = (float)(1.0 - lr * in.muon_weight_decay);
     }
 }
 
@@ -130,6 +158,25 @@ __global__ __launch_bounds__(1024) void k_clip_finalize(const float* __restrict_
 struct AdamArgs {
     float step_size, inv_sqrt_bc2, decay, beta1, beta2, one_m_beta1, one_m_beta2, eps;
 };
+
+// The step-independent constants of AdamW, completed from the step's
+// device values.
+struct AdamConst {
+    float beta1, beta2, one_m_beta1, one_m_beta2, eps;
+};
+
+__device__ __forceinline__ AdamArgs adam_args(const AdamConst& c, const StepDev* sd) {
+    AdamArgs a;
+    a.step_size = sd->step_size;
+    a.inv_sqrt_bc2 = sd->inv_sqrt_bc2;
+    a.decay = sd->adam_decay;
+    a.beta1 = c.beta1;
+    a.beta2 = c.beta2;
+    a.one_m_beta1 = c.one_m_beta1;
+    a.one_m_beta2 = c.one_m_beta2;
+    a.eps = c.eps;
+    return a;
+}
 
 __device__ __forceinline__ void adam_elem(float& p, float g, float& m, float& v, float coef,
                                           const AdamArgs& a) {
@@ -143,8 +190,9 @@ __device__ __forceinline__ void adam_elem(float& p, float g, float& m, float& v,
 
 template <int U>
 __global__ __launch_bounds__(kThreads) void k_adamw(const AdamTensor* __restrict__ tab, int n_tab,
-                                                    const float* __restrict__ coef_ptr,
-                                                    AdamArgs a) {
+                                                    const StepDev* __restrict__ sd,
+                                                    AdamConst ac) {
+    const AdamArgs a = adam_args(ac, sd);
     const int64_t chunk = blockIdx.x;
     const int t = find_tensor(tab, n_tab, chunk);
     const AdamTensor d = tab[t];
@@ -154,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(const AdamTensor* __restrict
     const float* g = reinterpret_cast<const float*>(d.g) + begin;
     float* m = reinterpret_cast<float*>(d.m) + begin;
     float* v = reinterpret_cast<float*>(d.v) + begin;
-    const float coef = *coef_ptr;
+    const float coef = sd->coef;
     if (d.vec_ok && len == kChunk) {
         f4* p4 = reinterpret_cast<f4*>(p);
         const f4* g4 = reinterpret_cast<const f4*>(g);
@@ -270,10 +318,12 @@ __device__ __forceinline__ void adamw_chunk_wave(const AdamTensor* __restrict__ 
 // allocation granule).
 template <int U>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) void k_adamw_claim(
-    const AdamTensor* __restrict__ tab, int n_tab, int64_t n_chunks,
-    const float* __restrict__ coef_ptr, AdamArgs a, int* __restrict__ counter) {
+    const AdamTensor* __restrict__ tab, int n_tab, int64_t n_chunks, StepDev* __restrict__ sd,
+    AdamConst ac) {
+    const AdamArgs a = adam_args(ac, sd);
+    int* counter = &sd->claim;
     const int lane = threadIdx.x & 63;
-    const float coef = *coef_ptr;
+    const float coef = sd->coef;
     for (;;) {
         int c = 0;
         if (lane == 0) c = atomicAdd(counter, 1);
@@ -359,7 +409,7 @@ __device__ __forceinline__ void write_operands_fp32(const MuonMat& d,
 // update: itself), which is exact up to rounding since every product is
 // homogeneous in X.
 __global__ __launch_bounds__(kThreads) void k_muon_prep(const MuonMat* __restrict__ tab, int n_tab,
-                                                        const float* __restrict__ coef_ptr,
+                                                        const StepDev* __restrict__ sd,
                                                         MomArgs a, float* __restrict__ partials) {
     constexpr int TS = kOrientTile;
     __shared__ float tile[TS][TS + 1];
@@ -369,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void k_muon_prep(const MuonMat* __restric
     const int64_t local = blk - d.orient_begin;
     const int tiles_c = d.C / TS;
     const int i0 = (int)(local / tiles_c) * TS, j0 = (int)(local % tiles_c) * TS;
-    const float coef = *coef_ptr;
+    const float coef = sd->coef;
     const float* g = reinterpret_cast<const float*>(d.g);
     float* buf = reinterpret_cast<float*>(d.buf);
     // stored tile origin: rows sr0.., cols sc0..
@@ -493,56 +543,48 @@ int launch_norm_partials(const NormTensor* tab, int32_t n_tab, int64_t n_chunks,
     return (int)hipGetLastError();
 }
 
-int launch_clip_finalize(const float* partials, int64_t n, float max_grad_norm, float* coef_out,
-                         float* norm_out, float* user_norm_out, int* claim_counter, void* stream) {
+int launch_clip_finalize(const float* partials, int64_t n, float max_grad_norm,
+                         const StepIn& in, StepDev* sd, float* user_norm_out, void* stream) {
     hipLaunchKernelGGL(k_clip_finalize, dim3(1), dim3(1024), 0, (hipStream_t)stream, partials, n,
-                       max_grad_norm, coef_out, norm_out, user_norm_out, claim_counter);
+                       max_grad_norm, in, sd, user_norm_out);
     return (int)hipGetLastError();
 }
 
-int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, const float* coef,
+AdamConst adam_const(const StepScalars& s) {
+    AdamConst c;
+    c.beta1 = s.beta1;
+    c.beta2 = s.beta2;
+    c.one_m_beta1 = s.one_m_beta1;
+    c.one_m_beta2 = s.one_m_beta2;
+    c.eps = s.eps;
+    return c;
+}
+
+int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, const StepDev* sd,
                  const StepScalars& s, void* stream) {
     if (n_chunks == 0) return (int)hipSuccess;
-    AdamArgs a;
-    a.step_size = s.step_size;
-    a.inv_sqrt_bc2 = s.inv_sqrt_bc2;
-    a.decay = s.adam_decay;
-    a.beta1 = s.beta1;
-    a.beta2 = s.beta2;
-    a.one_m_beta1 = s.one_m_beta1;
-    a.one_m_beta2 = s.one_m_beta2;
-    a.eps = s.eps;
     // four vectors per stream in flight (108 VGPRs) for the full HBM rate
     hipLaunchKernelGGL(k_adamw<4>, dim3((unsigned)n_chunks), dim3(kThreads), 0, (hipStream_t)stream,
-                       tab, n_tab, coef, a);
+                       tab, n_tab, sd, adam_const(s));
     return (int)hipGetLastError();
 }
 
-int launch_adamw_claim(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, const float* coef,
-                       const StepScalars& s, int* counter, int64_t grid, void* stream) {
+int launch_adamw_claim(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, StepDev* sd,
+                       const StepScalars& s, int64_t grid, void* stream) {
     if (n_chunks == 0 || grid <= 0) return (int)hipSuccess;
-    AdamArgs a;
-    a.step_size = s.step_size;
-    a.inv_sqrt_bc2 = s.inv_sqrt_bc2;
-    a.decay = s.adam_decay;
-    a.beta1 = s.beta1;
-    a.beta2 = s.beta2;
-    a.one_m_beta1 = s.one_m_beta1;
-    a.one_m_beta2 = s.one_m_beta2;
-    a.eps = s.eps;
     // four vectors per stream in flight in 80 VGPRs, which with a
     // Newton-Schulz GEMM wave's at most 432 registers fills a SIMD's 512
     hipLaunchKernelGGL(k_adamw_claim<4>, dim3((unsigned)grid), dim3(kThreads), 0,
-                       (hipStream_t)stream, tab, n_tab, n_chunks, coef, a, counter);
+                       (hipStream_t)stream, tab, n_tab, n_chunks, sd, adam_const(s));
     return (int)hipGetLastError();
 }
 
-int launch_muon_prep(const MuonMat* tab, int32_t n_tab, int64_t n_tiles, const float* coef,
+int launch_muon_prep(const MuonMat* tab, int32_t n_tab, int64_t n_tiles, const StepDev* sd,
                      const StepScalars& s, float* partials, void* stream) {
     if (n_tiles == 0) return (int)hipSuccess;
     MomArgs a{s.mu, s.nesterov};
     hipLaunchKernelGGL(k_muon_prep, dim3((unsigned)n_tiles), dim3(kThreads), 0, (hipStream_t)stream,
-                       tab, n_tab, coef, a, partials);
+                       tab, n_tab, sd, a, partials);
     return (int)hipGetLastError();
 }
 

@@ -75,8 +75,7 @@ struct MuonMat {
     int32_t  m, n, r, c, R, C;
     int32_t  transposed;
     int32_t  vec_ok;               // p, g, buf (and delta) 16-byte aligned and n % 4 == 0
-    float    lr_eff;               // lr * muon_lr_scale * lr_shape_scale
-    float    decay;                // 1 - lr * muon_weight_decay
+    float    shape_scale;          // lr_shape_scale: the update is muon_lr * this (StepDev)
     int32_t  op_bf16;              // NS operands are bf16 (else fp32)
 };
 
@@ -95,7 +94,7 @@ struct Layout {
     std::vector<int32_t> op_group;                   // per Muon matrix: kGroupBf16 / kGroupFp32
     std::vector<GemmTile> g1[2], g2[2], g3[2];       // cost-ordered tile lists per group
     size_t g1_off[2] = {0, 0}, g2_off[2] = {0, 0}, g3_off[2] = {0, 0};
-    size_t scalars_off = 0;                          // coef (float), norm (float), AdamW chunk counter (int)
+    size_t scalars_off = 0;                          // StepDev
     size_t norm_partials_off = 0;                    // float[n_norm_chunks]
     size_t muon_partials_off = 0;                    // float[n_orient_tiles]
     size_t muon_scale_off = 0;                       // float[n_muon]: factor applied in NS
@@ -151,9 +150,44 @@ struct ma_plan {
     mutable size_t staging_bytes[2] = {0, 0};
     mutable void* staging_event[2] = {nullptr, nullptr};
     mutable int staging_next = 0;
+    // the descriptor tables a step with a device-resident step counter last
+    // uploaded, and where: an identical upload into the same workspace is
+    // skipped, so such a step can be captured in a graph and replayed
+    mutable std::vector<char> table_cache;
+    mutable const void* table_cache_ws = nullptr;
+    mutable int32_t table_cache_prec = -1;
 };
 
 namespace ma {
+
+// Values of one step that depend on the step number or the gradients, in
+// device memory (the workspace's scalars).  The clip finaliser -- the one
+// workgroup that runs before any kernel reading them -- writes them, so
+// every launch of a step takes the same arguments whatever the step number,
+// and the step can be captured once and replayed.
+struct StepDev {
+    float   coef;          // clip factor
+    float   norm;          // global gradient norm
+    int32_t claim;         // AdamW chunk counter of the overlapped groups
+    int32_t pad_;
+    double  muon_lr;       // lr_t * muon_lr_scale (times a matrix's shape factor: its update rate)
+    float   step_size;     // lr_t / (1 - beta1^t)
+    float   inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
+    float   adam_decay;    // 1 - lr_t * weight_decay
+    float   muon_decay;    // 1 - lr_t * muon_weight_decay
+};
+
+// What the clip finaliser needs to form StepDev: the hyperparameters in
+// double and the step number t, taken from t_host or, when device_step is
+// set, read from and advanced in device memory.
+struct StepIn {
+    double  lr, muon_lr_scale, beta1, beta2, weight_decay, muon_weight_decay, min_lr_rate;
+    int64_t warmup_steps, total_steps;
+    int32_t schedule;      // MA_LR_*
+    int32_t pad_;
+    int64_t t_host;
+    int64_t* device_step;
+};
 
 void set_error(const char* fmt, ...);
 void clear_error();
@@ -162,14 +196,12 @@ void clear_error();
 void build_layout(ma_plan* plan, int32_t precision);
 
 // --------------------------------------------------------- launchers -----
-// Per-step constants, formed in double on the host from the double
-// hyperparameters and rounded once to the float32 the kernels use.
+// Constants of the step that do not depend on the step number, formed in
+// double on the host from the double hyperparameters and rounded once to the
+// float32 the kernels use (the step-dependent ones are in StepDev).
 struct StepScalars {
-    float lr, beta1, beta2, eps, weight_decay;
+    float beta1, beta2, eps;
     float one_m_beta1, one_m_beta2;
-    float step_size;        // lr / (1 - beta1^t)
-    float inv_sqrt_bc2;     // 1 / sqrt(1 - beta2^t)
-    float adam_decay;       // 1 - lr * weight_decay
     float max_grad_norm;
     float mu;
     int32_t nesterov;
@@ -180,13 +212,12 @@ struct StepScalars {
 // Each returns a hipError_t as int.
 int launch_norm_partials(const NormTensor* tab, int32_t n_tab, int64_t n_chunks,
                          float* partials, void* stream);
-// Also zeroes `claim_counter` (nullable), the chunk counter of
-// launch_adamw_claim, so every step starts claiming at chunk 0.
+// The clip factor and norm, and every other step-dependent value, into
+// *sd; also zeroes sd->claim, so every step's AdamW chunk claims start at 0.
 int launch_clip_finalize(const float* partials, int64_t n, float max_grad_norm,
-                         float* coef_out, float* norm_out, float* user_norm_out,
-                         int* claim_counter, void* stream);
+                         const StepIn& in, StepDev* sd, float* user_norm_out, void* stream);
 int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
-                 const float* coef, const StepScalars& s, void* stream);
+                 const StepDev* sd, const StepScalars& s, void* stream);
 // AdamW whose 16 Ki-element chunks are claimed one at a time by single waves
 // from `counter` until all n_chunks are taken.  Several such launches, on
 // different streams, may share one counter: each chunk is processed exactly
@@ -194,11 +225,10 @@ int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
 // launch takes it.  Its waves are lean enough (80 VGPRs) to share a SIMD with
 // a Newton-Schulz GEMM wave.
 int launch_adamw_claim(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
-                       const float* coef, const StepScalars& s, int* counter, int64_t grid,
-                       void* stream);
+                       StepDev* sd, const StepScalars& s, int64_t grid, void* stream);
 // Momentum/Nesterov and the unnormalised Newton-Schulz input operands, one
 // workgroup per 64 x 64 operand tile, with per-tile partials of ||u||_F^2.
-int launch_muon_prep(const MuonMat* tab, int32_t n_tab, int64_t n_tiles, const float* coef,
+int launch_muon_prep(const MuonMat* tab, int32_t n_tab, int64_t n_tiles, const StepDev* sd,
                      const StepScalars& s, float* partials, void* stream);
 // Per matrix, the normalising factor 1 / (||u||_F + eps): into ns_scale
 // (applied by the first Newton-Schulz launches), or, for a norm outside
@@ -207,9 +237,10 @@ int launch_muon_scale(const MuonMat* tab, int32_t n_tab, const float* partials, 
                       float* ns_scale, float* pre_scale, void* stream);
 // phase 1 = Gram, 2 = polynomial, 3 = X update (the parameter update when
 // `last`); group = kGroupBf16 / kGroupFp32 selects the operand type.
-// `ns_scale`: the per-matrix normalising factor, applied on iteration 0.
+// `ns_scale`: the per-matrix normalising factor, applied on iteration 0;
+// the last iteration's update reads its rate and decay from *sd.
 int launch_ns_phase(int phase, int32_t group, const MuonMat* tab, const GemmTile* tiles,
                     int64_t n_tiles, int iter, int last, const StepScalars& s,
-                    const float* ns_scale, void* stream);
+                    const float* ns_scale, const StepDev* sd, void* stream);
 
 }  // namespace ma

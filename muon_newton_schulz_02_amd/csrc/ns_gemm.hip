@@ -6,7 +6,7 @@
 //   POLY  B = b A + c (A A^T)            (r x r, K = r; A symmetric, mirrored)
 //   XUPD  X = a X + B X                  (r x c, K = r)
 // and on the last step XUPD is replaced by FINAL, whose epilogue writes the
-// parameter update p = p * decay - lr_eff * X back in the stored orientation.
+// parameter update p = p * decay - rate * X back in the stored orientation.
 //
 // MFMA operands are read from LDS as rows whose reduction index is
 // contiguous.  For GRAM and POLY both operands are such rows of a row-major
@@ -96,6 +96,13 @@ struct NsArgs {
     // per matrix 1 / (||u||_F + eps): the input operand is u itself, so the
     // first Gram scales by its square and the first X update by it
     const float* scales;
+    // the step's Muon rate and decay, read by the last X update
+    const StepDev* sd;
+};
+
+// A matrix's parameter update p = p * decay - rate * X.
+struct Upd {
+    float rate, decay;
 };
 
 // Global-memory accesses through address-space-1 pointers, so they are
@@ -174,9 +181,10 @@ __device__ __forceinline__ void lds_write16(float* dst, const float* v) {
 }
 
 // Stored-orientation update of 16 consecutive elements of parameter row
-// `row`, starting at column `col`: p = p * decay - lr_eff * x (and the
-// optional delta = lr_eff * x).
-__device__ __forceinline__ void update_run(const MuonMat& d, int row, int col, const float* x) {
+// `row`, starting at column `col`: p = p * decay - rate * x (and the
+// optional delta = rate * x).
+__device__ __forceinline__ void update_run(const MuonMat& d, const Upd& u, int row, int col,
+                                           const float* x) {
     if (row >= d.m || col >= d.n) return;
     float* p = reinterpret_cast<float*>(d.p) + (int64_t)row * d.n + col;
     float* dl = d.delta ? reinterpret_cast<float*>(d.delta) + (int64_t)row * d.n + col : nullptr;
@@ -185,8 +193,8 @@ __device__ __forceinline__ void update_run(const MuonMat& d, int row, int col, c
         load16(p, pv);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            dv[e] = d.lr_eff * x[e];
-            pv[e] = fmaf(pv[e], d.decay, -dv[e]);
+            dv[e] = u.rate * x[e];
+            pv[e] = fmaf(pv[e], u.decay, -dv[e]);
         }
         store16(p, pv);
         if (dl) store16(dl, dv);
@@ -197,8 +205,8 @@ __device__ __forceinline__ void update_run(const MuonMat& d, int row, int col, c
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             if (e < cnt) {
-                const float dv = d.lr_eff * x[e];
-                gp[e] = fmaf(gp[e], d.decay, -dv);
+                const float dv = u.rate * x[e];
+                gp[e] = fmaf(gp[e], u.decay, -dv);
                 if (dl) gd[e] = dv;
             }
         }
@@ -356,7 +364,8 @@ __device__ __forceinline__ void unpack16(const uint4* q, float* v, bool bf) {
 // stay in registers.
 template <typename T, int EPI, int SLD>
 __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, const MuonMat& d,
-                                          float* S, const NsArgs& args, float escale, int lane,
+                                          float* S, const NsArgs& args, float escale,
+                                          const Upd& up, int lane,
                                           int bi, int bj, int cur, bool need_cols,
                                           bool poly_direct, T* out_direct, int64_t ld_direct) {
     constexpr bool BF = sizeof(T) == 2;
@@ -401,7 +410,7 @@ __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, co
                 store16_hilo(reinterpret_cast<__bf16*>(d.x[cur ^ 1]) + ob,
                              reinterpret_cast<__bf16*>(d.xlo[cur ^ 1]) + ob, v);
             } else if (!d.transposed) {
-                update_run(d, gi, gj, v);
+                update_run(d, up, gi, gj, v);
             }
         } else {
             float xv[16];
@@ -411,7 +420,7 @@ __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, co
             if (EPI == EPI_XUPD) {
                 store16(reinterpret_cast<float*>(d.x[0]) + o, v);
             } else if (!d.transposed) {
-                update_run(d, gi, gj, v);
+                update_run(d, up, gi, gj, v);
             }
         }
         if (need_cols) lds_write16(S + rrow * SLD + rc0, v);
@@ -428,7 +437,7 @@ __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, co
             T* xt = reinterpret_cast<T*>(d.xt[cur ^ 1]);
             store16(xt + (int64_t)tr * d.R + tc, v);
         } else {
-            update_run(d, tr, tc, v);
+            update_run(d, up, tr, tc, v);
         }
         wave_lds_sync();
     }
@@ -769,6 +778,12 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
     const int bi0 = m0 + wm * 128, bj0 = n0 + wn * 128;
     const float s0 = args.iter == 0 ? args.scales[tile.mat] : 1.f;
     const float escale = EPI == EPI_GRAM ? s0 * s0 : (XT ? s0 : 1.f);
+    Upd up{0.f, 1.f};
+    if (EPI == EPI_FINAL) {
+        // rate = muon_lr * shape factor, formed in double and rounded once
+        up.rate = (float)(args.sd->muon_lr * (double)d.shape_scale);
+        up.decay = args.sd->muon_decay;
+    }
     // The 16 blocks go in row order; each block's global inputs are loaded
     // four blocks ahead (slots in0..in3), so their latency overlaps the
     // work on the blocks in between instead of stalling every block.
@@ -776,7 +791,7 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
 #define NS_LOAD(SLOT, I, J) \
     epi_load<T, EPI>(SLOT, d, lane, bi0 + (I) * 32, bj0 + (J) * 32, cur, poly_direct)
 #define NS_EPI(I, J, SLOT)                                                                   \
-    epi_block<T, EPI, SLD>(acc[I][J], SLOT, d, S, args, escale, lane, bi0 + (I) * 32,         \
+    epi_block<T, EPI, SLD>(acc[I][J], SLOT, d, S, args, escale, up, lane, bi0 + (I) * 32,     \
                            bj0 + (J) * 32, cur, need_cols, poly_direct, out_direct, ld_direct)
     NS_LOAD(in0, 0, 0); NS_LOAD(in1, 0, 1); NS_LOAD(in2, 0, 2); NS_LOAD(in3, 0, 3);
     NS_EPI(0, 0, in0); NS_LOAD(in0, 1, 0);
@@ -830,9 +845,9 @@ int launch_k(NsKernel k, const MuonMat* tab, const GemmTile* tiles, int64_t n, c
 
 int launch_ns_phase(int phase, int32_t group, const MuonMat* tab, const GemmTile* tiles,
                     int64_t n_tiles, int iter, int last, const StepScalars& s,
-                    const float* ns_scale, void* stream) {
+                    const float* ns_scale, const StepDev* sd, void* stream) {
     if (n_tiles == 0) return (int)hipSuccess;
-    NsArgs a{s.ns_a, s.ns_b, s.ns_c, iter, ns_scale};
+    NsArgs a{s.ns_a, s.ns_b, s.ns_c, iter, ns_scale, sd};
     hipStream_t st = (hipStream_t)stream;
     const int epi = phase == 1 ? EPI_GRAM : phase == 2 ? EPI_POLY : (last ? EPI_FINAL : EPI_XUPD);
     static const NsKernel bf[4] = {k_ns_gram_bf16, k_ns_poly_bf16, k_ns_xupd_bf16, k_ns_final_bf16};

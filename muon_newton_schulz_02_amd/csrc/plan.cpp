@@ -251,7 +251,7 @@ void build_layout(ma_plan* p, int32_t precision) {
     }
     L.tables_bytes = off - L.tables_off;
     L.scalars_off = off;
-    off = align256(off + 64);
+    off = align256(off + sizeof(StepDev));
     L.norm_partials_off = off;
     off = align256(off + sizeof(float) * (size_t)std::max<int64_t>(p->n_norm_chunks, 1));
     L.muon_partials_off = off;

@@ -64,20 +64,6 @@ int get_staging(const ma_plan* plan, size_t bytes, void** out, void** event) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Learning rate of optimizer step t (counted from 1): the base rate times
-// the schedule's factor at scheduler step t - 1 (cosine_with_min_lr of the
-// page's defaults table: linear warmup from 0, then half a cosine from 1 down
-// to min_lr_rate, held there past total_steps).
-double scheduled_lr(const ma_hparams& hp, int64_t t) {
-    if (hp.lr_schedule != MA_LR_COSINE_MIN) return hp.lr;
-    const int64_t k = t - 1;
-    if (k < hp.warmup_steps) return hp.lr * (double)k / (double)std::max<int64_t>(1, hp.warmup_steps);
-    const double span = (double)std::max<int64_t>(1, hp.total_steps - hp.warmup_steps);
-    const double progress = std::min(1.0, (double)(k - hp.warmup_steps) / span);
-    const double half_cosine = 0.5 * (1.0 + std::cos(M_PI * progress));
-    return hp.lr * (hp.min_lr_rate + (1.0 - hp.min_lr_rate) * half_cosine);
-}
-
 // Workgroups of the AdamW launch that runs beside the Muon group (one per CU
 // of the MI355X), and of the launch that finishes the remaining chunks.
 constexpr int64_t kSideAdamGroups = 256;
@@ -170,7 +156,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
                   "0 <= warmup_steps <= total_steps and min_lr_rate in [0, 1]");
         return MA_ERR_INVALID_ARG;
     }
-    if (state->step < 0 || state->step > (int64_t(1) << 40)) {
+    if (!state->device_step && (state->step < 0 || state->step > (int64_t(1) << 40))) {
         set_error("muon_adamw_step: state->step %lld out of range", (long long)state->step);
         return MA_ERR_INVALID_ARG;
     }
@@ -216,21 +202,26 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     }
 
     // -------------------------------------------------------- scalars ----
-    const int64_t t = state->step + 1;
-    const double lr = scheduled_lr(*hp, t);
+    // step-dependent values are formed on the device by the clip finaliser
+    StepIn in{};
+    in.lr = hp->lr;
+    in.muon_lr_scale = hp->muon_lr_scale;
+    in.beta1 = hp->beta1;
+    in.beta2 = hp->beta2;
+    in.weight_decay = hp->weight_decay;
+    in.muon_weight_decay = hp->muon_weight_decay;
+    in.min_lr_rate = hp->min_lr_rate;
+    in.warmup_steps = hp->warmup_steps;
+    in.total_steps = hp->total_steps;
+    in.schedule = hp->lr_schedule;
+    in.t_host = state->step + 1;
+    in.device_step = state->device_step;
     StepScalars sc;
-    sc.lr = (float)lr;
     sc.beta1 = (float)hp->beta1;
     sc.beta2 = (float)hp->beta2;
     sc.one_m_beta1 = (float)(1.0 - hp->beta1);
     sc.one_m_beta2 = (float)(1.0 - hp->beta2);
     sc.eps = (float)hp->eps;
-    sc.weight_decay = (float)hp->weight_decay;
-    const double bc1 = 1.0 - std::pow(hp->beta1, (double)t);
-    const double bc2 = 1.0 - std::pow(hp->beta2, (double)t);
-    sc.step_size = (float)(lr / (bc1 > 0.0 ? bc1 : 1.0));
-    sc.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2 > 0.0 ? bc2 : 1.0));
-    sc.adam_decay = (float)(1.0 - lr * hp->weight_decay);
     sc.max_grad_norm = (float)hp->max_grad_norm;
     sc.mu = (float)hp->muon_momentum;
     sc.nesterov = hp->muon_nesterov ? 1 : 0;
@@ -238,103 +229,140 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     sc.ns_a = (float)hp->ns_coeffs[0];
     sc.ns_b = (float)hp->ns_coeffs[1];
     sc.ns_c = (float)hp->ns_coeffs[2];
-    const float muon_decay = (float)(1.0 - lr * hp->muon_weight_decay);
-
-    std::lock_guard<std::mutex> lock(plan->mu);
-    void* host = nullptr;
-    void* event = nullptr;
-    int rc = get_staging(plan, L.tables_bytes, &host, &event);
-    if (rc != MA_OK) return rc;
-
-    // ------------------------------------------------- descriptor tables --
-    char* base = reinterpret_cast<char*>(workspace);
-    char* hb = reinterpret_cast<char*>(host);
-    std::memset(hb, 0, L.tables_bytes);
-    auto* norm_tab = reinterpret_cast<NormTensor*>(hb + L.norm_tab_off);
-    for (size_t k = 0; k < plan->train_ids.size(); ++k) {
-        const int32_t id = plan->train_ids[k];
-        NormTensor& d = norm_tab[k];
-        d.g = reinterpret_cast<uint64_t>(grads[id]);
-        d.numel = plan->entries[id].numel;
-        d.chunk_begin = plan->norm_chunk_begin[k];
-        d.vec_ok = aligned16(grads[id]) ? 1 : 0;
-    }
-    auto* adam_tab = reinterpret_cast<AdamTensor*>(hb + L.adam_tab_off);
-    for (size_t k = 0; k < plan->adam_ids.size(); ++k) {
-        const int32_t id = plan->adam_ids[k];
-        AdamTensor& d = adam_tab[k];
-        d.p = reinterpret_cast<uint64_t>(params[id]);
-        d.g = reinterpret_cast<uint64_t>(grads[id]);
-        d.m = reinterpret_cast<uint64_t>(state->adam_m[id]);
-        d.v = reinterpret_cast<uint64_t>(state->adam_v[id]);
-        d.numel = plan->entries[id].numel;
-        d.chunk_begin = plan->adam_chunk_begin[k];
-        d.vec_ok = (aligned16(params[id]) && aligned16(grads[id]) && aligned16(state->adam_m[id]) &&
-                    aligned16(state->adam_v[id]))
-                       ? 1
-                       : 0;
-    }
-    auto* muon_tab = reinterpret_cast<MuonMat*>(hb + L.muon_tab_off);
-    for (size_t k = 0; k < plan->muon_ids.size(); ++k) {
-        const int32_t id = plan->muon_ids[k];
-        const Entry& e = plan->entries[id];
-        MuonMat& d = muon_tab[k];
-        float* delta = muon_update_out ? muon_update_out[id] : nullptr;
-        d.p = reinterpret_cast<uint64_t>(params[id]);
-        d.g = reinterpret_cast<uint64_t>(grads[id]);
-        d.buf = reinterpret_cast<uint64_t>(state->muon_momentum[id]);
-        d.delta = reinterpret_cast<uint64_t>(delta);
-        auto ws = [&](size_t off) { return off ? reinterpret_cast<uint64_t>(base + off) : 0; };
-        d.x[0] = ws(L.x0[k]);
-        d.x[1] = ws(L.x1[k]);
-        d.xlo[0] = ws(L.lo0[k]);
-        d.xlo[1] = ws(L.lo1[k]);
-        d.xt[0] = ws(L.xt0[k]);
-        d.xt[1] = ws(L.xt1[k]);
-        d.a = reinterpret_cast<uint64_t>(base + L.a[k]);
-        d.b = reinterpret_cast<uint64_t>(base + L.b[k]);
-        d.numel = e.numel;
-        d.orient_begin = plan->muon_orient_begin[k];
-        d.m = (int32_t)e.m;
-        d.n = (int32_t)e.n;
-        d.r = (int32_t)e.r;
-        d.c = (int32_t)e.c;
-        d.R = (int32_t)round_up(e.r, kNsPad);
-        d.C = (int32_t)round_up(e.c, kNsPad);
-        d.transposed = e.transposed;
-        d.vec_ok = (aligned16(params[id]) && aligned16(grads[id]) &&
-                    aligned16(state->muon_momentum[id]) && (!delta || aligned16(delta)) &&
-                    (e.n % 4) == 0)
-                       ? 1
-                       : 0;
-        d.lr_eff = (float)(lr * hp->muon_lr_scale * (double)e.lr_shape_scale);
-        d.decay = muon_decay;
-        d.op_bf16 = L.op_group[k] == kGroupBf16 ? 1 : 0;
-    }
-    for (int g = 0; g < 2; ++g) {
-        std::memcpy(hb + L.g1_off[g], L.g1[g].data(), sizeof(GemmTile) * L.g1[g].size());
-        std::memcpy(hb + L.g2_off[g], L.g2[g].data(), sizeof(GemmTile) * L.g2[g].size());
-        std::memcpy(hb + L.g3_off[g], L.g3[g].data(), sizeof(GemmTile) * L.g3[g].size());
-    }
 
     hipStream_t st = (hipStream_t)stream;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(st, &cap);
+    if (e != hipSuccess) return hip_fail("hipStreamIsCapturing", e);
+    const bool capturing = cap != hipStreamCaptureStatusNone;
+    if (capturing && !state->device_step) {
+        set_error("muon_adamw_step: a captured step needs state->device_step");
+        return MA_ERR_CAPTURE;
+    }
+
+    std::lock_guard<std::mutex> lock(plan->mu);
+    // ------------------------------------------------- descriptor tables --
+    char* base = reinterpret_cast<char*>(workspace);
+    auto fill_tables = [&](char* hb) {
+        std::memset(hb, 0, L.tables_bytes);
+        auto* norm_tab = reinterpret_cast<NormTensor*>(hb + L.norm_tab_off);
+        for (size_t k = 0; k < plan->train_ids.size(); ++k) {
+            const int32_t id = plan->train_ids[k];
+            NormTensor& d = norm_tab[k];
+            d.g = reinterpret_cast<uint64_t>(grads[id]);
+            d.numel = plan->entries[id].numel;
+            d.chunk_begin = plan->norm_chunk_begin[k];
+            d.vec_ok = aligned16(grads[id]) ? 1 : 0;
+        }
+        auto* adam_tab = reinterpret_cast<AdamTensor*>(hb + L.adam_tab_off);
+        for (size_t k = 0; k < plan->adam_ids.size(); ++k) {
+            const int32_t id = plan->adam_ids[k];
+            AdamTensor& d = adam_tab[k];
+            d.p = reinterpret_cast<uint64_t>(params[id]);
+            d.g = reinterpret_cast<uint64_t>(grads[id]);
+            d.m = reinterpret_cast<uint64_t>(state->adam_m[id]);
+            d.v = reinterpret_cast<uint64_t>(state->adam_v[id]);
+            d.numel = plan->entries[id].numel;
+            d.chunk_begin = plan->adam_chunk_begin[k];
+            d.vec_ok = (aligned16(params[id]) && aligned16(grads[id]) && aligned16(state->adam_m[id]) &&
+                        aligned16(state->adam_v[id]))
+                           ? 1
+                           : 0;
+        }
+        auto* muon_tab = reinterpret_cast<MuonMat*>(hb + L.muon_tab_off);
+        for (size_t k = 0; k < plan->muon_ids.size(); ++k) {
+            const int32_t id = plan->muon_ids[k];
+            const Entry& e = plan->entries[id];
+            MuonMat& d = muon_tab[k];
+            float* delta = muon_update_out ? muon_update_out[id] : nullptr;
+            d.p = reinterpret_cast<uint64_t>(params[id]);
+            d.g = reinterpret_cast<uint64_t>(grads[id]);
+            d.buf = reinterpret_cast<uint64_t>(state->muon_momentum[id]);
+            d.delta = reinterpret_cast<uint64_t>(delta);
+            auto ws = [&](size_t off) { return off ? reinterpret_cast<uint64_t>(base + off) : 0; };
+            d.x[0] = ws(L.x0[k]);
+            d.x[1] = ws(L.x1[k]);
+            d.xlo[0] = ws(L.lo0[k]);
+            d.xlo[1] = ws(L.lo1[k]);
+            d.xt[0] = ws(L.xt0[k]);
+            d.xt[1] = ws(L.xt1[k]);
+            d.a = reinterpret_cast<uint64_t>(base + L.a[k]);
+            d.b = reinterpret_cast<uint64_t>(base + L.b[k]);
+            d.numel = e.numel;
+            d.orient_begin = plan->muon_orient_begin[k];
+            d.m = (int32_t)e.m;
+            d.n = (int32_t)e.n;
+            d.r = (int32_t)e.r;
+            d.c = (int32_t)e.c;
+            d.R = (int32_t)round_up(e.r, kNsPad);
+            d.C = (int32_t)round_up(e.c, kNsPad);
+            d.transposed = e.transposed;
+            d.vec_ok = (aligned16(params[id]) && aligned16(grads[id]) &&
+                        aligned16(state->muon_momentum[id]) && (!delta || aligned16(delta)) &&
+                        (e.n % 4) == 0)
+                           ? 1
+                           : 0;
+            d.shape_scale = e.lr_shape_scale;
+            d.op_bf16 = L.op_group[k] == kGroupBf16 ? 1 : 0;
+        }
+        for (int g = 0; g < 2; ++g) {
+            std::memcpy(hb + L.g1_off[g], L.g1[g].data(), sizeof(GemmTile) * L.g1[g].size());
+            std::memcpy(hb + L.g2_off[g], L.g2[g].data(), sizeof(GemmTile) * L.g2[g].size());
+            std::memcpy(hb + L.g3_off[g], L.g3[g].data(), sizeof(GemmTile) * L.g3[g].size());
+        }
+    };
+
     auto mark = [&](int k) -> int {
         if (!phase_events || !phase_events[k]) return 0;
         return (int)hipEventRecord((hipEvent_t)phase_events[k], st);
     };
     if (int er = mark(0)) return hip_fail("phase event", er);
-    hipError_t e = hipMemcpyAsync(base + L.tables_off, hb, L.tables_bytes, hipMemcpyHostToDevice, st);
-    if (e != hipSuccess) return hip_fail("hipMemcpyAsync (tables)", e);
-    e = hipEventRecord((hipEvent_t)event, st);
-    if (e != hipSuccess) return hip_fail("hipEventRecord", e);
+    // The tables go up through a pinned staging slot.  With a device step
+    // counter an upload identical to the one this plan last made into this
+    // workspace is skipped; under capture one is then never needed.
+    const char* upload = nullptr;
+    std::vector<char> fresh;
+    if (state->device_step) {
+        fresh.resize(L.tables_bytes);
+        fill_tables(fresh.data());
+        const bool cached = plan->table_cache_ws == workspace && plan->table_cache_prec == prec &&
+                            plan->table_cache == fresh;
+        if (!cached) {
+            if (capturing) {
+                set_error("muon_adamw_step: captured step would upload new descriptor tables; "
+                          "run one eager step with the same pointers and workspace first");
+                return MA_ERR_CAPTURE;
+            }
+            upload = fresh.data();
+        }
+    }
+    if (!state->device_step || upload) {
+        void* host = nullptr;
+        void* event = nullptr;
+        int rc = get_staging(plan, L.tables_bytes, &host, &event);
+        if (rc != MA_OK) return rc;
+        if (upload)
+            std::memcpy(host, upload, L.tables_bytes);
+        else
+            fill_tables(reinterpret_cast<char*>(host));
+        // a failure past this point may leave the workspace's tables stale
+        plan->table_cache_ws = nullptr;
+        e = hipMemcpyAsync(base + L.tables_off, host, L.tables_bytes, hipMemcpyHostToDevice, st);
+        if (e != hipSuccess) return hip_fail("hipMemcpyAsync (tables)", e);
+        e = hipEventRecord((hipEvent_t)event, st);
+        if (e != hipSuccess) return hip_fail("hipEventRecord", e);
+        if (upload) {
+            plan->table_cache.swap(fresh);
+            plan->table_cache_ws = workspace;
+            plan->table_cache_prec = prec;
+        }
+    }
 
     // ------------------------------------------------------------ launch --
     const auto* d_norm = reinterpret_cast<const NormTensor*>(base + L.norm_tab_off);
     const auto* d_adam = reinterpret_cast<const AdamTensor*>(base + L.adam_tab_off);
     const auto* d_muon = reinterpret_cast<const MuonMat*>(base + L.muon_tab_off);
-    float* scal = reinterpret_cast<float*>(base + L.scalars_off);
-    float* coef = scal + 0;
-    float* norm = scal + 1;
+    auto* sd = reinterpret_cast<StepDev*>(base + L.scalars_off);
     float* norm_partials = reinterpret_cast<float*>(base + L.norm_partials_off);
     float* muon_partials = reinterpret_cast<float*>(base + L.muon_partials_off);
     float* muon_scales = reinterpret_cast<float*>(base + L.muon_scale_off);
@@ -345,9 +373,8 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
 
     int err = launch_norm_partials(d_norm, n_train, plan->n_norm_chunks, norm_partials, stream);
     if (err) return hip_fail("clip norm partials", err);
-    int* claim = reinterpret_cast<int*>(scal + 2);
-    err = launch_clip_finalize(norm_partials, plan->n_norm_chunks, sc.max_grad_norm, coef, norm,
-                               grad_norm_out, claim, stream);
+    err = launch_clip_finalize(norm_partials, plan->n_norm_chunks, sc.max_grad_norm, in, sd,
+                               grad_norm_out, stream);
     if (err) return hip_fail("clip finalize", err);
     if ((err = mark(1))) return hip_fail("phase event", err);
     // AdamW: on the caller's stream, or forked to the side stream so it runs
@@ -365,8 +392,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         // one workgroup per CU: each of its waves shares a SIMD with a
         // Newton-Schulz GEMM wave (whose LDS and registers leave room for
         // exactly that) and streams AdamW chunks while the GEMMs run
-        err = launch_adamw_claim(d_adam, n_adam, plan->n_adam_chunks, coef, sc, claim,
-                                 kSideAdamGroups, ss);
+        err = launch_adamw_claim(d_adam, n_adam, plan->n_adam_chunks, sd, sc, kSideAdamGroups, ss);
         if (err) return hip_fail("adamw", err);
         if (phase_events && phase_events[2] &&
             (e = hipEventRecord((hipEvent_t)phase_events[2], ss)) != hipSuccess)
@@ -374,12 +400,12 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         if ((e = hipEventRecord((hipEvent_t)side->ev_join, ss)) != hipSuccess)
             return hip_fail("hipEventRecord (join)", e);
     } else {
-        err = launch_adamw(d_adam, n_adam, plan->n_adam_chunks, coef, sc, stream);
+        err = launch_adamw(d_adam, n_adam, plan->n_adam_chunks, sd, sc, stream);
         if (err) return hip_fail("adamw", err);
         if ((err = mark(2))) return hip_fail("phase event", err);
     }
     if (n_muon > 0) {
-        err = launch_muon_prep(d_muon, n_muon, plan->n_orient_tiles, coef, sc, muon_partials,
+        err = launch_muon_prep(d_muon, n_muon, plan->n_orient_tiles, sd, sc, muon_partials,
                                stream);
         if (err) return hip_fail("muon prep", err);
         err = launch_muon_scale(d_muon, n_muon, muon_partials, sc.ns_eps, muon_scales,
@@ -394,7 +420,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
                         phase == 1 ? L.g1[g] : phase == 2 ? L.g2[g] : L.g3[g];
                     const size_t off = phase == 1 ? L.g1_off[g] : phase == 2 ? L.g2_off[g] : L.g3_off[g];
                     err = launch_ns_phase(phase, g, d_muon, reinterpret_cast<const GemmTile*>(base + off),
-                                          (int64_t)tl.size(), it, last, sc, muon_scales, stream);
+                                          (int64_t)tl.size(), it, last, sc, muon_scales, sd, stream);
                     if (err) return hip_fail("newton-schulz", err);
                 }
             }
@@ -404,14 +430,14 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     }
     if (side) {
         // the chunks the side kernel has not claimed yet, at full occupancy
-        err = launch_adamw_claim(d_adam, n_adam, plan->n_adam_chunks, coef, sc, claim,
-                                 kFinishAdamGroups, stream);
+        err = launch_adamw_claim(d_adam, n_adam, plan->n_adam_chunks, sd, sc, kFinishAdamGroups,
+                                 stream);
         if (err) return hip_fail("adamw", err);
     }
     if (side && (e = hipStreamWaitEvent(st, (hipEvent_t)side->ev_join, 0)) != hipSuccess)
         return hip_fail("hipStreamWaitEvent (join)", e);
     if ((err = mark(4))) return hip_fail("phase event", err);
-    state->step = t;
+    if (!state->device_step) state->step = in.t_host;
     clear_error();
     return MA_OK;
 }

@@ -164,3 +164,17 @@ def oracle_norm_of_device_grads(run: GpuRun) -> float:
     """The oracle's global norm over every trainable gradient, each read back
     from the device as it is consumed."""
     return O.global_grad_norm(host(g) for g in run.grads if g is not None)
+
+
+def ragged_workload():
+    """Ragged Muon shapes in both orientations around tile edges, odd AdamW
+    sizes, a frozen entry and a 2-D norm weight (AdamW by name)."""
+    shapes = [(1, 7), (7, 1), (33, 65), (65, 33), (130, 300), (300, 130), (256, 256),
+              (257, 513), (513, 257), (64, 256), (3, 1000), (129, 129)]
+    params = [W.ParamSpec("action_expert.layers.%d.r.weight" % i, s) for i, s in enumerate(shapes)]
+    params += [W.ParamSpec("vlm.bias", (3,)), W.ParamSpec("vlm.w", (5, 7)),
+               W.ParamSpec("vlm.big", (16385,)), W.ParamSpec("vlm.cube", (4, 4, 4)),
+               W.ParamSpec("vlm.frozen", (9, 9), trainable=False),
+               W.ParamSpec("action_expert.layers.0.norm.weight", (40, 40))]
+    return W.Workload("ragged_small", seed=7, steps=2, ns_precision="bf16", params=params,
+                      grad_std=1e-3)

@@ -213,3 +213,49 @@ def test_workspace_size_grows_with_precision(lib):
     rc = sum(min(s) * max(s) for s in w.shapes)
     assert b >= rc * 8 and f >= rc * 12
     assert f > b
+
+
+def _header_defines():
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"#define\s+(MA_\w+)\s+\(?(-?\d+)\)?", text)}
+
+
+def test_binding_constants_match_header():
+    from muon_newton_schulz_02_amd import _abi
+    defs = _header_defines()
+    assert "MA_ERR_CAPTURE" in defs and "MA_PROFILE_EVENTS" in defs
+    for k, v in defs.items():
+        assert getattr(_abi, k) == v, k
+
+
+def test_binding_structs_match_header(tmp_path):
+    """sizeof and every field offset of the public structs, as the C compiler
+    lays them out from the header, equal the ctypes mirrors'."""
+    import shutil
+    import subprocess
+    from muon_newton_schulz_02_amd import _abi
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = [_abi.ma_param_desc, _abi.ma_plan_opts, _abi.ma_plan_entry, _abi.ma_state,
+               _abi.ma_hparams]
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "muon_adamw.h"',
+             "int main(void) {"]
+    for s in structs:
+        lines.append('printf("%s %%zu\\n", sizeof(%s));' % (s.__name__, s.__name__))
+        for f in s._fields_:
+            lines.append('printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (
+                s.__name__, f[0], s.__name__, f[0]))
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = dict(l.split() for l in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                 text=True).stdout.splitlines())
+    for s in structs:
+        assert int(out[s.__name__]) == C.sizeof(s), s.__name__
+        for f in s._fields_:
+            key = "%s.%s" % (s.__name__, f[0])
+            assert int(out[key]) == getattr(s, f[0]).offset, key

@@ -109,16 +109,7 @@ def test_tiny_hybrid_fp32_all_entries():
     _run_parity(W.tiny_hybrid_fp32(), "fp32", 3)
 
 
-def _ragged_workload():
-    shapes = [(1, 7), (7, 1), (33, 65), (65, 33), (130, 300), (300, 130), (256, 256),
-              (257, 513), (513, 257), (64, 256), (3, 1000), (129, 129)]
-    params = [W.ParamSpec("action_expert.layers.%d.r.weight" % i, s) for i, s in enumerate(shapes)]
-    params += [W.ParamSpec("vlm.bias", (3,)), W.ParamSpec("vlm.w", (5, 7)),
-               W.ParamSpec("vlm.big", (16385,)), W.ParamSpec("vlm.cube", (4, 4, 4)),
-               W.ParamSpec("vlm.frozen", (9, 9), trainable=False),
-               W.ParamSpec("action_expert.layers.0.norm.weight", (40, 40))]
-    return W.Workload("ragged_small", seed=7, steps=2, ns_precision="bf16", params=params,
-                      grad_std=1e-3)
+_ragged_workload = H.ragged_workload
 
 
 @pytest.mark.parametrize("prec,steps", [("bf16", 5), ("fp32", 5), ("bf16", 1), ("fp32", 2)])
