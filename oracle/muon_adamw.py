@@ -67,7 +67,7 @@ __all__ = [
     "route_one", "route", "lr_shape_scale", "plan_dump",
     "global_grad_norm", "clip_coefficient",
     "adamw_update", "nesterov_momentum", "frobenius_normalise",
-    "newton_schulz", "newton_schulz_bf16_emulated", "bf16_round",
+    "newton_schulz", "ns_spectral_map", "newton_schulz_bf16_emulated", "bf16_round",
     "muon_matrix_update", "optimizer_step",
 ]
 
@@ -338,6 +338,19 @@ def newton_schulz(u, steps: int, coeffs=DEFAULT_NS_COEFFS, eps: float = 1e-7):
         poly = b * gram + c * (gram @ gram)
         x = a * x + poly @ x
     return x.T if tall else x
+
+
+def ns_spectral_map(s, steps: int, coeffs=DEFAULT_NS_COEFFS) -> np.ndarray:
+    """What the NS iteration does to each singular value of its normalised
+    input [NS]: for X = U diag(s) V^T, A = X X^T = U diag(s^2) U^T, so one
+    step gives U diag(a s + b s^3 + c s^5) V^T; `steps` steps compose that
+    scalar map.  For inputs whose SVD is known by construction, at sizes the
+    matrix iteration cannot reach on a CPU."""
+    s = np.asarray(s, np.float64)
+    a, b, c = (float(v) for v in coeffs)
+    for _ in range(steps):
+        s = a * s + b * s ** 3 + c * s ** 5
+    return s
 
 
 def bf16_round(x) -> np.ndarray:

@@ -178,3 +178,21 @@ def ragged_workload():
                W.ParamSpec("action_expert.layers.0.norm.weight", (40, 40))]
     return W.Workload("ragged_small", seed=7, steps=2, ns_precision="bf16", params=params,
                       grad_std=1e-3)
+
+
+def known_svd_muon_delta_rows(ks, rows, hp: O.HParams, m: int, n: int, norm: float):
+    """Expected Muon update of the first step from a fresh state for the
+    gradient G = U diag(sigma) V^T of `ks` (canonical r x c; stored m x n),
+    at canonical rows `rows`, from the oracle's steps applied to the known
+    spectrum: the clip factor, the momentum direction (a multiple of G with
+    a zero buffer), the Frobenius normalisation, the NS map of every singular
+    value, and the rate.  Returns a (len(rows), c) float64 array."""
+    coef = O.clip_coefficient(norm, hp.max_grad_norm)
+    u, _ = O.nesterov_momentum(np.ones(1), np.zeros(1), coef, hp.muon_momentum, hp.muon_nesterov)
+    fac = float(u[0])                      # u = fac * G
+    fro = fac * math.sqrt(float(np.dot(ks.sigma, ks.sigma)))
+    x0 = fac * ks.sigma / (fro + hp.ns_eps)
+    phi = O.ns_spectral_map(x0, hp.muon_ns_steps, hp.ns_coeffs)
+    rate = (O.scheduled_lr(hp, 1) * float(hp.muon_lr_scale) *
+            float(O.lr_shape_scale(m, n)))
+    return np.stack([W.np_known_svd_row(ks, i, rate * phi) for i in rows])

@@ -45,6 +45,23 @@ def test_ns_equals_svd_spectral_map(shape, coeffs):
         assert np.linalg.norm(got - want) <= 1e-9 * np.linalg.norm(want)
 
 
+@pytest.mark.parametrize("coeffs", [O.DEFAULT_NS_COEFFS, O.PUBLISHED_NS_COEFFS])
+@pytest.mark.parametrize("shape", [(12, 30), (30, 12), (9, 9)])
+def test_spectral_map_is_the_iteration_on_singular_values(shape, coeffs):
+    """ns_spectral_map applied to the LAPACK singular values of a normalised
+    matrix, recombined with its singular vectors, is the matrix iteration."""
+    rng = np.random.default_rng(11 + shape[0])
+    g = rng.standard_normal(shape)
+    u, s, vt = np.linalg.svd(g, full_matrices=False)
+    s = s / math.sqrt(float(np.sum(s * s)))
+    for k in (1, 2, 5):
+        got = O.newton_schulz(g, k, coeffs, eps=0.0)
+        want = (u * O.ns_spectral_map(s, k, coeffs)) @ vt
+        assert np.linalg.norm(got - want) <= 1e-9 * np.linalg.norm(want)
+    assert float(O.ns_spectral_map(1.0, 5, O.DEFAULT_NS_COEFFS)) == pytest.approx(0.984131, abs=2e-6)
+    assert float(O.ns_spectral_map(0.0, 5, coeffs)) == 0.0
+
+
 def test_phi5_values_distinguish_step_count():
     """ns_steps = 5 (hyperparameter table of the page).  The fixed point of
     the map is not reached, so 4, 5 and 6 steps give visibly different gains

@@ -324,3 +324,93 @@ def hparams_for(w: Workload) -> Dict[str, object]:
     (lr 2.5e-5, momentum 0.95 Nesterov, 5 NS steps, moonlight 0.2, AdamW
     betas (0.9, 0.999), eps 1e-8, decay 0.01, clip 1.0)."""
     return dict(w.hparams)
+
+
+# --------------------------------------------------------------------------
+# Gradients with a singular value decomposition known by construction
+# --------------------------------------------------------------------------
+#
+# For matrices too large for any CPU check of the whole matrix: the canonical
+# r x c gradient (r <= c) is G = U diag(sigma) V^T with U the orthonormal r x r
+# DCT-II matrix and V^T a set of distinct rows of the orthonormal c x c one.
+# Any product U diag(w) V^T of these factors then has rows that cost one
+# length-c inverse DCT each.
+
+KIND_SVD = 3
+
+
+@dataclass(frozen=True)
+class KnownSvd:
+    r: int
+    c: int
+    sigma: np.ndarray    # (r,) float64, the singular values of G
+    rows: np.ndarray     # (r,) int64, distinct rows of the c x c DCT matrix: V^T
+
+
+def known_svd(seed: int, r: int, c: int, fro: float = 3.0,
+              spread: Tuple[float, float] = (0.5, 1.5)) -> KnownSvd:
+    """Singular values uniform in `spread`, scaled to Frobenius norm `fro`,
+    and r distinct rows out of c, from one seeded stream."""
+    if not 1 <= r <= c:
+        raise ValueError("need 1 <= r <= c")
+    g = _rng(seed, KIND_SVD, 0, 0)
+    sigma = g.uniform(spread[0], spread[1], r)
+    sigma *= fro / math.sqrt(float(np.dot(sigma, sigma)))
+    rows = g.choice(c, size=r, replace=False).astype(np.int64)
+    return KnownSvd(r, c, sigma, rows)
+
+
+def dct_entries(n: int, k, j) -> np.ndarray:
+    """Entries [k, j] (broadcast index arrays) of the orthonormal n x n DCT-II
+    matrix, sqrt((1 or 2)/n) cos(pi (2j+1) k / (2n)), in float64; the angle is
+    reduced exactly in integers first."""
+    k = np.asarray(k, np.int64)
+    j = np.asarray(j, np.int64)
+    a = ((2 * j + 1) * k) % (4 * n)
+    scale = np.where(k == 0, math.sqrt(1.0 / n), math.sqrt(2.0 / n))
+    return scale * np.cos(np.pi * a.astype(np.float64) / (2 * n))
+
+
+def np_known_svd_row(ks: KnownSvd, i: int, weights) -> np.ndarray:
+    """Row i of U diag(weights) V^T (length c, float64)."""
+    from scipy.fft import idct
+    w = np.zeros(ks.c)
+    w[ks.rows] = dct_entries(ks.r, i, np.arange(ks.r)) * np.asarray(weights, np.float64)
+    return idct(w, type=2, norm="ortho")
+
+
+def np_known_svd_matrix(ks: KnownSvd, weights) -> np.ndarray:
+    """U diag(weights) V^T in full (small sizes only), float64."""
+    r, c = ks.r, ks.c
+    u = dct_entries(r, np.arange(r)[:, None], np.arange(r)[None, :])
+    vt = dct_entries(c, ks.rows[:, None], np.arange(c)[None, :])
+    return (u * np.asarray(weights, np.float64)) @ vt
+
+
+def torch_known_svd_grad(ks: KnownSvd, device, transposed: bool = False, block: int = 2048):
+    """G (or G^T when `transposed`) as float32 on `device`: formed in float64,
+    rounded once.  V^T is built `block` rows at a time."""
+    import torch
+    r, c = ks.r, ks.c
+    f64 = dict(dtype=torch.float64, device=device)
+    i64 = dict(dtype=torch.int64, device=device)
+
+    def dct(n, k, j):
+        a = torch.remainder((2 * j + 1) * k, 4 * n).to(torch.float64)
+        scale = torch.where(k == 0, torch.tensor(math.sqrt(1.0 / n), **f64),
+                            torch.tensor(math.sqrt(2.0 / n), **f64))
+        return scale * torch.cos(a * (math.pi / (2 * n)))
+
+    ar = torch.arange(r, **i64)
+    us = dct(r, ar[:, None], ar[None, :]) * torch.as_tensor(ks.sigma, **f64)[None, :]
+    rows = torch.as_tensor(ks.rows, **i64)
+    jc = torch.arange(c, **i64)
+    g = torch.zeros((r, c), **f64)
+    for k0 in range(0, r, block):
+        k1 = min(r, k0 + block)
+        vt = dct(c, rows[k0:k1, None], jc[None, :])
+        g.addmm_(us[:, k0:k1].contiguous(), vt)
+        del vt
+    out = (g.t() if transposed else g).contiguous().to(torch.float32)
+    del g, us
+    return out
