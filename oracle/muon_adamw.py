@@ -25,6 +25,8 @@ Citations name the page and the part of it a function follows:
                  frozen by default
   [defaults]     defaults quick-reference table (max_grad_norm 1.0; learning
                  rate schedule cosine_with_min_lr with min_lr_rate 0.1)
+  [precision]    mixed-precision section: the default bf16_mixed policy
+                 stores the model in bfloat16; fp32_mixed keeps fp32 weights
 
 Readings where the page is silent (each also listed in the design notes):
   * NS quintic coefficients: the page gives none.  Default (3.2608, -3.6447,
@@ -49,6 +51,12 @@ Readings where the page is silent (each also listed in the design notes):
     linear warmup from 0 (0 warmup steps unless given); the scheduler step of
     optimizer step t (counted from 1) is t - 1; past total_steps the rate
     stays at its minimum.  The schedule scales the lr of both groups.
+  * bf16 parameter storage (bf16_mixed): parameters and their gradients are
+    bfloat16 values; optimizer states (AdamW moments, Muon momentum) stay
+    float32; the step computes as for fp32 storage and rounds the new
+    parameter once to bfloat16, ties to even.  There is no float32 master
+    copy, so an update smaller than half a bfloat16 spacing leaves the
+    parameter unchanged.
 """
 
 from __future__ import annotations
@@ -68,6 +76,7 @@ __all__ = [
     "global_grad_norm", "clip_coefficient",
     "adamw_update", "nesterov_momentum", "frobenius_normalise",
     "newton_schulz", "ns_spectral_map", "newton_schulz_bf16_emulated", "bf16_round",
+    "bf16_round_f64", "store_param",
     "muon_matrix_update", "optimizer_step",
 ]
 
@@ -101,6 +110,10 @@ class HParams:
     warmup_steps: int = 0
     total_steps: int = 0
     min_lr_rate: float = 0.1
+    # how parameters (and their gradients) are stored [precision]: "fp32",
+    # or "bf16" for the bf16_mixed policy's bfloat16 model; optimizer states
+    # stay float32 either way
+    param_storage: str = "fp32"
 
 
 def schedule_factor(hp: HParams, k: int) -> float:
@@ -276,7 +289,7 @@ def adamw_update(p, g, m, v, t: int, coef: float, hp: HParams):
     v  = beta2*v + (1-beta2)*g'^2
     p  = p - (lr / (1-beta1^t)) * m / (sqrt(v)/sqrt(1-beta2^t) + eps)
 
-    Returns float32 (p, m, v).
+    Returns (p as stored under hp.param_storage, m float32, v float32).
     """
     p = np.asarray(p, np.float64)
     g = np.asarray(g, np.float64) * coef
@@ -289,7 +302,7 @@ def adamw_update(p, g, m, v, t: int, coef: float, hp: HParams):
     v = hp.beta2 * v + (1.0 - hp.beta2) * g * g
     denom = np.sqrt(v) / math.sqrt(bc2) + hp.eps
     p = p - (hp.lr / bc1) * m / denom
-    return p.astype(np.float32), m.astype(np.float32), v.astype(np.float32)
+    return store_param(p, hp.param_storage), m.astype(np.float32), v.astype(np.float32)
 
 
 # --------------------------------------------------------------------------
@@ -353,6 +366,40 @@ def ns_spectral_map(s, steps: int, coeffs=DEFAULT_NS_COEFFS) -> np.ndarray:
     return s
 
 
+def bf16_round_f64(x) -> np.ndarray:
+    """Round float64 values directly to the nearest bfloat16 (ties to even),
+    returned as float32: no intermediate float32 rounding, which could move
+    a value onto a tie.  bfloat16 has 8 significant bits and float32's
+    exponent range (subnormals spaced 2^-133); beyond its largest value the
+    result is infinite."""
+    x = np.asarray(x, np.float64)
+    shape = x.shape
+    x = np.ascontiguousarray(x).ravel()
+    bits = x.view(np.uint64)
+    drop = np.uint64(52 - 7)                       # float64 mantissa bits below bf16's
+    lsb = (bits >> drop) & np.uint64(1)
+    half = np.uint64((1 << 44) - 1)
+    rounded = ((bits + half + lsb) & ~np.uint64((1 << 45) - 1)).view(np.float64)
+    tiny = np.abs(x) < 2.0 ** -126                  # bf16 subnormal range: fixed spacing
+    if np.any(tiny):
+        q = 2.0 ** -133
+        rounded = np.where(tiny, np.rint(x / q) * q, rounded)   # rint: ties to even
+    rounded = np.where(np.isnan(x), np.nan, rounded)
+    with np.errstate(over="ignore"):
+        out = rounded.astype(np.float32)
+    return out.reshape(shape)
+
+
+def store_param(p, storage: str) -> np.ndarray:
+    """A float64 parameter value as stored [precision]: rounded once to
+    float32, or to bfloat16 (ties to even) under bf16 storage."""
+    if storage == "fp32":
+        return np.asarray(p, np.float64).astype(np.float32)
+    if storage == "bf16":
+        return bf16_round_f64(p)
+    raise ValueError("unknown parameter storage %r" % (storage,))
+
+
 def bf16_round(x) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even), returned
     as float32.  Diagnostic helper for the bf16-emulating NS below."""
@@ -395,13 +442,13 @@ def muon_matrix_update(p, g, buf, coef: float, hp: HParams, shape_scale):
     delta  = lr * muon_lr_scale * shape_scale * O   [hparams]
     p      = p*(1 - lr*muon_wd) - delta
 
-    Returns (p float32, buf float32, delta float64)."""
+    Returns (p as stored under hp.param_storage, buf float32, delta float64)."""
     u, buf = nesterov_momentum(g, buf, coef, hp.muon_momentum, hp.muon_nesterov)
     o = newton_schulz(u, hp.muon_ns_steps, hp.ns_coeffs, hp.ns_eps)
     lr_eff = float(hp.lr) * float(hp.muon_lr_scale) * float(shape_scale)
     delta = lr_eff * o
     p = np.asarray(p, np.float64) * (1.0 - hp.lr * hp.muon_weight_decay) - delta
-    return p.astype(np.float32), buf.astype(np.float32), delta
+    return store_param(p, hp.param_storage), buf.astype(np.float32), delta
 
 
 @dataclass

@@ -492,3 +492,93 @@ def test_schedule_scales_the_whole_step():
     flat = O.optimizer_step(names, [p0, pm], [g, gm], [True, True], [None, np.zeros_like(gm)],
                             [z, None], [z, None], 51, O.HParams())
     np.testing.assert_allclose(res.deltas[1], 0.55 * flat.deltas[1], rtol=1e-12, atol=0)
+
+
+# --------------------------------------------------------------------------
+# bfloat16 parameter storage
+# --------------------------------------------------------------------------
+
+def _bf16_brute(x: float) -> float:
+    """Nearest bfloat16 by search: the bfloat16 values around x (float32 bit
+    patterns with the low 16 bits clear), the closest by exact float64
+    distance, ties to the even 16-bit pattern."""
+    import struct
+    if x == 0.0:
+        return x
+    f = np.float32(x) if abs(x) < 3.0e38 else np.float32(math.copysign(3.0e38, x))
+    base = struct.unpack("<I", struct.pack("<f", float(f)))[0] & 0xFFFF0000
+    best = None
+    for k in range(-2, 3):
+        b = (base + (k << 16)) & 0xFFFFFFFF
+        if (b & 0x7F800000) == 0x7F800000:
+            continue                                # inf / NaN patterns
+        v = struct.unpack("<f", struct.pack("<I", b))[0]
+        d = abs(x - v)
+        key = (d, (b >> 16) & 1)
+        if best is None or key < best[0]:
+            best = (key, v)
+    return best[1]
+
+
+def test_bf16_round_f64_brute_force():
+    """Direct float64 -> bfloat16 rounding against a search over the
+    neighbouring bfloat16 values, over many magnitudes and signs."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal(4000) * np.exp(rng.uniform(-60, 60, 4000))
+    got = O.bf16_round_f64(x)
+    want = np.array([_bf16_brute(float(v)) for v in x], np.float32)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_bf16_round_f64_ties_and_double_rounding():
+    """Exact midpoints go to the even neighbour; a value just above a
+    midpoint by less than float32 can hold goes up (rounding through float32
+    first would land on the tie and go to even instead)."""
+    lo = np.float64(1.0)                # bf16 neighbours 1 and 1 + 2^-7
+    mid = lo + 2.0 ** -8
+    assert float(O.bf16_round_f64(mid)) == 1.0                       # even
+    mid2 = 1.0 + 2.0 ** -7 + 2.0 ** -8                               # between odd and even
+    assert float(O.bf16_round_f64(mid2)) == 1.0 + 2.0 ** -6
+    above = mid + 2.0 ** -40
+    assert np.float32(above) == np.float32(mid)                      # float32 loses it
+    assert float(O.bf16_round_f64(above)) == 1.0 + 2.0 ** -7
+    assert float(O.bf16_round_f64(-above)) == -(1.0 + 2.0 ** -7)
+    # agrees with the float32 rounding wherever the input is a float32
+    rng = np.random.default_rng(4)
+    f = (rng.standard_normal(3000) * 10.0 ** rng.uniform(-30, 30, 3000)).astype(np.float32)
+    np.testing.assert_array_equal(O.bf16_round_f64(f.astype(np.float64)), O.bf16_round(f))
+    # subnormal spacing 2^-133, overflow to infinity, NaN kept
+    q = 2.0 ** -133
+    assert float(O.bf16_round_f64(2.5 * q)) == 2.0 * q
+    assert float(O.bf16_round_f64(3.5 * q)) == 4.0 * q
+    assert np.isinf(O.bf16_round_f64(np.float64(3.4e38)))
+    assert np.isnan(O.bf16_round_f64(np.float64("nan")))
+
+
+def test_bf16_storage_rounds_the_fp32_storage_step():
+    """The same step under bf16 storage gives the bfloat16 rounding of the
+    float64 result that fp32 storage rounds to float32 (checked through the
+    rounding window of the float32 value), for both groups; states are
+    unchanged by the storage."""
+    rng = np.random.default_rng(8)
+    hp32 = O.HParams(max_grad_norm=0.0)
+    hp16 = O.HParams(max_grad_norm=0.0, param_storage="bf16")
+    p = O.bf16_round(rng.standard_normal((16, 24)).astype(np.float32) * 0.02)
+    g = O.bf16_round(rng.standard_normal((16, 24)).astype(np.float32) * 1e-3)
+    z = np.zeros_like(p)
+    p32, m32, v32 = O.adamw_update(p, g, z, z, 1, 1.0, hp32)
+    p16, m16, v16 = O.adamw_update(p, g, z, z, 1, 1.0, hp16)
+    np.testing.assert_array_equal(m16, m32)
+    np.testing.assert_array_equal(v16, v32)
+    assert np.all(O.bf16_round(p16) == p16)                          # bf16 values
+    spacing = np.abs(p16) * 2.0 ** -7
+    assert np.all(np.abs(p16.astype(np.float64) - p32) <= 0.5 * spacing + 1e-12)
+    # AdamW's first step moves p by about lr = 2.5e-5, under half a bf16
+    # spacing at |p| ~ 0.02: most parameters stay where they were
+    assert np.mean(p16 == p) > 0.5
+    s = O.lr_shape_scale(16, 24)
+    q32, b32, d32 = O.muon_matrix_update(p, g, z, 1.0, hp32, s)
+    q16, b16, d16 = O.muon_matrix_update(p, g, z, 1.0, hp16, s)
+    np.testing.assert_array_equal(b16, b32)
+    np.testing.assert_array_equal(d16, d32)
+    np.testing.assert_array_equal(q16, O.bf16_round_f64(p.astype(np.float64) - d32))
