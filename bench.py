@@ -125,6 +125,31 @@ def copy_bandwidth(torch, mib: int = 2048, reps: int = 5) -> float:
     return 2.0 * n * 4 / (ms * 1e-3) / 1e9
 
 
+def gemm_tflops(torch, dtype, n: int = 8192, reps: int = 10) -> float:
+    """Dense n x n x n matrix product through torch (hipBLASLt), timed with
+    events: the matrix-core rate a library GEMM reaches on this GPU, next to
+    the datasheet peak."""
+    a = torch.randn((n, n), device="cuda").to(dtype)
+    b = torch.randn((n, n), device="cuda").to(dtype)
+    c = torch.mm(a, b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+
+
+def percentile(xs, q: float) -> float:
+    xs = sorted(xs)
+    k = (len(xs) - 1) * q
+    lo, hi = int(math.floor(k)), int(math.ceil(k))
+    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
+
+
 def cpu_baseline(w, hp_overrides) -> dict:
     """The oracle, as it stands, on a bounded sample of the workload: one of
     the action-expert layers (7 Muon matrices) and one of the VLM layers (9
@@ -136,9 +161,11 @@ def cpu_baseline(w, hp_overrides) -> dict:
     import workloads as W
 
     hp = O.HParams()
+    hp.param_storage = w.param_storage
     for k, v in hp_overrides.items():
         setattr(hp, k, v)
     names = w.names
+    as_stored = O.bf16_round if w.param_storage == "bf16" else (lambda x: x)
     k_ae, k_vlm = 4, 6   # sampled layers of each kind
     ae = [i for i, n in enumerate(names)
           if n.startswith("action_expert.layers.") and int(n.split(".")[2]) < k_ae]
@@ -150,8 +177,8 @@ def cpu_baseline(w, hp_overrides) -> dict:
     total_params = sum(w.params[i].numel for i in train)
 
     def timed(idx):
-        params = {i: W.np_param(w, i) for i in idx}
-        grads = {i: W.np_grad(w, 1, i) for i in idx}
+        params = {i: as_stored(W.np_param(w, i)) for i in idx}
+        grads = {i: as_stored(W.np_grad(w, 1, i)) for i in idx}
         bufs = {i: W.np_momentum(w, i) for i in idx}
         t0 = time.perf_counter()
         norm = O.global_grad_norm([grads[i] for i in idx])
@@ -235,8 +262,12 @@ def main():
     hp_over = W.hparams_for(w)
     hp = M.muon_adamw_default_hparams(ns_precision=w.ns_precision, **hp_over)
     table = list(zip(w.names, w.shapes, w.trainable))
-    plan = M.muon_adamw_plan(table, mode=W.mode_id(w), overlap_groups=not args.serial)
-    serial_plan = M.muon_adamw_plan(table, mode=W.mode_id(w), overlap_groups=False)
+    plan = M.muon_adamw_plan(table, mode=W.mode_id(w), overlap_groups=not args.serial,
+                             param_dtype=w.param_storage)
+    serial_plan = M.muon_adamw_plan(table, mode=W.mode_id(w), overlap_groups=False,
+                                    param_dtype=w.param_storage)
+    bf16_store = w.param_storage == "bf16"
+    pdt = torch.bfloat16 if bf16_store else torch.float32
     n = len(table)
     groups = [M.muon_adamw_plan_entry(plan, i)["group"] for i in range(n)]
     params, grads = [None] * n, [None] * n
@@ -245,8 +276,8 @@ def main():
     for i, spec in enumerate(w.params):
         if groups[i] == M.MA_GROUP_NONE:
             continue
-        params[i] = W.torch_param(w, i, dev)
-        grads[i] = W.torch_grad(w, 1, i, dev)
+        params[i] = W.torch_param(w, i, dev).to(pdt)
+        grads[i] = W.torch_grad(w, 1, i, dev).to(pdt)
         if groups[i] == M.MA_GROUP_MUON:
             state.muon_momentum[i] = W.torch_momentum(w, i, dev)
         else:
@@ -270,12 +301,18 @@ def main():
         M.muon_adamw_step(plan, params, grads, state, hp, ws, stream=stream)
     torch.cuda.synchronize()
     print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    # an event between steps on the caller's stream (the side stream joins
+    # it before a step's work ends) gives the per-step distribution
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
+    marks[0].record(stream)
     for s in range(args.steps):
         M.muon_adamw_step(plan, params, grads, state, hp, ws, stream=stream)
+        marks[s + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    step_ms = [marks[s].elapsed_time(marks[s + 1]) for s in range(args.steps)]
 
     # Per-kernel rooflines come from serial steps, where the library's phase
     # events bracket single kernels: [1] -> [2] is the one AdamW launch.
@@ -299,11 +336,17 @@ def main():
     evs.close()
     mean = {k: sum(v) / len(v) for k, v in phases.items()}
     copy_gbps = copy_bandwidth(torch)
+    gemm = gemm_tflops(torch, torch.bfloat16 if w.ns_precision == "bf16" else torch.float32) \
+        if n_muon > 0 else None
     flops = ns_flops(muon_shapes, hp.muon_ns_steps)
     ns_peak = PEAK_BF16_TFLOPS if w.ns_precision == "bf16" else PEAK_FP32_TFLOPS
     ns_tflops = flops / (mean["newton_schulz"] * 1e-3) / 1e12 if mean["newton_schulz"] > 0 else 0.0
-    adam_bytes = 28.0 * n_adam           # read p, g, m, v; write p, m, v (fp32)
-    norm_bytes = 4.0 * n_train           # read every gradient once
+    # AdamW reads p, g, m, v and writes p, m, v: 28 B per element with fp32
+    # parameters, 22 B with bf16 ones (m, v fp32 either way); the clip norm
+    # reads every gradient once
+    esz = 2.0 if bf16_store else 4.0
+    adam_bytes = (3.0 * esz + 16.0) * n_adam
+    norm_bytes = esz * n_train
     adam_gbps = adam_bytes / (mean["adamw"] * 1e-3) / 1e9 if mean["adamw"] > 0 else 0.0
     norm_gbps = norm_bytes / (mean["clip_norm"] * 1e-3) / 1e9 if mean["clip_norm"] > 0 else 0.0
     if n_adam > 0 and mean["adamw"] >= mean["newton_schulz"]:
@@ -326,18 +369,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16+fp32" if (n_muon > 0 and w.ns_precision == "bf16") else "fp32",
+        "dtype": ("bf16+fp32" if (bf16_store or (n_muon > 0 and w.ns_precision == "bf16"))
+                  else "fp32"),
         "data": "synthetic",
         "config": {"workload": w.name, "muon_params": n_muon, "adamw_params": n_adam,
                    "muon_matrices": len(muon_shapes), "ns_precision": w.ns_precision,
                    "ns_steps": hp.muon_ns_steps, "parallelism": "single GPU",
+                   "param_storage": w.param_storage,
                    "optimizer": w.mode, "lr_schedule": hp_over.get("lr_schedule", "constant"),
                    "streams": "one stream" if (args.serial or n_muon == 0 or n_adam == 0) else
                    "adamw beside the muon group (second stream)"},
+        "step_ms_p10_p50_p90": [percentile(step_ms, q) for q in (0.1, 0.5, 0.9)],
         "serial_ms_per_step": serial_ms,
         "phase_ms": mean,
         "ns_tflops": ns_tflops,
         "ns_mfma_frac": ns_tflops / ns_peak,
+        "gemm_tflops_measured": gemm,
+        "ns_frac_of_gemm": (ns_tflops / gemm) if gemm else None,
         "adamw_gbps": adam_gbps,
         "adamw_hbm_frac": adam_gbps / PEAK_HBM_GBPS,
         "clip_norm_gbps": norm_gbps,

@@ -61,6 +61,10 @@ extern "C" {
 #define MA_LR_CONSTANT   0     /* lr every step                            */
 #define MA_LR_COSINE_MIN 1     /* cosine_with_min_lr                       */
 
+/* ---- parameter storage (precision policies of the page) ---------------- */
+#define MA_PARAM_FP32 0        /* fp32_mixed: float32 weights              */
+#define MA_PARAM_BF16 1        /* bf16_mixed: the model stored in bfloat16 */
+
 #define MA_MAX_NDIM 8
 
 /* One model parameter, in the caller's order.  `name` is the dotted module
@@ -83,12 +87,25 @@ typedef struct {
  * Chunks are claimed from a counter in the workspace; AdamW is elementwise,
  * so the results are bitwise those of overlap 0.  The side stream is joined
  * back into the caller's stream before the step's work ends.  0 runs every
- * kernel on the caller's stream in order.  A NULL opts means mode
- * MA_MODE_MUON_ADAMW, moonlight 0.2, overlap 0. */
+ * kernel on the caller's stream in order.
+ *
+ * param_dtype: how every trainable parameter and its gradient are stored
+ * (the page's precision policies: bf16_mixed, the default there, stores the
+ * model in bfloat16; fp32_mixed keeps fp32 weights).  MA_PARAM_FP32 (0):
+ * float32.  MA_PARAM_BF16 (1): bfloat16; the step reads them as bf16,
+ * computes in float32 exactly as for float32 storage and rounds the new
+ * parameter once to bf16 (round to nearest, ties to even).  Optimizer states
+ * (Muon momentum, AdamW moments) and muon_update_out are float32 either way.
+ * With no float32 master copy an update below half a bf16 spacing leaves a
+ * parameter unchanged, as it does for any bf16-stored weight.
+ *
+ * A NULL opts means mode MA_MODE_MUON_ADAMW, moonlight 0.2, overlap 0,
+ * float32 parameters. */
 typedef struct {
     int32_t mode;                  /* MA_MODE_*                            */
     double  moonlight_coefficient; /* 0.2 on the page                      */
     int32_t overlap_groups;        /* 1: AdamW beside the Muon group       */
+    int32_t param_dtype;           /* MA_PARAM_FP32 / MA_PARAM_BF16        */
 } ma_plan_opts;
 
 typedef struct ma_plan ma_plan;    /* opaque, immutable once built         */
@@ -224,7 +241,9 @@ int muon_adamw_workspace_size(const ma_plan* plan, int32_t ns_precision, size_t*
  *      delta = lr * muon_lr_scale * lr_shape_scale * X (back in m x n);
  *      p = p (1 - lr muon_wd) - delta.
  *
- * params[i], grads[i]: entry i's tensors (NULL allowed for NONE entries).
+ * params[i], grads[i]: entry i's tensors (NULL allowed for NONE entries):
+ *   float32, or bfloat16 for a plan built with MA_PARAM_BF16 (the pointer
+ *   types stay float*; they then address 2-byte elements).
  * grad_norm_out: optional device float receiving N.
  * muon_update_out: optional array (indexed like entries) of device m x n
  *   float buffers receiving delta for Muon entries; the array itself or any

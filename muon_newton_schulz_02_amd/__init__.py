@@ -18,7 +18,7 @@ from . import _abi
 from ._abi import (MA_ERR_CAPTURE, MA_ERR_HIP, MA_ERR_INVALID_ARG, MA_ERR_SHAPE, MA_ERR_UNSUPPORTED,  # noqa: F401
                    MA_ERR_WORKSPACE, MA_GROUP_ADAMW, MA_GROUP_MUON, MA_GROUP_NONE,
                    MA_LR_CONSTANT, MA_LR_COSINE_MIN, MA_MODE_ADAMW, MA_MODE_MUON_ADAMW,
-                   MA_NS_BF16, MA_NS_FP32, MA_OK)
+                   MA_NS_BF16, MA_NS_FP32, MA_OK, MA_PARAM_BF16, MA_PARAM_FP32)
 
 __all__ = [
     "MuonAdamWError", "Plan", "State",
@@ -80,10 +80,12 @@ def muon_adamw_default_hparams(**overrides) -> _abi.ma_hparams:
 class Plan:
     """Owning handle of an ma_plan (freed with the object)."""
 
-    def __init__(self, handle: int, names: Sequence[str], shapes: Sequence[Tuple[int, ...]]):
+    def __init__(self, handle: int, names: Sequence[str], shapes: Sequence[Tuple[int, ...]],
+                 param_dtype: int = MA_PARAM_FP32):
         self.handle = C.c_void_p(handle)
         self.names = list(names)
         self.shapes = [tuple(s) for s in shapes]
+        self.param_dtype = param_dtype
 
     def __del__(self):
         try:
@@ -96,9 +98,14 @@ class Plan:
 
 def muon_adamw_plan(table: Sequence[Tuple[str, Sequence[int], bool]],
                     mode: int = MA_MODE_MUON_ADAMW,
-                    moonlight_coefficient: float = 0.2, overlap_groups: bool = False) -> Plan:
+                    moonlight_coefficient: float = 0.2, overlap_groups: bool = False,
+                    param_dtype="fp32") -> Plan:
     """Route a parameter table [(name, shape, trainable), ...] (host only).
-    overlap_groups: run the AdamW group concurrently with the Muon group."""
+    overlap_groups: run the AdamW group concurrently with the Muon group.
+    param_dtype: storage of parameters and gradients, 'fp32' or 'bf16' (or
+    MA_PARAM_*); optimizer states are float32 either way."""
+    if isinstance(param_dtype, str):
+        param_dtype = {"fp32": MA_PARAM_FP32, "bf16": MA_PARAM_BF16}[param_dtype]
     n = len(table)
     descs = (_abi.ma_param_desc * max(n, 1))()
     keep = []
@@ -110,10 +117,11 @@ def muon_adamw_plan(table: Sequence[Tuple[str, Sequence[int], bool]],
         descs[i].ndim = len(shape)
         descs[i].shape = C.cast(sh, C.POINTER(C.c_int64))
         descs[i].trainable = 1 if trainable else 0
-    opts = _abi.ma_plan_opts(int(mode), float(moonlight_coefficient), 1 if overlap_groups else 0)
+    opts = _abi.ma_plan_opts(int(mode), float(moonlight_coefficient), 1 if overlap_groups else 0,
+                             int(param_dtype))
     out = C.c_void_p()
     _check(_abi.load().muon_adamw_plan(descs, n, C.byref(opts), C.byref(out)), "muon_adamw_plan")
-    return Plan(out.value, [t[0] for t in table], [tuple(t[1]) for t in table])
+    return Plan(out.value, [t[0] for t in table], [tuple(t[1]) for t in table], int(param_dtype))
 
 
 def muon_adamw_plan_free(plan: Plan):
@@ -150,8 +158,9 @@ def muon_adamw_workspace_size(plan: Plan, ns_precision: int = MA_NS_BF16) -> int
     return n.value
 
 
-def _ptr(x) -> Optional[int]:
-    """Device address of a float32 contiguous torch tensor (or an int)."""
+def _ptr(x, bf16: bool = False) -> Optional[int]:
+    """Device address of a contiguous torch tensor (or an int): float32, or
+    bfloat16 where `bf16` (parameters and gradients of a bf16 plan)."""
     if x is None:
         return None
     if isinstance(x, int):
@@ -159,8 +168,9 @@ def _ptr(x) -> Optional[int]:
     import torch
     if not isinstance(x, torch.Tensor):
         raise TypeError("expected a torch tensor, an int address or None")
-    if x.dtype != torch.float32 and x.dtype != torch.uint8:
-        raise TypeError("tensors must be float32 (got %s)" % x.dtype)
+    want = torch.bfloat16 if bf16 else torch.float32
+    if x.dtype != want and x.dtype != torch.uint8:
+        raise TypeError("tensors must be %s (got %s)" % (want, x.dtype))
     if not x.is_contiguous():
         raise ValueError("tensors must be contiguous")
     if x.device.type != "cuda":
@@ -168,11 +178,11 @@ def _ptr(x) -> Optional[int]:
     return x.data_ptr()
 
 
-def _ptr_array(xs, n: int):
+def _ptr_array(xs, n: int, bf16: bool = False):
     arr = (C.c_void_p * max(n, 1))()
     if xs is not None:
         for i, x in enumerate(xs):
-            arr[i] = _ptr(x)
+            arr[i] = _ptr(x, bf16)
     return arr
 
 
@@ -229,8 +239,9 @@ def _step(plan, params, grads, state, hp, workspace, stream, grad_norm_out, muon
     st.adam_v = C.cast(av, C.POINTER(C.c_void_p))
     st.step = int(state.step)
     st.device_step = _step_ptr(getattr(state, "device_step", None)) or None
-    pa = _ptr_array(params, n)
-    ga = _ptr_array(grads, n)
+    bf16 = getattr(plan, "param_dtype", MA_PARAM_FP32) == MA_PARAM_BF16
+    pa = _ptr_array(params, n, bf16)
+    ga = _ptr_array(grads, n, bf16)
     ua = _ptr_array(muon_update_out, n) if muon_update_out is not None else None
     if stream is None:
         import torch
@@ -256,15 +267,19 @@ def _step(plan, params, grads, state, hp, workspace, stream, grad_norm_out, muon
 class MuonAdamW:
     """Plan + state + workspace for a list of (name, tensor, trainable).
 
-    Tensors are float32 CUDA tensors owned by the caller; gradients are passed
-    to `step`.  State tensors start at zero."""
+    Tensors are float32 (or, all of them, bfloat16: the bf16 parameter
+    storage) CUDA tensors owned by the caller; gradients are passed to
+    `step`.  State tensors are float32 and start at zero."""
 
     def __init__(self, named_params: Sequence[Tuple[str, object, bool]],
-                 mode: int = MA_MODE_MUON_ADAMW, **hparams):
+                 mode: int = MA_MODE_MUON_ADAMW, overlap_groups: bool = False, **hparams):
         import torch
         self.names = [n for n, _, _ in named_params]
         self.params = [p for _, p, _ in named_params]
-        self.plan = muon_adamw_plan([(n, tuple(p.shape), t) for n, p, t in named_params], mode)
+        bf16 = any(p is not None and p.dtype == torch.bfloat16 for p in self.params)
+        self.plan = muon_adamw_plan([(n, tuple(p.shape), t) for n, p, t in named_params], mode,
+                                    overlap_groups=overlap_groups,
+                                    param_dtype="bf16" if bf16 else "fp32")
         self.hp = muon_adamw_default_hparams(**hparams)
         self.state = State(len(self.names))
         self.groups = []
@@ -272,10 +287,10 @@ class MuonAdamW:
             g = muon_adamw_plan_entry(self.plan, i)["group"]
             self.groups.append(g)
             if g == MA_GROUP_MUON:
-                self.state.muon_momentum[i] = torch.zeros_like(p)
+                self.state.muon_momentum[i] = torch.zeros_like(p, dtype=torch.float32)
             elif g == MA_GROUP_ADAMW:
-                self.state.adam_m[i] = torch.zeros_like(p)
-                self.state.adam_v[i] = torch.zeros_like(p)
+                self.state.adam_m[i] = torch.zeros_like(p, dtype=torch.float32)
+                self.state.adam_v[i] = torch.zeros_like(p, dtype=torch.float32)
         dev = next((p.device for p in self.params if p is not None), torch.device("cuda"))
         nbytes = muon_adamw_workspace_size(self.plan, self.hp.ns_precision)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)

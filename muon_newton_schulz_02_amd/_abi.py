@@ -25,6 +25,7 @@ MA_GROUP_MUON, MA_GROUP_ADAMW, MA_GROUP_NONE = 0, 1, 2
 MA_MODE_MUON_ADAMW, MA_MODE_ADAMW = 0, 1
 MA_NS_BF16, MA_NS_FP32 = 0, 1
 MA_LR_CONSTANT, MA_LR_COSINE_MIN = 0, 1
+MA_PARAM_FP32, MA_PARAM_BF16 = 0, 1
 MA_MAX_NDIM = 8
 MA_PROFILE_EVENTS = 5
 
@@ -36,7 +37,7 @@ class ma_param_desc(C.Structure):
 
 class ma_plan_opts(C.Structure):
     _fields_ = [("mode", C.c_int32), ("moonlight_coefficient", C.c_double),
-                ("overlap_groups", C.c_int32)]
+                ("overlap_groups", C.c_int32), ("param_dtype", C.c_int32)]
 
 
 class ma_plan_entry(C.Structure):

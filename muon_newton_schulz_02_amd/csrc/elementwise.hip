@@ -26,6 +26,47 @@ namespace {
 constexpr int kThreads = 256;
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Parameters and gradients are stored as float or bf16 (the plan's
+// parameter storage); every value is computed on as float.  Four consecutive
+// elements move as one 16-byte (float) or 8-byte (bf16) access; a bf16 value
+// widens exactly and narrows with round to nearest, ties to even.
+template <typename P>
+struct Quad;
+template <>
+struct Quad<float> {
+    typedef f4 raw;
+    static __device__ __forceinline__ f4 get(raw r) { return r; }
+    static __device__ __forceinline__ raw put(f4 v) { return v; }
+};
+template <>
+struct Quad<__bf16> {
+    typedef u32x2 raw;
+    static __device__ __forceinline__ f4 get(raw r) {
+        f4 v;
+        v[0] = __uint_as_float(r[0] << 16);
+        v[1] = __uint_as_float(r[0] & 0xffff0000u);
+        v[2] = __uint_as_float(r[1] << 16);
+        v[3] = __uint_as_float(r[1] & 0xffff0000u);
+        return v;
+    }
+    static __device__ __forceinline__ raw put(f4 v) {
+        const bf16x2 a = {(__bf16)v[0], (__bf16)v[1]};
+        const bf16x2 b = {(__bf16)v[2], (__bf16)v[3]};
+        raw r;
+        r[0] = __builtin_bit_cast(unsigned int, a);
+        r[1] = __builtin_bit_cast(unsigned int, b);
+        return r;
+    }
+};
+
+__device__ __forceinline__ float ld1(const float* p) { return *p; }
+__device__ __forceinline__ float ld1(const __bf16* p) { return (float)*p; }
+__device__ __forceinline__ void st1(float* p, float v) { *p = v; }
+__device__ __forceinline__ void st1(__bf16* p, float v) { *p = (__bf16)v; }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -66,6 +107,7 @@ __device__ __forceinline__ int find_tensor(const Tab* tab, int n, int64_t chunk)
 }
 
 // ------------------------------------------------------------ clip norm --
+template <typename G>
 __global__ __launch_bounds__(kThreads) void k_norm_partials(const NormTensor* __restrict__ tab,
                                                             int n_tab,
                                                             float* __restrict__ partials) {
@@ -75,21 +117,31 @@ __global__ __launch_bounds__(kThreads) void k_norm_partials(const NormTensor* __
     const NormTensor d = tab[t];
     const int64_t begin = (chunk - d.chunk_begin) * kChunk;
     const int64_t len = min<int64_t>(kChunk, d.numel - begin);
-    const float* g = reinterpret_cast<const float*>(d.g) + begin;
+    const G* g = reinterpret_cast<const G*>(d.g) + begin;
     float acc = 0.f;
     if (d.vec_ok && len == kChunk) {
-        const f4* g4 = reinterpret_cast<const f4*>(g);
+        // 16-byte loads: 4 floats or 8 bf16, summed in element order
+        const u32x4* g16 = reinterpret_cast<const u32x4*>(g);
+        constexpr int kPer = 16 / (int)sizeof(G);
 #pragma unroll 4
-        for (int i = threadIdx.x; i < kChunk / 4; i += kThreads) {
-            const f4 v = __builtin_nontemporal_load(g4 + i);
-            acc = fmaf(v.x, v.x, acc);
-            acc = fmaf(v.y, v.y, acc);
-            acc = fmaf(v.z, v.z, acc);
-            acc = fmaf(v.w, v.w, acc);
+        for (int i = threadIdx.x; i < kChunk / kPer; i += kThreads) {
+            const u32x4 w = __builtin_nontemporal_load(g16 + i);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (sizeof(G) == 4) {
+                    const float x = __uint_as_float(w[q]);
+                    acc = fmaf(x, x, acc);
+                } else {
+                    const float lo = __uint_as_float(w[q] << 16);
+                    const float hi = __uint_as_float(w[q] & 0xffff0000u);
+                    acc = fmaf(lo, lo, acc);
+                    acc = fmaf(hi, hi, acc);
+                }
+            }
         }
     } else {
         for (int64_t i = threadIdx.x; i < len; i += kThreads) {
-            const float v = g[i];
+            const float v = ld1(g + i);
             acc = fmaf(v, v, acc);
         }
     }
@@ -188,7 +240,7 @@ __device__ __forceinline__ void adam_elem(float& p, float g, float& m, float& v,
     p = fmaf(-a.step_size, m / denom, p);
 }
 
-template <int U>
+template <int U, typename P>
 __global__ __launch_bounds__(kThreads) void k_adamw(const AdamTensor* __restrict__ tab, int n_tab,
                                                     const StepDev* __restrict__ sd,
                                                     AdamConst ac) {
@@ -198,53 +250,58 @@ __global__ __launch_bounds__(kThreads) void k_adamw(const AdamTensor* __restrict
     const AdamTensor d = tab[t];
     const int64_t begin = (chunk - d.chunk_begin) * kChunk;
     const int64_t len = min<int64_t>(kChunk, d.numel - begin);
-    float* p = reinterpret_cast<float*>(d.p) + begin;
-    const float* g = reinterpret_cast<const float*>(d.g) + begin;
+    P* p = reinterpret_cast<P*>(d.p) + begin;
+    const P* g = reinterpret_cast<const P*>(d.g) + begin;
     float* m = reinterpret_cast<float*>(d.m) + begin;
     float* v = reinterpret_cast<float*>(d.v) + begin;
     const float coef = sd->coef;
     if (d.vec_ok && len == kChunk) {
-        f4* p4 = reinterpret_cast<f4*>(p);
-        const f4* g4 = reinterpret_cast<const f4*>(g);
+        typedef typename Quad<P>::raw PR;
+        PR* p4 = reinterpret_cast<PR*>(p);
+        const PR* g4 = reinterpret_cast<const PR*>(g);
         f4* m4 = reinterpret_cast<f4*>(m);
         f4* v4 = reinterpret_cast<f4*>(v);
-        // U 16-byte vectors of each of the four streams in flight per thread
-        // before any arithmetic (the chunk is 16 of them per thread)
+        // U vectors of each of the four streams in flight per thread before
+        // any arithmetic (the chunk is 16 of them per thread)
         static_assert(kChunk / 4 % (kThreads * U) == 0, "chunk split");
         for (int i0 = threadIdx.x; i0 < kChunk / 4; i0 += kThreads * U) {
-            f4 pp[U], gg[U], mm[U], vv[U];
+            PR pr[U], gr[U];
+            f4 mm[U], vv[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int i = i0 + u * kThreads;
-                pp[u] = __builtin_nontemporal_load(p4 + i);
-                gg[u] = __builtin_nontemporal_load(g4 + i);
+                pr[u] = __builtin_nontemporal_load(p4 + i);
+                gr[u] = __builtin_nontemporal_load(g4 + i);
                 mm[u] = __builtin_nontemporal_load(m4 + i);
                 vv[u] = __builtin_nontemporal_load(v4 + i);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
+                f4 pp = Quad<P>::get(pr[u]);
+                const f4 gg = Quad<P>::get(gr[u]);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    float pq = pp[u][q], mq = mm[u][q], vq = vv[u][q];
-                    adam_elem(pq, gg[u][q], mq, vq, coef, a);
-                    pp[u][q] = pq;
+                    float pq = pp[q], mq = mm[u][q], vq = vv[u][q];
+                    adam_elem(pq, gg[q], mq, vq, coef, a);
+                    pp[q] = pq;
                     mm[u][q] = mq;
                     vv[u][q] = vq;
                 }
+                pr[u] = Quad<P>::put(pp);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int i = i0 + u * kThreads;
-                __builtin_nontemporal_store(pp[u], p4 + i);
+                __builtin_nontemporal_store(pr[u], p4 + i);
                 __builtin_nontemporal_store(mm[u], m4 + i);
                 __builtin_nontemporal_store(vv[u], v4 + i);
             }
         }
     } else {
         for (int64_t i = threadIdx.x; i < len; i += kThreads) {
-            float pp = p[i], mm = m[i], vv = v[i];
-            adam_elem(pp, g[i], mm, vv, coef, a);
-            p[i] = pp;
+            float pp = ld1(p + i), mm = m[i], vv = v[i];
+            adam_elem(pp, ld1(g + i), mm, vv, coef, a);
+            st1(p + i, pp);
             m[i] = mm;
             v[i] = vv;
         }
@@ -252,8 +309,8 @@ __global__ __launch_bounds__(kThreads) void k_adamw(const AdamTensor* __restrict
 }
 
 // One 16 Ki-element chunk of AdamW done by a single wave (64 lanes), U
-// 16-byte vectors of each of the four streams in flight per lane.
-template <int U>
+// four-element vectors of each of the four streams in flight per lane.
+template <int U, typename P>
 __device__ __forceinline__ void adamw_chunk_wave(const AdamTensor* __restrict__ tab, int n_tab,
                                                  int64_t chunk, float coef, const AdamArgs& a,
                                                  int lane) {
@@ -261,50 +318,55 @@ __device__ __forceinline__ void adamw_chunk_wave(const AdamTensor* __restrict__ 
     const AdamTensor d = tab[t];
     const int64_t begin = (chunk - d.chunk_begin) * kChunk;
     const int64_t len = min<int64_t>(kChunk, d.numel - begin);
-    float* p = reinterpret_cast<float*>(d.p) + begin;
-    const float* g = reinterpret_cast<const float*>(d.g) + begin;
+    P* p = reinterpret_cast<P*>(d.p) + begin;
+    const P* g = reinterpret_cast<const P*>(d.g) + begin;
     float* m = reinterpret_cast<float*>(d.m) + begin;
     float* v = reinterpret_cast<float*>(d.v) + begin;
     if (d.vec_ok && len == kChunk) {
-        f4* p4 = reinterpret_cast<f4*>(p);
-        const f4* g4 = reinterpret_cast<const f4*>(g);
+        typedef typename Quad<P>::raw PR;
+        PR* p4 = reinterpret_cast<PR*>(p);
+        const PR* g4 = reinterpret_cast<const PR*>(g);
         f4* m4 = reinterpret_cast<f4*>(m);
         f4* v4 = reinterpret_cast<f4*>(v);
         static_assert(kChunk / 4 % (64 * U) == 0, "chunk split");
         for (int i0 = lane; i0 < kChunk / 4; i0 += 64 * U) {
-            f4 pp[U], gg[U], mm[U], vv[U];
+            PR pr[U], gr[U];
+            f4 mm[U], vv[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int i = i0 + u * 64;
-                pp[u] = __builtin_nontemporal_load(p4 + i);
-                gg[u] = __builtin_nontemporal_load(g4 + i);
+                pr[u] = __builtin_nontemporal_load(p4 + i);
+                gr[u] = __builtin_nontemporal_load(g4 + i);
                 mm[u] = __builtin_nontemporal_load(m4 + i);
                 vv[u] = __builtin_nontemporal_load(v4 + i);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
+                f4 pp = Quad<P>::get(pr[u]);
+                const f4 gg = Quad<P>::get(gr[u]);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    float pq = pp[u][q], mq = mm[u][q], vq = vv[u][q];
-                    adam_elem(pq, gg[u][q], mq, vq, coef, a);
-                    pp[u][q] = pq;
+                    float pq = pp[q], mq = mm[u][q], vq = vv[u][q];
+                    adam_elem(pq, gg[q], mq, vq, coef, a);
+                    pp[q] = pq;
                     mm[u][q] = mq;
                     vv[u][q] = vq;
                 }
+                pr[u] = Quad<P>::put(pp);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int i = i0 + u * 64;
-                __builtin_nontemporal_store(pp[u], p4 + i);
+                __builtin_nontemporal_store(pr[u], p4 + i);
                 __builtin_nontemporal_store(mm[u], m4 + i);
                 __builtin_nontemporal_store(vv[u], v4 + i);
             }
         }
     } else {
         for (int64_t i = lane; i < len; i += 64) {
-            float pp = p[i], mm = m[i], vv = v[i];
-            adam_elem(pp, g[i], mm, vv, coef, a);
-            p[i] = pp;
+            float pp = ld1(p + i), mm = m[i], vv = v[i];
+            adam_elem(pp, ld1(g + i), mm, vv, coef, a);
+            st1(p + i, pp);
             m[i] = mm;
             v[i] = vv;
         }
@@ -316,7 +378,7 @@ __device__ __forceinline__ void adamw_chunk_wave(const AdamTensor* __restrict__ 
 // At most 80 VGPRs (six waves per SIMD), so a wave fits on a SIMD beside a
 // Newton-Schulz GEMM wave (at most 432 registers once rounded to the
 // allocation granule).
-template <int U>
+template <int U, typename P>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) void k_adamw_claim(
     const AdamTensor* __restrict__ tab, int n_tab, int64_t n_chunks, StepDev* __restrict__ sd,
     AdamConst ac) {
@@ -329,7 +391,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
         if (lane == 0) c = atomicAdd(counter, 1);
         c = __builtin_amdgcn_readfirstlane(c);
         if ((int64_t)c >= n_chunks) break;
-        adamw_chunk_wave<U>(tab, n_tab, c, coef, a, lane);
+        adamw_chunk_wave<U, P>(tab, n_tab, c, coef, a, lane);
     }
 }
 
@@ -421,6 +483,7 @@ __global__ __launch_bounds__(kThreads) void k_muon_prep(const MuonMat* __restric
     const int i0 = (int)(local / tiles_c) * TS, j0 = (int)(local % tiles_c) * TS;
     const float coef = sd->coef;
     const float* g = reinterpret_cast<const float*>(d.g);
+    const __bf16* gh = reinterpret_cast<const __bf16*>(d.g);   // bf16 storage
     float* buf = reinterpret_cast<float*>(d.buf);
     // stored tile origin: rows sr0.., cols sc0..
     const int sr0 = d.transposed ? j0 : i0;
@@ -431,12 +494,13 @@ __global__ __launch_bounds__(kThreads) void k_muon_prep(const MuonMat* __restric
         for (int q = threadIdx.x; q < TS * TS / 4; q += kThreads) {
             const int lr = q / (TS / 4), lc = (q % (TS / 4)) * 4;
             const int64_t o = (int64_t)(sr0 + lr) * d.n + (sc0 + lc);
-            const float4 gg = *reinterpret_cast<const float4*>(g + o);
+            const f4 gg = d.p_bf16 ? Quad<__bf16>::get(*reinterpret_cast<const u32x2*>(gh + o))
+                                   : *reinterpret_cast<const f4*>(g + o);
             float4 bb = *reinterpret_cast<const float4*>(buf + o);
-            const float u0 = momentum_elem(gg.x, bb.x, coef, a);
-            const float u1 = momentum_elem(gg.y, bb.y, coef, a);
-            const float u2 = momentum_elem(gg.z, bb.z, coef, a);
-            const float u3 = momentum_elem(gg.w, bb.w, coef, a);
+            const float u0 = momentum_elem(gg[0], bb.x, coef, a);
+            const float u1 = momentum_elem(gg[1], bb.y, coef, a);
+            const float u2 = momentum_elem(gg[2], bb.z, coef, a);
+            const float u3 = momentum_elem(gg[3], bb.w, coef, a);
             *reinterpret_cast<float4*>(buf + o) = bb;
             tile[lr][lc] = u0;
             tile[lr][lc + 1] = u1;
@@ -455,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void k_muon_prep(const MuonMat* __restric
             if (sr < d.m && sc < d.n) {
                 const int64_t o = (int64_t)sr * d.n + sc;
                 float bb = buf[o];
-                u = momentum_elem(g[o], bb, coef, a);
+                u = momentum_elem(d.p_bf16 ? (float)gh[o] : g[o], bb, coef, a);
                 buf[o] = bb;
             }
             tile[lr][lc] = u;
@@ -536,10 +600,11 @@ __global__ __launch_bounds__(kThreads) void k_operand_rescale(const MuonMat* __r
 }  // namespace
 
 int launch_norm_partials(const NormTensor* tab, int32_t n_tab, int64_t n_chunks, float* partials,
-                         void* stream) {
+                         int32_t param_dtype, void* stream) {
     if (n_chunks == 0) return (int)hipSuccess;
-    hipLaunchKernelGGL(k_norm_partials, dim3((unsigned)n_chunks), dim3(kThreads), 0,
-                       (hipStream_t)stream, tab, n_tab, partials);
+    auto k = param_dtype == MA_PARAM_BF16 ? k_norm_partials<__bf16> : k_norm_partials<float>;
+    hipLaunchKernelGGL(k, dim3((unsigned)n_chunks), dim3(kThreads), 0, (hipStream_t)stream, tab,
+                       n_tab, partials);
     return (int)hipGetLastError();
 }
 
@@ -561,21 +626,23 @@ AdamConst adam_const(const StepScalars& s) {
 }
 
 int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, const StepDev* sd,
-                 const StepScalars& s, void* stream) {
+                 const StepScalars& s, int32_t param_dtype, void* stream) {
     if (n_chunks == 0) return (int)hipSuccess;
     // four vectors per stream in flight (108 VGPRs) for the full HBM rate
-    hipLaunchKernelGGL(k_adamw<4>, dim3((unsigned)n_chunks), dim3(kThreads), 0, (hipStream_t)stream,
-                       tab, n_tab, sd, adam_const(s));
+    auto k = param_dtype == MA_PARAM_BF16 ? k_adamw<4, __bf16> : k_adamw<4, float>;
+    hipLaunchKernelGGL(k, dim3((unsigned)n_chunks), dim3(kThreads), 0, (hipStream_t)stream, tab,
+                       n_tab, sd, adam_const(s));
     return (int)hipGetLastError();
 }
 
 int launch_adamw_claim(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, StepDev* sd,
-                       const StepScalars& s, int64_t grid, void* stream) {
+                       const StepScalars& s, int32_t param_dtype, int64_t grid, void* stream) {
     if (n_chunks == 0 || grid <= 0) return (int)hipSuccess;
     // four vectors per stream in flight in 80 VGPRs, which with a
     // Newton-Schulz GEMM wave's at most 432 registers fills a SIMD's 512
-    hipLaunchKernelGGL(k_adamw_claim<4>, dim3((unsigned)grid), dim3(kThreads), 0,
-                       (hipStream_t)stream, tab, n_tab, n_chunks, sd, adam_const(s));
+    auto k = param_dtype == MA_PARAM_BF16 ? k_adamw_claim<4, __bf16> : k_adamw_claim<4, float>;
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, tab, n_tab,
+                       n_chunks, sd, adam_const(s));
     return (int)hipGetLastError();
 }
 

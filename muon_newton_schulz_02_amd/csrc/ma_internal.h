@@ -74,9 +74,10 @@ struct MuonMat {
     int64_t  orient_begin;         // first 64 x 64 operand tile of the prep pass
     int32_t  m, n, r, c, R, C;
     int32_t  transposed;
-    int32_t  vec_ok;               // p, g, buf (and delta) 16-byte aligned and n % 4 == 0
+    int32_t  vec_ok;               // 16-byte row runs of p and buf (and delta), 4-element g loads
     float    shape_scale;          // lr_shape_scale: the update is muon_lr * this (StepDev)
     int32_t  op_bf16;              // NS operands are bf16 (else fp32)
+    int32_t  p_bf16;               // p and g stored as bf16 (else float)
 };
 
 // One GEMM tile of an NS phase: matrix index and tile coordinates.
@@ -135,6 +136,7 @@ struct ma_plan {
     std::string dump;
 
     int32_t overlap = 0;    // 1: AdamW on a second stream, concurrent with Muon
+    int32_t param_dtype = MA_PARAM_FP32;   // storage of parameters and gradients
 
     // step-time staging (pinned host ring) and the per-device side stream of
     // the overlapped AdamW group; guarded by mu
@@ -210,14 +212,15 @@ struct StepScalars {
 };
 
 // Each returns a hipError_t as int.
+// `param_dtype` (MA_PARAM_*) is the storage of parameters and gradients.
 int launch_norm_partials(const NormTensor* tab, int32_t n_tab, int64_t n_chunks,
-                         float* partials, void* stream);
+                         float* partials, int32_t param_dtype, void* stream);
 // The clip factor and norm, and every other step-dependent value, into
 // *sd; also zeroes sd->claim, so every step's AdamW chunk claims start at 0.
 int launch_clip_finalize(const float* partials, int64_t n, float max_grad_norm,
                          const StepIn& in, StepDev* sd, float* user_norm_out, void* stream);
 int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
-                 const StepDev* sd, const StepScalars& s, void* stream);
+                 const StepDev* sd, const StepScalars& s, int32_t param_dtype, void* stream);
 // AdamW whose 16 Ki-element chunks are claimed one at a time by single waves
 // from `counter` until all n_chunks are taken.  Several such launches, on
 // different streams, may share one counter: each chunk is processed exactly
@@ -225,7 +228,8 @@ int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
 // launch takes it.  Its waves are lean enough (80 VGPRs) to share a SIMD with
 // a Newton-Schulz GEMM wave.
 int launch_adamw_claim(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
-                       StepDev* sd, const StepScalars& s, int64_t grid, void* stream);
+                       StepDev* sd, const StepScalars& s, int32_t param_dtype, int64_t grid,
+                       void* stream);
 // Momentum/Nesterov and the unnormalised Newton-Schulz input operands, one
 // workgroup per 64 x 64 operand tile, with per-tile partials of ||u||_F^2.
 int launch_muon_prep(const MuonMat* tab, int32_t n_tab, int64_t n_tiles, const StepDev* sd,

@@ -146,6 +146,15 @@ __device__ __forceinline__ void load16(const float* src, float* v) {
     }
 }
 
+__device__ __forceinline__ void load16(const __bf16* src, float* v) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const bf16x8 t = __builtin_bit_cast(bf16x8, gld(src + 8 * h));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[8 * h + e] = (float)t[e];
+    }
+}
+
 // Split 16 fp32 values into bf16 hi = RNE(x) and lo = RNE(x - hi).
 __device__ __forceinline__ void store16_hilo(__bf16* dhi, __bf16* dlo, const float* v) {
     float lo[16];
@@ -180,14 +189,12 @@ __device__ __forceinline__ void lds_write16(float* dst, const float* v) {
     for (int q = 0; q < 4; ++q) d4[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
 }
 
-// Stored-orientation update of 16 consecutive elements of parameter row
-// `row`, starting at column `col`: p = p * decay - rate * x (and the
-// optional delta = rate * x).
-__device__ __forceinline__ void update_run(const MuonMat& d, const Upd& u, int row, int col,
-                                           const float* x) {
-    if (row >= d.m || col >= d.n) return;
-    float* p = reinterpret_cast<float*>(d.p) + (int64_t)row * d.n + col;
-    float* dl = d.delta ? reinterpret_cast<float*>(d.delta) + (int64_t)row * d.n + col : nullptr;
+template <typename P>
+__device__ __forceinline__ void update_run_as(const MuonMat& d, const Upd& u, int row, int col,
+                                              const float* x) {
+    const int64_t o = (int64_t)row * d.n + col;
+    P* p = reinterpret_cast<P*>(d.p) + o;
+    float* dl = d.delta ? reinterpret_cast<float*>(d.delta) + o : nullptr;
     if (d.vec_ok && col + 16 <= d.n) {
         float pv[16], dv[16];
         load16(p, pv);
@@ -200,17 +207,29 @@ __device__ __forceinline__ void update_run(const MuonMat& d, const Upd& u, int r
         if (dl) store16(dl, dv);
     } else {
         const int cnt = min(16, d.n - col);
-        g_float* gp = (g_float*)p;
+        typedef __attribute__((address_space(1))) P g_P;
+        g_P* gp = (g_P*)p;
         g_float* gd = (g_float*)dl;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             if (e < cnt) {
                 const float dv = u.rate * x[e];
-                gp[e] = fmaf(gp[e], u.decay, -dv);
+                gp[e] = (P)fmaf((float)gp[e], u.decay, -dv);
                 if (dl) gd[e] = dv;
             }
         }
     }
+}
+
+// Stored-orientation update of 16 consecutive elements of parameter row
+// `row`, starting at column `col`: p = p * decay - rate * x (and the
+// optional delta = rate * x), with p stored as float or bf16 (rounded to
+// nearest even once).
+__device__ __forceinline__ void update_run(const MuonMat& d, const Upd& u, int row, int col,
+                                           const float* x) {
+    if (row >= d.m || col >= d.n) return;
+    if (d.p_bf16) update_run_as<__bf16>(d, u, row, col, x);
+    else update_run_as<float>(d, u, row, col, x);
 }
 
 // Buffer resource of one operand (gfx9 layout): base address, stride 0,

@@ -344,6 +344,11 @@ int muon_adamw_plan(const ma_param_desc* table, int32_t n, const ma_plan_opts* o
     int32_t mode = opts ? opts->mode : MA_MODE_MUON_ADAMW;
     double moon = opts ? opts->moonlight_coefficient : 0.2;
     int32_t overlap = opts ? opts->overlap_groups : 0;
+    int32_t param_dtype = opts ? opts->param_dtype : MA_PARAM_FP32;
+    if (param_dtype != MA_PARAM_FP32 && param_dtype != MA_PARAM_BF16) {
+        set_error("muon_adamw_plan: unknown param_dtype %d", param_dtype);
+        return MA_ERR_INVALID_ARG;
+    }
     if (overlap != 0 && overlap != 1) {
         set_error("muon_adamw_plan: overlap_groups must be 0 or 1");
         return MA_ERR_INVALID_ARG;
@@ -408,6 +413,7 @@ int muon_adamw_plan(const ma_param_desc* table, int32_t n, const ma_plan_opts* o
     p->mode = mode;
     p->moonlight = moon;
     p->overlap = overlap;
+    p->param_dtype = param_dtype;
     p->entries.resize(n);
     std::map<std::pair<int64_t, int64_t>, int32_t> bucket_of;
     for (int32_t i = 0; i < n; ++i) {

@@ -63,11 +63,20 @@ int get_staging(const ma_plan* plan, size_t bytes, void** out, void** event) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7) == 0; }
 
 // Workgroups of the AdamW launch that runs beside the Muon group (one per CU
 // of the MI355X), and of the launch that finishes the remaining chunks.
 constexpr int64_t kSideAdamGroups = 256;
 constexpr int64_t kFinishAdamGroups = 2048;
+// Where the side AdamW launch forks off: right after the clip factor (false)
+// or after the Muon momentum pass, beside the Newton-Schulz GEMMs only
+// (true).  Forked early, its streaming waves starve the momentum pass -- the
+// pass's many short workgroups get a small share of HBM and it ends when
+// AdamW does -- and the GEMMs then run alone: with bf16 parameters the
+// overlapped step was slower than the serial one.  Forked late it costs the
+// momentum pass nothing and overlaps the whole GEMM phase.
+constexpr bool kForkAfterPrep = true;
 
 // The side stream and fork/join events of the current device (created on
 // first use; default priority, non-blocking with respect to the null stream).
@@ -243,6 +252,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     std::lock_guard<std::mutex> lock(plan->mu);
     // ------------------------------------------------- descriptor tables --
     char* base = reinterpret_cast<char*>(workspace);
+    const bool bf16 = plan->param_dtype == MA_PARAM_BF16;
     auto fill_tables = [&](char* hb) {
         std::memset(hb, 0, L.tables_bytes);
         auto* norm_tab = reinterpret_cast<NormTensor*>(hb + L.norm_tab_off);
@@ -252,7 +262,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
             d.g = reinterpret_cast<uint64_t>(grads[id]);
             d.numel = plan->entries[id].numel;
             d.chunk_begin = plan->norm_chunk_begin[k];
-            d.vec_ok = aligned16(grads[id]) ? 1 : 0;
+            d.vec_ok = aligned16(grads[id]) ? 1 : 0;   // 16-byte loads, either storage
         }
         auto* adam_tab = reinterpret_cast<AdamTensor*>(hb + L.adam_tab_off);
         for (size_t k = 0; k < plan->adam_ids.size(); ++k) {
@@ -264,10 +274,10 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
             d.v = reinterpret_cast<uint64_t>(state->adam_v[id]);
             d.numel = plan->entries[id].numel;
             d.chunk_begin = plan->adam_chunk_begin[k];
-            d.vec_ok = (aligned16(params[id]) && aligned16(grads[id]) && aligned16(state->adam_m[id]) &&
-                        aligned16(state->adam_v[id]))
-                           ? 1
-                           : 0;
+            // four-element accesses: 16 bytes of float, 8 of bf16
+            const bool pg = bf16 ? aligned8(params[id]) && aligned8(grads[id])
+                                 : aligned16(params[id]) && aligned16(grads[id]);
+            d.vec_ok = (pg && aligned16(state->adam_m[id]) && aligned16(state->adam_v[id])) ? 1 : 0;
         }
         auto* muon_tab = reinterpret_cast<MuonMat*>(hb + L.muon_tab_off);
         for (size_t k = 0; k < plan->muon_ids.size(); ++k) {
@@ -297,13 +307,16 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
             d.R = (int32_t)round_up(e.r, kNsPad);
             d.C = (int32_t)round_up(e.c, kNsPad);
             d.transposed = e.transposed;
-            d.vec_ok = (aligned16(params[id]) && aligned16(grads[id]) &&
+            // 16-byte row runs of p (16 elements), buf and delta; four-element
+            // loads of g
+            d.vec_ok = (aligned16(params[id]) && (bf16 ? aligned8(grads[id]) : aligned16(grads[id])) &&
                         aligned16(state->muon_momentum[id]) && (!delta || aligned16(delta)) &&
-                        (e.n % 4) == 0)
+                        (e.n % (bf16 ? 8 : 4)) == 0)
                            ? 1
                            : 0;
             d.shape_scale = e.lr_shape_scale;
             d.op_bf16 = L.op_group[k] == kGroupBf16 ? 1 : 0;
+            d.p_bf16 = bf16 ? 1 : 0;
         }
         for (int g = 0; g < 2; ++g) {
             std::memcpy(hb + L.g1_off[g], L.g1[g].data(), sizeof(GemmTile) * L.g1[g].size());
@@ -371,7 +384,8 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     const int32_t n_adam = (int32_t)plan->adam_ids.size();
     const int32_t n_muon = (int32_t)plan->muon_ids.size();
 
-    int err = launch_norm_partials(d_norm, n_train, plan->n_norm_chunks, norm_partials, stream);
+    int err = launch_norm_partials(d_norm, n_train, plan->n_norm_chunks, norm_partials,
+                                   plan->param_dtype, stream);
     if (err) return hip_fail("clip norm partials", err);
     err = launch_clip_finalize(norm_partials, plan->n_norm_chunks, sc.max_grad_norm, in, sd,
                                grad_norm_out, stream);
@@ -381,7 +395,9 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     // concurrently with the Muon group and joined back at the end
     ma_plan::Side* side = nullptr;
     // (the chunk counter is an int: beyond 2^30 chunks run serially)
-    if (plan->overlap && n_adam > 0 && n_muon > 0 && plan->n_adam_chunks < (int64_t(1) << 30)) {
+    const bool overlap =
+        plan->overlap && n_adam > 0 && n_muon > 0 && plan->n_adam_chunks < (int64_t(1) << 30);
+    auto fork_adamw = [&]() -> int {
         int rs = get_side(plan, &side);
         if (rs != MA_OK) return rs;
         hipStream_t ss = (hipStream_t)side->stream;
@@ -392,17 +408,22 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         // one workgroup per CU: each of its waves shares a SIMD with a
         // Newton-Schulz GEMM wave (whose LDS and registers leave room for
         // exactly that) and streams AdamW chunks while the GEMMs run
-        err = launch_adamw_claim(d_adam, n_adam, plan->n_adam_chunks, sd, sc, kSideAdamGroups, ss);
-        if (err) return hip_fail("adamw", err);
+        int er = launch_adamw_claim(d_adam, n_adam, plan->n_adam_chunks, sd, sc, plan->param_dtype,
+                                    kSideAdamGroups, ss);
+        if (er) return hip_fail("adamw", er);
         if (phase_events && phase_events[2] &&
             (e = hipEventRecord((hipEvent_t)phase_events[2], ss)) != hipSuccess)
             return hip_fail("phase event", e);
         if ((e = hipEventRecord((hipEvent_t)side->ev_join, ss)) != hipSuccess)
             return hip_fail("hipEventRecord (join)", e);
-    } else {
-        err = launch_adamw(d_adam, n_adam, plan->n_adam_chunks, sd, sc, stream);
+        return MA_OK;
+    };
+    if (!overlap) {
+        err = launch_adamw(d_adam, n_adam, plan->n_adam_chunks, sd, sc, plan->param_dtype, stream);
         if (err) return hip_fail("adamw", err);
         if ((err = mark(2))) return hip_fail("phase event", err);
+    } else if (!kForkAfterPrep) {
+        if ((err = fork_adamw()) != MA_OK) return err;
     }
     if (n_muon > 0) {
         err = launch_muon_prep(d_muon, n_muon, plan->n_orient_tiles, sd, sc, muon_partials,
@@ -411,6 +432,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         err = launch_muon_scale(d_muon, n_muon, muon_partials, sc.ns_eps, muon_scales,
                                 muon_prescales, stream);
         if (err) return hip_fail("muon scale", err);
+        if (overlap && kForkAfterPrep && (err = fork_adamw()) != MA_OK) return err;
         if ((err = mark(3))) return hip_fail("phase event", err);
         for (int it = 0; it < hp->muon_ns_steps; ++it) {
             const int last = it == hp->muon_ns_steps - 1;
@@ -430,8 +452,8 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     }
     if (side) {
         // the chunks the side kernel has not claimed yet, at full occupancy
-        err = launch_adamw_claim(d_adam, n_adam, plan->n_adam_chunks, sd, sc, kFinishAdamGroups,
-                                 stream);
+        err = launch_adamw_claim(d_adam, n_adam, plan->n_adam_chunks, sd, sc, plan->param_dtype,
+                                 kFinishAdamGroups, stream);
         if (err) return hip_fail("adamw", err);
     }
     if (side && (e = hipStreamWaitEvent(st, (hipEvent_t)side->ev_join, 0)) != hipSuccess)

@@ -34,6 +34,7 @@ def say(*a):
 
 def oracle_hparams(w: W.Workload, ns_steps: Optional[int] = None, **kw) -> O.HParams:
     hp = O.HParams()
+    hp.param_storage = w.param_storage
     for k, v in W.hparams_for(w).items():
         setattr(hp, k, v)
     for k, v in kw.items():
@@ -89,6 +90,27 @@ def check_adamw(p, m, v, rp, rm, rv, where: str, m_terms=None):
     assert rel.size == 0 or rel.max() <= 1e-5, "%s AdamW m relative %g" % (where, rel.max())
 
 
+def check_adamw_bf16(p, m, v, rp32, rm, rv, rp16, where: str, m_terms=None) -> float:
+    """bf16-stored parameters: m and v as check_adamw; p must be the bfloat16
+    rounding (ties to even) of some value within the stated gate of the
+    oracle's unrounded result -- rounding is monotone, so p lies between the
+    roundings of the gate's two ends (only near a rounding midpoint are both
+    neighbours allowed).  rp32: the oracle's result with float32 storage
+    (rounding error 6e-8, far inside the gate); rp16: the oracle's own bf16
+    result.  Returns the fraction of elements equal to rp16."""
+    check_adamw(rp32, m, v, rp32, rm, rv, where, m_terms)
+    p = np.asarray(p, np.float32)
+    r = np.asarray(rp32, np.float64)
+    d = 1e-5 * np.abs(r) + 1e-9
+    lo = O.bf16_round_f64(r - d)
+    hi = O.bf16_round_f64(r + d)
+    bad = (p < lo) | (p > hi)
+    assert not bad.any(), "%s AdamW bf16 p: %d elements outside the rounding window, e.g. %r " \
+        "not in [%r, %r]" % (where, int(bad.sum()), p[bad][:3], lo[bad][:3], hi[bad][:3])
+    assert np.all(O.bf16_round(p) == p), "%s: p holds values that are not bfloat16" % where
+    return float(np.mean(p == np.asarray(rp16, np.float32)))
+
+
 @dataclass
 class GpuRun:
     """Device tensors of one workload and the library objects around them."""
@@ -110,7 +132,8 @@ def setup_gpu(M, torch, w: W.Workload, hp: O.HParams, ns_precision: str, backend
     of entry indices that get a delta output buffer."""
     dev = torch.device("cuda", 0)
     table = list(zip(w.names, w.shapes, w.trainable))
-    plan = M.muon_adamw_plan(table, mode=W.mode_id(w))
+    plan = M.muon_adamw_plan(table, mode=W.mode_id(w), param_dtype=w.param_storage)
+    pdt = torch.bfloat16 if w.param_storage == "bf16" else torch.float32
     n = len(w.params)
     groups = [M.muon_adamw_plan_entry(plan, i)["group"] for i in range(n)]
     params, grads, dl = [None] * n, [None] * n, [None] * n
@@ -119,10 +142,10 @@ def setup_gpu(M, torch, w: W.Workload, hp: O.HParams, ns_precision: str, backend
         if groups[i] == M.MA_GROUP_NONE:
             continue
         if backend == "numpy":
-            params[i] = torch.from_numpy(W.np_param(w, i)).to(dev)
+            params[i] = torch.from_numpy(W.np_param(w, i)).to(dev).to(pdt)
         else:
-            params[i] = W.torch_param(w, i, dev)
-        grads[i] = torch.empty(spec.shape, dtype=torch.float32, device=dev)
+            params[i] = W.torch_param(w, i, dev).to(pdt)
+        grads[i] = torch.empty(spec.shape, dtype=pdt, device=dev)
         if groups[i] == M.MA_GROUP_MUON:
             if backend == "numpy":
                 state.muon_momentum[i] = torch.from_numpy(W.np_momentum(w, i)).to(dev)
@@ -157,7 +180,11 @@ def gpu_step(M, torch, run: GpuRun):
 
 
 def host(t) -> np.ndarray:
-    return t.detach().cpu().numpy()
+    """A device tensor's values on the host (bfloat16 widened to float32)."""
+    t = t.detach()
+    if str(t.dtype) == "torch.bfloat16":
+        t = t.float()
+    return t.cpu().numpy()
 
 
 def oracle_norm_of_device_grads(run: GpuRun) -> float:

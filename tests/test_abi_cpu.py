@@ -259,3 +259,12 @@ def test_binding_structs_match_header(tmp_path):
         for f in s._fields_:
             key = "%s.%s" % (s.__name__, f[0])
             assert int(out[key]) == getattr(s, f[0]).offset, key
+
+
+def test_plan_param_dtype(lib):
+    table = [("action_expert.layers.0.q.weight", (8, 8), True)]
+    for dt in ("fp32", "bf16", M.MA_PARAM_FP32, M.MA_PARAM_BF16):
+        M.muon_adamw_plan(table, param_dtype=dt)
+    with pytest.raises(M.MuonAdamWError) as e:
+        M.muon_adamw_plan(table, param_dtype=2)
+    assert e.value.code == M.MA_ERR_INVALID_ARG

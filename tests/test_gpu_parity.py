@@ -34,13 +34,28 @@ def _gpu():
 
 
 def _run_parity(w, ns_precision, steps, hp=None, sampled=None, backend="numpy",
-                check_params=True, say_every=1):
+                check_params=True, say_every=1, overlap=False, prepare=None):
     """Run `steps` steps on both sides; compare the whole table (or only the
-    entries in `sampled`)."""
+    entries in `sampled`).
+
+    With bf16 parameter storage a parameter rounds to one of two bfloat16
+    neighbours where the unrounded value lies near their midpoint, and a
+    one-spacing difference would then persist; so each step starts the
+    oracle from the GPU's parameters of the step before (states, which do
+    not depend on the parameters, keep their own trajectories), and the
+    parameters are checked against the rounding window of the gate."""
     hp = hp or H.oracle_hparams(w)
+    bf16 = w.param_storage == "bf16"
+    assert hp.param_storage == w.param_storage
     tol = H.BF16_TOL if ns_precision == "bf16" else H.FP32_TOL
     deltas = "all" if sampled is None else set(sampled)
     run = H.setup_gpu(M, torch, w, hp, ns_precision, backend, deltas=deltas)
+    if overlap:
+        run.plan = M.muon_adamw_plan(list(zip(w.names, w.shapes, w.trainable)),
+                                     mode=W.mode_id(w), overlap_groups=True,
+                                     param_dtype=w.param_storage)
+    if prepare is not None:
+        prepare(run)
     idx = range(len(w.params)) if sampled is None else sorted(sampled)
     # oracle-side state of the compared entries, from the same seeded inputs
     op, obuf, om, ov, omabs = {}, {}, {}, {}, {}
@@ -62,6 +77,9 @@ def _run_parity(w, ns_precision, steps, hp=None, sampled=None, backend="numpy",
         H.say("%s step %d: oracle norm" % (w.name, t))
         norm = H.oracle_norm_of_device_grads(run)
         coef = O.clip_coefficient(norm, hp.max_grad_norm)
+        if bf16:
+            for i in op:
+                op[i] = H.host(run.params[i]).copy()
         H.say("%s step %d: gpu step" % (w.name, t))
         H.gpu_step(M, torch, run)
         gnorm = float(H.host(run.norm_out)[0])
@@ -77,9 +95,17 @@ def _run_parity(w, ns_precision, steps, hp=None, sampled=None, backend="numpy",
             if g == O.ADAMW:
                 p, m, v = O.adamw_update(op[i], grad, om[i], ov[i], t, coef, hp_t)
                 omabs[i] = hp.beta1 * omabs[i] + (1 - hp.beta1) * np.abs(coef * grad.astype(np.float64))
-                H.check_adamw(H.host(run.params[i]), H.host(run.state.adam_m[i]),
-                              H.host(run.state.adam_v[i]), p, m, v, "%s[%d] step %d" % (w.name, i, t),
-                              m_terms=omabs[i])
+                where = "%s[%d] step %d" % (w.name, i, t)
+                if bf16:
+                    p32, _, _ = O.adamw_update(op[i], grad, om[i], ov[i], t, coef,
+                                               replace(hp_t, param_storage="fp32"))
+                    same = H.check_adamw_bf16(H.host(run.params[i]), H.host(run.state.adam_m[i]),
+                                              H.host(run.state.adam_v[i]), p32, m, v, p, where,
+                                              m_terms=omabs[i])
+                    assert same >= 0.98, "%s: only %.4f of p equal the oracle's" % (where, same)
+                else:
+                    H.check_adamw(H.host(run.params[i]), H.host(run.state.adam_m[i]),
+                                  H.host(run.state.adam_v[i]), p, m, v, where, m_terms=omabs[i])
                 op[i], om[i], ov[i] = p, m, v
             else:
                 m_, n_ = w.params[i].shape
@@ -93,7 +119,14 @@ def _run_parity(w, ns_precision, steps, hp=None, sampled=None, backend="numpy",
                 worst = max(worst, err)
                 assert err <= tol, "%s[%d] %s step %d: delta rel err %.3g > %.1g" % (
                     w.name, i, w.params[i].shape, t, err, tol)
-                if check_params:
+                if check_params and bf16:
+                    # p = RNE_bf16(p_before - delta) in float32, with the delta the
+                    # GPU reports (gated above); Muon decay 0 makes it exact
+                    assert hp.muon_weight_decay == 0.0
+                    gd = H.host(run.deltas[i])
+                    want = O.bf16_round((op[i] - gd).astype(np.float32))
+                    np.testing.assert_array_equal(H.host(run.params[i]), want)
+                elif check_params:
                     gp = H.host(run.params[i]).astype(np.float64)
                     # parameter error = update error + one fp32 rounding per step
                     slack = t * (tol * np.linalg.norm(delta) + 6e-8 * np.linalg.norm(p)) + 1e-30
@@ -278,6 +311,63 @@ def test_vla_hybrid_full_size_sampled():
             "action_expert.layers.9.mlp.down_proj.weight"]
     sampled = {names.index(n) for n in pick}
     _run_parity(w, "bf16", 2, sampled=sampled, backend="torch")
+
+
+def _bf16_ragged():
+    w = _ragged_workload()
+    w.name = "ragged_small_bf16store"
+    w.param_storage = "bf16"
+    w.params.append(W.ParamSpec("vlm.model.layers.0.mlp.up_proj.weight", (512, 300)))
+    return w
+
+
+@pytest.mark.parametrize("prec,overlap", [("bf16", False), ("bf16", True), ("fp32", False)])
+def test_bf16_storage_ragged(prec, overlap):
+    """bf16 parameter storage (the page's bf16_mixed policy): bf16
+    parameters and gradients, float32 states.  Ragged shapes take the vector
+    paths and the scalar tails of every kernel; AdamW in order or beside the
+    Muon group; three steps."""
+    _run_parity(_bf16_ragged(), prec, 3, overlap=overlap)
+
+
+def test_bf16_storage_misaligned_views():
+    """bf16 tensors that start 2 or 8 bytes into their storage: the norm,
+    AdamW, Muon momentum and update kernels fall back to their narrower
+    paths and give the same results."""
+    w = _bf16_ragged()
+    names = w.names
+    shift = {"vlm.big": 1, "vlm.w": 4, "vlm.model.layers.0.mlp.up_proj.weight": 4,
+             "action_expert.layers.6.r.weight": 4, "action_expert.layers.9.r.weight": 1}
+
+    def prepare(run):
+        for name, k in shift.items():
+            i = names.index(name)
+            for lst in (run.params, run.grads):
+                t = lst[i]
+                store = torch.zeros(t.numel() + k, dtype=t.dtype, device=t.device)
+                view = store[k:].view(t.shape)
+                view.copy_(t)
+                assert view.data_ptr() % 16 == 2 * k
+                lst[i] = view
+
+    _run_parity(w, "bf16", 2, prepare=prepare)
+
+
+def test_vla_bf16_mixed_full_size_sampled():
+    """The full hybrid step with bf16 parameters and gradients (bf16_mixed):
+    the global norm over all 2.15e9 bf16 gradients, six AdamW tensors and
+    four Muon matrices followed for two steps."""
+    w = W.vla_hybrid_bf16_mixed()
+    names = w.names
+    pick = ["vlm.model.layers.0.self_attn.q_proj.weight", "vlm.model.layers.3.mlp.gate_proj.weight",
+            "vlm.model.layers.27.mlp.down_proj.weight", "vlm.model.layers.13.input_layernorm.weight",
+            "vlm.model.norm.weight", "vlm.model.layers.27.post_attention_layernorm.weight",
+            "action_expert.layers.0.self_attn.q_proj.weight",
+            "action_expert.layers.5.self_attn.k_proj.weight",
+            "action_expert.layers.17.mlp.gate_proj.weight",
+            "action_expert.layers.9.mlp.down_proj.weight"]
+    sampled = {names.index(n) for n in pick}
+    _run_parity(w, "bf16", 2, sampled=sampled, backend="torch", overlap=True)
 
 
 def test_vla_adamw_full_size_sampled():

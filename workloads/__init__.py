@@ -60,6 +60,7 @@ class Workload:
     hparams: Dict[str, object] = field(default_factory=dict)
     description: str = ""
     mode: str = "muon_adamw"          # or "adamw": every trainable tensor to AdamW
+    param_storage: str = "fp32"       # or "bf16": parameters and gradients stored as bfloat16
 
     @property
     def names(self) -> List[str]:
@@ -204,12 +205,24 @@ def ragged_stress_bf16(clip: bool = True) -> Workload:
                                 "gradients, preloaded momentum")
 
 
+def vla_hybrid_bf16_mixed() -> Workload:
+    """vla_hybrid_bf16 under the page's default precision policy bf16_mixed:
+    parameters and gradients stored in bfloat16 (the seeded values rounded
+    to bfloat16), float32 optimizer states."""
+    w = vla_hybrid_bf16()
+    w.name = "vla_hybrid_bf16_mixed"
+    w.param_storage = "bf16"
+    w.description = "vla_hybrid parameter set, bf16 parameters and gradients, bf16 NS"
+    return w
+
+
 WORKLOADS = {
     "tiny_hybrid_fp32": tiny_hybrid_fp32,
     "ae18_muon_bf16": ae18_muon_bf16,
     "vla_hybrid_bf16": vla_hybrid_bf16,
     "vla_hybrid_fp32ns": vla_hybrid_fp32ns,
     "vla_hybrid_adamw": vla_hybrid_adamw,
+    "vla_hybrid_bf16_mixed": vla_hybrid_bf16_mixed,
     "ragged_stress_bf16": ragged_stress_bf16,
     "ragged_stress_bf16_noclip": lambda: ragged_stress_bf16(clip=False),
 }
