@@ -636,13 +636,15 @@ int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, const S
 }
 
 int launch_adamw_claim(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, StepDev* sd,
-                       const StepScalars& s, int32_t param_dtype, int64_t grid, void* stream) {
+                       const StepScalars& s, int32_t param_dtype, int64_t grid, int waves,
+                       void* stream) {
     if (n_chunks == 0 || grid <= 0) return (int)hipSuccess;
+    if (waves < 1 || waves > kThreads / 64) return (int)hipErrorInvalidValue;
     // four vectors per stream in flight in 80 VGPRs, which with a
     // Newton-Schulz GEMM wave's at most 432 registers fills a SIMD's 512
     auto k = param_dtype == MA_PARAM_BF16 ? k_adamw_claim<4, __bf16> : k_adamw_claim<4, float>;
-    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream, tab, n_tab,
-                       n_chunks, sd, adam_const(s));
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64 * waves), 0, (hipStream_t)stream, tab,
+                       n_tab, n_chunks, sd, adam_const(s));
     return (int)hipGetLastError();
 }
 

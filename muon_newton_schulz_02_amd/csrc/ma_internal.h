@@ -227,9 +227,10 @@ int launch_adamw(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
 // once, and since AdamW is elementwise the result does not depend on which
 // launch takes it.  Its waves are lean enough (80 VGPRs) to share a SIMD with
 // a Newton-Schulz GEMM wave.
+// `grid` workgroups of `waves` (1..4) waves each.
 int launch_adamw_claim(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
                        StepDev* sd, const StepScalars& s, int32_t param_dtype, int64_t grid,
-                       void* stream);
+                       int waves, void* stream);
 // Momentum/Nesterov and the unnormalised Newton-Schulz input operands, one
 // workgroup per 64 x 64 operand tile, with per-tile partials of ||u||_F^2.
 int launch_muon_prep(const MuonMat* tab, int32_t n_tab, int64_t n_tiles, const StepDev* sd,

@@ -69,6 +69,12 @@ bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7) == 0;
 // of the MI355X), and of the launch that finishes the remaining chunks.
 constexpr int64_t kSideAdamGroups = 256;
 constexpr int64_t kFinishAdamGroups = 2048;
+// Waves per side workgroup, by parameter storage.  Measured on the full
+// hybrid table: the side waves take HBM from the GEMMs, and the best share
+// depends on the bytes AdamW moves.  fp32 (28 B per element): 1..4 waves per
+// CU gave 18.7 / 17.6 / 16.9 / 16.5 ms per step; bf16 (22 B): 15.3 / 13.6 /
+// 14.1 / 15.0 ms -- with four, AdamW is done when the GEMMs are a third done.
+constexpr int kSideAdamWaves[2] = {4, 2};
 // Where the side AdamW launch forks off: right after the clip factor (false)
 // or after the Muon momentum pass, beside the Newton-Schulz GEMMs only
 // (true).  Forked early, its streaming waves starve the momentum pass -- the
@@ -409,7 +415,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         // Newton-Schulz GEMM wave (whose LDS and registers leave room for
         // exactly that) and streams AdamW chunks while the GEMMs run
         int er = launch_adamw_claim(d_adam, n_adam, plan->n_adam_chunks, sd, sc, plan->param_dtype,
-                                    kSideAdamGroups, ss);
+                                    kSideAdamGroups, kSideAdamWaves[bf16 ? 1 : 0], ss);
         if (er) return hip_fail("adamw", er);
         if (phase_events && phase_events[2] &&
             (e = hipEventRecord((hipEvent_t)phase_events[2], ss)) != hipSuccess)
@@ -453,7 +459,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     if (side) {
         // the chunks the side kernel has not claimed yet, at full occupancy
         err = launch_adamw_claim(d_adam, n_adam, plan->n_adam_chunks, sd, sc, plan->param_dtype,
-                                 kFinishAdamGroups, stream);
+                                 kFinishAdamGroups, 4, stream);
         if (err) return hip_fail("adamw", err);
     }
     if (side && (e = hipStreamWaitEvent(st, (hipEvent_t)side->ev_join, 0)) != hipSuccess)
