@@ -370,6 +370,19 @@ def test_vla_bf16_mixed_full_size_sampled():
     _run_parity(w, "bf16", 2, sampled=sampled, backend="torch", overlap=True)
 
 
+def test_rank_share_full_size_sampled():
+    """One GPU's share of the hybrid step sharded over 8 GPUs by
+    owner-compute (11 whole matrices by LPT, 1/8 of the AdamW elements as
+    1-D pieces cut at arbitrary offsets), in the configuration the benchmark
+    times; two steps."""
+    w = W.vla_hybrid_share(0, 8)
+    names = w.names
+    pieces = [i for i, n in enumerate(names) if "[" in n]
+    mats = [i for i, n in enumerate(names) if "[" not in n]
+    sampled = {pieces[0], pieces[len(pieces) // 2], pieces[-1], mats[0], mats[-1]}
+    _run_parity(w, "bf16", 2, sampled=sampled, backend="torch", overlap=True)
+
+
 def test_vla_adamw_full_size_sampled():
     """The page's default optimizer (optim = adamw) over the full hybrid
     table: all 2.15e9 trainable elements through the clip and AdamW (the

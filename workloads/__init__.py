@@ -216,6 +216,53 @@ def vla_hybrid_bf16_mixed() -> Workload:
     return w
 
 
+def ns_cost(shape: Tuple[int, ...]) -> float:
+    """Partitioning cost of one Muon matrix: the dense flop count of five
+    Newton-Schulz steps on its canonical r x c (20 r^2 c + 10 r^3)."""
+    r, c = min(shape), max(shape)
+    return 20.0 * r * r * c + 10.0 * float(r) ** 3
+
+
+def lpt_owners(shapes, world: int) -> List[int]:
+    """Owner GPU of each matrix, longest processing time first: by falling
+    cost (ties in table order), each to the least-loaded GPU (ties to the
+    lower index)."""
+    order = sorted(range(len(shapes)), key=lambda i: (-ns_cost(shapes[i]), i))
+    load = [0.0] * world
+    owner = [0] * len(shapes)
+    for i in order:
+        k = min(range(world), key=lambda j: (load[j], j))
+        owner[i] = k
+        load[k] += ns_cost(shapes[i])
+    return owner
+
+
+def vla_hybrid_share(rank: int = 0, world: int = 8) -> Workload:
+    """One GPU's share of vla_hybrid_bf16 when the step is sharded over
+    `world` GPUs by owner-compute: the action-expert matrices that LPT
+    assigns to `rank` (whole, as Newton-Schulz needs them), and the rank's
+    contiguous 1/world range of the concatenated AdamW elements, as 1-D
+    pieces.  Same seed and gradient scale; the clip norm is the share's own
+    (the all-reduce of the partial sums is not part of one GPU's work)."""
+    muon = _action_expert_18()
+    owner = lpt_owners([p.shape for p in muon], world)
+    mine = [p for p, o in zip(muon, owner) if o == rank]
+    adam = [p for p in _vlm_backbone() if p.trainable]
+    total = sum(p.numel for p in adam)
+    lo, hi = rank * total // world, (rank + 1) * total // world
+    pieces, off = [], 0
+    for p in adam:
+        a, b = max(lo, off), min(hi, off + p.numel)
+        if a < b:
+            pieces.append(ParamSpec("%s[%d:%d]" % (p.name, a - off, b - off), (b - a,)))
+        off += p.numel
+    name = "vla_hybrid_rank%d_of%d" % (rank, world)
+    return Workload(name, seed=2, steps=5, ns_precision="bf16", params=pieces + mine,
+                    grad_std=1e-2,
+                    description="GPU %d of %d: %d Muon matrices (LPT by NS flops) + AdamW "
+                                "elements [%d, %d) of %d" % (rank, world, len(mine), lo, hi, total))
+
+
 WORKLOADS = {
     "tiny_hybrid_fp32": tiny_hybrid_fp32,
     "ae18_muon_bf16": ae18_muon_bf16,
@@ -223,6 +270,7 @@ WORKLOADS = {
     "vla_hybrid_fp32ns": vla_hybrid_fp32ns,
     "vla_hybrid_adamw": vla_hybrid_adamw,
     "vla_hybrid_bf16_mixed": vla_hybrid_bf16_mixed,
+    "vla_hybrid_rank0_of8": lambda: vla_hybrid_share(0, 8),
     "ragged_stress_bf16": ragged_stress_bf16,
     "ragged_stress_bf16_noclip": lambda: ragged_stress_bf16(clip=False),
 }
