@@ -244,6 +244,79 @@ def test_adamw_mode_and_misaligned_views():
     assert float(store[0]) == 0.0
 
 
+@pytest.mark.parametrize("kind", ["nan_in_adamw", "inf_in_muon"])
+def test_non_finite_gradients_propagate(kind):
+    """Non-finite gradients are not skipped: a NaN makes the global norm and
+    the clip factor NaN, so every updated tensor turns NaN; an infinity makes
+    the norm infinite and the factor 0, so the infinite element turns NaN
+    (0 * inf), its matrix's whole update turns NaN through Newton-Schulz,
+    and the rest is updated with a zero gradient.  The NaN pattern of every
+    tensor equals the oracle's; finite values pass the usual gates."""
+    w = _ragged_workload()
+    hp = H.oracle_hparams(w)
+    run = H.setup_gpu(M, torch, w, hp, "bf16")
+    H.fill_grads(run, torch, 1)
+    names = w.names
+    if kind == "nan_in_adamw":
+        run.grads[names.index("vlm.big")][7] = float("nan")
+    else:
+        run.grads[names.index("action_expert.layers.4.r.weight")][3, 5] = float("inf")
+    torch.cuda.synchronize()
+    p0 = [None if p is None else H.host(p).copy() for p in run.params]
+    b0 = [None if b is None else H.host(b).copy() for b in run.state.muon_momentum]
+    g0 = [None if g is None else H.host(g).copy() for g in run.grads]
+    z = [None if p is None else np.zeros_like(p) for p in p0]
+    H.say("non-finite gradients: %s" % kind)
+    H.gpu_step(M, torch, run)
+    res = O.optimizer_step(names, p0, g0, w.trainable, b0, z, z, 1, hp, groups=run.groups)
+    gnorm = float(H.host(run.norm_out)[0])
+    if kind == "nan_in_adamw":
+        assert math.isnan(gnorm) and math.isnan(res.grad_norm)
+    else:
+        assert math.isinf(gnorm) and math.isinf(res.grad_norm) and res.clip_coef == 0.0
+    for i, g in enumerate(run.groups):
+        if g == O.NONE:
+            continue
+        pairs = [(H.host(run.params[i]), res.params[i])]
+        if g == O.ADAMW:
+            pairs += [(H.host(run.state.adam_m[i]), res.adam_m[i]),
+                      (H.host(run.state.adam_v[i]), res.adam_v[i])]
+        else:
+            pairs += [(H.host(run.state.muon_momentum[i]), res.muon_momentum[i]),
+                      (H.host(run.deltas[i]), res.deltas[i])]
+        for k, (a, b) in enumerate(pairs):
+            np.testing.assert_array_equal(np.isnan(a), np.isnan(b), "%s tensor %d" % (names[i], k))
+            fin = ~np.isnan(b)
+            if g == O.ADAMW or k < 2:
+                np.testing.assert_allclose(a[fin], b[fin], rtol=1e-5, atol=1e-9)
+            elif fin.all():
+                assert H.rel_fro(a, b) <= H.BF16_TOL
+
+
+def test_degenerate_tables():
+    """Edge cases of the table: only frozen entries (the step launches the
+    norm finaliser alone: norm 0, nothing else touched, the counter still
+    advances); a 1 x 1 Muon matrix next to a one-element AdamW tensor, both
+    against the oracle over two steps."""
+    dev = torch.device("cuda", 0)
+    plan = M.muon_adamw_plan([("vlm.model.embed_tokens.weight", (151, 20), False),
+                              ("lm_head.weight", (151, 20), False)])
+    st = M.State(2)
+    hp = M.muon_adamw_default_hparams()
+    ws = torch.empty(max(M.muon_adamw_workspace_size(plan, 0), 256), dtype=torch.uint8, device=dev)
+    norm = torch.full((1,), 7.0, device=dev)
+    H.say("all-frozen table")
+    M.muon_adamw_step(plan, None, None, st, hp, ws, grad_norm_out=norm)
+    torch.cuda.synchronize()
+    assert float(norm[0]) == 0.0 and st.step == 1
+
+    w = W.Workload("one_by_one", seed=5, steps=2, ns_precision="bf16", grad_std=1e-3,
+                   params=[W.ParamSpec("action_expert.layers.0.x.weight", (1, 1)),
+                           W.ParamSpec("vlm.scalar", (1,))])
+    _run_parity(w, "bf16", 2)
+    _run_parity(w, "fp32", 2)
+
+
 def test_bitwise_deterministic_reruns():
     """Two runs from identical inputs give bit-identical parameters, states,
     deltas and norms (fixed reduction trees, no float atomics)."""

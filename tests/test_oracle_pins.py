@@ -582,3 +582,27 @@ def test_bf16_storage_rounds_the_fp32_storage_step():
     np.testing.assert_array_equal(b16, b32)
     np.testing.assert_array_equal(d16, d32)
     np.testing.assert_array_equal(q16, O.bf16_round_f64(p.astype(np.float64) - d32))
+
+
+def test_rank_shares_partition_the_hybrid_table():
+    """The per-GPU shares of the owner-compute sharding cover the hybrid
+    table exactly once: every Muon matrix on one GPU (LPT loads within 1 %
+    of the mean), the AdamW elements cut into equal contiguous ranges."""
+    import workloads as W
+    world = 8
+    full = W.vla_hybrid_bf16()
+    muon = [p for p in full.params if p.name.startswith("action_expert.")]
+    adam = [p for p in full.params if p.trainable and not p.name.startswith("action_expert.")]
+    seen, loads, adam_total = [], [], 0
+    for r in range(world):
+        w = W.vla_hybrid_share(r, world)
+        mats = [p for p in w.params if "[" not in p.name]
+        seen += [p.name for p in mats]
+        loads.append(sum(W.ns_cost(p.shape) for p in mats))
+        n = sum(p.numel for p in w.params if "[" in p.name)
+        assert n == sum(p.numel for p in adam) // world
+        adam_total += n
+    assert sorted(seen) == sorted(p.name for p in muon)
+    mean = sum(loads) / world
+    assert max(loads) <= 1.01 * mean and min(loads) >= 0.99 * mean
+    assert adam_total == sum(p.numel for p in adam)
