@@ -201,6 +201,16 @@ def cpu_baseline(w, hp_overrides) -> dict:
     except AttributeError:
         cores = os.cpu_count() or 1
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    blas = "unknown BLAS"
+    try:
+        from threadpoolctl import threadpool_info
+        pools = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        if pools:
+            threads = int(pools[0].get("num_threads") or threads)
+            blas = "%s %s, %d threads" % (pools[0].get("internal_api"), pools[0].get("version"),
+                                          threads)
+    except ImportError:
+        pass
     sample_params = sum(w.params[i].numel for i in ae + vlm)
     return {
         "value": total_params / est,
@@ -214,6 +224,8 @@ def cpu_baseline(w, hp_overrides) -> dict:
                    % (k_ae - 1, len(ae), t_ae, k_vlm - 1, len(vlm), t_vlm, sample_params,
                       n_ae_layers, n_vlm_layers)),
         "sample_seconds": t_ae + t_vlm,
+        "numpy": np.__version__,
+        "blas": blas,
     }
 
 

@@ -157,13 +157,15 @@ typedef struct {
  * (3.2608, -3.6447, 1.3650), NS epsilon 1e-7, AdamW betas (0.9, 0.999), eps
  * 1e-8, decay 0.01, Muon decay 0, bf16 NS.  max_grad_norm <= 0 turns the
  * global clip off.  ns_coeffs (a, b, c) define X <- a X + (b A + c A^2) X.
- * Scalars are double on the host: derived constants (1 - beta, bias
- * corrections, lr * shape factor) are formed in double and rounded once to
- * the float32 the kernels compute in.
+ * Scalars are double: derived constants (1 - beta, bias corrections, the
+ * scheduled rate, lr * shape factor) are formed in double -- those that
+ * depend on the step number on the device, at the start of the step -- and
+ * rounded once to the float32 the kernels compute in.
  *
  * lr_schedule (the page's defaults table: cosine_with_min_lr, min_lr_rate
- * 0.1; default MA_LR_CONSTANT) sets the rate of optimizer step t = step + 1
- * for both groups to lr * f(t - 1): MA_LR_CONSTANT f = 1; MA_LR_COSINE_MIN
+ * 0.1; default MA_LR_CONSTANT) sets the rate of optimizer step t (step + 1,
+ * or the device counter + 1) for both groups to lr * f(t - 1):
+ * MA_LR_CONSTANT f = 1; MA_LR_COSINE_MIN
  * f(k) = k / warmup_steps for k < warmup_steps, else min_lr_rate +
  * (1 - min_lr_rate) (1 + cos(pi p)) / 2 with p = (k - warmup_steps) /
  * max(1, total_steps - warmup_steps) held at 1 past the end.  It needs

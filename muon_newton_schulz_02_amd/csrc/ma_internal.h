@@ -45,16 +45,16 @@ inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
 // ---------------------------------------------------------------- tables --
 // One trainable tensor in the global-norm pass.
 struct NormTensor {
-    uint64_t g;            // const float*
+    uint64_t g;            // const float* or bf16* (the plan's parameter storage)
     int64_t  numel;
     int64_t  chunk_begin;  // first chunk index of this tensor
-    int32_t  vec_ok;       // 16-byte aligned base: float4 path allowed
+    int32_t  vec_ok;       // 16-byte aligned base: 16-byte loads allowed
     int32_t  pad_;
 };
 
 // One AdamW tensor.
 struct AdamTensor {
-    uint64_t p, g, m, v;   // float*
+    uint64_t p, g, m, v;   // p, g: float* or bf16* (parameter storage); m, v: float*
     int64_t  numel;
     int64_t  chunk_begin;
     int32_t  vec_ok;
@@ -63,7 +63,7 @@ struct AdamTensor {
 
 // One Muon matrix: the elementwise view (momentum pass) and the NS view.
 struct MuonMat {
-    uint64_t p, g, buf, delta;     // float* (delta may be 0)
+    uint64_t p, g, buf, delta;     // p, g: float* or bf16*; buf, delta: float* (delta may be 0)
     // NS operands, zero-padded to R x C (X), C x R (X^T), R x R (A, B):
     //   bf16: x[k] = hi part of X (row-major; the MFMA operand) and xlo[k] =
     //         its lo part, ping-pong buffers k = step parity; xt unused
