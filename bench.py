@@ -239,6 +239,9 @@ def main():
     ap.add_argument("--serial", action="store_true",
                     help="time the groups one after the other on one stream (default: the AdamW "
                          "group runs beside the Muon group)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the extra pass that times replays of one step captured in a "
+                         "HIP graph (device step counter)")
     ap.add_argument("--roofline-steps", type=int, default=10,
                     help="serial steps timed after the headline ones, for per-kernel rooflines")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -312,6 +315,9 @@ def main():
     for _ in range(args.warmup):
         M.muon_adamw_step(plan, params, grads, state, hp, ws, stream=stream)
     torch.cuda.synchronize()
+
+    def one_step():
+        M.muon_adamw_step(plan, params, grads, state, hp, ws, stream=stream)
     print("[bench] timing %d steps" % args.steps, file=sys.stderr, flush=True)
     # an event between steps on the caller's stream (the side stream joins
     # it before a step's work ends) gives the per-step distribution
@@ -319,12 +325,41 @@ def main():
     t0 = time.perf_counter()
     marks[0].record(stream)
     for s in range(args.steps):
-        M.muon_adamw_step(plan, params, grads, state, hp, ws, stream=stream)
+        one_step()
         marks[s + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     step_ms = [marks[s].elapsed_time(marks[s + 1]) for s in range(args.steps)]
+
+    # The same step captured once in a HIP graph and replayed: every launch
+    # of a step takes the same arguments with the step number on the device,
+    # and an eager step has just uploaded the descriptor tables it reuses.
+    graph_out = None
+    if not args.no_graph:
+        print("[bench] graph replay: %d steps" % args.steps, file=sys.stderr, flush=True)
+        state.device_step = torch.full((1,), state.step, dtype=torch.int64, device=dev)
+        M.muon_adamw_step(plan, params, grads, state, hp, ws, stream=stream)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            M.muon_adamw_step(plan, params, grads, state, hp, ws)
+        graph.replay()
+        torch.cuda.synchronize()
+        gm = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        tg = time.perf_counter()
+        gm[0].record(stream)
+        for s in range(args.steps):
+            graph.replay()
+            gm[s + 1].record(stream)
+        torch.cuda.synchronize()
+        g_wall = (time.perf_counter() - tg) * 1e3 / args.steps
+        g_ms = [gm[s].elapsed_time(gm[s + 1]) for s in range(args.steps)]
+        graph_out = {"ms_per_step": g_wall, "value": n_train / (g_wall * 1e-3),
+                     "step_ms_p10_p50_p90": [percentile(g_ms, q) for q in (0.1, 0.5, 0.9)]}
+        del graph
+        state.step = int(state.device_step.item())
+        state.device_step = None
 
     # Per-kernel rooflines come from serial steps, where the library's phase
     # events bracket single kernels: [1] -> [2] is the one AdamW launch.
@@ -388,10 +423,12 @@ def main():
                    "muon_matrices": len(muon_shapes), "ns_precision": w.ns_precision,
                    "ns_steps": hp.muon_ns_steps, "parallelism": "single GPU",
                    "param_storage": w.param_storage,
+                   "launch": "eager (graph_replay: the same step replayed from a HIP graph)",
                    "optimizer": w.mode, "lr_schedule": hp_over.get("lr_schedule", "constant"),
                    "streams": "one stream" if (args.serial or n_muon == 0 or n_adam == 0) else
                    "adamw beside the muon group (second stream)"},
         "step_ms_p10_p50_p90": [percentile(step_ms, q) for q in (0.1, 0.5, 0.9)],
+        "graph_replay": graph_out,
         "serial_ms_per_step": serial_ms,
         "phase_ms": mean,
         "ns_tflops": ns_tflops,
