@@ -428,6 +428,7 @@ def main():
                    "streams": "one stream" if (args.serial or n_muon == 0 or n_adam == 0) else
                    "adamw beside the muon group (second stream)"},
         "step_ms_p10_p50_p90": [percentile(step_ms, q) for q in (0.1, 0.5, 0.9)],
+        "step_ms_events": [round(x, 3) for x in step_ms],
         "graph_replay": graph_out,
         "serial_ms_per_step": serial_ms,
         "phase_ms": mean,

@@ -106,6 +106,15 @@ __device__ __forceinline__ int find_tensor(const Tab* tab, int n, int64_t chunk)
     return lo;
 }
 
+// ------------------------------------------------------- table upload --
+// The step's descriptor tables, from mapped host memory into the workspace.
+__global__ __launch_bounds__(kThreads) void k_copy_tables(const uint4* __restrict__ src,
+                                                          uint4* __restrict__ dst, int64_t n16) {
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16;
+         i += (int64_t)gridDim.x * kThreads)
+        dst[i] = src[i];
+}
+
 // ------------------------------------------------------------ clip norm --
 template <typename G>
 __global__ __launch_bounds__(kThreads) void k_norm_partials(const NormTensor* __restrict__ tab,
@@ -598,6 +607,16 @@ __global__ __launch_bounds__(kThreads) void k_operand_rescale(const MuonMat* __r
     }
 }
 }  // namespace
+
+int launch_copy_tables(void* dst, const void* src, size_t bytes, void* stream) {
+    if (bytes == 0) return (int)hipSuccess;
+    if (bytes % 16 != 0) return (int)hipErrorInvalidValue;
+    const int64_t n16 = (int64_t)(bytes / 16);
+    const int64_t grid = std::min<int64_t>(64, (n16 + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(k_copy_tables, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream,
+                       reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst), n16);
+    return (int)hipGetLastError();
+}
 
 int launch_norm_partials(const NormTensor* tab, int32_t n_tab, int64_t n_chunks, float* partials,
                          int32_t param_dtype, void* stream) {

@@ -149,6 +149,7 @@ struct ma_plan {
     mutable std::vector<Side> side;
     mutable std::mutex mu;
     mutable void* staging[2] = {nullptr, nullptr};
+    mutable void* staging_dev[2] = {nullptr, nullptr};   // device address of staging[k]
     mutable size_t staging_bytes[2] = {0, 0};
     mutable void* staging_event[2] = {nullptr, nullptr};
     mutable int staging_next = 0;
@@ -212,6 +213,9 @@ struct StepScalars {
 };
 
 // Each returns a hipError_t as int.
+// Copies `bytes` (a multiple of 16) from host memory mapped into the device
+// address space (`src`) to device memory.
+int launch_copy_tables(void* dst, const void* src, size_t bytes, void* stream);
 // `param_dtype` (MA_PARAM_*) is the storage of parameters and gradients.
 int launch_norm_partials(const NormTensor* tab, int32_t n_tab, int64_t n_chunks,
                          float* partials, int32_t param_dtype, void* stream);

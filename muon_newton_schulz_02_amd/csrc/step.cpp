@@ -35,7 +35,8 @@ int hip_fail(const char* what, int err) {
 // A pinned host staging buffer of at least `bytes`, whose previous copy (if
 // any) has completed.  Two buffers alternate so consecutive steps do not
 // wait on each other's copies.
-int get_staging(const ma_plan* plan, size_t bytes, void** out, void** event) {
+int get_staging(const ma_plan* plan, size_t bytes, void** out, const void** out_dev,
+                void** event) {
     const int k = plan->staging_next;
     plan->staging_next ^= 1;
     if (plan->staging_event[k]) {
@@ -50,14 +51,26 @@ int get_staging(const ma_plan* plan, size_t bytes, void** out, void** event) {
     if (plan->staging_bytes[k] < bytes) {
         if (plan->staging[k]) (void)hipHostFree(plan->staging[k]);
         plan->staging[k] = nullptr;
+        plan->staging_dev[k] = nullptr;
         plan->staging_bytes[k] = 0;
+        // mapped and coherent: the copy kernel reads it straight over the bus
         void* p = nullptr;
-        hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocPortable);
+        hipError_t e = hipHostMalloc(&p, bytes,
+                                     hipHostMallocPortable | hipHostMallocMapped |
+                                         hipHostMallocCoherent);
         if (e != hipSuccess) return hip_fail("hipHostMalloc (staging)", e);
+        void* dp = nullptr;
+        e = hipHostGetDevicePointer(&dp, p, 0);
+        if (e != hipSuccess) {
+            (void)hipHostFree(p);
+            return hip_fail("hipHostGetDevicePointer (staging)", e);
+        }
         plan->staging[k] = p;
+        plan->staging_dev[k] = dp;
         plan->staging_bytes[k] = bytes;
     }
     *out = plan->staging[k];
+    *out_dev = plan->staging_dev[k];
     *event = plan->staging_event[k];
     return MA_OK;
 }
@@ -357,8 +370,9 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     }
     if (!state->device_step || upload) {
         void* host = nullptr;
+        const void* host_dev = nullptr;
         void* event = nullptr;
-        int rc = get_staging(plan, L.tables_bytes, &host, &event);
+        int rc = get_staging(plan, L.tables_bytes, &host, &host_dev, &event);
         if (rc != MA_OK) return rc;
         if (upload)
             std::memcpy(host, upload, L.tables_bytes);
@@ -366,8 +380,12 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
             fill_tables(reinterpret_cast<char*>(host));
         // a failure past this point may leave the workspace's tables stale
         plan->table_cache_ws = nullptr;
-        e = hipMemcpyAsync(base + L.tables_off, host, L.tables_bytes, hipMemcpyHostToDevice, st);
-        if (e != hipSuccess) return hip_fail("hipMemcpyAsync (tables)", e);
+        // a kernel on the step's stream reads the staging buffer over the bus:
+        // no copy engine, so no cross-engine waits between consecutive steps
+        // (a copy-engine upload stalled the second of back-to-back steps by
+        // about 5 ms)
+        int er = launch_copy_tables(base + L.tables_off, host_dev, L.tables_bytes, stream);
+        if (er) return hip_fail("table upload", er);
         e = hipEventRecord((hipEvent_t)event, st);
         if (e != hipSuccess) return hip_fail("hipEventRecord", e);
         if (upload) {

@@ -244,6 +244,7 @@ def test_adamw_mode_and_misaligned_views():
     assert float(store[0]) == 0.0
 
 
+@pytest.mark.filterwarnings("ignore:invalid value encountered")
 @pytest.mark.parametrize("kind", ["nan_in_adamw", "inf_in_muon"])
 def test_non_finite_gradients_propagate(kind):
     """Non-finite gradients are not skipped: a NaN makes the global norm and
