@@ -70,6 +70,7 @@ def _run_parity(w, ns_precision, steps, hp=None, sampled=None, backend="numpy",
             ov[i] = np.zeros(w.params[i].shape, np.float32)
             omabs[i] = np.zeros(w.params[i].shape, np.float64)
     worst = 0.0
+    errs = []
     for t in range(1, steps + 1):
         H.say("%s ns=%s step %d: inputs" % (w.name, ns_precision, t))
         H.fill_grads(run, torch, t, backend)
@@ -117,6 +118,7 @@ def _run_parity(w, ns_precision, steps, hp=None, sampled=None, backend="numpy",
                 np.testing.assert_allclose(gbuf, buf, rtol=1e-5, atol=1e-7 * (np.abs(buf).max() + 1e-30))
                 err = H.rel_fro(H.host(run.deltas[i]), delta)
                 worst = max(worst, err)
+                errs.append(err)
                 assert err <= tol, "%s[%d] %s step %d: delta rel err %.3g > %.1g" % (
                     w.name, i, w.params[i].shape, t, err, tol)
                 if check_params and bf16:
@@ -133,6 +135,9 @@ def _run_parity(w, ns_precision, steps, hp=None, sampled=None, backend="numpy",
                     assert np.linalg.norm(gp - p.astype(np.float64)) <= 2 * slack
                 op[i], obuf[i] = p, buf
         H.say("%s step %d ok (worst muon rel err %.3g)" % (w.name, t, worst))
+    if errs:
+        H.say("%s ns=%s: Muon update rel err over %d matrix-steps: max %.3g, median %.3g"
+              % (w.name, ns_precision, len(errs), max(errs), float(np.median(errs))))
     return worst
 
 
