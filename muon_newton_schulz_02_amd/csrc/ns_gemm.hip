@@ -189,48 +189,6 @@ __device__ __forceinline__ void lds_write16(float* dst, const float* v) {
     for (int q = 0; q < 4; ++q) d4[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
 }
 
-template <typename P>
-__device__ __forceinline__ void update_run_as(const MuonMat& d, const Upd& u, int row, int col,
-                                              const float* x) {
-    const int64_t o = (int64_t)row * d.n + col;
-    P* p = reinterpret_cast<P*>(d.p) + o;
-    float* dl = d.delta ? reinterpret_cast<float*>(d.delta) + o : nullptr;
-    if (d.vec_ok && col + 16 <= d.n) {
-        float pv[16], dv[16];
-        load16(p, pv);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            dv[e] = u.rate * x[e];
-            pv[e] = fmaf(pv[e], u.decay, -dv[e]);
-        }
-        store16(p, pv);
-        if (dl) store16(dl, dv);
-    } else {
-        const int cnt = min(16, d.n - col);
-        typedef __attribute__((address_space(1))) P g_P;
-        g_P* gp = (g_P*)p;
-        g_float* gd = (g_float*)dl;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            if (e < cnt) {
-                const float dv = u.rate * x[e];
-                gp[e] = (P)fmaf((float)gp[e], u.decay, -dv);
-                if (dl) gd[e] = dv;
-            }
-        }
-    }
-}
-
-// Stored-orientation update of 16 consecutive elements of parameter row
-// `row`, starting at column `col`: p = p * decay - rate * x (and the
-// optional delta = rate * x), with p stored as float or bf16 (rounded to
-// nearest even once).
-__device__ __forceinline__ void update_run(const MuonMat& d, const Upd& u, int row, int col,
-                                           const float* x) {
-    if (row >= d.m || col >= d.n) return;
-    if (d.p_bf16) update_run_as<__bf16>(d, u, row, col, x);
-    else update_run_as<float>(d, u, row, col, x);
-}
 
 // Buffer resource of one operand (gfx9 layout): base address, stride 0,
 // extent in bytes (reads past it return zero) and the raw 32-bit-element
@@ -326,6 +284,56 @@ struct EpiIn {
     uint4 q[4];
 };
 
+// The parameter run a lane of the final update rewrites for one block,
+// loaded two blocks ahead: 16 values (fp32 or bf16) of stored row `row` from
+// column `col`, where the update takes its 16-byte path.
+struct PIn {
+    uint4 v[4];
+};
+
+__device__ __forceinline__ bool p_run_vec(const MuonMat& d, int row, int col) {
+    return row < d.m && d.vec_ok && col + 16 <= d.n;
+}
+
+// Stored coordinates of a lane's run: a row run of the block (lanes 2r and
+// 2r + 1 share row r) or, for a transposed matrix, a column run of it.
+__device__ __forceinline__ void p_run_at(const MuonMat& d, int lane, int bi, int bj, int& row,
+                                         int& col) {
+    if (d.transposed) {
+        row = bj + (lane & 31);
+        col = bi + (lane >> 5) * 16;
+    } else {
+        row = bi + (lane >> 1);
+        col = bj + (lane & 1) * 16;
+    }
+}
+
+template <int EPI>
+__device__ __forceinline__ void p_load(PIn& pin, const MuonMat& d, int lane, int bi, int bj) {
+    if (EPI != EPI_FINAL) return;
+    int row, col;
+    p_run_at(d, lane, bi, bj, row, col);
+    if (!p_run_vec(d, row, col)) return;
+    const int64_t o = (int64_t)row * d.n + col;
+    // both storages write every slot, so no slot index depends on the storage
+    // (a merged tail would index the slots at run time, through scratch)
+    if (d.p_bf16) {
+        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const __bf16*>(d.p) + o);
+        const uint4 a = gld(p), b = gld(p + 1);
+        pin.v[0] = a;
+        pin.v[1] = b;
+        pin.v[2] = make_uint4(0u, 0u, 0u, 0u);
+        pin.v[3] = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(d.p) + o);
+        const uint4 a = gld(p), b = gld(p + 1), c = gld(p + 2), e = gld(p + 3);
+        pin.v[0] = a;
+        pin.v[1] = b;
+        pin.v[2] = c;
+        pin.v[3] = e;
+    }
+}
+
 template <typename T, int EPI>
 __device__ __forceinline__ void epi_load(EpiIn& in, const MuonMat& d, int lane, int bi, int bj,
                                          int cur, bool poly_direct) {
@@ -374,6 +382,51 @@ __device__ __forceinline__ void unpack16(const uint4* q, float* v, bool bf) {
     }
 }
 
+template <typename P>
+__device__ __forceinline__ void update_run_as(const MuonMat& d, const Upd& u, int row, int col,
+                                              const float* x, const uint4* pre) {
+    const int64_t o = (int64_t)row * d.n + col;
+    P* p = reinterpret_cast<P*>(d.p) + o;
+    float* dl = d.delta ? reinterpret_cast<float*>(d.delta) + o : nullptr;
+    if (d.vec_ok && col + 16 <= d.n) {
+        // the run was prefetched (p_load takes the same path)
+        float pv[16], dv[16];
+        unpack16(pre, pv, sizeof(P) == 2);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            dv[e] = u.rate * x[e];
+            pv[e] = fmaf(pv[e], u.decay, -dv[e]);
+        }
+        store16(p, pv);
+        if (dl) store16(dl, dv);
+    } else {
+        const int cnt = min(16, d.n - col);
+        typedef __attribute__((address_space(1))) P g_P;
+        g_P* gp = (g_P*)p;
+        g_float* gd = (g_float*)dl;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            if (e < cnt) {
+                const float dv = u.rate * x[e];
+                gp[e] = (P)fmaf((float)gp[e], u.decay, -dv);
+                if (dl) gd[e] = dv;
+            }
+        }
+    }
+}
+
+// Stored-orientation update of 16 consecutive elements of parameter row
+// `row`, starting at column `col`: p = p * decay - rate * x (and the
+// optional delta = rate * x), with p stored as float or bf16 (rounded to
+// nearest even once).  `pre` holds the run's old values where p_load
+// prefetched them.
+__device__ __forceinline__ void update_run(const MuonMat& d, const Upd& u, int row, int col,
+                                           const float* x, const PIn& pre) {
+    if (row >= d.m || col >= d.n) return;
+    if (d.p_bf16) update_run_as<__bf16>(d, u, row, col, x, pre.v);
+    else update_run_as<float>(d, u, row, col, x, pre.v);
+}
+
 // Epilogue of one 32x32 accumulator block at output rows bi.., columns
 // bj..: stage it in the wave's LDS region, then move 16-element row runs
 // (row-major outputs) and, where needed, column runs (transposed outputs).
@@ -382,7 +435,8 @@ __device__ __forceinline__ void unpack16(const uint4* q, float* v, bool bf) {
 // X, which arrives in `in`; in fp32 they are added here from `in`.  Called with literal block indices so the accumulators
 // stay in registers.
 template <typename T, int EPI, int SLD>
-__device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, const MuonMat& d,
+__device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, const PIn& pin,
+                                          const MuonMat& d,
                                           float* S, const NsArgs& args, float escale,
                                           const Upd& up, int lane,
                                           int bi, int bj, int cur, bool need_cols,
@@ -429,7 +483,7 @@ __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, co
                 store16_hilo(reinterpret_cast<__bf16*>(d.x[cur ^ 1]) + ob,
                              reinterpret_cast<__bf16*>(d.xlo[cur ^ 1]) + ob, v);
             } else if (!d.transposed) {
-                update_run(d, up, gi, gj, v);
+                update_run(d, up, gi, gj, v, pin);
             }
         } else {
             float xv[16];
@@ -439,7 +493,7 @@ __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, co
             if (EPI == EPI_XUPD) {
                 store16(reinterpret_cast<float*>(d.x[0]) + o, v);
             } else if (!d.transposed) {
-                update_run(d, up, gi, gj, v);
+                update_run(d, up, gi, gj, v, pin);
             }
         }
         if (need_cols) lds_write16(S + rrow * SLD + rc0, v);
@@ -456,7 +510,7 @@ __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, co
             T* xt = reinterpret_cast<T*>(d.xt[cur ^ 1]);
             store16(xt + (int64_t)tr * d.R + tc, v);
         } else {
-            update_run(d, up, tr, tc, v);
+            update_run(d, up, tr, tc, v, pin);
         }
         wave_lds_sync();
     }
@@ -849,32 +903,38 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
         up.decay = args.sd->muon_decay;
     }
     // The 16 blocks go in row order; each block's global inputs are loaded
-    // four blocks ahead (slots in0..in3), so their latency overlaps the
-    // work on the blocks in between instead of stalling every block.
+    // four blocks ahead (slots in0..in3), and the final update's old
+    // parameter values two blocks ahead (p0, p1), so their latency overlaps
+    // the work on the blocks in between instead of stalling every block.
     EpiIn in0, in1, in2, in3;
+    PIn p0, p1;
 #define NS_LOAD(SLOT, I, J) \
     epi_load<T, EPI>(SLOT, d, lane, bi0 + (I) * 32, bj0 + (J) * 32, cur, poly_direct)
-#define NS_EPI(I, J, SLOT)                                                                   \
-    epi_block<T, EPI, SLD>(acc[I][J], SLOT, d, S, args, escale, up, lane, bi0 + (I) * 32,     \
-                           bj0 + (J) * 32, cur, need_cols, poly_direct, out_direct, ld_direct)
+#define NS_PLOAD(SLOT, I, J) p_load<EPI>(SLOT, d, lane, bi0 + (I) * 32, bj0 + (J) * 32)
+#define NS_EPI(I, J, SLOT, PSLOT)                                                            \
+    epi_block<T, EPI, SLD>(acc[I][J], SLOT, PSLOT, d, S, args, escale, up, lane,              \
+                           bi0 + (I) * 32, bj0 + (J) * 32, cur, need_cols, poly_direct,       \
+                           out_direct, ld_direct)
     NS_LOAD(in0, 0, 0); NS_LOAD(in1, 0, 1); NS_LOAD(in2, 0, 2); NS_LOAD(in3, 0, 3);
-    NS_EPI(0, 0, in0); NS_LOAD(in0, 1, 0);
-    NS_EPI(0, 1, in1); NS_LOAD(in1, 1, 1);
-    NS_EPI(0, 2, in2); NS_LOAD(in2, 1, 2);
-    NS_EPI(0, 3, in3); NS_LOAD(in3, 1, 3);
-    NS_EPI(1, 0, in0); NS_LOAD(in0, 2, 0);
-    NS_EPI(1, 1, in1); NS_LOAD(in1, 2, 1);
-    NS_EPI(1, 2, in2); NS_LOAD(in2, 2, 2);
-    NS_EPI(1, 3, in3); NS_LOAD(in3, 2, 3);
-    NS_EPI(2, 0, in0); NS_LOAD(in0, 3, 0);
-    NS_EPI(2, 1, in1); NS_LOAD(in1, 3, 1);
-    NS_EPI(2, 2, in2); NS_LOAD(in2, 3, 2);
-    NS_EPI(2, 3, in3); NS_LOAD(in3, 3, 3);
-    NS_EPI(3, 0, in0);
-    NS_EPI(3, 1, in1);
-    NS_EPI(3, 2, in2);
-    NS_EPI(3, 3, in3);
+    NS_PLOAD(p0, 0, 0); NS_PLOAD(p1, 0, 1);
+    NS_EPI(0, 0, in0, p0); NS_LOAD(in0, 1, 0); NS_PLOAD(p0, 0, 2);
+    NS_EPI(0, 1, in1, p1); NS_LOAD(in1, 1, 1); NS_PLOAD(p1, 0, 3);
+    NS_EPI(0, 2, in2, p0); NS_LOAD(in2, 1, 2); NS_PLOAD(p0, 1, 0);
+    NS_EPI(0, 3, in3, p1); NS_LOAD(in3, 1, 3); NS_PLOAD(p1, 1, 1);
+    NS_EPI(1, 0, in0, p0); NS_LOAD(in0, 2, 0); NS_PLOAD(p0, 1, 2);
+    NS_EPI(1, 1, in1, p1); NS_LOAD(in1, 2, 1); NS_PLOAD(p1, 1, 3);
+    NS_EPI(1, 2, in2, p0); NS_LOAD(in2, 2, 2); NS_PLOAD(p0, 2, 0);
+    NS_EPI(1, 3, in3, p1); NS_LOAD(in3, 2, 3); NS_PLOAD(p1, 2, 1);
+    NS_EPI(2, 0, in0, p0); NS_LOAD(in0, 3, 0); NS_PLOAD(p0, 2, 2);
+    NS_EPI(2, 1, in1, p1); NS_LOAD(in1, 3, 1); NS_PLOAD(p1, 2, 3);
+    NS_EPI(2, 2, in2, p0); NS_LOAD(in2, 3, 2); NS_PLOAD(p0, 3, 0);
+    NS_EPI(2, 3, in3, p1); NS_LOAD(in3, 3, 3); NS_PLOAD(p1, 3, 1);
+    NS_EPI(3, 0, in0, p0); NS_PLOAD(p0, 3, 2);
+    NS_EPI(3, 1, in1, p1); NS_PLOAD(p1, 3, 3);
+    NS_EPI(3, 2, in2, p0);
+    NS_EPI(3, 3, in3, p1);
 #undef NS_LOAD
+#undef NS_PLOAD
 #undef NS_EPI
 }
 
