@@ -164,6 +164,17 @@ __device__ __forceinline__ void store16_hilo(__bf16* dhi, __bf16* dlo, const flo
     store16(dlo, lo);
 }
 
+__device__ __forceinline__ void store8_hilo(__bf16* dhi, __bf16* dlo, const float* v) {
+    bf16x8 h, l;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        h[e] = (__bf16)v[e];
+        l[e] = (__bf16)(v[e] - (float)h[e]);
+    }
+    gst(dhi, __builtin_bit_cast(uint4, h));
+    gst(dlo, __builtin_bit_cast(uint4, l));
+}
+
 // Make this wave's LDS writes visible to its other lanes before they read.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -347,7 +358,12 @@ __device__ __forceinline__ void epi_load(EpiIn& in, const MuonMat& d, int lane, 
             for (int q = 0; q < (BF ? 2 : 4); ++q) in.q[q] = gld(a + q);
         }
     } else if (EPI == EPI_XUPD || EPI == EPI_FINAL) {
-        if (BF) {
+        if (BF && EPI == EPI_XUPD) {
+            const int lr = lane >> 2, lc = (lane & 3) * 8;
+            const __bf16* lo = reinterpret_cast<const __bf16*>(d.xlo[cur]);
+            in.q[0] = gld(lo + xblk(bi + lr, bj + lc, d.C));
+            in.q[1] = gld(lo + xblk(bi + lr + 16, bj + lc, d.C));
+        } else if (BF) {
             const uint4* lo =
                 reinterpret_cast<const uint4*>(reinterpret_cast<const __bf16*>(d.xlo[cur]) + xblk(gi, gj, d.C));
             in.q[0] = gld(lo);
@@ -454,8 +470,24 @@ __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, co
     wave_lds_sync();
     {
         float v[16];
-        lds_read16(S + rrow * SLD + rc0, v);
-        const int gi = bi + rrow, gj = bj + rc0;
+        // bf16 X update: a lane takes 8 values of rows r and r + 16 of the
+        // block, so each store instruction covers a contiguous 1 KB half of
+        // the 2 KB block (with 16-element row runs every 128-byte line took
+        // two instructions; this cut the epilogue per tile 15.3 -> 10.4 us)
+        constexpr bool LINES = EPI == EPI_XUPD && BF;
+        const int lr = LINES ? lane >> 2 : rrow, lc = LINES ? (lane & 3) * 8 : rc0;
+        if (LINES) {
+            const float4* a = reinterpret_cast<const float4*>(S + lr * SLD + lc);
+            const float4* b = reinterpret_cast<const float4*>(S + (lr + 16) * SLD + lc);
+            const float4 a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
+            v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+            v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+            v[8] = b0.x; v[9] = b0.y; v[10] = b0.z; v[11] = b0.w;
+            v[12] = b1.x; v[13] = b1.y; v[14] = b1.z; v[15] = b1.w;
+        } else {
+            lds_read16(S + rrow * SLD + rc0, v);
+        }
+        const int gi = bi + lr, gj = bj + lc;
         const int64_t o = (int64_t)gi * d.C + gj;
         if (EPI == EPI_GRAM) {
 #pragma unroll
@@ -479,9 +511,11 @@ __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, co
 #pragma unroll
             for (int e = 0; e < 16; ++e) v[e] = escale * fmaf(args.a, lv[e], v[e]);
             if (EPI == EPI_XUPD) {
-                const int64_t ob = xblk(gi, gj, d.C);
-                store16_hilo(reinterpret_cast<__bf16*>(d.x[cur ^ 1]) + ob,
-                             reinterpret_cast<__bf16*>(d.xlo[cur ^ 1]) + ob, v);
+                const int64_t o0 = xblk(gi, gj, d.C), o1 = xblk(gi + 16, gj, d.C);
+                __bf16* hi = reinterpret_cast<__bf16*>(d.x[cur ^ 1]);
+                __bf16* lo = reinterpret_cast<__bf16*>(d.xlo[cur ^ 1]);
+                store8_hilo(hi + o0, lo + o0, v);
+                store8_hilo(hi + o1, lo + o1, v + 8);
             } else if (!d.transposed) {
                 update_run(d, up, gi, gj, v, pin);
             }
