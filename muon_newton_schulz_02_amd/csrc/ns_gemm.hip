@@ -12,11 +12,20 @@
 // contiguous.  For GRAM and POLY both operands are such rows of a row-major
 // matrix.  For B X the right operand is X with the reduction index along its
 // rows:
-//   * bf16: X is kept row-major only and the loader transposes 8x8 bf16
-//     blocks in registers on their way to LDS;
+//   * bf16: X is kept row-major (in 32x32 blocks) only, and its fragments
+//     are read out of LDS with transposing loads (ds_read_b64_tr_b16);
 //   * fp32: a transposed copy X^T is kept and read directly.
 // Operands are zero-padded to multiples of 256 in both dimensions, so no
 // tile needs bounds checks.
+//
+// A workgroup (4 waves, 2 x 2 of 128 x 128 each, accumulators in the 256
+// AGPRs) computes one 256 x 256 output tile.  Operands stream through a ring
+// of 4 LDS stages of 32 reduction columns, copied by buffer loads straight
+// into LDS three stages ahead; each stage's fragment reads and copies sit
+// between its matrix instructions, since a SIMD holds only this one wave.
+// The epilogue stages each 32 x 32 accumulator block through the wave's own
+// LDS region and writes it in 16-byte runs (whole 1 KB halves of a 2 KB
+// block for the bf16 X update).
 //
 // Method: OpenDM training-stack page, Muon/AdamW hybrid section, the
 // Newton-Schulz paragraph (a few quintic Newton-Schulz steps on the whole
