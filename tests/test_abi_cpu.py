@@ -268,3 +268,30 @@ def test_plan_param_dtype(lib):
     with pytest.raises(M.MuonAdamWError) as e:
         M.muon_adamw_plan(table, param_dtype=2)
     assert e.value.code == M.MA_ERR_INVALID_ARG
+
+
+def test_binding_rejects_wrong_tensors(lib):
+    """The binding checks dtype, layout and device before any call: a CPU
+    tensor, a non-contiguous view, a float16 tensor and, for a bf16 plan, a
+    float32 parameter are refused."""
+    torch = pytest.importorskip("torch")
+    plan = M.muon_adamw_plan([("vlm.w", (4, 4), True)])
+    st = M.State(1)
+    st.adam_m[0] = 1 << 40
+    st.adam_v[0] = 1 << 40
+    hp = M.muon_adamw_default_hparams()
+    ws = (1 << 40, M.muon_adamw_workspace_size(plan, 0))
+    cpu = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        M.muon_adamw_step(plan, [cpu], [cpu], st, hp, ws, stream=0)
+    with pytest.raises(ValueError):
+        M.muon_adamw_step(plan, [torch.zeros(4, 8)[:, :4]], [1 << 40], st, hp, ws, stream=0)
+    with pytest.raises(TypeError):
+        M.muon_adamw_step(plan, [torch.zeros(4, 4, dtype=torch.float16)], [1 << 40], st, hp, ws,
+                          stream=0)
+    bplan = M.muon_adamw_plan([("vlm.w", (4, 4), True)], param_dtype="bf16")
+    with pytest.raises(TypeError):
+        M.muon_adamw_step(bplan, [torch.zeros(4, 4)], [1 << 40], st, hp, ws, stream=0)
+    with pytest.raises(TypeError):
+        st.device_step = torch.zeros(1, dtype=torch.int32)
+        M.muon_adamw_step(plan, [1 << 40], [1 << 40], st, hp, ws, stream=0)
