@@ -38,6 +38,10 @@ constexpr int64_t kBf16MinRows = 16;
 // XCDs of an MI355X: consecutive workgroups of a launch are dispatched to
 // XCDs round-robin, and each XCD has its own L2.
 constexpr int kXcds = 8;
+// Newton-Schulz runs the Muon matrices as this many groups, each on its own
+// stream (the caller's and a library-owned one), balanced by their flops, so
+// the tail of one group's launch overlaps the other group's work.
+constexpr int kNsStreams = 2;
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
@@ -93,8 +97,10 @@ struct Layout {
     size_t tables_off = 0, tables_bytes = 0;
     size_t norm_tab_off = 0, adam_tab_off = 0, muon_tab_off = 0;
     std::vector<int32_t> op_group;                   // per Muon matrix: kGroupBf16 / kGroupFp32
-    std::vector<GemmTile> g1[2], g2[2], g3[2];       // cost-ordered tile lists per group
-    size_t g1_off[2] = {0, 0}, g2_off[2] = {0, 0}, g3_off[2] = {0, 0};
+    // cost-ordered tile lists per operand group and NS stream
+    std::vector<GemmTile> g1[2][kNsStreams], g2[2][kNsStreams], g3[2][kNsStreams];
+    size_t g1_off[2][kNsStreams] = {}, g2_off[2][kNsStreams] = {}, g3_off[2][kNsStreams] = {};
+    std::vector<int32_t> ns_stream;                  // per Muon matrix: the stream its NS runs on
     size_t scalars_off = 0;                          // StepDev
     size_t norm_partials_off = 0;                    // float[n_norm_chunks]
     size_t muon_partials_off = 0;                    // float[n_orient_tiles]
@@ -142,9 +148,12 @@ struct ma_plan {
     // the overlapped AdamW group; guarded by mu
     struct Side {
         int device;
-        void* stream;
+        void* stream;       // AdamW beside the Muon group
         void* ev_fork;
         void* ev_join;
+        void* ns_stream;    // the second Newton-Schulz stream
+        void* ev_ns_fork;
+        void* ev_ns_join;
     };
     mutable std::vector<Side> side;
     mutable std::mutex mu;

@@ -210,29 +210,54 @@ void build_layout(ma_plan* p, int32_t precision) {
     // operand group and GEMM tiles of every matrix: Gram and polynomial
     // phases cover the upper triangle of the r x r result (mirrored on
     // write), the X update the whole r x c result in column-major order
-    for (size_t k = 0; k < p->muon_ids.size(); ++k) {
+    // NS stream of every matrix: longest processing time first on the padded
+    // GEMM work (Gram and square over the upper tiles, the X update over all)
+    const size_t nm = p->muon_ids.size();
+    std::vector<double> cost(nm);
+    for (size_t k = 0; k < nm; ++k) {
+        const auto& e = p->entries[p->muon_ids[k]];
+        const double R = (double)round_up(e.r, kNsPad), C = (double)round_up(e.c, kNsPad);
+        cost[k] = R * R * C + R * R * R / 2.0 + R * R * C;
+    }
+    std::vector<size_t> order(nm);
+    for (size_t k = 0; k < nm; ++k) order[k] = k;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](size_t a, size_t b) { return cost[a] > cost[b]; });
+    L.ns_stream.assign(nm, 0);
+    double sload[kNsStreams] = {};
+    for (size_t k : order) {
+        int best = 0;
+        for (int q = 1; q < kNsStreams; ++q)
+            if (sload[q] < sload[best]) best = q;
+        L.ns_stream[k] = best;
+        sload[best] += cost[k];
+    }
+    for (size_t k = 0; k < nm; ++k) {
         const auto& e = p->entries[p->muon_ids[k]];
         const int32_t grp =
             (precision == MA_NS_BF16 && e.r >= kBf16MinRows) ? kGroupBf16 : kGroupFp32;
+        const int32_t sg = L.ns_stream[k];
         L.op_group.push_back(grp);
         const int64_t R = round_up(e.r, kNsPad), C = round_up(e.c, kNsPad);
         const int32_t TR = (int32_t)(R / kGemmTile), TC = (int32_t)(C / kGemmTile);
         for (int32_t i = 0; i < TR; ++i)
             for (int32_t j = i; j < TR; ++j) {
-                L.g1[grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)C});
-                L.g2[grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R});
+                L.g1[grp][sg].push_back(GemmTile{(int32_t)k, i, j, (int32_t)C});
+                L.g2[grp][sg].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R});
             }
         // column-major: the tiles of one column block (all readers of that
         // X panel) are consecutive, so the tiles an XCD runs together read
         // each panel once from HBM while the r x r B stays in its L2
         for (int32_t j = 0; j < TC; ++j)
-            for (int32_t i = 0; i < TR; ++i) L.g3[grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R});
+            for (int32_t i = 0; i < TR; ++i)
+                L.g3[grp][sg].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R});
     }
-    for (int g = 0; g < 2; ++g) {
-        schedule_tiles(L.g1[g]);
-        schedule_tiles(L.g2[g]);
-        schedule_tiles(L.g3[g]);
-    }
+    for (int g = 0; g < 2; ++g)
+        for (int q = 0; q < kNsStreams; ++q) {
+            schedule_tiles(L.g1[g][q]);
+            schedule_tiles(L.g2[g][q]);
+            schedule_tiles(L.g3[g][q]);
+        }
     size_t off = 0;
     L.tables_off = off;
     L.norm_tab_off = off;
@@ -241,14 +266,15 @@ void build_layout(ma_plan* p, int32_t precision) {
     off = align256(off + sizeof(AdamTensor) * p->adam_ids.size());
     L.muon_tab_off = off;
     off = align256(off + sizeof(MuonMat) * p->muon_ids.size());
-    for (int g = 0; g < 2; ++g) {
-        L.g1_off[g] = off;
-        off = align256(off + sizeof(GemmTile) * L.g1[g].size());
-        L.g2_off[g] = off;
-        off = align256(off + sizeof(GemmTile) * L.g2[g].size());
-        L.g3_off[g] = off;
-        off = align256(off + sizeof(GemmTile) * L.g3[g].size());
-    }
+    for (int g = 0; g < 2; ++g)
+        for (int q = 0; q < kNsStreams; ++q) {
+            L.g1_off[g][q] = off;
+            off = align256(off + sizeof(GemmTile) * L.g1[g][q].size());
+            L.g2_off[g][q] = off;
+            off = align256(off + sizeof(GemmTile) * L.g2[g][q].size());
+            L.g3_off[g][q] = off;
+            off = align256(off + sizeof(GemmTile) * L.g3[g][q].size());
+        }
     L.tables_bytes = off - L.tables_off;
     L.scalars_off = off;
     off = align256(off + sizeof(StepDev));

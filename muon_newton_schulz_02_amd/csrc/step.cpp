@@ -97,8 +97,10 @@ constexpr int kSideAdamWaves[2] = {4, 2};
 // momentum pass nothing and overlaps the whole GEMM phase.
 constexpr bool kForkAfterPrep = true;
 
-// The side stream and fork/join events of the current device (created on
-// first use; default priority, non-blocking with respect to the null stream).
+// The side streams and their fork/join events on the current device (created
+// on first use; default priority, non-blocking with respect to the null
+// stream): one for the overlapped AdamW group, one for the second
+// Newton-Schulz matrix group.
 int get_side(const ma_plan* plan, ma_plan::Side** out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -109,18 +111,27 @@ int get_side(const ma_plan* plan, ma_plan::Side** out) {
             return MA_OK;
         }
     }
-    ma_plan::Side s{dev, nullptr, nullptr, nullptr};
-    hipStream_t st;
-    e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
-    if (e != hipSuccess) return hip_fail("hipStreamCreate (side)", e);
-    s.stream = st;
-    hipEvent_t a, b;
-    e = hipEventCreateWithFlags(&a, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail("hipEventCreate (fork)", e);
-    s.ev_fork = a;
-    e = hipEventCreateWithFlags(&b, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail("hipEventCreate (join)", e);
-    s.ev_join = b;
+    ma_plan::Side s{dev, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    // on failure the objects made so far are released before returning
+    auto undo = [&](const char* what, hipError_t er) {
+        for (void* ev : {s.ev_fork, s.ev_join, s.ev_ns_fork, s.ev_ns_join})
+            if (ev) (void)hipEventDestroy((hipEvent_t)ev);
+        for (void* q : {s.stream, s.ns_stream})
+            if (q) (void)hipStreamDestroy((hipStream_t)q);
+        return hip_fail(what, er);
+    };
+    for (void** q : {&s.stream, &s.ns_stream}) {
+        hipStream_t st;
+        e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+        if (e != hipSuccess) return undo("hipStreamCreate (side)", e);
+        *q = st;
+    }
+    for (void** ev : {&s.ev_fork, &s.ev_join, &s.ev_ns_fork, &s.ev_ns_join}) {
+        hipEvent_t a;
+        e = hipEventCreateWithFlags(&a, hipEventDisableTiming);
+        if (e != hipSuccess) return undo("hipEventCreate (fork/join)", e);
+        *ev = a;
+    }
     plan->side.push_back(s);
     *out = &plan->side.back();
     return MA_OK;
@@ -337,11 +348,15 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
             d.op_bf16 = L.op_group[k] == kGroupBf16 ? 1 : 0;
             d.p_bf16 = bf16 ? 1 : 0;
         }
-        for (int g = 0; g < 2; ++g) {
-            std::memcpy(hb + L.g1_off[g], L.g1[g].data(), sizeof(GemmTile) * L.g1[g].size());
-            std::memcpy(hb + L.g2_off[g], L.g2[g].data(), sizeof(GemmTile) * L.g2[g].size());
-            std::memcpy(hb + L.g3_off[g], L.g3[g].data(), sizeof(GemmTile) * L.g3[g].size());
-        }
+        for (int g = 0; g < 2; ++g)
+            for (int q = 0; q < kNsStreams; ++q) {
+                std::memcpy(hb + L.g1_off[g][q], L.g1[g][q].data(),
+                            sizeof(GemmTile) * L.g1[g][q].size());
+                std::memcpy(hb + L.g2_off[g][q], L.g2[g][q].data(),
+                            sizeof(GemmTile) * L.g2[g][q].size());
+                std::memcpy(hb + L.g3_off[g][q], L.g3[g][q].data(),
+                            sizeof(GemmTile) * L.g3[g][q].size());
+            }
     };
 
     auto mark = [&](int k) -> int {
@@ -418,6 +433,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     // AdamW: on the caller's stream, or forked to the side stream so it runs
     // concurrently with the Muon group and joined back at the end
     ma_plan::Side* side = nullptr;
+    bool ns_joined = false;
     // (the chunk counter is an int: beyond 2^30 chunks run serially)
     const bool overlap =
         plan->overlap && n_adam > 0 && n_muon > 0 && plan->n_adam_chunks < (int64_t(1) << 30);
@@ -458,30 +474,62 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         if (err) return hip_fail("muon scale", err);
         if (overlap && kForkAfterPrep && (err = fork_adamw()) != MA_OK) return err;
         if ((err = mark(3))) return hip_fail("phase event", err);
+        // The matrices are split into kNsStreams groups of about equal GEMM
+        // work, the first on the caller's stream and the others on a side
+        // stream: one group's launch tail (the last tiles of a phase, when
+        // most CUs already idle) overlaps the other group's next phase.
+        bool split = false;
+        for (int g = 0; g < 2; ++g)
+            if (!L.g1[g][1].empty()) split = true;
+        hipStream_t nss = nullptr;
+        if (split) {
+            if (!side) {
+                int rs = get_side(plan, &side);
+                if (rs != MA_OK) return rs;
+            }
+            nss = (hipStream_t)side->ns_stream;
+            if ((e = hipEventRecord((hipEvent_t)side->ev_ns_fork, st)) != hipSuccess)
+                return hip_fail("hipEventRecord (ns fork)", e);
+            if ((e = hipStreamWaitEvent(nss, (hipEvent_t)side->ev_ns_fork, 0)) != hipSuccess)
+                return hip_fail("hipStreamWaitEvent (ns fork)", e);
+        }
         for (int it = 0; it < hp->muon_ns_steps; ++it) {
             const int last = it == hp->muon_ns_steps - 1;
             for (int phase = 1; phase <= 3; ++phase) {
-                for (int g = 0; g < 2; ++g) {
-                    const std::vector<GemmTile>& tl =
-                        phase == 1 ? L.g1[g] : phase == 2 ? L.g2[g] : L.g3[g];
-                    const size_t off = phase == 1 ? L.g1_off[g] : phase == 2 ? L.g2_off[g] : L.g3_off[g];
-                    err = launch_ns_phase(phase, g, d_muon, reinterpret_cast<const GemmTile*>(base + off),
-                                          (int64_t)tl.size(), it, last, sc, muon_scales, sd, stream);
-                    if (err) return hip_fail("newton-schulz", err);
+                for (int q = 0; q < kNsStreams; ++q) {
+                    for (int g = 0; g < 2; ++g) {
+                        const std::vector<GemmTile>& tl =
+                            phase == 1 ? L.g1[g][q] : phase == 2 ? L.g2[g][q] : L.g3[g][q];
+                        const size_t off = phase == 1   ? L.g1_off[g][q]
+                                           : phase == 2 ? L.g2_off[g][q]
+                                                        : L.g3_off[g][q];
+                        err = launch_ns_phase(phase, g, d_muon,
+                                              reinterpret_cast<const GemmTile*>(base + off),
+                                              (int64_t)tl.size(), it, last, sc, muon_scales, sd,
+                                              q == 0 ? stream : (void*)nss);
+                        if (err) return hip_fail("newton-schulz", err);
+                    }
                 }
             }
+        }
+        if (split) {
+            if ((e = hipEventRecord((hipEvent_t)side->ev_ns_join, nss)) != hipSuccess)
+                return hip_fail("hipEventRecord (ns join)", e);
+            ns_joined = true;
         }
     } else if ((err = mark(3))) {
         return hip_fail("phase event", err);
     }
-    if (side) {
+    if (overlap && side) {
         // the chunks the side kernel has not claimed yet, at full occupancy
         err = launch_adamw_claim(d_adam, n_adam, plan->n_adam_chunks, sd, sc, plan->param_dtype,
                                  kFinishAdamGroups, 4, stream);
         if (err) return hip_fail("adamw", err);
     }
-    if (side && (e = hipStreamWaitEvent(st, (hipEvent_t)side->ev_join, 0)) != hipSuccess)
+    if (overlap && side && (e = hipStreamWaitEvent(st, (hipEvent_t)side->ev_join, 0)) != hipSuccess)
         return hip_fail("hipStreamWaitEvent (join)", e);
+    if (ns_joined && (e = hipStreamWaitEvent(st, (hipEvent_t)side->ev_ns_join, 0)) != hipSuccess)
+        return hip_fail("hipStreamWaitEvent (ns join)", e);
     if ((err = mark(4))) return hip_fail("phase event", err);
     if (!state->device_step) state->step = in.t_host;
     clear_error();
@@ -492,9 +540,11 @@ void muon_adamw_plan_free(ma_plan* plan) {
     if (!plan) return;
     for (auto& sd : plan->side) {
         (void)hipStreamSynchronize((hipStream_t)sd.stream);
-        (void)hipEventDestroy((hipEvent_t)sd.ev_fork);
-        (void)hipEventDestroy((hipEvent_t)sd.ev_join);
+        (void)hipStreamSynchronize((hipStream_t)sd.ns_stream);
+        for (void* ev : {sd.ev_fork, sd.ev_join, sd.ev_ns_fork, sd.ev_ns_join})
+            (void)hipEventDestroy((hipEvent_t)ev);
         (void)hipStreamDestroy((hipStream_t)sd.stream);
+        (void)hipStreamDestroy((hipStream_t)sd.ns_stream);
     }
     for (int k = 0; k < 2; ++k) {
         if (plan->staging_event[k]) {
