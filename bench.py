@@ -298,8 +298,10 @@ def main():
         else:
             state.adam_m[i] = torch.zeros(spec.shape, dtype=torch.float32, device=dev)
             state.adam_v[i] = torch.zeros(spec.shape, dtype=torch.float32, device=dev)
-    ws = torch.empty(M.muon_adamw_workspace_size(plan, hp.ns_precision), dtype=torch.uint8,
-                     device=dev)
+    # one workspace serves both plans (their tile lists differ in length)
+    ws = torch.empty(max(M.muon_adamw_workspace_size(plan, hp.ns_precision),
+                         M.muon_adamw_workspace_size(serial_plan, hp.ns_precision)),
+                     dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     muon_shapes = [w.params[i].shape for i in range(n) if groups[i] == M.MA_GROUP_MUON]

@@ -38,10 +38,16 @@ constexpr int64_t kBf16MinRows = 16;
 // XCDs of an MI355X: consecutive workgroups of a launch are dispatched to
 // XCDs round-robin, and each XCD has its own L2.
 constexpr int kXcds = 8;
-// Newton-Schulz runs the Muon matrices as this many groups, each on its own
-// stream (the caller's and a library-owned one), balanced by their flops, so
-// the tail of one group's launch overlaps the other group's work.
+// Newton-Schulz runs the Muon matrices in batches, each batch through all of
+// its iterations; consecutive batches alternate between this many streams
+// (the caller's and a library-owned one), so the tail of one batch's launch
+// overlaps the other stream's work.
 constexpr int kNsStreams = 2;
+// When the AdamW group runs beside bf16 Newton-Schulz, batches hold about
+// this many operand bytes (X as hi + lo bf16): the plan makes kNsStreams x
+// ceil(total / (kNsStreams x this)) batches of about equal GEMM work.
+// Otherwise there are kNsStreams batches.
+constexpr size_t kNsOverlapBatchBytes = size_t(160) << 20;
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
@@ -97,10 +103,13 @@ struct Layout {
     size_t tables_off = 0, tables_bytes = 0;
     size_t norm_tab_off = 0, adam_tab_off = 0, muon_tab_off = 0;
     std::vector<int32_t> op_group;                   // per Muon matrix: kGroupBf16 / kGroupFp32
-    // cost-ordered tile lists per operand group and NS stream
-    std::vector<GemmTile> g1[2][kNsStreams], g2[2][kNsStreams], g3[2][kNsStreams];
-    size_t g1_off[2][kNsStreams] = {}, g2_off[2][kNsStreams] = {}, g3_off[2][kNsStreams] = {};
-    std::vector<int32_t> ns_stream;                  // per Muon matrix: the stream its NS runs on
+    // Newton-Schulz batches; batch b runs on NS stream b % kNsStreams
+    struct NsBatch {
+        std::vector<GemmTile> tiles[3][2];           // [phase - 1][operand group], cost-ordered
+        size_t off[3][2] = {};                       // their offsets in the workspace
+    };
+    std::vector<NsBatch> ns_batches;
+    std::vector<int32_t> ns_batch;                   // per Muon matrix: its batch
     size_t scalars_off = 0;                          // StepDev
     size_t norm_partials_off = 0;                    // float[n_norm_chunks]
     size_t muon_partials_off = 0;                    // float[n_orient_tiles]

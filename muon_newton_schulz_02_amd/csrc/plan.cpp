@@ -210,54 +210,64 @@ void build_layout(ma_plan* p, int32_t precision) {
     // operand group and GEMM tiles of every matrix: Gram and polynomial
     // phases cover the upper triangle of the r x r result (mirrored on
     // write), the X update the whole r x c result in column-major order
-    // NS stream of every matrix: longest processing time first on the padded
+    // NS batch of every matrix: longest processing time first on the padded
     // GEMM work (Gram and square over the upper tiles, the X update over all)
     const size_t nm = p->muon_ids.size();
     std::vector<double> cost(nm);
-    for (size_t k = 0; k < nm; ++k) {
-        const auto& e = p->entries[p->muon_ids[k]];
-        const double R = (double)round_up(e.r, kNsPad), C = (double)round_up(e.c, kNsPad);
-        cost[k] = R * R * C + R * R * R / 2.0 + R * R * C;
-    }
-    std::vector<size_t> order(nm);
-    for (size_t k = 0; k < nm; ++k) order[k] = k;
-    std::stable_sort(order.begin(), order.end(),
-                     [&](size_t a, size_t b) { return cost[a] > cost[b]; });
-    L.ns_stream.assign(nm, 0);
-    double sload[kNsStreams] = {};
-    for (size_t k : order) {
-        int best = 0;
-        for (int q = 1; q < kNsStreams; ++q)
-            if (sload[q] < sload[best]) best = q;
-        L.ns_stream[k] = best;
-        sload[best] += cost[k];
-    }
+    size_t operand_bytes = 0;
     for (size_t k = 0; k < nm; ++k) {
         const auto& e = p->entries[p->muon_ids[k]];
         const int32_t grp =
             (precision == MA_NS_BF16 && e.r >= kBf16MinRows) ? kGroupBf16 : kGroupFp32;
-        const int32_t sg = L.ns_stream[k];
         L.op_group.push_back(grp);
+        const int64_t R = round_up(e.r, kNsPad), C = round_up(e.c, kNsPad);
+        cost[k] = (double)R * R * C + (double)R * R * R / 2.0 + (double)R * R * C;
+        operand_bytes += (size_t)(R * C) * (grp == kGroupBf16 ? 4 : 8);
+    }
+    // With AdamW streaming beside it, bf16 Newton-Schulz in smaller batches
+    // (whose operands can stay in the 256 MB memory-side cache through the
+    // iterations) contends less for HBM: measured 16.1 -> 15.6 ms per step on
+    // the full hybrid table.  Alone, or with fp32 products (bound by the
+    // matrix cores, 46 -> 52 ms when batched), fewer and fuller launches win.
+    const bool batched = precision == MA_NS_BF16 && p->overlap && !p->adam_ids.empty() &&
+                         p->n_adam_chunks < (int64_t(1) << 30);
+    const size_t per = batched ? kNsOverlapBatchBytes : std::max<size_t>(operand_bytes, 1);
+    size_t nb = kNsStreams * ((operand_bytes + kNsStreams * per - 1) / (kNsStreams * per));
+    nb = std::max<size_t>(1, std::min(nb, nm));
+    std::vector<size_t> order(nm);
+    for (size_t k = 0; k < nm; ++k) order[k] = k;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](size_t a, size_t b) { return cost[a] > cost[b]; });
+    L.ns_batch.assign(nm, 0);
+    std::vector<double> bload(nb, 0.0);
+    for (size_t k : order) {
+        size_t best = 0;
+        for (size_t q = 1; q < nb; ++q)
+            if (bload[q] < bload[best]) best = q;
+        L.ns_batch[k] = (int32_t)best;
+        bload[best] += cost[k];
+    }
+    L.ns_batches.assign(nm ? nb : 0, Layout::NsBatch());
+    for (size_t k = 0; k < nm; ++k) {
+        const auto& e = p->entries[p->muon_ids[k]];
+        const int32_t grp = L.op_group[k];
+        auto& t = L.ns_batches[L.ns_batch[k]].tiles;
         const int64_t R = round_up(e.r, kNsPad), C = round_up(e.c, kNsPad);
         const int32_t TR = (int32_t)(R / kGemmTile), TC = (int32_t)(C / kGemmTile);
         for (int32_t i = 0; i < TR; ++i)
             for (int32_t j = i; j < TR; ++j) {
-                L.g1[grp][sg].push_back(GemmTile{(int32_t)k, i, j, (int32_t)C});
-                L.g2[grp][sg].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R});
+                t[0][grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)C});
+                t[1][grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R});
             }
         // column-major: the tiles of one column block (all readers of that
         // X panel) are consecutive, so the tiles an XCD runs together read
         // each panel once from HBM while the r x r B stays in its L2
         for (int32_t j = 0; j < TC; ++j)
-            for (int32_t i = 0; i < TR; ++i)
-                L.g3[grp][sg].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R});
+            for (int32_t i = 0; i < TR; ++i) t[2][grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R});
     }
-    for (int g = 0; g < 2; ++g)
-        for (int q = 0; q < kNsStreams; ++q) {
-            schedule_tiles(L.g1[g][q]);
-            schedule_tiles(L.g2[g][q]);
-            schedule_tiles(L.g3[g][q]);
-        }
+    for (auto& bt : L.ns_batches)
+        for (auto& ph : bt.tiles)
+            for (auto& tl : ph) schedule_tiles(tl);
     size_t off = 0;
     L.tables_off = off;
     L.norm_tab_off = off;
@@ -266,15 +276,12 @@ void build_layout(ma_plan* p, int32_t precision) {
     off = align256(off + sizeof(AdamTensor) * p->adam_ids.size());
     L.muon_tab_off = off;
     off = align256(off + sizeof(MuonMat) * p->muon_ids.size());
-    for (int g = 0; g < 2; ++g)
-        for (int q = 0; q < kNsStreams; ++q) {
-            L.g1_off[g][q] = off;
-            off = align256(off + sizeof(GemmTile) * L.g1[g][q].size());
-            L.g2_off[g][q] = off;
-            off = align256(off + sizeof(GemmTile) * L.g2[g][q].size());
-            L.g3_off[g][q] = off;
-            off = align256(off + sizeof(GemmTile) * L.g3[g][q].size());
-        }
+    for (auto& bt : L.ns_batches)
+        for (int ph = 0; ph < 3; ++ph)
+            for (int g = 0; g < 2; ++g) {
+                bt.off[ph][g] = off;
+                off = align256(off + sizeof(GemmTile) * bt.tiles[ph][g].size());
+            }
     L.tables_bytes = off - L.tables_off;
     L.scalars_off = off;
     off = align256(off + sizeof(StepDev));

@@ -348,15 +348,11 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
             d.op_bf16 = L.op_group[k] == kGroupBf16 ? 1 : 0;
             d.p_bf16 = bf16 ? 1 : 0;
         }
-        for (int g = 0; g < 2; ++g)
-            for (int q = 0; q < kNsStreams; ++q) {
-                std::memcpy(hb + L.g1_off[g][q], L.g1[g][q].data(),
-                            sizeof(GemmTile) * L.g1[g][q].size());
-                std::memcpy(hb + L.g2_off[g][q], L.g2[g][q].data(),
-                            sizeof(GemmTile) * L.g2[g][q].size());
-                std::memcpy(hb + L.g3_off[g][q], L.g3[g][q].data(),
-                            sizeof(GemmTile) * L.g3[g][q].size());
-            }
+        for (const auto& bt : L.ns_batches)
+            for (int ph = 0; ph < 3; ++ph)
+                for (int g = 0; g < 2; ++g)
+                    std::memcpy(hb + bt.off[ph][g], bt.tiles[ph][g].data(),
+                                sizeof(GemmTile) * bt.tiles[ph][g].size());
     };
 
     auto mark = [&](int k) -> int {
@@ -474,13 +470,14 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         if (err) return hip_fail("muon scale", err);
         if (overlap && kForkAfterPrep && (err = fork_adamw()) != MA_OK) return err;
         if ((err = mark(3))) return hip_fail("phase event", err);
-        // The matrices are split into kNsStreams groups of about equal GEMM
-        // work, the first on the caller's stream and the others on a side
-        // stream: one group's launch tail (the last tiles of a phase, when
-        // most CUs already idle) overlaps the other group's next phase.
-        bool split = false;
-        for (int g = 0; g < 2; ++g)
-            if (!L.g1[g][1].empty()) split = true;
+        // The matrices run in batches of about equal GEMM work, each through
+        // all of its iterations, consecutive batches alternating between the
+        // caller's stream and a side stream: one batch's launch tail (the last
+        // tiles of a phase, when most CUs already idle) overlaps the other
+        // stream's next launch.
+        static_assert(kNsStreams == 2, "one caller stream and one side stream");
+        const int nb = (int)L.ns_batches.size();
+        const bool split = nb > 1;
         hipStream_t nss = nullptr;
         if (split) {
             if (!side) {
@@ -493,21 +490,20 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
             if ((e = hipStreamWaitEvent(nss, (hipEvent_t)side->ev_ns_fork, 0)) != hipSuccess)
                 return hip_fail("hipStreamWaitEvent (ns fork)", e);
         }
-        for (int it = 0; it < hp->muon_ns_steps; ++it) {
-            const int last = it == hp->muon_ns_steps - 1;
-            for (int phase = 1; phase <= 3; ++phase) {
-                for (int q = 0; q < kNsStreams; ++q) {
-                    for (int g = 0; g < 2; ++g) {
-                        const std::vector<GemmTile>& tl =
-                            phase == 1 ? L.g1[g][q] : phase == 2 ? L.g2[g][q] : L.g3[g][q];
-                        const size_t off = phase == 1   ? L.g1_off[g][q]
-                                           : phase == 2 ? L.g2_off[g][q]
-                                                        : L.g3_off[g][q];
-                        err = launch_ns_phase(phase, g, d_muon,
-                                              reinterpret_cast<const GemmTile*>(base + off),
-                                              (int64_t)tl.size(), it, last, sc, muon_scales, sd,
-                                              q == 0 ? stream : (void*)nss);
-                        if (err) return hip_fail("newton-schulz", err);
+        for (int b0 = 0; b0 < nb; b0 += kNsStreams) {
+            for (int it = 0; it < hp->muon_ns_steps; ++it) {
+                const int last = it == hp->muon_ns_steps - 1;
+                for (int ph = 0; ph < 3; ++ph) {
+                    for (int q = 0; q < kNsStreams && b0 + q < nb; ++q) {
+                        const auto& bt = L.ns_batches[b0 + q];
+                        for (int g = 0; g < 2; ++g) {
+                            err = launch_ns_phase(
+                                ph + 1, g, d_muon,
+                                reinterpret_cast<const GemmTile*>(base + bt.off[ph][g]),
+                                (int64_t)bt.tiles[ph][g].size(), it, last, sc, muon_scales, sd,
+                                q == 0 ? stream : (void*)nss);
+                            if (err) return hip_fail("newton-schulz", err);
+                        }
                     }
                 }
             }

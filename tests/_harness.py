@@ -127,12 +127,14 @@ class GpuRun:
 
 
 def setup_gpu(M, torch, w: W.Workload, hp: O.HParams, ns_precision: str, backend: str = "numpy",
-              deltas: str = "all"):
+              deltas: str = "all", overlap: bool = False):
     """Allocate and seed a workload on cuda:0.  deltas: 'all', 'none' or a set
-    of entry indices that get a delta output buffer."""
+    of entry indices that get a delta output buffer; overlap: the plan's
+    overlap_groups (the workspace is sized for that plan)."""
     dev = torch.device("cuda", 0)
     table = list(zip(w.names, w.shapes, w.trainable))
-    plan = M.muon_adamw_plan(table, mode=W.mode_id(w), param_dtype=w.param_storage)
+    plan = M.muon_adamw_plan(table, mode=W.mode_id(w), param_dtype=w.param_storage,
+                             overlap_groups=overlap)
     pdt = torch.bfloat16 if w.param_storage == "bf16" else torch.float32
     n = len(w.params)
     groups = [M.muon_adamw_plan_entry(plan, i)["group"] for i in range(n)]

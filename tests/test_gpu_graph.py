@@ -43,9 +43,7 @@ def _hparams(w):
 
 
 def _setup(w, hp, overlap, device_counter):
-    run = H.setup_gpu(M, torch, w, hp, "bf16")
-    run.plan = M.muon_adamw_plan(list(zip(w.names, w.shapes, w.trainable)),
-                                 overlap_groups=overlap)
+    run = H.setup_gpu(M, torch, w, hp, "bf16", overlap=overlap)
     if device_counter:
         run.state.device_step = torch.zeros(1, dtype=torch.int64, device="cuda")
     return run

@@ -49,11 +49,7 @@ def _run_parity(w, ns_precision, steps, hp=None, sampled=None, backend="numpy",
     assert hp.param_storage == w.param_storage
     tol = H.BF16_TOL if ns_precision == "bf16" else H.FP32_TOL
     deltas = "all" if sampled is None else set(sampled)
-    run = H.setup_gpu(M, torch, w, hp, ns_precision, backend, deltas=deltas)
-    if overlap:
-        run.plan = M.muon_adamw_plan(list(zip(w.names, w.shapes, w.trainable)),
-                                     mode=W.mode_id(w), overlap_groups=True,
-                                     param_dtype=w.param_storage)
+    run = H.setup_gpu(M, torch, w, hp, ns_precision, backend, deltas=deltas, overlap=overlap)
     if prepare is not None:
         prepare(run)
     idx = range(len(w.params)) if sampled is None else sorted(sampled)
@@ -373,12 +369,14 @@ def test_ae18_full_size_sampled():
     _run_parity(w, "bf16", w.steps, sampled=sampled, backend="torch")
 
 
-def test_vla_hybrid_full_size_sampled():
+@pytest.mark.parametrize("overlap", [True, False])
+def test_vla_hybrid_full_size_sampled(overlap):
     """The full hybrid step in the benchmark's configuration: 126 Muon
     matrices (bf16 NS) + 253 AdamW tensors (1.88e9 elements) + a frozen
     embedding; clip triggers.  The oracle follows the global norm over all
     2.15e9 gradients, eight AdamW tensors of every shape and four Muon
-    matrices, for two steps."""
+    matrices, for two steps; AdamW beside the Muon group (the benchmark's
+    launch, with Newton-Schulz in batches on two streams) and serial."""
     w = W.vla_hybrid_bf16()
     names = w.names
     pick = ["vlm.model.layers.0.self_attn.q_proj.weight", "vlm.model.layers.3.mlp.gate_proj.weight",
@@ -389,7 +387,7 @@ def test_vla_hybrid_full_size_sampled():
             "action_expert.layers.17.mlp.gate_proj.weight",
             "action_expert.layers.9.mlp.down_proj.weight"]
     sampled = {names.index(n) for n in pick}
-    _run_parity(w, "bf16", 2, sampled=sampled, backend="torch")
+    _run_parity(w, "bf16", 2, sampled=sampled, backend="torch", overlap=overlap)
 
 
 def _bf16_ragged():
@@ -488,9 +486,7 @@ def test_overlapped_groups_match_serial_bitwise():
     hp = H.oracle_hparams(w)
     outs = []
     for overlap in (False, True):
-        run = H.setup_gpu(M, torch, w, hp, "bf16")
-        run.plan = M.muon_adamw_plan(list(zip(w.names, w.shapes, w.trainable)),
-                                     overlap_groups=overlap)
+        run = H.setup_gpu(M, torch, w, hp, "bf16", overlap=overlap)
         for t in (1, 2):
             H.fill_grads(run, torch, t)
             H.say("overlap=%s step %d" % (overlap, t))
@@ -499,6 +495,33 @@ def test_overlapped_groups_match_serial_bitwise():
                      run.state.adam_m + run.state.adam_v + [run.norm_out] if x is not None])
     for a, b in zip(*outs):
         np.testing.assert_array_equal(a, b)
+
+
+def test_batched_newton_schulz_matches_serial_bitwise():
+    """The 126 full-size action-expert matrices plus one AdamW tensor: with
+    the AdamW group beside them, Newton-Schulz runs in several batches over
+    two streams; every Muon result equals the serial step's bit for bit."""
+    w = W.ae18_muon_bf16()
+    w.params.append(W.ParamSpec("vlm.model.norm.weight", (2048,)))
+    hp = H.oracle_hparams(w)
+    keys = [i for i, p in enumerate(w.params) if p.trainable]
+    ref = None
+    for overlap in (False, True):
+        run = H.setup_gpu(M, torch, w, hp, "bf16", "torch", deltas="all", overlap=overlap)
+        H.fill_grads(run, torch, 1, "torch")
+        H.say("batched NS: overlap=%s step" % overlap)
+        H.gpu_step(M, torch, run)
+        got = [(H.host(run.params[i]).copy(), H.host(run.deltas[i]).copy()
+                if run.deltas[i] is not None else None) for i in keys]
+        del run
+        torch.cuda.empty_cache()
+        if ref is None:
+            ref = got
+            continue
+        for i, (a, b) in zip(keys, zip(ref, got)):
+            np.testing.assert_array_equal(a[0], b[0], err_msg=w.names[i])
+            if a[1] is not None:
+                np.testing.assert_array_equal(a[1], b[1], err_msg=w.names[i])
 
 
 def test_vla_hybrid_fp32ns_full_size_sampled():
