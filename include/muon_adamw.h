@@ -25,7 +25,12 @@
  *     allocates device memory; its scratch lives in a caller-provided
  *     workspace.
  *   - Device work is asynchronous on the caller's HIP stream; device faults
- *     surface at the caller's next synchronisation (HIP semantics).
+ *     surface at the caller's next synchronisation (HIP semantics).  Part of
+ *     a step may run on streams the library creates on the same device
+ *     (default priority, one set per plan and device, released by
+ *     muon_adamw_plan_free); they fork from the caller's stream and are
+ *     joined back into it before the step's work ends, so the caller's
+ *     stream order covers the whole step, under graph capture too.
  */
 #ifndef MUON_ADAMW_H_
 #define MUON_ADAMW_H_
@@ -86,8 +91,16 @@ typedef struct {
  * AdamW launch on the caller's stream finishes whatever chunks are left.
  * Chunks are claimed from a counter in the workspace; AdamW is elementwise,
  * so the results are bitwise those of overlap 0.  The side stream is joined
- * back into the caller's stream before the step's work ends.  0 runs every
- * kernel on the caller's stream in order.
+ * back into the caller's stream before the step's work ends.  With bf16
+ * Newton-Schulz products the Muon matrices then also run in smaller batches
+ * (each through all of its iterations; about 160 MB of operands per batch),
+ * which leaves more HBM bandwidth to the AdamW stream.
+ *
+ * In both modes the Newton-Schulz GEMMs run in batches of matrices that
+ * alternate between the caller's stream and a second library-owned stream;
+ * every matrix's iterations stay in order on one stream, so the results do
+ * not depend on the batching.  0 runs AdamW on the caller's stream, in order
+ * before the Muon group.
  *
  * param_dtype: how every trainable parameter and its gradient are stored
  * (the page's precision policies: bf16_mixed, the default there, stores the
@@ -277,7 +290,8 @@ int muon_adamw_step(const ma_plan* plan,
  * at [0] the start of the step, [1] after the clip norm, [2] after the AdamW
  * group, [3] after the Muon momentum/normalise pass, [4] at the end of the
  * step.  Without overlap_groups each interval is exactly its phase's
- * kernels ([1] -> [2] is the one AdamW launch).  With overlap_groups, [2] is
+ * kernels ([1] -> [2] is the one AdamW launch; [3] -> [4] spans the
+ * Newton-Schulz launches on both of its streams).  With overlap_groups, [2] is
  * recorded on the side stream after its AdamW launch and the remaining
  * AdamW chunks run between [3] and [4], so only [0] -> [4] is meaningful.
  * Same errors as muon_adamw_step. */
