@@ -1,0 +1,38 @@
+"""Host-side accounting of the benchmark (no GPU): the dense and executed
+Newton-Schulz flop counts and the multi-GPU refusal."""
+
+import subprocess
+import sys
+import os
+
+import pytest
+
+HERE = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, HERE)
+import bench  # noqa: E402
+
+
+def test_dense_ns_flops_of_one_matrix():
+    # per step: Gram 2 r^2 c, square 2 r^3, B X 2 r^2 c, with r = min side
+    r, c = 1024, 4096
+    want = 5 * (2 * r * r * c + 2 * r ** 3 + 2 * r * r * c)
+    assert bench.ns_flops([(c, r)], 5) == want
+    assert bench.ns_flops([(r, c)], 5) == want
+
+
+def test_executed_ns_flops_counts_upper_tiles_and_padding():
+    # 1024 x 4096: 4 x 4 tiles of 256, of which 10 are upper tiles
+    up = 10 * 256 * 256
+    want = 2 * up * 4096 + 2 * up * 1024 + 2 * 1024 * 1024 * 4096
+    assert bench.ns_executed_flops([(1024, 4096)], 1) == want
+    # 64 x 256 pads to one 256 x 256 tile in every product
+    assert bench.ns_executed_flops([(256, 64)], 1) == 3 * 2 * 256.0 ** 3
+    # one tile row: symmetric saving is nil, so executed == dense at r = 256
+    assert bench.ns_executed_flops([(256, 1024)], 1) == bench.ns_flops([(256, 1024)], 1)
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, os.path.join(HERE, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode != 0
+    assert "one GPU" in (p.stdout + p.stderr) or "1 GPU" in (p.stdout + p.stderr)
