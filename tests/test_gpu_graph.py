@@ -182,3 +182,54 @@ def test_capture_needing_new_tables_is_refused():
     torch.cuda.synchronize()
     assert code == M.MA_ERR_CAPTURE
     assert int(run.state.device_step.item()) == 0
+
+
+def test_graph_replays_with_batched_newton_schulz():
+    """The 126 full-size action-expert matrices plus one AdamW tensor, AdamW
+    beside the Muon group: Newton-Schulz runs as several batches over two
+    streams, all forked from and joined into the captured stream.  Replays
+    equal eager steps bit for bit."""
+    w = W.ae18_muon_bf16()
+    w.params.append(W.ParamSpec("vlm.model.norm.weight", (2048,)))
+    hp = _hparams(w)
+
+    def setup():
+        run = H.setup_gpu(M, torch, w, hp, "bf16", "torch", deltas="none", overlap=True)
+        run.state.device_step = torch.zeros(1, dtype=torch.int64, device="cuda")
+        return run
+
+    def snap(run):
+        return [H.host(x).copy() for x in run.params + run.state.muon_momentum +
+                run.state.adam_m + run.state.adam_v + [run.norm_out] if x is not None]
+
+    eager = setup()
+    ref = []
+    for t in (1, 2, 3):
+        H.fill_grads(eager, torch, t, "torch")
+        H.say("batched NS eager step %d" % t)
+        _step(eager)
+        torch.cuda.synchronize()
+        ref.append(snap(eager))
+    del eager
+    torch.cuda.empty_cache()
+
+    run = setup()
+    H.fill_grads(run, torch, 1, "torch")
+    H.say("batched NS graph run: eager step 1")
+    _step(run)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    H.say("batched NS graph run: capture")
+    with torch.cuda.graph(g, stream=cap):
+        _step(run)
+    torch.cuda.synchronize()
+    for t in (2, 3):
+        H.fill_grads(run, torch, t, "torch")
+        torch.cuda.synchronize()
+        H.say("batched NS graph run: replay as step %d" % t)
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(run.state.device_step.item()) == t
+        _assert_same(snap(run), ref[t - 1], "replay as step %d" % t)
+    del g
