@@ -12,8 +12,9 @@ The headline steps run the AdamW group beside the Muon group (the library's
 overlap_groups plan option; --serial turns it off).  After them, a roofline
 pass times serial steps with HIP events that the library records on its own
 stream at the phase boundaries, so the AdamW phase is exactly one k_adamw
-launch and the Newton-Schulz phase its GEMM launches; a plain device copy
-is timed as the HBM rate reachable on this GPU.
+launch and the Newton-Schulz phase its GEMM launches (two batches on two
+streams, joined before the closing event); a plain device copy is timed as
+the HBM rate reachable on this GPU.
 
 Prints one JSON line: whole-step params/s (the metric's headline value),
 step time, the serial pass's per-phase times, Newton-Schulz TFLOP/s and
@@ -251,8 +252,8 @@ def main():
     ap.add_argument("--workload", default="vla_hybrid_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--serial", action="store_true",
-                    help="time the groups one after the other on one stream (default: the AdamW "
-                         "group runs beside the Muon group)")
+                    help="time the groups one after the other (default: the AdamW group runs "
+                         "beside the Muon group on its own stream)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the extra pass that times replays of one step captured in a "
                          "HIP graph (device step counter)")

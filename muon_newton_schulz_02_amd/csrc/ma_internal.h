@@ -153,8 +153,9 @@ struct ma_plan {
     int32_t overlap = 0;    // 1: AdamW on a second stream, concurrent with Muon
     int32_t param_dtype = MA_PARAM_FP32;   // storage of parameters and gradients
 
-    // step-time staging (pinned host ring) and the per-device side stream of
-    // the overlapped AdamW group; guarded by mu
+    // step-time staging (pinned host ring) and the per-device side streams
+    // (the overlapped AdamW group, the second Newton-Schulz stream); guarded
+    // by mu
     struct Side {
         int device;
         void* stream;       // AdamW beside the Muon group
