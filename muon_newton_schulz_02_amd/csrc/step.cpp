@@ -430,6 +430,25 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     // concurrently with the Muon group and joined back at the end
     ma_plan::Side* side = nullptr;
     bool ns_joined = false;
+    // Whatever a forked side stream has queued is joined back into the
+    // caller's stream on every return, errors included (an unjoined fork
+    // would also invalidate an enclosing graph capture).
+    struct JoinGuard {
+        hipStream_t main = nullptr;
+        ma_plan::Side** side = nullptr;
+        bool adam = false, ns = false;
+        ~JoinGuard() {
+            if (!*side) return;
+            if (adam && hipEventRecord((hipEvent_t)(*side)->ev_join,
+                                       (hipStream_t)(*side)->stream) == hipSuccess)
+                (void)hipStreamWaitEvent(main, (hipEvent_t)(*side)->ev_join, 0);
+            if (ns && hipEventRecord((hipEvent_t)(*side)->ev_ns_join,
+                                     (hipStream_t)(*side)->ns_stream) == hipSuccess)
+                (void)hipStreamWaitEvent(main, (hipEvent_t)(*side)->ev_ns_join, 0);
+        }
+    } guard;
+    guard.main = st;
+    guard.side = &side;
     // (the chunk counter is an int: beyond 2^30 chunks run serially)
     const bool overlap =
         plan->overlap && n_adam > 0 && n_muon > 0 && plan->n_adam_chunks < (int64_t(1) << 30);
@@ -441,6 +460,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
             return hip_fail("hipEventRecord (fork)", e);
         if ((e = hipStreamWaitEvent(ss, (hipEvent_t)side->ev_fork, 0)) != hipSuccess)
             return hip_fail("hipStreamWaitEvent (fork)", e);
+        guard.adam = true;
         // one workgroup per CU: each of its waves shares a SIMD with a
         // Newton-Schulz GEMM wave (whose LDS and registers leave room for
         // exactly that) and streams AdamW chunks while the GEMMs run
@@ -489,6 +509,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
                 return hip_fail("hipEventRecord (ns fork)", e);
             if ((e = hipStreamWaitEvent(nss, (hipEvent_t)side->ev_ns_fork, 0)) != hipSuccess)
                 return hip_fail("hipStreamWaitEvent (ns fork)", e);
+            guard.ns = true;
         }
         for (int b0 = 0; b0 < nb; b0 += kNsStreams) {
             for (int it = 0; it < hp->muon_ns_steps; ++it) {
@@ -516,16 +537,22 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     } else if ((err = mark(3))) {
         return hip_fail("phase event", err);
     }
-    if (overlap && side) {
+    if (guard.adam) {
         // the chunks the side kernel has not claimed yet, at full occupancy
         err = launch_adamw_claim(d_adam, n_adam, plan->n_adam_chunks, sd, sc, plan->param_dtype,
                                  kFinishAdamGroups, 4, stream);
         if (err) return hip_fail("adamw", err);
     }
-    if (overlap && side && (e = hipStreamWaitEvent(st, (hipEvent_t)side->ev_join, 0)) != hipSuccess)
-        return hip_fail("hipStreamWaitEvent (join)", e);
-    if (ns_joined && (e = hipStreamWaitEvent(st, (hipEvent_t)side->ev_ns_join, 0)) != hipSuccess)
-        return hip_fail("hipStreamWaitEvent (ns join)", e);
+    if (guard.adam) {
+        if ((e = hipStreamWaitEvent(st, (hipEvent_t)side->ev_join, 0)) != hipSuccess)
+            return hip_fail("hipStreamWaitEvent (join)", e);
+        guard.adam = false;
+    }
+    if (ns_joined) {
+        if ((e = hipStreamWaitEvent(st, (hipEvent_t)side->ev_ns_join, 0)) != hipSuccess)
+            return hip_fail("hipStreamWaitEvent (ns join)", e);
+        guard.ns = false;
+    }
     if ((err = mark(4))) return hip_fail("phase event", err);
     if (!state->device_step) state->step = in.t_host;
     clear_error();
