@@ -3,13 +3,20 @@
 //
 // Order of work (OpenDM training-stack page: clip from the defaults table,
 // then the two optimizer groups of the Muon/AdamW hybrid section):
-//   1. one async copy of this step's descriptor tables into the workspace
+//   1. this step's descriptor tables copied into the workspace by a small
+//      kernel reading mapped pinned host memory (skipped with a device step
+//      counter while they are unchanged)
 //   2. clip norm partials over every trainable gradient, then the clip factor
-//   3. AdamW over the AdamW group
+//      and the step's rates
+//   3. AdamW over the AdamW group (or, with overlap_groups, forked onto a
+//      side stream after step 4 and finished after step 5)
 //   4. Muon momentum + unnormalised operands + ||u||^2 partials, then the
 //      per-matrix normalising factor
-//   5. ns_steps x (GRAM, POLY, XUPD), the first GRAM and XUPD applying the
-//      normalising factor; the last XUPD writes the update.
+//   5. per Newton-Schulz batch, ns_steps x (GRAM, POLY, XUPD), the first GRAM
+//      and XUPD applying the normalising factor and the last XUPD writing the
+//      update; batches alternate between the caller's stream and a side
+//      stream
+// Side streams are joined back into the caller's stream before returning.
 // Nothing is launched before every argument has been checked.
 
 #include <hip/hip_runtime.h>
