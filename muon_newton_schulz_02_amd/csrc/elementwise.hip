@@ -481,12 +481,14 @@ __device__ __forceinline__ void write_operands_fp32(const MuonMat& d,
 // homogeneous in X.
 __global__ __launch_bounds__(kThreads) void k_muon_prep(const MuonMat* __restrict__ tab, int n_tab,
                                                         const StepDev* __restrict__ sd,
-                                                        MomArgs a, float* __restrict__ partials) {
+                                                        MomArgs a, float* __restrict__ partials,
+                                                        int batch) {
     constexpr int TS = kOrientTile;
     __shared__ float tile[TS][TS + 1];
     __shared__ float smem[kThreads / 64];
     const int64_t blk = blockIdx.x;
     const MuonMat& d = tab[find_matrix(tab, n_tab, blk)];
+    if (batch >= 0 && d.ns_batch != batch) return;   // uniform over the workgroup
     const int64_t local = blk - d.orient_begin;
     const int tiles_c = d.C / TS;
     const int i0 = (int)(local / tiles_c) * TS, j0 = (int)(local % tiles_c) * TS;
@@ -553,9 +555,10 @@ constexpr double kNormLo = 0x1p-40, kNormHi = 0x1p40;
 __global__ __launch_bounds__(256) void k_muon_scale(const MuonMat* __restrict__ tab,
                                                     const float* __restrict__ partials,
                                                     float ns_eps, float* __restrict__ ns_scale,
-                                                    float* __restrict__ pre_scale) {
+                                                    float* __restrict__ pre_scale, int batch) {
     __shared__ double smem[256 / 64];
     const MuonMat& d = tab[blockIdx.x];
+    if (batch >= 0 && d.ns_batch != batch) return;   // uniform over the workgroup
     const int64_t n_tiles = (int64_t)(d.R / kOrientTile) * (d.C / kOrientTile);
     double acc = 0.0;
     for (int64_t i = threadIdx.x; i < n_tiles; i += blockDim.x)
@@ -581,11 +584,14 @@ __global__ __launch_bounds__(256) void k_muon_scale(const MuonMat* __restrict__ 
 constexpr int kRescaleSplit = 16;
 
 __global__ __launch_bounds__(kThreads) void k_operand_rescale(const MuonMat* __restrict__ tab,
-                                                              const float* __restrict__ pre_scale) {
+                                                              const float* __restrict__ pre_scale,
+                                                              int batch) {
     const int k = blockIdx.x / kRescaleSplit, part = blockIdx.x % kRescaleSplit;
+    const MuonMat& d = tab[k];
+    // pre_scale of another batch's matrix belongs to another launch
+    if (batch >= 0 && d.ns_batch != batch) return;
     const float f = pre_scale[k];
     if (f == 0.f) return;
-    const MuonMat& d = tab[k];
     const int64_t n = (int64_t)d.R * d.C;
     const int64_t stride = (int64_t)kRescaleSplit * kThreads;
     if (d.op_bf16) {
@@ -668,23 +674,23 @@ int launch_adamw_claim(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks, S
 }
 
 int launch_muon_prep(const MuonMat* tab, int32_t n_tab, int64_t n_tiles, const StepDev* sd,
-                     const StepScalars& s, float* partials, void* stream) {
+                     const StepScalars& s, float* partials, int32_t batch, void* stream) {
     if (n_tiles == 0) return (int)hipSuccess;
     MomArgs a{s.mu, s.nesterov};
     hipLaunchKernelGGL(k_muon_prep, dim3((unsigned)n_tiles), dim3(kThreads), 0, (hipStream_t)stream,
-                       tab, n_tab, sd, a, partials);
+                       tab, n_tab, sd, a, partials, (int)batch);
     return (int)hipGetLastError();
 }
 
 int launch_muon_scale(const MuonMat* tab, int32_t n_tab, const float* partials, float ns_eps,
-                      float* ns_scale, float* pre_scale, void* stream) {
+                      float* ns_scale, float* pre_scale, int32_t batch, void* stream) {
     if (n_tab == 0) return (int)hipSuccess;
     hipLaunchKernelGGL(k_muon_scale, dim3((unsigned)n_tab), dim3(256), 0, (hipStream_t)stream, tab,
-                       partials, ns_eps, ns_scale, pre_scale);
+                       partials, ns_eps, ns_scale, pre_scale, (int)batch);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     hipLaunchKernelGGL(k_operand_rescale, dim3((unsigned)n_tab * kRescaleSplit), dim3(kThreads), 0,
-                       (hipStream_t)stream, tab, pre_scale);
+                       (hipStream_t)stream, tab, pre_scale, (int)batch);
     return (int)hipGetLastError();
 }
 

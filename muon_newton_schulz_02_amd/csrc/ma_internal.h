@@ -88,6 +88,7 @@ struct MuonMat {
     float    shape_scale;          // lr_shape_scale: the update is muon_lr * this (StepDev)
     int32_t  op_bf16;              // NS operands are bf16 (else fp32)
     int32_t  p_bf16;               // p and g stored as bf16 (else float)
+    int32_t  ns_batch;             // its Newton-Schulz batch
 };
 
 // One GEMM tile of an NS phase: matrix index and tile coordinates.
@@ -256,13 +257,15 @@ int launch_adamw_claim(const AdamTensor* tab, int32_t n_tab, int64_t n_chunks,
                        int waves, void* stream);
 // Momentum/Nesterov and the unnormalised Newton-Schulz input operands, one
 // workgroup per 64 x 64 operand tile, with per-tile partials of ||u||_F^2.
+// batch >= 0 restricts both passes to the matrices of that Newton-Schulz
+// batch (the other workgroups return at once); -1 covers every matrix.
 int launch_muon_prep(const MuonMat* tab, int32_t n_tab, int64_t n_tiles, const StepDev* sd,
-                     const StepScalars& s, float* partials, void* stream);
+                     const StepScalars& s, float* partials, int32_t batch, void* stream);
 // Per matrix, the normalising factor 1 / (||u||_F + eps): into ns_scale
 // (applied by the first Newton-Schulz launches), or, for a norm outside
 // [2^-40, 2^40], applied to the operands in place (ns_scale = 1).
 int launch_muon_scale(const MuonMat* tab, int32_t n_tab, const float* partials, float ns_eps,
-                      float* ns_scale, float* pre_scale, void* stream);
+                      float* ns_scale, float* pre_scale, int32_t batch, void* stream);
 // phase 1 = Gram, 2 = polynomial, 3 = X update (the parameter update when
 // `last`); group = kGroupBf16 / kGroupFp32 selects the operand type.
 // `ns_scale`: the per-matrix normalising factor, applied on iteration 0;

@@ -352,6 +352,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
                            ? 1
                            : 0;
             d.shape_scale = e.lr_shape_scale;
+            d.ns_batch = L.ns_batch[k];
             d.op_bf16 = L.op_group[k] == kGroupBf16 ? 1 : 0;
             d.p_bf16 = bf16 ? 1 : 0;
         }
@@ -489,12 +490,25 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         if ((err = fork_adamw()) != MA_OK) return err;
     }
     if (n_muon > 0) {
-        err = launch_muon_prep(d_muon, n_muon, plan->n_orient_tiles, sd, sc, muon_partials,
-                               stream);
-        if (err) return hip_fail("muon prep", err);
-        err = launch_muon_scale(d_muon, n_muon, muon_partials, sc.ns_eps, muon_scales,
-                                muon_prescales, stream);
-        if (err) return hip_fail("muon scale", err);
+        static_assert(kNsStreams == 2, "one caller stream and one side stream");
+        const int nb = (int)L.ns_batches.size();
+        const bool split = nb > 1;
+        // With two batches and nothing beside them, the second batch's
+        // momentum/normalise pass (HBM-bound) runs on the side stream while
+        // the first batch's Gram launches (matrix-core bound) start.  A
+        // profiled step keeps the passes whole, so each phase interval holds
+        // its own kernels only.
+        const bool pipelined = split && nb == kNsStreams && !overlap && !phase_events;
+        auto prep = [&](int32_t batch, hipStream_t q) -> int {
+            int er = launch_muon_prep(d_muon, n_muon, plan->n_orient_tiles, sd, sc, muon_partials,
+                                      batch, q);
+            if (er) return hip_fail("muon prep", er);
+            er = launch_muon_scale(d_muon, n_muon, muon_partials, sc.ns_eps, muon_scales,
+                                   muon_prescales, batch, q);
+            if (er) return hip_fail("muon scale", er);
+            return MA_OK;
+        };
+        if ((err = prep(pipelined ? 0 : -1, st)) != MA_OK) return err;
         if (overlap && kForkAfterPrep && (err = fork_adamw()) != MA_OK) return err;
         if ((err = mark(3))) return hip_fail("phase event", err);
         // The matrices run in batches of about equal GEMM work, each through
@@ -502,9 +516,6 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         // caller's stream and a side stream: one batch's launch tail (the last
         // tiles of a phase, when most CUs already idle) overlaps the other
         // stream's next launch.
-        static_assert(kNsStreams == 2, "one caller stream and one side stream");
-        const int nb = (int)L.ns_batches.size();
-        const bool split = nb > 1;
         hipStream_t nss = nullptr;
         if (split) {
             if (!side) {
@@ -517,6 +528,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
             if ((e = hipStreamWaitEvent(nss, (hipEvent_t)side->ev_ns_fork, 0)) != hipSuccess)
                 return hip_fail("hipStreamWaitEvent (ns fork)", e);
             guard.ns = true;
+            if (pipelined && (err = prep(1, nss)) != MA_OK) return err;
         }
         for (int b0 = 0; b0 < nb; b0 += kNsStreams) {
             for (int it = 0; it < hp->muon_ns_steps; ++it) {
