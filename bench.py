@@ -166,11 +166,11 @@ def percentile(xs, q: float) -> float:
 
 
 def cpu_baseline(w, hp_overrides) -> dict:
-    """The oracle, as it stands, on a bounded sample of the workload: one of
-    the action-expert layers (7 Muon matrices) and one of the VLM layers (9
-    AdamW tensors) of the full hybrid table, each timed whole (clip norm of
-    the sampled gradients + updates) and scaled by the layer counts to the
-    whole table's params/s."""
+    """The oracle, as it stands, on a bounded sample of the workload: the
+    first k_ae action-expert layers (7 Muon matrices each) and the first
+    k_vlm VLM layers (9 AdamW tensors each) of the full hybrid table, each
+    set timed whole (clip norm of the sampled gradients + updates) and
+    scaled by the layer counts to the whole table's params/s."""
     import numpy as np
     import oracle as O
     import workloads as W
@@ -181,7 +181,7 @@ def cpu_baseline(w, hp_overrides) -> dict:
         setattr(hp, k, v)
     names = w.names
     as_stored = O.bf16_round if w.param_storage == "bf16" else (lambda x: x)
-    k_ae, k_vlm = 4, 6   # sampled layers of each kind
+    k_ae, k_vlm = 5, 8   # sampled layers of each kind (about 10-15 s on 16 host cores)
     ae = [i for i, n in enumerate(names)
           if n.startswith("action_expert.layers.") and int(n.split(".")[2]) < k_ae]
     vlm = [i for i, n in enumerate(names)
