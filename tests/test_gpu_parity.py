@@ -497,12 +497,31 @@ def test_overlapped_groups_match_serial_bitwise():
         np.testing.assert_array_equal(a, b)
 
 
-def test_batched_newton_schulz_matches_serial_bitwise():
-    """The 126 full-size action-expert matrices plus one AdamW tensor: with
-    the AdamW group beside them, Newton-Schulz runs in several batches over
-    two streams; every Muon result equals the serial step's bit for bit."""
+def _three_wide_matrices():
+    # 3 x 134 MB of bf16 operands: three batches beside AdamW, the last one
+    # without a partner on the other stream
+    params = [W.ParamSpec("action_expert.layers.%d.mlp.up_proj.weight" % i, (8192, 4096))
+              for i in range(3)]
+    params.append(W.ParamSpec("vlm.model.norm.weight", (2048,)))
+    return W.Workload("three_wide", seed=11, steps=1, ns_precision="bf16", params=params,
+                      grad_std=1e-3)
+
+
+def _ae18_plus_norm():
     w = W.ae18_muon_bf16()
     w.params.append(W.ParamSpec("vlm.model.norm.weight", (2048,)))
+    return w
+
+
+@pytest.mark.parametrize("make", [_ae18_plus_norm, _three_wide_matrices],
+                         ids=["ae18_eight_batches", "three_batches"])
+def test_batched_newton_schulz_matches_serial_bitwise(make):
+    """Full-size Muon matrices plus one AdamW tensor: with the AdamW group
+    beside them, Newton-Schulz runs in several batches over two streams
+    (eight for the 126 action-expert matrices, an odd three for three
+    8192 x 4096 ones); every Muon result equals the serial step's bit for
+    bit."""
+    w = make()
     hp = H.oracle_hparams(w)
     keys = [i for i, p in enumerate(w.params) if p.trainable]
     ref = None
