@@ -65,8 +65,9 @@ def test_spectral_map_is_the_iteration_on_singular_values(shape, coeffs):
 def test_phi5_values_distinguish_step_count():
     """ns_steps = 5 (hyperparameter table of the page).  The fixed point of
     the map is not reached, so 4, 5 and 6 steps give visibly different gains
-    on a unit singular value.  Numbers are the scalar compositions, recorded
-    at survey time for both triples."""
+    on a unit singular value.  Numbers are the scalar compositions of each
+    quintic, evaluated once in double precision by a script separate from
+    the oracle, for both triples."""
     d, p = O.DEFAULT_NS_COEFFS, O.PUBLISHED_NS_COEFFS
     assert _phi(1.0, d, 5) == pytest.approx(0.984131, abs=2e-6)
     assert _phi(1.0, d, 4) == pytest.approx(0.996466, abs=2e-6)
