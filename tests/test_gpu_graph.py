@@ -30,8 +30,9 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _workload():
+def _workload(storage="fp32"):
     w = H.ragged_workload()
+    w.param_storage = storage
     # an AdamW matrix large enough that the overlapped launch has chunks to claim
     w.params.append(W.ParamSpec("vlm.model.layers.0.mlp.up_proj.weight", (512, 300)))
     return w
@@ -93,13 +94,13 @@ def test_device_counter_matches_host_counter_bitwise(overlap):
         _assert_same(a, b, "step %d" % t)
 
 
-@pytest.mark.parametrize("overlap", [False, True])
-def test_graph_replays_match_eager_steps(overlap):
+@pytest.mark.parametrize("overlap,storage", [(False, "fp32"), (True, "fp32"), (True, "bf16")])
+def test_graph_replays_match_eager_steps(overlap, storage):
     """Step 1 eager, then one step captured in a graph and replayed as steps
     2..5, with eager work (new gradients, unrelated kernels, host syncs)
     between replays: after every replay the state equals that of eager steps
-    on the same inputs, bit for bit."""
-    w = _workload()
+    on the same inputs, bit for bit (float32 or bfloat16 parameters)."""
+    w = _workload(storage)
     hp = _hparams(w)
     eager = _setup(w, hp, overlap, True)
     ref = []
