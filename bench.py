@@ -158,6 +158,42 @@ def gemm_tflops(torch, dtype, n: int = 8192, reps: int = 10) -> float:
     return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
 
 
+def library_ns_ms(torch, shapes, ns_steps: int, coeffs, dtype, reps: int = 3) -> float:
+    """The same Newton-Schulz iterations written as plain torch batched
+    matrix products (hipBLASLt) over the same canonical shapes, one bmm
+    batch per shape bucket, timed with events: a library implementation of
+    the phase on identical work, for comparison only.  X X^T takes a
+    contiguous copy of X^T (torch's batched bf16 product with a transposed
+    right operand is avoided on this platform); operands are random and
+    normalised, the arithmetic is not checked here."""
+    a, b, c = (float(x) for x in coeffs)
+    buckets = {}
+    for m, n in shapes:
+        r, cc = min(m, n), max(m, n)
+        buckets[(r, cc)] = buckets.get((r, cc), 0) + 1
+    xs = [torch.randn((cnt, r, cc), device="cuda").div_(math.sqrt(r * cc)).to(dtype)
+          for (r, cc), cnt in buckets.items()]
+
+    def one():
+        for k, x in enumerate(xs):
+            for _ in range(ns_steps):
+                at = torch.bmm(x, x.transpose(1, 2).contiguous())
+                bm = torch.bmm(at, at).mul_(c).add_(at, alpha=b)
+                x = torch.bmm(bm, x).add_(x, alpha=a)
+            xs[k] = x
+
+    one()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        one()
+    e1.record()
+    torch.cuda.synchronize()
+    del xs
+    return e0.elapsed_time(e1) / reps
+
+
 def percentile(xs, q: float) -> float:
     xs = sorted(xs)
     k = (len(xs) - 1) * q
@@ -403,6 +439,9 @@ def main():
     gemm = gemm_tflops(torch, torch.bfloat16 if w.ns_precision == "bf16" else torch.float32) \
         if n_muon > 0 else None
     flops = ns_flops(muon_shapes, hp.muon_ns_steps)
+    lib_ms = (library_ns_ms(torch, muon_shapes, hp.muon_ns_steps, hp.ns_coeffs,
+                            torch.bfloat16 if w.ns_precision == "bf16" else torch.float32)
+              if n_muon > 0 else None)
     ns_peak = PEAK_BF16_TFLOPS if w.ns_precision == "bf16" else PEAK_FP32_TFLOPS
     ns_tflops = flops / (mean["newton_schulz"] * 1e-3) / 1e12 if mean["newton_schulz"] > 0 else 0.0
     ns_exec_tflops = (ns_executed_flops(muon_shapes, hp.muon_ns_steps) /
@@ -460,6 +499,8 @@ def main():
         "ns_tflops": ns_tflops,
         "ns_mfma_frac": ns_tflops / ns_peak,
         "ns_executed_tflops": ns_exec_tflops,
+        "ns_library_ms": lib_ms,
+        "ns_library_tflops": flops / (lib_ms * 1e-3) / 1e12 if lib_ms else None,
         "gemm_tflops_measured": gemm,
         "ns_frac_of_gemm": (ns_tflops / gemm) if gemm else None,
         "adamw_gbps": adam_gbps,
