@@ -38,6 +38,8 @@ constexpr int64_t kBf16MinRows = 16;
 // XCDs of an MI355X: consecutive workgroups of a launch are dispatched to
 // XCDs round-robin, and each XCD has its own L2.
 constexpr int kXcds = 8;
+constexpr int kCus = 256;          // compute units of an MI355X
+constexpr int kGramMaxSlices = 4;  // most slices of a split Gram reduction
 // Newton-Schulz runs the Muon matrices in batches, each batch through all of
 // its iterations; consecutive batches alternate between this many streams
 // (the caller's and a library-owned one), so the tail of one batch's launch
@@ -89,11 +91,14 @@ struct MuonMat {
     int32_t  op_bf16;              // NS operands are bf16 (else fp32)
     int32_t  p_bf16;               // p and g stored as bf16 (else float)
     int32_t  ns_batch;             // its Newton-Schulz batch
+    int32_t  gram_ks;              // Gram reduction split into this many slices (fp32 only)
+    uint64_t apart;                // gram_ks - 1 fp32 R x R partial Grams (slices 1..)
 };
 
 // One GEMM tile of an NS phase: matrix index and tile coordinates.
 struct GemmTile {
     int32_t mat, tm, tn, k;        // k = reduction length (padded), for ordering
+    int32_t slice;                 // Gram with a split reduction: which slice
 };
 
 // ------------------------------------------------------------ workspace --
@@ -108,6 +113,7 @@ struct Layout {
     struct NsBatch {
         std::vector<GemmTile> tiles[3][2];           // [phase - 1][operand group], cost-ordered
         size_t off[3][2] = {};                       // their offsets in the workspace
+        bool gram_split = false;                     // fp32 Gram partials to sum after the launch
     };
     std::vector<NsBatch> ns_batches;
     std::vector<int32_t> ns_batch;                   // per Muon matrix: its batch
@@ -118,6 +124,8 @@ struct Layout {
     size_t muon_prescale_off = 0;                    // float[n_muon]: operand rescale (0: none)
     size_t ns_off = 0;                               // start of per-matrix NS buffers
     std::vector<size_t> x0, x1, lo0, lo1, xt0, xt1, a, b;  // per Muon matrix (0: unused)
+    std::vector<int32_t> gram_ks;                    // per Muon matrix: Gram reduction slices
+    std::vector<size_t> apart;                       // per Muon matrix: partial Grams (0: none)
     size_t total = 0;
 };
 
@@ -266,6 +274,8 @@ int launch_muon_prep(const MuonMat* tab, int32_t n_tab, int64_t n_tiles, const S
 // [2^-40, 2^40], applied to the operands in place (ns_scale = 1).
 int launch_muon_scale(const MuonMat* tab, int32_t n_tab, const float* partials, float ns_eps,
                       float* ns_scale, float* pre_scale, int32_t batch, void* stream);
+// After a batch's fp32 Gram launch: A += its split reductions' partial Grams.
+int launch_gram_reduce(const MuonMat* tab, int32_t n_tab, int32_t batch, void* stream);
 // phase 1 = Gram, 2 = polynomial, 3 = X update (the parameter update when
 // `last`); group = kGroupBf16 / kGroupFp32 selects the operand type.
 // `ns_scale`: the per-matrix normalising factor, applied on iteration 0;

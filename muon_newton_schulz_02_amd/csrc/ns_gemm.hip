@@ -804,12 +804,22 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
     const char* P;
     const char* Q;
     int64_t ldp, ldq;  // bytes
+    int64_t shift = 0;  // bytes from the operand start to this slice's first column
     int K, rows_p, rows_q;
     if (EPI == EPI_GRAM) {
         P = Q = reinterpret_cast<const char*>(BF ? d.x[cur] : d.x[0]);
         ldp = ldq = (int64_t)d.C * sizeof(T);
         K = d.C;
         rows_p = rows_q = d.R;
+        if (d.gram_ks > 1) {
+            // slice tile.slice of a split reduction: columns [slice K, (slice + 1) K)
+            // of X, which the stage copies address from a shifted base
+            K = d.C / d.gram_ks;
+            const int64_t k0 = (int64_t)tile.slice * K;
+            shift = BF ? (k0 / 32) * 2048 : k0 * (int64_t)sizeof(T);
+            P += shift;
+            Q += shift;
+        }
     } else if (EPI == EPI_POLY) {
         P = Q = reinterpret_cast<const char*>(d.a);
         ldp = ldq = (int64_t)d.R * sizeof(T);
@@ -833,8 +843,8 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
     const int m0 = tile.tm * 256, n0 = tile.tn * 256;
     const int nk = K / KE;  // a multiple of 8: K is padded to 256
 
-    const u32x4 rp = make_rsrc(P, (int64_t)rows_p * ldp);
-    const u32x4 rq = make_rsrc(Q, (int64_t)rows_q * ldq);
+    const u32x4 rp = make_rsrc(P, (int64_t)rows_p * ldp - shift);
+    const u32x4 rq = make_rsrc(Q, (int64_t)rows_q * ldq - shift);
     Addr ad;
     {
         const uint32_t c = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
@@ -930,7 +940,10 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
     T* out_direct = nullptr;
     int64_t ld_direct = 0;
     if (EPI == EPI_GRAM) {
-        out_direct = reinterpret_cast<T*>(d.a);
+        // a split reduction's slices 1.. write partial Grams, added to A later
+        out_direct = reinterpret_cast<T*>(
+            tile.slice == 0 ? d.a
+                            : d.apart + (uint64_t)(tile.slice - 1) * d.R * d.R * sizeof(T));
         ld_direct = d.R;
     } else if (EPI == EPI_POLY) {
         out_direct = reinterpret_cast<T*>(d.b);
@@ -1008,7 +1021,33 @@ int launch_k(NsKernel k, const MuonMat* tab, const GemmTile* tiles, int64_t n, c
     return (int)hipGetLastError();
 }
 
+// A += the partial Grams of a split reduction, in slice order, for the fp32
+// matrices of one Newton-Schulz batch (kReduceSplit workgroups per matrix,
+// those of other matrices return at once).
+constexpr int kReduceSplit = 16;
+
+__global__ __launch_bounds__(256) void k_gram_reduce(const MuonMat* __restrict__ tab, int batch) {
+    const int k = blockIdx.x / kReduceSplit, part = blockIdx.x % kReduceSplit;
+    const MuonMat& d = tab[k];
+    if (d.gram_ks <= 1 || d.op_bf16 || d.ns_batch != batch) return;
+    float* a = reinterpret_cast<float*>(d.a);
+    const float* pa = reinterpret_cast<const float*>(d.apart);
+    const int64_t n = (int64_t)d.R * d.R;
+    for (int64_t i = (int64_t)part * 256 + threadIdx.x; i < n; i += (int64_t)kReduceSplit * 256) {
+        float v = a[i];
+        for (int sl = 1; sl < d.gram_ks; ++sl) v += pa[(int64_t)(sl - 1) * n + i];
+        a[i] = v;
+    }
+}
+
 }  // namespace
+
+int launch_gram_reduce(const MuonMat* tab, int32_t n_tab, int32_t batch, void* stream) {
+    if (n_tab == 0) return (int)hipSuccess;
+    hipLaunchKernelGGL(k_gram_reduce, dim3((unsigned)n_tab * kReduceSplit), dim3(256), 0,
+                       (hipStream_t)stream, tab, (int)batch);
+    return (int)hipGetLastError();
+}
 
 int launch_ns_phase(int phase, int32_t group, const MuonMat* tab, const GemmTile* tiles,
                     int64_t n_tiles, int iter, int last, const StepScalars& s,

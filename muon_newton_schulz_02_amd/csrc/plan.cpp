@@ -173,7 +173,7 @@ void schedule_tiles(std::vector<GemmTile>& t) {
     t.clear();
     for (size_t j = 0; j < longest; ++j)
         for (int x = 0; x < kXcds; ++x)
-            t.push_back(j < lists[x].size() ? lists[x][j] : GemmTile{-1, 0, 0, 0});
+            t.push_back(j < lists[x].size() ? lists[x][j] : GemmTile{-1, 0, 0, 0, 0});
 }
 
 void build_tables(ma_plan* p) {
@@ -248,22 +248,53 @@ void build_layout(ma_plan* p, int32_t precision) {
         bload[best] += cost[k];
     }
     L.ns_batches.assign(nm ? nb : 0, Layout::NsBatch());
+    // A batch whose fp32 Gram launch has fewer tiles than the GPU has CUs
+    // (small matrices, where one long-reduction tile per matrix would leave
+    // most CUs idle) splits each of those Gram reductions into up to
+    // kGramMaxSlices slices of whole 256-column blocks: slice 0 writes A, the
+    // others fp32 partials that a reduction kernel adds to A in slice order.
+    // bf16 operands keep whole reductions (their A is rounded once, from
+    // the fp32 sum).
+    L.gram_ks.assign(nm, 1);
+    {
+        std::vector<int64_t> f32_gram(nb, 0);
+        for (size_t k = 0; k < nm; ++k) {
+            if (L.op_group[k] != kGroupFp32) continue;
+            const auto& e = p->entries[p->muon_ids[k]];
+            const int64_t TR = round_up(e.r, kNsPad) / kGemmTile;
+            f32_gram[L.ns_batch[k]] += TR * (TR + 1) / 2;
+        }
+        for (size_t k = 0; k < nm; ++k) {
+            if (L.op_group[k] != kGroupFp32 || f32_gram[L.ns_batch[k]] >= kCus) continue;
+            const auto& e = p->entries[p->muon_ids[k]];
+            const int64_t blocks = round_up(e.c, kNsPad) / kGemmTile;
+            int32_t ks = 1;
+            for (int32_t d = 2; d <= kGramMaxSlices; ++d)
+                if (blocks % d == 0) ks = d;
+            L.gram_ks[k] = ks;
+            if (ks > 1) L.ns_batches[L.ns_batch[k]].gram_split = true;
+        }
+    }
     for (size_t k = 0; k < nm; ++k) {
         const auto& e = p->entries[p->muon_ids[k]];
         const int32_t grp = L.op_group[k];
         auto& t = L.ns_batches[L.ns_batch[k]].tiles;
         const int64_t R = round_up(e.r, kNsPad), C = round_up(e.c, kNsPad);
         const int32_t TR = (int32_t)(R / kGemmTile), TC = (int32_t)(C / kGemmTile);
+        const int32_t ks = L.gram_ks[k];
+        for (int32_t sl = 0; sl < ks; ++sl)
+            for (int32_t i = 0; i < TR; ++i)
+                for (int32_t j = i; j < TR; ++j)
+                    t[0][grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)(C / ks), sl});
         for (int32_t i = 0; i < TR; ++i)
-            for (int32_t j = i; j < TR; ++j) {
-                t[0][grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)C});
-                t[1][grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R});
-            }
+            for (int32_t j = i; j < TR; ++j)
+                t[1][grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R, 0});
         // column-major: the tiles of one column block (all readers of that
         // X panel) are consecutive, so the tiles an XCD runs together read
         // each panel once from HBM while the r x r B stays in its L2
         for (int32_t j = 0; j < TC; ++j)
-            for (int32_t i = 0; i < TR; ++i) t[2][grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R});
+            for (int32_t i = 0; i < TR; ++i)
+                t[2][grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R, 0});
     }
     for (auto& bt : L.ns_batches)
         for (auto& ph : bt.tiles)
@@ -324,6 +355,7 @@ void build_layout(ma_plan* p, int32_t precision) {
         off = align256(off + R * R * esz);
         L.b.push_back(off);
         off = align256(off + R * R * esz);
+        L.apart.push_back(L.gram_ks[k] > 1 ? take(R * R * 4 * (size_t)(L.gram_ks[k] - 1)) : 0);
     }
     L.total = std::max<size_t>(off, 256);
 }

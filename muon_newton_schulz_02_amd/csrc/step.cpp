@@ -353,6 +353,8 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
                            : 0;
             d.shape_scale = e.lr_shape_scale;
             d.ns_batch = L.ns_batch[k];
+            d.gram_ks = L.gram_ks[k];
+            d.apart = L.apart[k] ? reinterpret_cast<uint64_t>(base + L.apart[k]) : 0;
             d.op_bf16 = L.op_group[k] == kGroupBf16 ? 1 : 0;
             d.p_bf16 = bf16 ? 1 : 0;
         }
@@ -537,12 +539,16 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
                     for (int q = 0; q < kNsStreams && b0 + q < nb; ++q) {
                         const auto& bt = L.ns_batches[b0 + q];
                         for (int g = 0; g < 2; ++g) {
+                            void* qs = q == 0 ? stream : (void*)nss;
                             err = launch_ns_phase(
                                 ph + 1, g, d_muon,
                                 reinterpret_cast<const GemmTile*>(base + bt.off[ph][g]),
                                 (int64_t)bt.tiles[ph][g].size(), it, last, sc, muon_scales, sd,
-                                q == 0 ? stream : (void*)nss);
+                                qs);
                             if (err) return hip_fail("newton-schulz", err);
+                            if (ph == 0 && g == kGroupFp32 && bt.gram_split &&
+                                (err = launch_gram_reduce(d_muon, n_muon, b0 + q, qs)))
+                                return hip_fail("gram reduce", err);
                         }
                     }
                 }
