@@ -7,6 +7,9 @@
 //   XUPD  X = a X + B X                  (r x c, K = r)
 // and on the last step XUPD is replaced by FINAL, whose epilogue writes the
 // parameter update p = p * decay - rate * X back in the stored orientation.
+// A launch with fewer fp32 Gram tiles than CUs runs each of those Gram
+// reductions as up to four column slices (slice 0 writes A, the others
+// partial Grams that k_gram_reduce adds to A in slice order).
 //
 // MFMA operands are read from LDS as rows whose reduction index is
 // contiguous.  For GRAM and POLY both operands are such rows of a row-major
