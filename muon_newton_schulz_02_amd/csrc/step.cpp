@@ -538,18 +538,19 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
                 for (int ph = 0; ph < 3; ++ph) {
                     for (int q = 0; q < kNsStreams && b0 + q < nb; ++q) {
                         const auto& bt = L.ns_batches[b0 + q];
+                        void* qs = q == 0 ? stream : (void*)nss;
                         for (int g = 0; g < 2; ++g) {
-                            void* qs = q == 0 ? stream : (void*)nss;
                             err = launch_ns_phase(
                                 ph + 1, g, d_muon,
                                 reinterpret_cast<const GemmTile*>(base + bt.off[ph][g]),
                                 (int64_t)bt.tiles[ph][g].size(), it, last, sc, muon_scales, sd,
                                 qs);
                             if (err) return hip_fail("newton-schulz", err);
-                            if (ph == 0 && g == kGroupFp32 && bt.gram_split &&
-                                (err = launch_gram_reduce(d_muon, n_muon, b0 + q, qs)))
-                                return hip_fail("gram reduce", err);
                         }
+                        // the Grams of split reductions, before the square reads them
+                        if (ph == 0 && bt.gram_split &&
+                            (err = launch_gram_reduce(d_muon, n_muon, b0 + q, qs)))
+                            return hip_fail("gram reduce", err);
                     }
                 }
             }
