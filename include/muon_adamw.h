@@ -266,7 +266,10 @@ int muon_adamw_workspace_size(const ma_plan* plan, int32_t ns_precision, size_t*
  * workspace / ws_bytes: device scratch of at least muon_adamw_workspace_size
  *   bytes for hp->ns_precision, 256-byte aligned.
  * Errors (nothing launched): INVALID_ARG (null plan/state/hp, a required
- * pointer NULL, hp values out of range), UNSUPPORTED (ns_steps < 1 or > 64,
+ * pointer NULL, hp values out of range, or two of the buffers the step
+ * touches overlapping: parameters, gradients, states, update outputs,
+ * grad_norm_out, device_step and the workspace must be pairwise disjoint,
+ * judged from their addresses and sizes), UNSUPPORTED (ns_steps < 1 or > 64,
  * unknown precision), WORKSPACE (null, too small, misaligned), CAPTURE (the
  * stream is capturing and the descriptor tables would have to be uploaded:
  * run one eager step with the same pointers and workspace first, with

@@ -246,6 +246,51 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         set_error("muon_adamw_step: workspace must be 256-byte aligned");
         return MA_ERR_WORKSPACE;
     }
+    // Every buffer the step writes or reads must be disjoint from every other
+    // (a parameter passed again as its gradient, a state shared by two
+    // entries, a workspace over a tensor): such aliasing would give wrong
+    // results with no error, so it is refused here, from the pointers alone.
+    {
+        struct Span {
+            uintptr_t lo, hi;
+            int32_t id;
+            const char* what;
+        };
+        std::vector<Span> spans;
+        const size_t esz = plan->param_dtype == MA_PARAM_BF16 ? 2 : 4;
+        auto add = [&](const void* ptr, size_t bytes, int32_t id, const char* what) {
+            if (!ptr) return;
+            const uintptr_t a = reinterpret_cast<uintptr_t>(ptr);
+            spans.push_back(Span{a, a + bytes, id, what});
+        };
+        for (int32_t id : plan->train_ids) {
+            const size_t n = (size_t)plan->entries[id].numel;
+            add(params[id], n * esz, id, "parameter");
+            add(grads[id], n * esz, id, "gradient");
+        }
+        for (int32_t id : plan->muon_ids) {
+            const size_t n = (size_t)plan->entries[id].numel;
+            add(state->muon_momentum[id], n * 4, id, "momentum");
+            if (muon_update_out) add(muon_update_out[id], n * 4, id, "update output");
+        }
+        for (int32_t id : plan->adam_ids) {
+            const size_t n = (size_t)plan->entries[id].numel;
+            add(state->adam_m[id], n * 4, id, "adam_m");
+            add(state->adam_v[id], n * 4, id, "adam_v");
+        }
+        add(workspace, L.total, -1, "workspace");
+        add(grad_norm_out, 4, -1, "grad_norm_out");
+        add(state->device_step, 8, -1, "device_step");
+        std::sort(spans.begin(), spans.end(),
+                  [](const Span& x, const Span& y) { return x.lo < y.lo; });
+        for (size_t i = 1; i < spans.size(); ++i) {
+            if (spans[i].lo < spans[i - 1].hi) {
+                set_error("muon_adamw_step: %s of entry %d overlaps %s of entry %d",
+                          spans[i].what, spans[i].id, spans[i - 1].what, spans[i - 1].id);
+                return MA_ERR_INVALID_ARG;
+            }
+        }
+    }
 
     // -------------------------------------------------------- scalars ----
     // step-dependent values are formed on the device by the clip finaliser

@@ -203,6 +203,45 @@ def test_step_argument_errors_launch_nothing(lib):
     assert st.step == 0
 
 
+def test_step_refuses_overlapping_buffers(lib):
+    """Aliased buffers (a parameter passed again as its gradient, moments
+    that share memory, a workspace over a tensor) are refused from the
+    pointers alone, before any HIP call; only overlapping cases are tried
+    here, since a disjoint set would go on to launch."""
+    plan = M.muon_adamw_plan(_table_small())
+    ws_need = M.muon_adamw_workspace_size(plan, M.MA_NS_BF16)
+    n0 = M.muon_adamw_plan_entry(plan, 0)["m"] * M.muon_adamw_plan_entry(plan, 0)["n"]
+    base = 1 << 40
+    gap = 1 << 30
+
+    def addr(k):
+        return base + k * gap
+
+    def run(params, grads, mom, am, av, ws):
+        st = M.State(3)
+        st.muon_momentum[0] = mom
+        st.adam_m[1] = am
+        st.adam_v[1] = av
+        with pytest.raises(M.MuonAdamWError) as e:
+            M.muon_adamw_step(plan, params, grads, st, M.muon_adamw_default_hparams(),
+                              (ws, ws_need), stream=0)
+        assert st.step == 0
+        return e.value.code, M.muon_adamw_last_error()
+
+    ok = dict(params=[addr(0), addr(1), None], grads=[addr(2), addr(3), None],
+              mom=addr(4), am=addr(5), av=addr(6), ws=addr(7))
+
+    code, msg = run(**dict(ok, grads=[addr(0), addr(3), None]))
+    assert code == M.MA_ERR_INVALID_ARG and "overlaps" in msg
+    # the momentum starts in the last float of the Muon parameter
+    code, msg = run(**dict(ok, mom=addr(0) + 4 * (n0 - 1)))
+    assert code == M.MA_ERR_INVALID_ARG and "momentum" in msg
+    code, _ = run(**dict(ok, av=addr(5) + 4))
+    assert code == M.MA_ERR_INVALID_ARG
+    code, _ = run(**dict(ok, ws=addr(1) - 256))
+    assert code == M.MA_ERR_INVALID_ARG
+
+
 def test_workspace_size_grows_with_precision(lib):
     w = W.ae18_muon_bf16()
     plan = M.muon_adamw_plan(list(zip(w.names, w.shapes, w.trainable)))
