@@ -1027,7 +1027,7 @@ int launch_k(NsKernel k, const MuonMat* tab, const GemmTile* tiles, int64_t n, c
 // A += the partial Grams of a split reduction, in slice order, for the fp32
 // matrices of one Newton-Schulz batch (kReduceSplit workgroups per matrix,
 // those of other matrices return at once).
-constexpr int kReduceSplit = 16;
+constexpr int kReduceSplit = 256;  // one element per thread at R = 256
 
 __global__ __launch_bounds__(256) void k_gram_reduce(const MuonMat* __restrict__ tab, int batch) {
     const int k = blockIdx.x / kReduceSplit, part = blockIdx.x % kReduceSplit;
