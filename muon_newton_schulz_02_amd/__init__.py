@@ -158,9 +158,13 @@ def muon_adamw_workspace_size(plan: Plan, ns_precision: int = MA_NS_BF16) -> int
     return n.value
 
 
-def _ptr(x, bf16: bool = False) -> Optional[int]:
-    """Device address of a contiguous torch tensor (or an int): float32, or
-    bfloat16 where `bf16` (parameters and gradients of a bf16 plan)."""
+def _ptr(x, bf16: bool = False, numel: Optional[int] = None, what: str = "tensor") -> Optional[int]:
+    """Device address of a contiguous torch tensor (or an int, taken as is):
+    float32, or bfloat16 where `bf16` (parameters and gradients of a bf16
+    plan).  With `numel` given, a tensor must hold exactly that many
+    elements (a uint8 tensor standing for raw memory: at least that many
+    elements' bytes), so a mis-sized or mis-ordered list is refused before
+    the library could read or write past a buffer."""
     if x is None:
         return None
     if isinstance(x, int):
@@ -170,19 +174,39 @@ def _ptr(x, bf16: bool = False) -> Optional[int]:
         raise TypeError("expected a torch tensor, an int address or None")
     want = torch.bfloat16 if bf16 else torch.float32
     if x.dtype != want and x.dtype != torch.uint8:
-        raise TypeError("tensors must be %s (got %s)" % (want, x.dtype))
+        raise TypeError("%s must be %s (got %s)" % (what, want, x.dtype))
     if not x.is_contiguous():
-        raise ValueError("tensors must be contiguous")
+        raise ValueError("%s must be contiguous" % what)
+    if numel is not None:
+        if x.dtype == torch.uint8:
+            need = numel * (2 if bf16 else 4)
+            if x.numel() < need:
+                raise ValueError("%s: %d bytes, the plan needs %d" % (what, x.numel(), need))
+        elif x.numel() != numel:
+            raise ValueError("%s: %d elements, the plan says %d" % (what, x.numel(), numel))
     if x.device.type != "cuda":
-        raise ValueError("tensors must live on the GPU")
+        raise ValueError("%s must live on the GPU" % what)
     return x.data_ptr()
 
 
-def _ptr_array(xs, n: int, bf16: bool = False):
+def _numel(shape) -> int:
+    n = 1
+    for d in shape:
+        n *= int(d)
+    return n
+
+
+def _ptr_array(xs, n: int, bf16: bool = False, plan: Optional["Plan"] = None,
+               what: str = "tensor"):
+    """ctypes array of n addresses; with `plan`, each tensor is checked
+    against its entry's element count."""
     arr = (C.c_void_p * max(n, 1))()
     if xs is not None:
+        if plan is not None and len(xs) > n:
+            raise ValueError("%s list has %d items for %d plan entries" % (what, len(xs), n))
         for i, x in enumerate(xs):
-            arr[i] = _ptr(x, bf16)
+            numel = _numel(plan.shapes[i]) if plan is not None else None
+            arr[i] = _ptr(x, bf16, numel, "%s %d" % (what, i))
     return arr
 
 
@@ -231,18 +255,19 @@ def _step(plan, params, grads, state, hp, workspace, stream, grad_norm_out, muon
           phase_events):
     n = len(plan.names)
     st = _abi.ma_state()
-    mm = _ptr_array(state.muon_momentum, n)
-    am = _ptr_array(state.adam_m, n)
-    av = _ptr_array(state.adam_v, n)
+    mm = _ptr_array(state.muon_momentum, n, plan=plan, what="muon_momentum")
+    am = _ptr_array(state.adam_m, n, plan=plan, what="adam_m")
+    av = _ptr_array(state.adam_v, n, plan=plan, what="adam_v")
     st.muon_momentum = C.cast(mm, C.POINTER(C.c_void_p))
     st.adam_m = C.cast(am, C.POINTER(C.c_void_p))
     st.adam_v = C.cast(av, C.POINTER(C.c_void_p))
     st.step = int(state.step)
     st.device_step = _step_ptr(getattr(state, "device_step", None)) or None
     bf16 = getattr(plan, "param_dtype", MA_PARAM_FP32) == MA_PARAM_BF16
-    pa = _ptr_array(params, n, bf16)
-    ga = _ptr_array(grads, n, bf16)
-    ua = _ptr_array(muon_update_out, n) if muon_update_out is not None else None
+    pa = _ptr_array(params, n, bf16, plan=plan, what="param")
+    ga = _ptr_array(grads, n, bf16, plan=plan, what="grad")
+    ua = (_ptr_array(muon_update_out, n, plan=plan, what="muon_update_out")
+          if muon_update_out is not None else None)
     if stream is None:
         import torch
         stream = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
@@ -252,9 +277,17 @@ def _step(plan, params, grads, state, hp, workspace, stream, grad_norm_out, muon
         ws_ptr, ws_bytes = int(workspace[0]), int(workspace[1])
     else:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        # (an unknown precision is left for the library to report)
+        need = (muon_adamw_workspace_size(plan, hp.ns_precision)
+                if hp.ns_precision in (MA_NS_BF16, MA_NS_FP32) else 0)
+        if ws_bytes < need:
+            raise ValueError("workspace of %d bytes, the plan needs %d" % (ws_bytes, need))
+        if workspace.device.type != "cuda":
+            raise ValueError("workspace must live on the GPU")
     ua = C.cast(ua, C.POINTER(C.c_void_p)) if ua is not None else None
     args = (plan.handle, pa, ga, C.byref(st), C.byref(hp), C.c_void_p(ws_ptr), ws_bytes,
-            C.c_void_p(stream), C.c_void_p(_ptr(grad_norm_out) or 0), ua)
+            C.c_void_p(stream), C.c_void_p(_ptr(grad_norm_out, numel=1, what="grad_norm_out") or 0),
+            ua)
     if phase_events is None:
         rc = _abi.load().muon_adamw_step(*args)
     else:

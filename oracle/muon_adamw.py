@@ -46,11 +46,13 @@ Readings where the page is silent (each also listed in the design notes):
   * Clipping is global over every trainable gradient of both groups, with the
     1e-6 guard of the usual clip_grad_norm_, and is applied before both
     updates; max_grad_norm <= 0 disables it; non-finite norms propagate.
-  * The schedule cosine_with_min_lr is the usual half-cosine from the base
-    lr down to min_lr_rate * lr over total_steps scheduler steps after a
-    linear warmup from 0 (0 warmup steps unless given); the scheduler step of
-    optimizer step t (counted from 1) is t - 1; past total_steps the rate
-    stays at its minimum.  The schedule scales the lr of both groups.
+  * The schedule cosine_with_min_lr is the half-cosine from the base lr down
+    to min_lr_rate * lr over total_steps scheduler steps after a linear
+    warmup from 0 (0 warmup steps unless given), as the HF-Trainer family's
+    scheduler of that name computes it up to total_steps; the scheduler step
+    of optimizer step t (counted from 1) is t - 1.  Past total_steps the rate
+    stays at its minimum: this oracle's own reading (that scheduler would
+    follow the cosine back up).  The schedule scales the lr of both groups.
   * bf16 parameter storage (bf16_mixed): parameters and their gradients are
     bfloat16 values; optimizer states (AdamW moments, Muon momentum) stay
     float32; the step computes as for fp32 storage and rounds the new
@@ -75,7 +77,8 @@ __all__ = [
     "route_one", "route", "lr_shape_scale", "plan_dump",
     "global_grad_norm", "clip_coefficient",
     "adamw_update", "nesterov_momentum", "frobenius_normalise",
-    "newton_schulz", "ns_spectral_map", "newton_schulz_bf16_emulated", "bf16_round",
+    "newton_schulz", "ns_spectral_map", "newton_schulz_bf16_emulated", "ns_bf16_policy_iterate",
+    "bf16_split", "bf16_round",
     "bf16_round_f64", "store_param",
     "muon_matrix_update", "optimizer_step",
 ]
@@ -413,25 +416,64 @@ def bf16_round(x) -> np.ndarray:
     return out.reshape(f.shape)
 
 
-def newton_schulz_bf16_emulated(u, steps: int, coeffs=DEFAULT_NS_COEFFS,
-                                eps: float = 1e-7):
-    """Diagnostic only, not a parity target: the NS iteration with the
-    products' operands rounded to bfloat16 and float32 results, keeping a
-    float32 copy of X for the linear a*X term.  It tells how much of a bf16
-    GPU result's distance from `newton_schulz` is inherent to bf16."""
-    u = np.asarray(u, np.float64)
+def bf16_split(x):
+    """A float32 value as a pair of bfloat16 values: hi = bf16(x) and
+    lo = bf16(x - hi), so hi + lo holds 16 significant bits of x (x - hi is
+    exact in float32).  Returned as float64 arrays."""
+    x = np.asarray(x, np.float32)
+    hi = bf16_round(x)
+    lo = bf16_round(x - hi)
+    return hi.astype(np.float64), lo.astype(np.float64)
+
+
+def _f32(x) -> np.ndarray:
+    """float64 values rounded once to float32, returned as float64 (the
+    float32 accumulators of a product, modelled as exact sums rounded
+    once)."""
+    return np.asarray(x, np.float64).astype(np.float32).astype(np.float64)
+
+
+def ns_bf16_policy_iterate(x0, steps: int, coeffs=DEFAULT_NS_COEFFS, lo_iters=None):
+    """Diagnostic model of a bfloat16 precision policy for the NS iteration
+    [NS] (not a parity target; the pages fix no precision for it).  x0 is the
+    normalised input in rows <= cols orientation, as float32.
+
+    The master X is a bf16 pair (hi, lo) (bf16_split).  Each step:
+        A   = bf16(f32(hi hi^T))                 Gram of the bf16 operand
+        B   = bf16(f32(b A + c f32(A A)))        the same bf16 A in both terms
+        Y   = f32(a (hi + lo) + f32(B hi))       linear term from the pair
+        (hi, lo) = bf16_split(Y)
+    and the result is the last Y (float32).  Steps numbered lo_iters and
+    later (default: none) take the linear term from hi alone, so the lo half
+    is neither needed nor kept for them.  f32(.) is a float64 value rounded
+    once to float32; bf16(.) rounds float32 to bfloat16, ties to even."""
     a, b, c = (float(v) for v in coeffs)
+    lo_iters = steps if lo_iters is None else int(lo_iters)
+    hi, lo = bf16_split(x0)
+    y = np.asarray(x0, np.float64)
+    for k in range(steps):
+        gram = bf16_round(_f32(hi @ hi.T)).astype(np.float64)
+        poly = bf16_round(_f32(b * gram + c * _f32(gram @ gram))).astype(np.float64)
+        lin = hi + lo if k < lo_iters else hi
+        y = _f32(a * lin + _f32(poly @ hi))
+        if k + 1 < steps:
+            hi, lo = bf16_split(y)
+    return y
+
+
+def newton_schulz_bf16_emulated(u, steps: int, coeffs=DEFAULT_NS_COEFFS,
+                                eps: float = 1e-7, lo_iters=None):
+    """Diagnostic only, not a parity target: newton_schulz with its products
+    taken under the bf16 policy of ns_bf16_policy_iterate (orientation and
+    normalisation as in newton_schulz, the normalised input rounded once to
+    float32).  It tells how much of a bf16 GPU result's distance from
+    `newton_schulz` is inherent to that policy."""
+    u = np.asarray(u, np.float64)
     tall = u.shape[0] > u.shape[1]
     x = (u.T if tall else u)
-    x32 = frobenius_normalise(x, eps).astype(np.float32)
-    for _ in range(steps):
-        xb = bf16_round(x32).astype(np.float64)
-        gram_b = bf16_round((xb @ xb.T).astype(np.float32)).astype(np.float64)
-        poly = (b * gram_b + c * (gram_b @ gram_b)).astype(np.float32)
-        poly_b = bf16_round(poly).astype(np.float64)
-        x32 = (a * x32.astype(np.float64) + (poly_b @ xb).astype(np.float32)).astype(np.float32)
-    x = x32.astype(np.float64)
-    return x.T if tall else x
+    x0 = frobenius_normalise(x, eps).astype(np.float32)
+    y = ns_bf16_policy_iterate(x0, steps, coeffs, lo_iters)
+    return y.T if tall else y
 
 
 def muon_matrix_update(p, g, buf, coef: float, hp: HParams, shape_scale):

@@ -334,3 +334,45 @@ def test_binding_rejects_wrong_tensors(lib):
     with pytest.raises(TypeError):
         st.device_step = torch.zeros(1, dtype=torch.int32)
         M.muon_adamw_step(plan, [1 << 40], [1 << 40], st, hp, ws, stream=0)
+
+
+def test_binding_checks_sizes_against_the_plan(lib):
+    """Every tensor the binding passes is compared with its plan entry's
+    element count (and the workspace with the plan's workspace size) before
+    the library is called: a mis-sized parameter, gradient, state or update
+    output, a list with more items than entries, or a short workspace is
+    refused (here on CPU tensors: the size check comes before the device
+    check)."""
+    torch = pytest.importorskip("torch")
+    plan = M.muon_adamw_plan([("action_expert.layers.0.q.weight", (4, 6), True),
+                              ("vlm.b", (5,), True)])
+    hp = M.muon_adamw_default_hparams()
+    need = M.muon_adamw_workspace_size(plan, hp.ns_precision)
+    ws = (1 << 40, need)
+    A = 1 << 40
+
+    def state(mom=A, m=A, v=A):
+        st = M.State(2)
+        st.muon_momentum[0] = mom
+        st.adam_m[1] = m
+        st.adam_v[1] = v
+        return st
+
+    def refused(params, grads, st=None, workspace=ws, upd=None, norm=None):
+        with pytest.raises(ValueError, match="plan"):
+            M.muon_adamw_step(plan, params, grads, st or state(), hp, workspace, stream=0,
+                              grad_norm_out=norm, muon_update_out=upd)
+
+    refused([torch.zeros(4, 5), A], [A, A])                     # 20 elements for 24
+    refused([A, torch.zeros(6)], [A, A])                        # entry 1: 6 for 5
+    refused([A, A], [A, torch.zeros(4, 6)])                      # entries swapped
+    refused([A, A], [A, A], st=state(mom=torch.zeros(4, 7)))
+    refused([A, A], [A, A], st=state(v=torch.zeros(4)))
+    refused([A, A], [A, A], upd=[torch.zeros(3, 6), None])
+    refused([A, A, A], [A, A])                                   # three items, two entries
+    refused([A, A], [A, A], workspace=torch.zeros(need - 1, dtype=torch.uint8))
+    refused([A, A], [A, A], norm=torch.zeros(0))
+    refused([torch.zeros(4 * 6 * 4 - 1, dtype=torch.uint8), A], [A, A])   # raw bytes too few
+    # the right sizes get as far as the device check
+    with pytest.raises(ValueError, match="GPU"):
+        M.muon_adamw_step(plan, [torch.zeros(4, 6), A], [A, A], state(), hp, ws, stream=0)

@@ -425,14 +425,101 @@ def test_bf16_round_matches_torch():
     np.testing.assert_array_equal(O.bf16_round(x), want)
 
 
-def test_bf16_emulated_ns_close_to_exact():
-    """The bf16-emulating diagnostic stays within the bf16 tolerance of the
-    fp64 iteration on a C1-like matrix (a sanity bound, not a parity gate)."""
-    rng = np.random.default_rng(14)
-    g = rng.standard_normal((64, 256)) * np.exp(rng.uniform(np.log(0.1), np.log(10), 64))[:, None]
-    a = O.newton_schulz(g, 5)
-    b = O.newton_schulz_bf16_emulated(g, 5)
-    assert np.linalg.norm(a - b) / np.linalg.norm(a) < 2e-2
+def test_bf16_split_hand_worked():
+    """hi = bf16(x), lo = bf16(x - hi), worked by hand:
+    1 + 2^-6 + 2^-12 + 2^-20 -> hi 1 + 2^-6 (the rest is below half a spacing
+    2^-8), lo = bf16(2^-12 (1 + 2^-8)) = 2^-12 (a tie, to the even 2^-12);
+    -(3 + 2^-9) -> hi -3, lo -2^-9; 0.5 -> (0.5, 0)."""
+    x = np.array([1 + 2 ** -6 + 2 ** -12 + 2 ** -20, -(3 + 2 ** -9), 0.5], np.float32)
+    hi, lo = O.bf16_split(x)
+    np.testing.assert_array_equal(hi, [1 + 2 ** -6, -3.0, 0.5])
+    np.testing.assert_array_equal(lo, [2 ** -12, -2 ** -9, 0.0])
+
+
+# Hand-worked 2 x 3 inputs of the bf16 policy model.  X_LIN needs more than
+# 16 significant bits in its first entry; X_POLY's first entry is not a
+# bf16 value (1 + 2^-10 rounds to 1), so hi differs from X there, and its
+# Gram has an entry that bf16 rounds (9.828125 -> 9.8125).
+X_LIN = np.array([[1 + 2 ** -6 + 2 ** -12 + 2 ** -20, 0.5, 0.0],
+                  [0.0, 0.25, -(3 + 2 ** -9)]], np.float32)
+X_POLY = np.array([[1 + 2 ** -10, 0.5, 0.0],
+                   [0.0, 0.25, 3.125]], np.float32)
+
+
+def test_bf16_policy_linear_term_uses_the_hi_lo_master():
+    """Coefficients (2, 0, 0): B = 0, so each step doubles the master hi + lo
+    exactly and the result after two steps is 4 (hi + lo) of the input:
+    4 (1 + 2^-6 + 2^-12) = 4.0634765625 and -4 (3 + 2^-9) = -12.0078125.
+    A float32 master would keep the 2^-20 (4.06348037...), a bf16-only X
+    would give 4.0625.  With the lo half used in the first step only, the
+    second step doubles hi(2 (1 + 2^-6 + 2^-12)) = 2.03125 -> 4.0625, and
+    hi(-(6 + 2^-8)) = -6 -> -12."""
+    y = O.ns_bf16_policy_iterate(X_LIN, 2, (2.0, 0.0, 0.0))
+    np.testing.assert_array_equal(y, [[4.0634765625, 2.0, 0.0], [0.0, 1.0, -12.0078125]])
+    y1 = O.ns_bf16_policy_iterate(X_LIN, 2, (2.0, 0.0, 0.0), lo_iters=1)
+    np.testing.assert_array_equal(y1, [[4.0625, 2.0, 0.0], [0.0, 1.0, -12.0]])
+
+
+def test_bf16_policy_gram_rounding():
+    """Coefficients (0, 1, 0): Y = bf16(A) hi with A = hi hi^T, by hand.
+    hi = [[1, .5, 0], [0, .25, 3.125]]; A = [[1.25, .125], [.125, 9.828125]],
+    and 9.828125 = 1.001110101b x 2^3 rounds to 1.0011101b x 2^3 = 9.8125.
+    Y = A hi = [[1.25, .65625, .390625], [.125, 2.515625, 30.6640625]]
+    (an unrounded Gram would give 2.51953125 and 30.712890625)."""
+    y = O.ns_bf16_policy_iterate(X_POLY, 1, (0.0, 1.0, 0.0))
+    np.testing.assert_array_equal(y, [[1.25, 0.65625, 0.390625], [0.125, 2.515625, 30.6640625]])
+
+
+def test_bf16_policy_square_rounding():
+    """Coefficients (0, 0, 1): Y = bf16(A A) hi with the bf16 A above, by
+    hand.  A A = [[1.578125, 1.3828125], [1.3828125, 96.30078125]]; the last
+    is 1.10000001001101b x 2^6 and rounds up to 96.5.
+    Y = [[1.578125, 1.134765625, 4.3212890625], [1.3828125, 24.81640625, 301.5625]]."""
+    y = O.ns_bf16_policy_iterate(X_POLY, 1, (0.0, 0.0, 1.0))
+    np.testing.assert_array_equal(y, [[1.578125, 1.134765625, 4.3212890625],
+                                      [1.3828125, 24.81640625, 301.5625]])
+
+
+def test_bf16_policy_same_bf16_gram_in_both_terms():
+    """Coefficients (0, 1, 1): B = bf16(A + A A) with the same bf16 A in
+    both terms, by hand: A + A A = [[2.828125, 1.5078125], [1.5078125,
+    106.11328125]], and the last (1.10101000011101b x 2^6) rounds down to
+    106.  Y = B hi = [[2.828125, 1.791015625, 4.7119140625],
+    [1.5078125, 27.25390625, 331.25]]."""
+    y = O.ns_bf16_policy_iterate(X_POLY, 1, (0.0, 1.0, 1.0))
+    np.testing.assert_array_equal(y, [[2.828125, 1.791015625, 4.7119140625],
+                                      [1.5078125, 27.25390625, 331.25]])
+
+
+def test_bf16_emulated_orientation_and_scale():
+    """The wrapper orients and normalises like newton_schulz: a tall input
+    gives the transpose of its wide transpose's result, bit for bit, and a
+    power-of-two scaling of the input changes nothing (it commutes with
+    every rounding)."""
+    rng = np.random.default_rng(15)
+    g = rng.standard_normal((24, 96))
+    w = O.newton_schulz_bf16_emulated(g, 5)
+    np.testing.assert_array_equal(O.newton_schulz_bf16_emulated(g.T.copy(), 5), w.T)
+    np.testing.assert_array_equal(O.newton_schulz_bf16_emulated(g * 2.0 ** 20, 5, eps=0.0),
+                                  O.newton_schulz_bf16_emulated(g, 5, eps=0.0))
+
+
+def test_bf16_emulated_error_band_and_thin_matrices():
+    """Against the fp64 iteration the bf16 policy costs about 1e-2 on
+    Gaussian and row-scaled inputs (0.3-1.6 times the 2e-2 bf16 gate), and
+    the matrices with one to three rows reach past the gate: the reason
+    very thin Muon matrices run their Newton-Schulz in fp32."""
+    rng = np.random.default_rng(5)
+
+    def err(g, **kw):
+        a = O.newton_schulz(g, 5)
+        return np.linalg.norm(O.newton_schulz_bf16_emulated(g, 5, **kw) - a) / np.linalg.norm(a)
+
+    for shape in ((64, 256), (32, 1024)):
+        g = rng.standard_normal(shape) * np.exp(rng.uniform(np.log(0.1), np.log(10), shape[0]))[:, None]
+        assert 4e-3 < err(g) < 1.6e-2
+    thin = [max(err(rng.standard_normal((r, 1024))) for _ in range(20)) for r in (2, 3)]
+    assert max(thin) > 2e-2, thin
 
 
 # ---------------------------------------------------------------------------
@@ -458,6 +545,29 @@ def test_schedule_special_points():
     assert all(O.schedule_factor(const, k) == 1.0 for k in (0, 7, 10 ** 6))
     with pytest.raises(ValueError):
         O.schedule_factor(O.HParams(lr_schedule="linear"), 0)
+
+
+def test_schedule_matches_the_trainer_family_scheduler():
+    """Special case reducing to a library routine: up to total_steps the
+    schedule equals the learning-rate multipliers of transformers'
+    get_cosine_with_min_lr_schedule_with_warmup (the scheduler behind the
+    name cosine_with_min_lr in the HF-Trainer family the page's trainer
+    belongs to), with and without warmup.  Past total_steps that scheduler
+    runs on along the cosine; the oracle holds the minimum instead (its own
+    reading, pinned in test_schedule_special_points)."""
+    torch = pytest.importorskip("torch")
+    transformers = pytest.importorskip("transformers")
+    for warm, total in ((0, 100), (10, 30), (7, 7), (0, 1)):
+        hp = O.HParams(lr_schedule="cosine_with_min_lr", warmup_steps=warm, total_steps=total,
+                       min_lr_rate=0.1)
+        opt = torch.optim.SGD([torch.zeros(1, requires_grad=True)], lr=1.0)
+        sched = transformers.get_cosine_with_min_lr_schedule_with_warmup(
+            opt, num_warmup_steps=warm, num_training_steps=total, min_lr_rate=0.1)
+        for k in range(total + 1):
+            assert O.schedule_factor(hp, k) == pytest.approx(sched.get_last_lr()[0], rel=1e-12,
+                                                             abs=1e-15), (warm, total, k)
+            opt.step()
+            sched.step()
 
 
 def test_schedule_monotone_and_bounded():
