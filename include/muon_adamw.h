@@ -25,7 +25,11 @@
  *     allocates device memory; its scratch lives in a caller-provided
  *     workspace.
  *   - Device work is asynchronous on the caller's HIP stream; device faults
- *     surface at the caller's next synchronisation (HIP semantics).  Part of
+ *     surface at the caller's next synchronisation (HIP semantics).  The
+ *     host blocks in a step only when it runs more than four steps of the
+ *     same plan ahead of the device: each eager step stages its descriptor
+ *     tables in one of four pinned host buffers used in turn, and waits
+ *     until the device has read the one it reuses.  Part of
  *     a step may run on streams the library creates on the same device
  *     (default priority, one set per plan and device, released by
  *     muon_adamw_plan_free); they fork from the caller's stream and are
@@ -151,11 +155,13 @@ typedef struct {
  * instead of `step`, which is then neither read nor changed.  Each step
  * reads it on the device, uses t = *device_step + 1 and stores t back, in
  * stream order.  Every launch of such a step takes the same arguments for
- * any t, and the step skips re-uploading descriptor tables identical to the
- * ones it last put in the same workspace; so after one eager step, a step
- * with the same pointers and workspace can be captured in a HIP graph and
- * replayed, each replay advancing *device_step.  In this mode nothing but
- * this plan's steps may write the workspace between calls. */
+ * any t.  Every eager step uploads its descriptor tables (the tensor
+ * addresses and tile lists) into the workspace; a step under stream capture
+ * cannot, and reads the tables the last eager step of this plan with
+ * device_step set put there.  So after one eager step, a step with the same
+ * pointers and workspace can be captured in a HIP graph and replayed, each
+ * replay advancing *device_step, provided nothing else writes that
+ * workspace between that eager step and the replays. */
 typedef struct {
     float* const* muon_momentum;
     float* const* adam_m;
@@ -239,7 +245,11 @@ int muon_adamw_plan_dump(const ma_plan* plan, char* buf, size_t cap, size_t* len
 
 /* Bytes of device workspace one muon_adamw_step call needs for this plan
  * and NS precision.  The caller allocates it (256-byte aligned) and may
- * reuse it across steps; contents between calls are scratch.
+ * reuse it across steps.  An eager step writes everything it reads there
+ * (its descriptor tables included), so between eager steps the contents are
+ * scratch and the caller may use or free the memory; only replays of a
+ * captured step depend on what an earlier eager step left in it (see
+ * ma_state.device_step).
  * Errors: INVALID_ARG (null, bad precision). */
 int muon_adamw_workspace_size(const ma_plan* plan, int32_t ns_precision, size_t* bytes);
 

@@ -31,8 +31,9 @@ constexpr int kGemmTile = 256;
 
 // Under the bf16 policy, matrices whose smaller side is below this run their
 // Newton-Schulz in fp32: for such thin matrices the bf16 rounding error is
-// inherent and reaches the 2e-2 tolerance (rank-1 inputs give 2-3 %), while
-// their share of the work is negligible.
+// inherent and reaches the 2e-2 tolerance (Gaussian inputs with two or three
+// rows reach 2.1-2.4e-2 under this policy, against at most 1.6e-2 from four
+// rows on), while their share of the work is negligible.
 constexpr int64_t kBf16MinRows = 16;
 
 // XCDs of an MI355X: consecutive workgroups of a launch are dispatched to
@@ -50,6 +51,9 @@ constexpr int kNsStreams = 2;
 // ceil(total / (kNsStreams x this)) batches of about equal GEMM work.
 // Otherwise there are kNsStreams batches.
 constexpr size_t kNsOverlapBatchBytes = size_t(160) << 20;
+// Pinned host buffers the descriptor tables are staged in, used in rotation:
+// a step waits for the upload of the step this many calls before it.
+constexpr int kStagingSlots = 4;
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
@@ -176,14 +180,14 @@ struct ma_plan {
     };
     mutable std::vector<Side> side;
     mutable std::mutex mu;
-    mutable void* staging[2] = {nullptr, nullptr};
-    mutable void* staging_dev[2] = {nullptr, nullptr};   // device address of staging[k]
-    mutable size_t staging_bytes[2] = {0, 0};
-    mutable void* staging_event[2] = {nullptr, nullptr};
+    mutable void* staging[ma::kStagingSlots] = {};
+    mutable void* staging_dev[ma::kStagingSlots] = {};   // device address of staging[k]
+    mutable size_t staging_bytes[ma::kStagingSlots] = {};
+    mutable void* staging_event[ma::kStagingSlots] = {};
     mutable int staging_next = 0;
-    // the descriptor tables a step with a device-resident step counter last
-    // uploaded, and where: an identical upload into the same workspace is
-    // skipped, so such a step can be captured in a graph and replayed
+    // the descriptor tables the last eager step with a device-resident step
+    // counter uploaded, and where: a captured step with the same tables and
+    // workspace reads them from the workspace instead of uploading
     mutable std::vector<char> table_cache;
     mutable const void* table_cache_ws = nullptr;
     mutable int32_t table_cache_prec = -1;

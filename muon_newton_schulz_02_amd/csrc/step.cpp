@@ -19,7 +19,7 @@
 // Side streams are joined back into the caller's stream before returning.
 // Nothing is launched before every argument has been checked.
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cmath>
@@ -40,12 +40,12 @@ int hip_fail(const char* what, int err) {
 }
 
 // A pinned host staging buffer of at least `bytes`, whose previous copy (if
-// any) has completed.  Two buffers alternate so consecutive steps do not
-// wait on each other's copies.
+// any) has completed.  kStagingSlots buffers rotate, so the host waits here
+// only when it is that many steps of this plan ahead of the device.
 int get_staging(const ma_plan* plan, size_t bytes, void** out, const void** out_dev,
                 void** event) {
     const int k = plan->staging_next;
-    plan->staging_next ^= 1;
+    plan->staging_next = (k + 1) % kStagingSlots;
     if (plan->staging_event[k]) {
         hipError_t e = hipEventSynchronize((hipEvent_t)plan->staging_event[k]);
         if (e != hipSuccess) return hip_fail("staging event wait", e);
@@ -415,37 +415,37 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         return (int)hipEventRecord((hipEvent_t)phase_events[k], st);
     };
     if (int er = mark(0)) return hip_fail("phase event", er);
-    // The tables go up through a pinned staging slot.  With a device step
-    // counter an upload identical to the one this plan last made into this
-    // workspace is skipped; under capture one is then never needed.
-    const char* upload = nullptr;
-    std::vector<char> fresh;
-    if (state->device_step) {
-        fresh.resize(L.tables_bytes);
+    // The tables go up through a pinned staging slot on every eager step.  A
+    // captured step cannot upload (the staging slot would be reused by later
+    // eager steps while the graph still points at it): it relies on the
+    // tables the last eager step with a device step counter put in this
+    // workspace, and is refused unless those are the tables it needs.
+    if (capturing) {
+        std::vector<char> fresh(L.tables_bytes);
         fill_tables(fresh.data());
         const bool cached = plan->table_cache_ws == workspace && plan->table_cache_prec == prec &&
                             plan->table_cache == fresh;
         if (!cached) {
-            if (capturing) {
-                set_error("muon_adamw_step: captured step would upload new descriptor tables; "
-                          "run one eager step with the same pointers and workspace first");
-                return MA_ERR_CAPTURE;
-            }
-            upload = fresh.data();
+            set_error("muon_adamw_step: captured step would upload new descriptor tables; "
+                      "run one eager step with the same pointers and workspace first");
+            return MA_ERR_CAPTURE;
         }
-    }
-    if (!state->device_step || upload) {
+    } else {
         void* host = nullptr;
         const void* host_dev = nullptr;
         void* event = nullptr;
         int rc = get_staging(plan, L.tables_bytes, &host, &host_dev, &event);
         if (rc != MA_OK) return rc;
-        if (upload)
-            std::memcpy(host, upload, L.tables_bytes);
-        else
-            fill_tables(reinterpret_cast<char*>(host));
         // a failure past this point may leave the workspace's tables stale
         plan->table_cache_ws = nullptr;
+        if (state->device_step) {
+            // remembered for a later capture with the same pointers
+            plan->table_cache.resize(L.tables_bytes);
+            fill_tables(plan->table_cache.data());
+            std::memcpy(host, plan->table_cache.data(), L.tables_bytes);
+        } else {
+            fill_tables(reinterpret_cast<char*>(host));
+        }
         // a kernel on the step's stream reads the staging buffer over the bus:
         // no copy engine, so no cross-engine waits between consecutive steps
         // (a copy-engine upload stalled the second of back-to-back steps by
@@ -454,8 +454,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         if (er) return hip_fail("table upload", er);
         e = hipEventRecord((hipEvent_t)event, st);
         if (e != hipSuccess) return hip_fail("hipEventRecord", e);
-        if (upload) {
-            plan->table_cache.swap(fresh);
+        if (state->device_step) {
             plan->table_cache_ws = workspace;
             plan->table_cache_prec = prec;
         }
@@ -640,7 +639,7 @@ void muon_adamw_plan_free(ma_plan* plan) {
         (void)hipStreamDestroy((hipStream_t)sd.stream);
         (void)hipStreamDestroy((hipStream_t)sd.ns_stream);
     }
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kStagingSlots; ++k) {
         if (plan->staging_event[k]) {
             (void)hipEventSynchronize((hipEvent_t)plan->staging_event[k]);
             (void)hipEventDestroy((hipEvent_t)plan->staging_event[k]);

@@ -2,8 +2,9 @@
 
 With state.device_step set, every value that depends on the step number (the
 scheduled rate, AdamW's bias corrections and decays, the Muon rate) is formed
-on the GPU, and the descriptor tables are not re-uploaded while they are
-unchanged, so a step captured once replays as the following steps.  These
+on the GPU; a captured step reads the descriptor tables the last eager step
+put in the workspace, so a step captured once replays as the following
+steps.  These
 tests compare bit for bit: the device-counter path with the host-counter path
 (which the parity tests check against the oracle), and graph replays with
 eager steps on identical inputs.
@@ -89,6 +90,32 @@ def test_device_counter_matches_host_counter_bitwise(overlap):
             assert run.state.step == 0
         else:
             assert run.state.step == 4
+        outs.append(snaps)
+    for t, (a, b) in enumerate(zip(*outs), start=1):
+        _assert_same(a, b, "step %d" % t)
+
+
+def test_eager_steps_reupload_after_the_workspace_was_overwritten():
+    """The workspace is scratch between eager steps: with the device counter
+    set, a caller that overwrites it (or frees it and gets the same memory
+    back from the caching allocator holding other data) between two eager
+    steps still gets exactly the results of an untouched workspace, since
+    every eager step uploads its descriptor tables again."""
+    w = _workload()
+    hp = _hparams(w)
+    outs = []
+    for clobber in (False, True):
+        run = _setup(w, hp, False, True)
+        snaps = []
+        for t in range(1, 4):
+            H.fill_grads(run, torch, t)
+            if clobber and t > 1:
+                run.workspace.fill_(0xA5)      # garbage where the tables were
+                torch.cuda.synchronize()
+            H.say("workspace clobber=%s step %d" % (clobber, t))
+            _step(run)
+            torch.cuda.synchronize()
+            snaps.append(_snapshot(run))
         outs.append(snaps)
     for t, (a, b) in enumerate(zip(*outs), start=1):
         _assert_same(a, b, "step %d" % t)

@@ -374,9 +374,10 @@ def test_vla_hybrid_full_size_sampled(overlap):
     """The full hybrid step in the benchmark's configuration: 126 Muon
     matrices (bf16 NS) + 253 AdamW tensors (1.88e9 elements) + a frozen
     embedding; clip triggers.  The oracle follows the global norm over all
-    2.15e9 gradients, eight AdamW tensors of every shape and four Muon
-    matrices, for two steps; AdamW beside the Muon group (the benchmark's
-    launch, with Newton-Schulz in batches on two streams) and serial."""
+    2.15e9 gradients, six AdamW tensors of every shape and four Muon
+    matrices, over all five configured steps; AdamW beside the Muon group
+    (the benchmark's launch, with Newton-Schulz in batches on two streams)
+    and serial."""
     w = W.vla_hybrid_bf16()
     names = w.names
     pick = ["vlm.model.layers.0.self_attn.q_proj.weight", "vlm.model.layers.3.mlp.gate_proj.weight",
@@ -387,7 +388,7 @@ def test_vla_hybrid_full_size_sampled(overlap):
             "action_expert.layers.17.mlp.gate_proj.weight",
             "action_expert.layers.9.mlp.down_proj.weight"]
     sampled = {names.index(n) for n in pick}
-    _run_parity(w, "bf16", 2, sampled=sampled, backend="torch", overlap=overlap)
+    _run_parity(w, "bf16", w.steps, sampled=sampled, backend="torch", overlap=overlap)
 
 
 def _bf16_ragged():
@@ -546,7 +547,8 @@ def test_batched_newton_schulz_matches_serial_bitwise(make):
 def test_vla_hybrid_fp32ns_full_size_sampled():
     """The full hybrid parameter set with the Newton-Schulz products in fp32
     (true fp32 MFMA): delta relative error <= 1e-4 per matrix and step, on
-    four Muon matrices of every shape and four AdamW tensors, two steps."""
+    four Muon matrices of every shape and four AdamW tensors, over all five
+    configured steps."""
     w = W.vla_hybrid_fp32ns()
     names = w.names
     pick = ["vlm.model.layers.1.mlp.down_proj.weight", "vlm.model.layers.20.input_layernorm.weight",
@@ -556,7 +558,7 @@ def test_vla_hybrid_fp32ns_full_size_sampled():
             "action_expert.layers.4.mlp.up_proj.weight",
             "action_expert.layers.16.mlp.down_proj.weight"]
     sampled = {names.index(n) for n in pick}
-    _run_parity(w, "fp32", 2, sampled=sampled, backend="torch")
+    _run_parity(w, "fp32", w.steps, sampled=sampled, backend="torch")
 
 
 def test_ragged_stress_noclip_full_size():
@@ -568,9 +570,18 @@ def test_ragged_stress_noclip_full_size():
     _run_parity(w, "bf16", 1, backend="torch")
 
 
+def test_ragged_stress_noclip_three_steps_sampled():
+    """Clip off, all three configured steps, with the momentum carried
+    forward: the 8192^2 matrix (60 % of the workload's flops), the tall and
+    wide 4096/14336 pair, the 128x8192 matrix and three of the 64x256 ones
+    compared at every step."""
+    w = W.ragged_stress_bf16(clip=False)
+    _run_parity(w, "bf16", w.steps, sampled={0, 1, 2, 3, 4, 30, 67}, backend="torch")
+
+
 def test_ragged_stress_clip_full_size_sampled():
     """The same workload with the clip on (it triggers: the spike makes the
-    norm ~1e5), three steps, on the tall and wide 4096/14336 pair, the
-    128x8192 matrix and four of the 64x256 ones."""
+    norm ~1e5), three steps, on the 8192^2 matrix, the tall and wide
+    4096/14336 pair, the 128x8192 matrix and four of the 64x256 ones."""
     w = W.ragged_stress_bf16(clip=True)
-    _run_parity(w, "bf16", w.steps, sampled={1, 2, 3, 4, 30, 50, 67}, backend="torch")
+    _run_parity(w, "bf16", w.steps, sampled={0, 1, 2, 3, 4, 30, 50, 67}, backend="torch")
