@@ -201,12 +201,19 @@ def percentile(xs, q: float) -> float:
     return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
 
 
-def cpu_baseline(w, hp_overrides) -> dict:
-    """The oracle, as it stands, on a bounded sample of the workload: the
-    first k_ae action-expert layers (7 Muon matrices each) and the first
-    k_vlm VLM layers (9 AdamW tensors each) of the full hybrid table, each
-    set timed whole (clip norm of the sampled gradients + updates) and
-    scaled by the layer counts to the whole table's params/s."""
+def cpu_baseline(w, hp_overrides, budget_s: float = 12.0) -> dict:
+    """The oracle, as it stands, on a bounded sample of the workload, scaled
+    to the whole table's params/s:
+
+      * Muon: per distinct canonical shape (rows <= cols), matrices are
+        timed one by one (momentum, Newton-Schulz, update) until the shape's
+        share of the budget is spent, then scaled by the shape's count; a
+        shape whose dense Newton-Schulz cost exceeds 6 TFLOP is not run and
+        takes the flop rate of the costliest shape that was;
+      * AdamW: tensors in table order until a quarter of the budget is
+        spent, scaled by element count;
+      * clip norm: over the sampled gradients, scaled by element count.
+    A table small enough to fit the budget is thereby timed whole."""
     import numpy as np
     import oracle as O
     import workloads as W
@@ -217,36 +224,84 @@ def cpu_baseline(w, hp_overrides) -> dict:
         setattr(hp, k, v)
     names = w.names
     as_stored = O.bf16_round if w.param_storage == "bf16" else (lambda x: x)
-    k_ae, k_vlm = 5, 8   # sampled layers of each kind (about 10-15 s on 16 host cores)
-    ae = [i for i, n in enumerate(names)
-          if n.startswith("action_expert.layers.") and int(n.split(".")[2]) < k_ae]
-    vlm = [i for i, n in enumerate(names)
-           if n.startswith("vlm.model.layers.") and int(n.split(".")[3]) < k_vlm]
-    n_ae_layers = len({n.split(".")[2] for n in names if n.startswith("action_expert.layers.")})
-    n_vlm_layers = len({n.split(".")[3] for n in names if n.startswith("vlm.model.layers.")})
+    mode = W.mode_id(w)
     train = [i for i, p in enumerate(w.params) if p.trainable]
-    total_params = sum(w.params[i].numel for i in train)
+    groups = {i: O.route_one(names[i], w.params[i].shape, True, mode) for i in train}
+    muon_by_shape = {}
+    for i in train:
+        if groups[i] == O.MUON:
+            sh = tuple(sorted(w.params[i].shape))
+            muon_by_shape.setdefault(sh, []).append(i)
+    adam = [i for i in train if groups[i] == O.ADAMW]
+    cap = 6e12
 
-    def timed(idx):
-        params = {i: as_stored(W.np_param(w, i)) for i in idx}
-        grads = {i: as_stored(W.np_grad(w, 1, i)) for i in idx}
-        bufs = {i: W.np_momentum(w, i) for i in idx}
+    def muon_time(i):
+        p, g = as_stored(W.np_param(w, i)), as_stored(W.np_grad(w, 1, i))
+        buf = W.np_momentum(w, i)
+        m, n = w.params[i].shape
+        s = O.lr_shape_scale(m, n, hp.moonlight_coefficient)
         t0 = time.perf_counter()
-        norm = O.global_grad_norm([grads[i] for i in idx])
-        coef = O.clip_coefficient(norm, hp.max_grad_norm)
-        for i in idx:
-            shape = w.params[i].shape
-            if O.route_one(names[i], shape, True, W.mode_id(w)) == O.MUON:
-                s = O.lr_shape_scale(shape[0], shape[1], hp.moonlight_coefficient)
-                O.muon_matrix_update(params[i], grads[i], bufs[i], coef, hp, s)
-            else:
-                z = np.zeros(shape, np.float32)
-                O.adamw_update(params[i], grads[i], z, z, 1, coef, hp)
+        O.muon_matrix_update(p, g, buf, 0.5, hp, s)
         return time.perf_counter() - t0
 
-    t_ae = timed(ae)
-    t_vlm = timed(vlm)
-    est = t_ae * n_ae_layers / k_ae + t_vlm * n_vlm_layers / k_vlm
+    est, notes, sample_params, sample_s = 0.0, [], 0, 0.0
+    sampled_grads = []
+    shapes = sorted(muon_by_shape, key=lambda sh: W.ns_cost(sh))
+    per_shape = 0.5 * budget_s / max(1, len(shapes))
+    rate = None    # flops per second of the costliest shape timed
+    skipped = []
+    for sh in shapes:
+        idx = muon_by_shape[sh]
+        if W.ns_cost(sh) > cap:
+            skipped.append(sh)
+            continue
+        ts = []
+        for i in idx:
+            ts.append(muon_time(i))
+            sample_params += w.params[i].numel
+            if sum(ts) >= per_shape:
+                break
+        t_one = sum(ts) / len(ts)
+        est += t_one * len(idx)
+        sample_s += sum(ts)
+        rate = W.ns_cost(sh) / t_one
+        notes.append("%d of %d %dx%d (%.2f s each)" % (len(ts), len(idx), sh[0], sh[1], t_one))
+    for sh in skipped:
+        if rate is None:
+            raise RuntimeError("no Muon shape cheap enough to time")
+        t_one = W.ns_cost(sh) / rate
+        est += t_one * len(muon_by_shape[sh])
+        notes.append("%d %dx%d at the flop rate of the largest timed shape (%.1f s each)"
+                     % (len(muon_by_shape[sh]), sh[0], sh[1], t_one))
+    if adam:
+        t_adam, n_done, k = 0.0, 0, 0
+        for i in adam:
+            p, g = as_stored(W.np_param(w, i)), as_stored(W.np_grad(w, 1, i))
+            z = np.zeros(w.params[i].shape, np.float32)
+            t0 = time.perf_counter()
+            O.adamw_update(p, g, z, z, 1, 0.5, hp)
+            t_adam += time.perf_counter() - t0
+            n_done += w.params[i].numel
+            sampled_grads.append(g)
+            k += 1
+            if t_adam >= 0.25 * budget_s:
+                break
+        n_adam = sum(w.params[i].numel for i in adam)
+        est += t_adam * n_adam / n_done
+        sample_s += t_adam
+        sample_params += n_done
+        notes.append("%d of %d AdamW tensors (%d of %d elements, %.2f s)"
+                     % (k, len(adam), n_done, n_adam, t_adam))
+    if not sampled_grads:
+        sampled_grads = [as_stored(W.np_grad(w, 1, i)) for i in muon_by_shape[shapes[0]][:4]]
+    t0 = time.perf_counter()
+    O.global_grad_norm(sampled_grads)
+    t_norm = time.perf_counter() - t0
+    n_sampled = sum(g.size for g in sampled_grads)
+    total_params = sum(w.params[i].numel for i in train)
+    est += t_norm * total_params / n_sampled
+    sample_s += t_norm
+    notes.append("clip norm over %d sampled gradient elements (%.2f s)" % (n_sampled, t_norm))
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -262,19 +317,16 @@ def cpu_baseline(w, hp_overrides) -> dict:
                                           threads)
     except ImportError:
         pass
-    sample_params = sum(w.params[i].numel for i in ae + vlm)
     return {
         "value": total_params / est,
         "unit": "params/s",
         "cores": min(cores, threads),
         "kind": "oracle",
-        "sample": ("action_expert.layers.0-%d (%d Muon matrices, %.1f s) + "
-                   "vlm.model.layers.0-%d (%d AdamW tensors, %.1f s), %d params, scaled by "
-                   "layer count (%d and %d layers) to the whole table; NumPy fp64, BLAS "
-                   "threads for matmuls, elementwise single-threaded"
-                   % (k_ae - 1, len(ae), t_ae, k_vlm - 1, len(vlm), t_vlm, sample_params,
-                      n_ae_layers, n_vlm_layers)),
-        "sample_seconds": t_ae + t_vlm,
+        "sample": ("%s: %s; scaled to the whole table (%d params, est. %.1f s per step); NumPy "
+                   "fp64, BLAS threads for matmuls, elementwise single-threaded"
+                   % (w.name, "; ".join(notes), total_params, est)),
+        "sample_seconds": sample_s,
+        "step_seconds_estimated": est,
         "numpy": np.__version__,
         "blas": blas,
     }
@@ -295,6 +347,8 @@ def main():
                          "HIP graph (device step counter)")
     ap.add_argument("--roofline-steps", type=int, default=10,
                     help="serial steps timed after the headline ones, for per-kernel rooflines")
+    ap.add_argument("--no-b2", action="store_true",
+                    help="skip the ceiling probes (MFMA issue rate, LDS reads, HBM streams)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times), to calibrate "
                          "the FETCH_SIZE / WRITE_SIZE counters against known bytes")
@@ -435,6 +489,11 @@ def main():
         phases["step"].append(evs.elapsed(b, b + 4))
     evs.close()
     mean = {k: sum(v) / len(v) for k, v in phases.items()}
+    b2 = None
+    if not args.no_b2:
+        print("[bench] ceiling probes (b2)", file=sys.stderr, flush=True)
+        from muon_newton_schulz_02_amd import peaks
+        b2 = peaks.measure_all(torch)
     copy_gbps = copy_bandwidth(torch)
     gemm = gemm_tflops(torch, torch.bfloat16 if w.ns_precision == "bf16" else torch.float32) \
         if n_muon > 0 else None
@@ -454,19 +513,24 @@ def main():
     norm_bytes = esz * n_train
     adam_gbps = adam_bytes / (mean["adamw"] * 1e-3) / 1e9 if mean["adamw"] > 0 else 0.0
     norm_gbps = norm_bytes / (mean["clip_norm"] * 1e-3) / 1e9 if mean["clip_norm"] > 0 else 0.0
+    b2_mfma = (b2 or {}).get("mfma_bf16_tflops" if w.ns_precision == "bf16" else "mfma_fp32_tflops")
+    b2_mix = (b2 or {}).get("hbm_adamw_mix_gbps")
     if n_adam > 0 and mean["adamw"] >= mean["newton_schulz"]:
         roofline = {"kernel": "k_adamw", "bound": "hbm", "achieved": adam_gbps,
                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": adam_gbps / PEAK_HBM_GBPS,
                     "traffic": measured_traffic("k_adamw", w.name),
-                    "algorithmic_bytes": adam_bytes, "frac_of_copy": adam_gbps / copy_gbps}
+                    "algorithmic_bytes": adam_bytes, "frac_of_copy": adam_gbps / copy_gbps,
+                    "b2_peak": b2_mix, "frac_of_b2": adam_gbps / b2_mix if b2_mix else None}
     else:
-        # achieved counts the dense algorithmic flops; the matrix cores
-        # execute fewer (upper tiles of the symmetric products), so frac can
-        # pass 1 where the executed rate is still below the peak
+        # achieved: the flops the matrix cores execute (the symmetric
+        # products' upper tiles, padded; the MFMA counters agree), so frac
+        # is the matrix-core utilisation and cannot pass 1; the dense
+        # algorithmic rate is reported beside it
         roofline = {"kernel": "k_ns_* GEMMs (5 steps x 3 launches)", "bound": "mfma",
-                    "achieved": ns_tflops, "peak": ns_peak, "unit": "TFLOP/s",
-                    "frac": ns_tflops / ns_peak, "traffic": None,
-                    "executed_tflops": ns_exec_tflops, "executed_frac": ns_exec_tflops / ns_peak}
+                    "achieved": ns_exec_tflops, "peak": ns_peak, "unit": "TFLOP/s",
+                    "frac": ns_exec_tflops / ns_peak, "traffic": None,
+                    "dense_tflops": ns_tflops, "dense_frac": ns_tflops / ns_peak,
+                    "b2_peak": b2_mfma, "frac_of_b2": ns_exec_tflops / b2_mfma if b2_mfma else None}
     out = {
         "metric": METRIC,
         "value": n_train / (ms_per_step * 1e-3),
@@ -497,21 +561,26 @@ def main():
         "serial_ms_per_step": serial_ms,
         "phase_ms": mean,
         "ns_tflops": ns_tflops,
-        "ns_mfma_frac": ns_tflops / ns_peak,
+        "ns_dense_frac": ns_tflops / ns_peak,
         "ns_executed_tflops": ns_exec_tflops,
+        "ns_mfma_frac": ns_exec_tflops / ns_peak,
+        "ns_mfma_frac_of_b2": ns_exec_tflops / b2_mfma if b2_mfma else None,
         "ns_library_ms": lib_ms,
         "ns_library_tflops": flops / (lib_ms * 1e-3) / 1e12 if lib_ms else None,
         "gemm_tflops_measured": gemm,
         "ns_frac_of_gemm": (ns_tflops / gemm) if gemm else None,
         "adamw_gbps": adam_gbps,
         "adamw_hbm_frac": adam_gbps / PEAK_HBM_GBPS,
+        "adamw_frac_of_b2": adam_gbps / b2_mix if b2_mix else None,
         "clip_norm_gbps": norm_gbps,
+        "clip_norm_frac_of_b2": (norm_gbps / b2["hbm_read_gbps"]) if b2 else None,
         "hbm_copy_gbps": copy_gbps,
+        "b2": b2,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle on a sample)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, hp_over) if w.name.startswith("vla_hybrid") else None
+        out["cpu_baseline"] = cpu_baseline(w, hp_over)
     print(json.dumps(out), flush=True)
 
 

@@ -1,10 +1,13 @@
-"""Build the HIP library libmuon_adamw.so in-tree for gfx950.
+"""Build the HIP libraries in-tree for gfx950.
 
     python -m muon_newton_schulz_02_amd.build        # or build() from Python
 
-Every source is compiled by hipcc with --offload-arch=gfx950; packed-fp32
-instruction selection is disabled for device code.  The shared object lands
-next to this file, where the binding loads it.
+libmuon_adamw.so is the optimizer (the C ABI of include/muon_adamw.h);
+libma_peaks.so holds the ceiling probes the benchmark measures beside it
+(csrc/peaks.hip).  Every source is compiled by hipcc with
+--offload-arch=gfx950; packed-fp32 instruction selection is disabled for
+device code.  The shared objects land next to this file, where the binding
+loads them.
 """
 
 from __future__ import annotations
@@ -22,6 +25,8 @@ LIB = os.path.join(HERE, "libmuon_adamw.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["plan.cpp", "step.cpp", "elementwise.hip", "ns_gemm.hip"]
+PEAKS_SOURCES = ["peaks.hip"]
+PEAKS_LIB = os.path.join(HERE, "libma_peaks.so")
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
@@ -48,20 +53,27 @@ def _compile(hipcc: str, src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(hipcc, s), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(hipcc: str, objs, out: str):
+    tmp = out + ".tmp"
     cmd = [hipcc, "-shared", "--offload-arch=gfx950", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed: %s\n%s\n%s" % (" ".join(cmd), res.stdout, res.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link both shared libraries; returns the
+    optimizer library's path."""
+    hipcc = _hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(5, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(hipcc, s), SOURCES + PEAKS_SOURCES))
+    _link(hipcc, objs[:len(SOURCES)], LIB)
+    _link(hipcc, objs[len(SOURCES):], PEAKS_LIB)
     if verbose:
         print("built", LIB)
+        print("built", PEAKS_LIB)
     return LIB
 
 

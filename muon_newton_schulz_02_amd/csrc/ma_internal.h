@@ -36,6 +36,13 @@ constexpr int kGemmTile = 256;
 // rows on), while their share of the work is negligible.
 constexpr int64_t kBf16MinRows = 16;
 
+// bf16 Newton-Schulz iterations whose linear term a X uses the 16-bit
+// master (the bf16 pair hi + lo); later iterations use hi alone and keep no
+// lo half.  Modelled by the oracle's bf16-policy diagnostic: on the rank-8
+// spike input 3 gives 1.1e-2 relative error against fp64 (5: 1e-3, 2: 3.7e-2)
+// and on Gaussian or row-scaled inputs 6-9e-3 (5: 7-10e-3).
+constexpr int kNsLoIters = 3;
+
 // XCDs of an MI355X: consecutive workgroups of a launch are dispatched to
 // XCDs round-robin, and each XCD has its own L2.
 constexpr int kXcds = 8;

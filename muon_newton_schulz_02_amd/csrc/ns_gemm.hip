@@ -38,7 +38,12 @@
 // bf16 mode: operands bf16 (round to nearest even), v_mfma_f32_32x32x16_bf16
 // with fp32 accumulation.  The linear a*X term uses a master copy of X held
 // as a pair of bf16 values (hi = bf16(x), lo = bf16(x - hi): a 16-bit
-// mantissa), and hi is itself the MFMA operand.
+// mantissa), and hi is itself the MFMA operand.  Only the first kNsLoIters
+// iterations take the linear term from hi + lo: later ones use hi alone, so
+// the lo half of their X is neither written nor read.  The 16-bit master
+// matters while the smallest singular values are still small (an
+// ill-conditioned input loses them to a bf16-only X); after three
+// iterations they have grown enough.
 // fp32 mode: v_mfma_f32_32x32x2_f32 on fp32 operands (no reduced-precision
 // fp32 mode), master X in fp32.
 
@@ -105,6 +110,8 @@ struct Mma<float> {
 struct NsArgs {
     float a, b, c;
     int iter;
+    int use_lo;     // bf16: this iteration's linear term reads the lo half of X
+    int write_lo;   // bf16 X update: the next X keeps its lo half
     // per matrix 1 / (||u||_F + eps): the input operand is u itself, so the
     // first Gram scales by its square and the first X update by it
     const float* scales;
@@ -185,6 +192,13 @@ __device__ __forceinline__ void store8_hilo(__bf16* dhi, __bf16* dlo, const floa
     }
     gst(dhi, __builtin_bit_cast(uint4, h));
     gst(dlo, __builtin_bit_cast(uint4, l));
+}
+
+__device__ __forceinline__ void store8_hi(__bf16* dhi, const float* v) {
+    bf16x8 h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = (__bf16)v[e];
+    gst(dhi, __builtin_bit_cast(uint4, h));
 }
 
 // Make this wave's LDS writes visible to its other lanes before they read.
@@ -359,7 +373,7 @@ __device__ __forceinline__ void p_load(PIn& pin, const MuonMat& d, int lane, int
 
 template <typename T, int EPI>
 __device__ __forceinline__ void epi_load(EpiIn& in, const MuonMat& d, int lane, int bi, int bj,
-                                         int cur, bool poly_direct) {
+                                         int cur, bool poly_direct, bool use_lo) {
     constexpr bool BF = sizeof(T) == 2;
     const int gi = bi + (lane >> 1), gj = bj + (lane & 1) * 16;
     if (EPI == EPI_POLY) {
@@ -370,7 +384,10 @@ __device__ __forceinline__ void epi_load(EpiIn& in, const MuonMat& d, int lane, 
             for (int q = 0; q < (BF ? 2 : 4); ++q) in.q[q] = gld(a + q);
         }
     } else if (EPI == EPI_XUPD || EPI == EPI_FINAL) {
-        if (BF && EPI == EPI_XUPD) {
+        if (BF && !use_lo) {
+            // the linear term takes X's hi half alone (already in the
+            // accumulators): nothing to load
+        } else if (BF && EPI == EPI_XUPD) {
             const int lr = lane >> 2, lc = (lane & 3) * 8;
             const __bf16* lo = reinterpret_cast<const __bf16*>(d.xlo[cur]);
             in.q[0] = gld(lo + xblk(bi + lr, bj + lc, d.C));
@@ -517,17 +534,28 @@ __device__ __forceinline__ void epi_block(const f32x16& blk, const EpiIn& in, co
             }
             store16(out_direct + op_off<T>(gi, gj, ld_direct), v);
         } else if (BF) {
-            // a * lo of the master X; a * hi was added in the main loop
-            float lv[16];
-            unpack16(in.q, lv, true);
+            // a * lo of the master X where this iteration uses it; a * hi was
+            // added in the main loop
+            if (args.use_lo) {
+                float lv[16];
+                unpack16(in.q, lv, true);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) v[e] = escale * fmaf(args.a, lv[e], v[e]);
+                for (int e = 0; e < 16; ++e) v[e] = escale * fmaf(args.a, lv[e], v[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) v[e] *= escale;
+            }
             if (EPI == EPI_XUPD) {
                 const int64_t o0 = xblk(gi, gj, d.C), o1 = xblk(gi + 16, gj, d.C);
                 __bf16* hi = reinterpret_cast<__bf16*>(d.x[cur ^ 1]);
-                __bf16* lo = reinterpret_cast<__bf16*>(d.xlo[cur ^ 1]);
-                store8_hilo(hi + o0, lo + o0, v);
-                store8_hilo(hi + o1, lo + o1, v + 8);
+                if (args.write_lo) {
+                    __bf16* lo = reinterpret_cast<__bf16*>(d.xlo[cur ^ 1]);
+                    store8_hilo(hi + o0, lo + o0, v);
+                    store8_hilo(hi + o1, lo + o1, v + 8);
+                } else {
+                    store8_hi(hi + o0, v);
+                    store8_hi(hi + o1, v + 8);
+                }
             } else if (!d.transposed) {
                 update_run(d, up, gi, gj, v, pin);
             }
@@ -953,6 +981,7 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
         ld_direct = d.R;
     }
     const int bi0 = m0 + wm * 128, bj0 = n0 + wn * 128;
+    const bool use_lo = args.use_lo != 0;
     const float s0 = args.iter == 0 ? args.scales[tile.mat] : 1.f;
     const float escale = EPI == EPI_GRAM ? s0 * s0 : (XT ? s0 : 1.f);
     Upd up{0.f, 1.f};
@@ -968,7 +997,7 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
     EpiIn in0, in1, in2, in3;
     PIn p0, p1;
 #define NS_LOAD(SLOT, I, J) \
-    epi_load<T, EPI>(SLOT, d, lane, bi0 + (I) * 32, bj0 + (J) * 32, cur, poly_direct)
+    epi_load<T, EPI>(SLOT, d, lane, bi0 + (I) * 32, bj0 + (J) * 32, cur, poly_direct, use_lo)
 #define NS_PLOAD(SLOT, I, J) p_load<EPI>(SLOT, d, lane, bi0 + (I) * 32, bj0 + (J) * 32)
 #define NS_EPI(I, J, SLOT, PSLOT)                                                            \
     epi_block<T, EPI, SLD>(acc[I][J], SLOT, PSLOT, d, S, args, escale, up, lane,              \
@@ -1056,7 +1085,8 @@ int launch_ns_phase(int phase, int32_t group, const MuonMat* tab, const GemmTile
                     int64_t n_tiles, int iter, int last, const StepScalars& s,
                     const float* ns_scale, const StepDev* sd, void* stream) {
     if (n_tiles == 0) return (int)hipSuccess;
-    NsArgs a{s.ns_a, s.ns_b, s.ns_c, iter, ns_scale, sd};
+    NsArgs a{s.ns_a, s.ns_b, s.ns_c, iter, iter < kNsLoIters ? 1 : 0,
+             iter + 1 < kNsLoIters ? 1 : 0, ns_scale, sd};
     hipStream_t st = (hipStream_t)stream;
     const int epi = phase == 1 ? EPI_GRAM : phase == 2 ? EPI_POLY : (last ? EPI_FINAL : EPI_XUPD);
     static const NsKernel bf[4] = {k_ns_gram_bf16, k_ns_poly_bf16, k_ns_xupd_bf16, k_ns_final_bf16};
