@@ -296,11 +296,13 @@ __device__ __forceinline__ uint2 lds_tr8(const char* p) {
 }
 
 // s_waitcnt with only the vector-memory counter constrained (expcnt and
-// lgkmcnt at their maxima): vmcnt(n) for n in {0, 8, 16, 24}.  The 6-bit
+// lgkmcnt at their maxima): vmcnt(n) for n in {0, 4, 8, 12, 16, 24}.  The 6-bit
 // count is split into bits [3:0] and [15:14] of the immediate.
 __device__ __forceinline__ void wait_vm(int n) {
     if (n <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+    else if (n == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
     else if (n == 8) __builtin_amdgcn_s_waitcnt(0x0F78);
+    else if (n == 12) __builtin_amdgcn_s_waitcnt(0x0F7C);
     else if (n == 16) __builtin_amdgcn_s_waitcnt(0x4F70);
     else __builtin_amdgcn_s_waitcnt(0x4F78);
 }
@@ -1026,6 +1028,331 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
 #undef NS_EPI
 }
 
+// ---------------------------------------------------------------------------
+// bf16 tiles: eight waves per workgroup, two per SIMD.
+//
+// The 256 x 256 output tile is split into 2 x 4 wave tiles of 128 x 64 rows
+// x columns (4 x 2 accumulator blocks of 32 x 32: 128 accumulator registers),
+// so each SIMD holds two waves and the matrix instructions of one run while
+// the other waits on its LDS reads, the stage copies or the workgroup
+// barrier; with one 128 x 128 wave per SIMD every such wait left the matrix
+// core idle.  Operand staging is the same ring of four 32 KB stages with the
+// same row layouts and swizzles; each wave copies one eighth of a stage (two
+// 1 KB loads of P and two of Q).  Per stage a CU reads 96 (Gram, square) or
+// 128 (update: transposing reads of X) LDS fragments, within the LDS read
+// rate the matrix instructions leave room for.
+// ---------------------------------------------------------------------------
+constexpr int kW8Waves = 8;
+// Ring depth of these kernels: five 32 KB stages fill the 160 KB of LDS, and
+// copies run four stages ahead, so a stage's operands have three stages'
+// time (not two) to arrive from L2 or the memory-side cache.
+constexpr int kW8Stages = 5;
+
+struct Addr8 {
+    uint32_t dma_p;          // P copy: this lane's row and chunk
+    uint32_t dma_q[2];       // Q copy (row operand: [0]; transposed: first / second load)
+    uint32_t frag_a[2];      // A fragment of row block 0, per k-group
+    uint32_t frag_b[2];      // B fragment (row operand) of column block 0, per k-group
+    uint32_t frag_t[2];      // B fragment (transposed), per column block, k-group 0
+    uint32_t lin_t[2];       // linear-term reads (transposed), per column block
+    uint32_t lin_r[4];       // linear-term reads (row operand) of column block 0, per quarter
+};
+
+// Part i (0, 1) of this wave's copy of stage s: 1 KB of P rows (16 rows of
+// 64 bytes in one 32-row block row of the blocked operand), or of Q.
+__device__ __forceinline__ void copy_p8(uint32_t buf, u32x4 rp, const Addr8& ad, uint32_t wbase,
+                                        int s, int i) {
+    dma16(rp, buf + wbase + i * 1024, ad.dma_p, (uint32_t)s * 2048 + (uint32_t)i * 1024);
+}
+
+template <bool QT>
+__device__ __forceinline__ void copy_q8(uint32_t buf, u32x4 rq, const Addr8& ad, uint32_t wbase,
+                                        int s, int i, uint32_t ldq) {
+    if (QT)  // rows 4 w + 2 i, 4 w + 2 i + 1 of the stage's 32 rows of X (block row s)
+        dma16(rq, buf + kRegionBytes + wbase + i * 1024, ad.dma_q[i],
+              (uint32_t)s * 32 * ldq + (uint32_t)(2 * i) * 64);
+    else
+        dma16(rq, buf + kRegionBytes + wbase + i * 1024, ad.dma_q[0],
+              (uint32_t)s * 2048 + (uint32_t)i * 1024);
+}
+
+__device__ __forceinline__ uint4 lds16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+
+template <bool QT>
+__device__ __forceinline__ uint4 frag_b8(const char* buf, const Addr8& ad, int kg, int j) {
+    if (QT) {
+        const char* p = buf + ad.frag_t[j] + kg * 16 * 512;
+        const uint2 lo = lds_tr8(p), hi = lds_tr8(p + 4 * 512);
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+    return lds16(buf + ad.frag_b[kg] + j * 2048);
+}
+
+// Linear term of the update (a X_hi) and polynomial ((b / c) A) steps for
+// accumulator row block IB, from the stage buffer (see stage_linear).
+template <bool QT, int IB>
+__device__ __forceinline__ void lin8(f32x16 (&acc)[4][2], const char* buf, const Addr8& ad,
+                                     float scale) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint2 w = QT ? lds_tr8(buf + ad.lin_t[j] + q * 8 * 512)
+                               : *reinterpret_cast<const uint2*>(buf + ad.lin_r[q] + j * 2048);
+            const bf16x8 b = __builtin_bit_cast(bf16x8, make_uint4(w.x, w.y, 0u, 0u));
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                acc[IB][j][4 * q + e] = fmaf(scale, (float)b[e], acc[IB][j][4 * q + e]);
+        }
+    }
+}
+
+// One stage: k-group 0 with the k-group-1 fragment reads between its matrix
+// instructions, the barrier that publishes stage s + 1 and frees the buffer
+// of stage s - 1, the linear term of accumulator row block LINB (-1: none),
+// then k-group 1 with this wave's copies of stage s + kW8Stages - 1 into the
+// freed buffer and the next stage's k-group-0 reads.
+template <bool QT, int LINB>
+__device__ __forceinline__ void step8(f32x16 (&acc)[4][2], uint4 (&fa)[4], uint4 (&fb)[2],
+                                      const char* cur, const char* nxt, uint32_t tgt, u32x4 rp,
+                                      u32x4 rq, const Addr8& ad, uint32_t wbase, int s, int nk,
+                                      uint32_t ldq, float scale) {
+    uint4 ga[4], gb[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc[i][0] = Mma<__bf16>::run(fa[i], fb[0], acc[i][0]);
+        __builtin_amdgcn_sched_barrier(0);
+        ga[i] = lds16(cur + ad.frag_a[1] + i * 2048);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[i][1] = Mma<__bf16>::run(fa[i], fb[1], acc[i][1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < 2) gb[i] = frag_b8<QT>(cur, ad, 1, i);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // stage s + 1 has landed once at most the copies of the stages after it
+    // (four loads each, at most kW8Stages - 3 stages) are outstanding
+    wait_vm(4 * min(nk - 2 - s, kW8Stages - 3));
+    stage_barrier();
+    if (LINB >= 0) lin8<QT, (LINB < 0 ? 0 : LINB)>(acc, cur, ad, scale);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool cp = s + kW8Stages - 1 < nk;
+    const int sc = s + kW8Stages - 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc[i][0] = Mma<__bf16>::run(ga[i], gb[0], acc[i][0]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (cp) {
+            if (i < 2) copy_p8(tgt, rp, ad, wbase, sc, i);
+            else copy_q8<QT>(tgt, rq, ad, wbase, sc, i - 2, ldq);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        acc[i][1] = Mma<__bf16>::run(ga[i], gb[1], acc[i][1]);
+        __builtin_amdgcn_sched_barrier(0);
+        fa[i] = lds16(nxt + ad.frag_a[0] + i * 2048);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < 2) fb[i] = frag_b8<QT>(nxt, ad, 0, i);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int EPI>
+__device__ __forceinline__ void ns_gemm_tile_w8(const MuonMat* __restrict__ tab,
+                                                const GemmTile* __restrict__ tiles,
+                                                const NsArgs& args) {
+    typedef __bf16 T;
+    constexpr bool XT = EPI == EPI_XUPD || EPI == EPI_FINAL;
+    constexpr bool QT = XT;      // B X reads X row-major through transposing loads
+    constexpr int KE = kRowBytes / 2;
+    constexpr int SLD = 36;
+    __shared__ __attribute__((aligned(1024))) char ring[kW8Stages * kStageBytes];
+    static_assert(kW8Waves * 32 * SLD * 4 <= kW8Stages * kStageBytes, "epilogue staging fits in the ring");
+    static_assert(kW8Stages * kStageBytes <= 160 * 1024, "the ring fits in a CU's LDS");
+
+    const GemmTile tile = tiles[blockIdx.x];
+    if (tile.mat < 0) return;
+    const MuonMat& d = tab[tile.mat];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int cur = args.iter & 1;
+
+    const char* P;
+    const char* Q;
+    int64_t ldp, ldq;
+    int K, rows_p, rows_q;
+    if (EPI == EPI_GRAM) {
+        P = Q = reinterpret_cast<const char*>(d.x[cur]);
+        ldp = ldq = (int64_t)d.C * 2;
+        K = d.C;
+        rows_p = rows_q = d.R;
+    } else if (EPI == EPI_POLY) {
+        P = Q = reinterpret_cast<const char*>(d.a);
+        ldp = ldq = (int64_t)d.R * 2;
+        K = d.R;
+        rows_p = rows_q = d.R;
+    } else {
+        P = reinterpret_cast<const char*>(d.b);
+        ldp = (int64_t)d.R * 2;
+        K = d.R;
+        rows_p = d.R;
+        Q = reinterpret_cast<const char*>(d.x[cur]);   // R rows (the reduction index) of C
+        ldq = (int64_t)d.C * 2;
+        rows_q = d.R;
+    }
+    const int m0 = tile.tm * 256, n0 = tile.tn * 256;
+    const int nk = K / KE;
+
+    const u32x4 rp = make_rsrc(P, (int64_t)rows_p * ldp);
+    const u32x4 rq = make_rsrc(Q, (int64_t)rows_q * ldq);
+    Addr8 ad;
+    {
+        const uint32_t c = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+        ad.dma_p = (uint32_t)((m0 + wave * 32) * ldp) + (uint32_t)(lane >> 2) * 64 + c * 16;
+        if (QT) {
+            const uint32_t r = (uint32_t)(4 * wave + (lane >> 5));
+            const uint32_t ce = (uint32_t)((lane & 31) ^ (((lane >> 5) & 3) << 2));
+            const uint32_t co = (uint32_t)((lane & 31) ^ (((2 + (lane >> 5)) & 3) << 2));
+            ad.dma_q[0] = ((uint32_t)n0 / 32 + (ce >> 2)) * 2048 + r * 64 + (ce & 3) * 16;
+            ad.dma_q[1] = ((uint32_t)n0 / 32 + (co >> 2)) * 2048 + r * 64 + (co & 3) * 16;
+        } else {
+            ad.dma_q[0] = (uint32_t)((n0 + wave * 32) * ldq) + (uint32_t)(lane >> 2) * 64 + c * 16;
+            ad.dma_q[1] = ad.dma_q[0];
+        }
+        const int r32 = lane & 31, sw = (r32 >> 2) & 3, half = lane >> 5;
+#pragma unroll
+        for (int kg = 0; kg < 2; ++kg) {
+            const int slot = (2 * kg + half) ^ sw;
+            ad.frag_a[kg] = (uint32_t)((wm * 128 + r32) * kRowBytes + (slot << 4));
+            ad.frag_b[kg] = (uint32_t)(kRegionBytes + (wn * 64 + r32) * kRowBytes + (slot << 4));
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int rowb = kRegionBytes + (wn * 64 + r32) * kRowBytes;
+            ad.lin_r[q] = (uint32_t)(rowb + ((q ^ sw) << 4) + 8 * half);
+        }
+        const int g = lane >> 4, jj = lane & 15;
+        const int tsw = (jj >> 2) & 3;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int chunk = (((wn * 2 + j) ^ tsw) << 2) + 2 * (g & 1) + ((jj & 3) >> 1);
+            const int row_f = 8 * (g >> 1) + (jj >> 2);
+            const int row_l = 4 * (g >> 1) + (jj >> 2);
+            ad.frag_t[j] = (uint32_t)(kRegionBytes + row_f * 512 + (chunk << 4) + 8 * (jj & 1));
+            ad.lin_t[j] = (uint32_t)(kRegionBytes + row_l * 512 + (chunk << 4) + 8 * (jj & 1));
+        }
+    }
+    const uint32_t uldq = (uint32_t)ldq;
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const bool poly_direct = EPI == EPI_POLY && args.c != 0.f;
+    const float scale = XT ? args.a : (poly_direct ? args.b / args.c : 0.f);
+    // The linear term (a X_hi of the update, (b / c) A of the polynomial)
+    // comes from the four stages whose reduction indices are this wave's
+    // output rows: stages lin0 .. lin0 + 3, accumulator row blocks 0 .. 3.
+    const int lin0 = (XT || poly_direct) ? (m0 + wm * 128) / KE : nk;
+
+    const uint32_t wbase = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 2 * 1024);
+    const uint32_t lring = lds_addr(ring);
+#pragma unroll
+    for (int st = 0; st < kW8Stages - 1; ++st) {
+        const uint32_t b = lring + st * kStageBytes;
+        copy_p8(b, rp, ad, wbase, st, 0);
+        copy_p8(b, rp, ad, wbase, st, 1);
+        copy_q8<QT>(b, rq, ad, wbase, st, 0, uldq);
+        copy_q8<QT>(b, rq, ad, wbase, st, 1, uldq);
+    }
+    // stage 0 has landed once only the copies of stages 1 .. kW8Stages - 2
+    // are outstanding (nk >= 8 > kW8Stages - 1: all of them were issued)
+    wait_vm(4 * (kW8Stages - 2));
+    stage_barrier();
+    uint4 fa[4], fb[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = lds16(ring + ad.frag_a[0] + i * 2048);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[j] = frag_b8<QT>(ring, ad, 0, j);
+    // the ring is walked by a scalar slot index rather than unrolled: stage
+    // buffers beyond 64 KB cannot be reached by the LDS instructions'
+    // immediate offsets, so an unrolled ring would hold one set of fragment
+    // addresses per stage in registers
+    // (every wave runs all nk stages, so all take the same barriers)
+    int slot = 0, s = 0;
+#define W8_STEP(LINB)                                                                        \
+    {                                                                                        \
+        const int nslot = slot == kW8Stages - 1 ? 0 : slot + 1;                              \
+        const int tslot = slot == 0 ? kW8Stages - 1 : slot - 1; /* stage s + depth - 1 */    \
+        step8<QT, LINB>(acc, fa, fb, ring + slot * kStageBytes, ring + nslot * kStageBytes,  \
+                        lring + tslot * kStageBytes, rp, rq, ad, wbase, s, nk, uldq, scale); \
+        slot = nslot;                                                                        \
+        ++s;                                                                                 \
+    }
+#pragma unroll 1
+    while (s < lin0) W8_STEP(-1)
+    if (s < nk) {
+        W8_STEP(0)
+        W8_STEP(1)
+        W8_STEP(2)
+        W8_STEP(3)
+    }
+#pragma unroll 1
+    while (s < nk) W8_STEP(-1)
+#undef W8_STEP
+    stage_barrier();
+
+    float* S = reinterpret_cast<float*>(ring) + wave * (32 * SLD);
+    const bool mirror = (EPI == EPI_GRAM || EPI == EPI_POLY) && tile.tm != tile.tn;
+    const bool need_cols = mirror || (EPI == EPI_FINAL && d.transposed);
+    T* out_direct = nullptr;
+    int64_t ld_direct = 0;
+    if (EPI == EPI_GRAM) {
+        out_direct = reinterpret_cast<T*>(d.a);
+        ld_direct = d.R;
+    } else if (EPI == EPI_POLY) {
+        out_direct = reinterpret_cast<T*>(d.b);
+        ld_direct = d.R;
+    }
+    const int bi0 = m0 + wm * 128, bj0 = n0 + wn * 64;
+    const bool use_lo = args.use_lo != 0;
+    const float s0 = args.iter == 0 ? args.scales[tile.mat] : 1.f;
+    const float escale = EPI == EPI_GRAM ? s0 * s0 : (XT ? s0 : 1.f);
+    Upd up{0.f, 1.f};
+    if (EPI == EPI_FINAL) {
+        up.rate = (float)(args.sd->muon_lr * (double)d.shape_scale);
+        up.decay = args.sd->muon_decay;
+    }
+    // blocks in row order; each block's global inputs loaded two blocks
+    // ahead, the final update's old parameter run one block ahead (the other
+    // wave of the SIMD covers its latency; a second slot would pass the
+    // register budget below)
+    EpiIn in0, in1;
+    PIn p0;
+#define W8_LOAD(SLOT, I, J) \
+    epi_load<T, EPI>(SLOT, d, lane, bi0 + (I) * 32, bj0 + (J) * 32, cur, poly_direct, use_lo)
+#define W8_PLOAD(SLOT, I, J) p_load<EPI>(SLOT, d, lane, bi0 + (I) * 32, bj0 + (J) * 32)
+#define W8_EPI(I, J, SLOT, PSLOT)                                                            \
+    epi_block<T, EPI, SLD>(acc[I][J], SLOT, PSLOT, d, S, args, escale, up, lane,              \
+                           bi0 + (I) * 32, bj0 + (J) * 32, cur, need_cols, poly_direct,       \
+                           out_direct, ld_direct)
+    W8_LOAD(in0, 0, 0); W8_LOAD(in1, 0, 1); W8_PLOAD(p0, 0, 0);
+    W8_EPI(0, 0, in0, p0); W8_LOAD(in0, 1, 0); W8_PLOAD(p0, 0, 1);
+    W8_EPI(0, 1, in1, p0); W8_LOAD(in1, 1, 1); W8_PLOAD(p0, 1, 0);
+    W8_EPI(1, 0, in0, p0); W8_LOAD(in0, 2, 0); W8_PLOAD(p0, 1, 1);
+    W8_EPI(1, 1, in1, p0); W8_LOAD(in1, 2, 1); W8_PLOAD(p0, 2, 0);
+    W8_EPI(2, 0, in0, p0); W8_LOAD(in0, 3, 0); W8_PLOAD(p0, 2, 1);
+    W8_EPI(2, 1, in1, p0); W8_LOAD(in1, 3, 1); W8_PLOAD(p0, 3, 0);
+    W8_EPI(3, 0, in0, p0); W8_PLOAD(p0, 3, 1);
+    W8_EPI(3, 1, in1, p0);
+#undef W8_LOAD
+#undef W8_PLOAD
+#undef W8_EPI
+}
+
 // One kernel per phase and operand type, named for what it computes so that
 // traces and counters read directly.
 #define NS_KERNEL(NAME, T, EPI)                                                           \
@@ -1034,10 +1361,21 @@ __device__ __forceinline__ void ns_gemm_tile(const MuonMat* __restrict__ tab,
                                                 NsArgs args) {                            \
         ns_gemm_tile<T, EPI>(tab, tiles, args);                                          \
     }
-NS_KERNEL(k_ns_gram_bf16, __bf16, EPI_GRAM)
-NS_KERNEL(k_ns_poly_bf16, __bf16, EPI_POLY)
-NS_KERNEL(k_ns_xupd_bf16, __bf16, EPI_XUPD)
-NS_KERNEL(k_ns_final_bf16, __bf16, EPI_FINAL)
+// These kernels stay within 216 registers per wave (checked when built):
+// two GEMM waves and one AdamW wave (80 registers) of the overlapped step
+// then fill a SIMD's 512, so the side AdamW launch and the GEMM launches
+// share every CU.
+#define NS_KERNEL_W8(NAME, EPI)                                                           \
+    __global__ __launch_bounds__(kW8Waves * 64) void NAME(const MuonMat* __restrict__ tab, \
+                                                           const GemmTile* __restrict__ tiles, \
+                                                           NsArgs args) {                  \
+        ns_gemm_tile_w8<EPI>(tab, tiles, args);                                          \
+    }
+NS_KERNEL_W8(k_ns_gram_bf16, EPI_GRAM)
+NS_KERNEL_W8(k_ns_poly_bf16, EPI_POLY)
+NS_KERNEL_W8(k_ns_xupd_bf16, EPI_XUPD)
+NS_KERNEL_W8(k_ns_final_bf16, EPI_FINAL)
+#undef NS_KERNEL_W8
 NS_KERNEL(k_ns_gram_f32, float, EPI_GRAM)
 NS_KERNEL(k_ns_poly_f32, float, EPI_POLY)
 NS_KERNEL(k_ns_xupd_f32, float, EPI_XUPD)
@@ -1047,9 +1385,9 @@ NS_KERNEL(k_ns_final_f32, float, EPI_FINAL)
 typedef void (*NsKernel)(const MuonMat*, const GemmTile*, NsArgs);
 
 int launch_k(NsKernel k, const MuonMat* tab, const GemmTile* tiles, int64_t n, const NsArgs& a,
-             hipStream_t st) {
+             int threads, hipStream_t st) {
     static_assert(kGemmTile == 256, "tile lists are built for 256x256 tiles");
-    hipLaunchKernelGGL(k, dim3((unsigned)n), dim3(256), 0, st, tab, tiles, a);
+    hipLaunchKernelGGL(k, dim3((unsigned)n), dim3(threads), 0, st, tab, tiles, a);
     return (int)hipGetLastError();
 }
 
@@ -1091,7 +1429,8 @@ int launch_ns_phase(int phase, int32_t group, const MuonMat* tab, const GemmTile
     const int epi = phase == 1 ? EPI_GRAM : phase == 2 ? EPI_POLY : (last ? EPI_FINAL : EPI_XUPD);
     static const NsKernel bf[4] = {k_ns_gram_bf16, k_ns_poly_bf16, k_ns_xupd_bf16, k_ns_final_bf16};
     static const NsKernel f32[4] = {k_ns_gram_f32, k_ns_poly_f32, k_ns_xupd_f32, k_ns_final_f32};
-    return launch_k((group == kGroupBf16 ? bf : f32)[epi - 1], tab, tiles, n_tiles, a, st);
+    return group == kGroupBf16 ? launch_k(bf[epi - 1], tab, tiles, n_tiles, a, kW8Waves * 64, st)
+                               : launch_k(f32[epi - 1], tab, tiles, n_tiles, a, 256, st);
 }
 
 }  // namespace ma

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void k_peak_mfma(int iters, float* sink, uint6
 constexpr int kLdsBytes = 65536;
 
 template <bool TR>
-__global__ __launch_bounds__(256) void k_peak_lds(int iters, float* sink) {
+__global__ __launch_bounds__(256) void k_peak_lds(int iters, float* sink, uint64_t* clocks) {
     __shared__ __attribute__((aligned(16))) char buf[kLdsBytes];
     for (int i = threadIdx.x * 16; i < kLdsBytes; i += blockDim.x * 16)
         *reinterpret_cast<uint4*>(buf + i) = make_uint4(i, i + 1, i + 2, i + 3);
@@ -84,6 +84,8 @@ __global__ __launch_bounds__(256) void k_peak_lds(int iters, float* sink) {
     // addresses (a whole 1 KB row per instruction), or transposing 8-byte
     // reads at the addresses a 16 x 16 bf16 fragment load uses
     const char* base = buf + wave * 16384;
+    const uint64_t t0 = __builtin_readcyclecounter();
+    const uint64_t w0 = __builtin_amdgcn_s_memrealtime();
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
@@ -98,8 +100,17 @@ __global__ __launch_bounds__(256) void k_peak_lds(int iters, float* sink) {
                 x ^= v.x + v.y + v.z + v.w;
             }
         }
+        // the buffer may have changed as far as the compiler knows, so every
+        // pass reads LDS again (the addresses do not depend on the pass)
+        asm volatile("" ::: "memory");
     }
+    const uint64_t t1 = __builtin_readcyclecounter();
+    const uint64_t w1 = __builtin_amdgcn_s_memrealtime();
     sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = (float)x;
+    if (threadIdx.x == 0) {
+        clocks[2 * blockIdx.x] = t1 - t0;
+        clocks[2 * blockIdx.x + 1] = w1 - w0;
+    }
 }
 
 // One chunk of 16 Ki elements (4096 float4) per workgroup, 4 float4 of each
@@ -170,15 +181,17 @@ int ma_peaks_mfma(int fp32, int64_t blocks, int iters, float* sink, uint64_t* cl
 
 // `blocks` workgroups of 256 threads with 64 KB of LDS each; every wave
 // reads `iters` x 16 instructions.  Bytes read per launch: blocks * 4 *
-// iters * 16 * (1024 plain | 512 transposing).  sink: blocks * 256 floats.
-int ma_peaks_lds(int transposing, int64_t blocks, int iters, float* sink, void* stream) {
-    if (blocks < 1 || iters < 1 || !sink) return (int)hipErrorInvalidValue;
+// iters * 16 * (1024 plain | 512 transposing).  sink: blocks * 256 floats;
+// clocks: 2 * blocks uint64, as for ma_peaks_mfma.
+int ma_peaks_lds(int transposing, int64_t blocks, int iters, float* sink, uint64_t* clocks,
+                 void* stream) {
+    if (blocks < 1 || iters < 1 || !sink || !clocks) return (int)hipErrorInvalidValue;
     if (transposing)
         hipLaunchKernelGGL(k_peak_lds<true>, dim3((unsigned)blocks), dim3(256), 0,
-                           (hipStream_t)stream, iters, sink);
+                           (hipStream_t)stream, iters, sink, clocks);
     else
         hipLaunchKernelGGL(k_peak_lds<false>, dim3((unsigned)blocks), dim3(256), 0,
-                           (hipStream_t)stream, iters, sink);
+                           (hipStream_t)stream, iters, sink, clocks);
     return (int)hipGetLastError();
 }
 

@@ -28,7 +28,8 @@ def load(path: str = LIB_PATH):
                            "`python -m muon_newton_schulz_02_amd.build` first" % path)
     lib = C.CDLL(path)
     lib.ma_peaks_mfma.argtypes = [C.c_int, C.c_int64, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
-    lib.ma_peaks_lds.argtypes = [C.c_int, C.c_int64, C.c_int, C.c_void_p, C.c_void_p]
+    lib.ma_peaks_lds.argtypes = [C.c_int, C.c_int64, C.c_int, C.c_void_p, C.c_void_p,
+                                 C.c_void_p]
     lib.ma_peaks_stream.argtypes = [C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.c_int64, C.c_void_p, C.c_void_p]
     for f in (lib.ma_peaks_mfma, lib.ma_peaks_lds, lib.ma_peaks_stream):
@@ -79,19 +80,24 @@ def mfma(torch, fp32: bool = False, blocks: int = CUS, iters: int = 0, reps: int
 
 def lds(torch, transposing: bool = False, blocks: int = 2 * CUS, iters: int = 4000,
         reps: int = 3) -> dict:
-    """LDS read bandwidth: total GB/s and bytes per shader cycle per CU at
-    `sclk_mhz` (two 64 KB workgroups per CU, four waves each)."""
+    """LDS read bandwidth: total GB/s, the shader clock during the loop and
+    bytes per shader cycle per CU (two 64 KB workgroups per CU, four waves
+    each)."""
     lib = load()
     sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
     st = torch.cuda.current_stream().cuda_stream
 
     def go():
-        _check(lib.ma_peaks_lds(1 if transposing else 0, blocks, iters, sink.data_ptr(), st),
-               "ma_peaks_lds")
+        _check(lib.ma_peaks_lds(1 if transposing else 0, blocks, iters, sink.data_ptr(),
+                                clocks.data_ptr(), st), "ma_peaks_lds")
 
     ms = _timed(torch, go, reps)
     nbytes = blocks * 4.0 * iters * 16 * (512.0 if transposing else 1024.0)
-    return {"gbps": nbytes / (ms * 1e-3) / 1e9}
+    cyc = clocks.view(-1, 2).double()
+    mhz = float((cyc[:, 0] / (cyc[:, 1] / 100.0)).median())
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"gbps": gbps, "sclk_mhz": mhz, "bytes_per_clk_per_cu": gbps * 1e9 / (mhz * 1e6) / CUS}
 
 
 def stream(torch, kind: str, gib: float = 1.0, reps: int = 3) -> dict:
@@ -126,14 +132,14 @@ def measure_all(torch) -> dict:
     f32 = mfma(torch, True)
     l16 = lds(torch, False)
     ltr = lds(torch, True)
-    mhz = bf["sclk_mhz"]
     out = {
         "mfma_bf16_tflops": bf["tflops"], "mfma_bf16_sclk_mhz": bf["sclk_mhz"],
         "mfma_fp32_tflops": f32["tflops"], "mfma_fp32_sclk_mhz": f32["sclk_mhz"],
         "lds_read_b128_gbps": l16["gbps"],
-        "lds_read_b128_bytes_per_clk_per_cu": l16["gbps"] * 1e9 / (mhz * 1e6) / CUS,
+        "lds_read_b128_bytes_per_clk_per_cu": l16["bytes_per_clk_per_cu"],
         "lds_read_tr_b64_gbps": ltr["gbps"],
-        "lds_read_tr_b64_bytes_per_clk_per_cu": ltr["gbps"] * 1e9 / (mhz * 1e6) / CUS,
+        "lds_read_tr_b64_bytes_per_clk_per_cu": ltr["bytes_per_clk_per_cu"],
+        "lds_sclk_mhz": l16["sclk_mhz"],
         "hbm_read_gbps": stream(torch, "read", 4.0)["gbps"],
         "hbm_copy_gbps": stream(torch, "copy", 2.0)["gbps"],
         "hbm_adamw_mix_gbps": stream(torch, "adamw_mix", 1.0)["gbps"],
