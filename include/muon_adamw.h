@@ -319,6 +319,41 @@ int muon_adamw_step_profiled(const ma_plan* plan,
                              float* const* muon_update_out,
                              void* const* phase_events);
 
+/* Largest workspace (bytes) of a plan that muon_adamw_step_noalloc accepts:
+ * the size of its per-device scratch. */
+#define MA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* muon_adamw_step for callers that cannot allocate memory (code in tight
+ * serving loops, or harnesses that forbid allocation calls): the same
+ * computation, arguments and errors, with the workspace replaced by a
+ * device scratch array that the library holds in its code object -- one
+ * copy of MA_NOALLOC_SCRATCH_BYTES on every GPU it runs on, kept until the
+ * process ends.  This call allocates nothing: no device or pinned memory,
+ * and no streams or events (every kernel of the step runs on `stream`; the
+ * AdamW group does not run beside the Muon group and Newton-Schulz batches
+ * run one after another, so it is slower than muon_adamw_step with
+ * overlap).  Its descriptor tables travel in kernel arguments.
+ *
+ * All calls on one GPU share that GPU's scratch, which keeps the last call's
+ * contents; each call writes every part of it that it reads before reading
+ * it, so no state carries over.  Calls that overlap on one GPU (on
+ * different streams or host threads) race on the scratch and give wrong
+ * results: callers must order them.  A step under stream capture is refused
+ * (a replay could meet another plan's data in the shared scratch).
+ *
+ * Errors: as muon_adamw_step, plus WORKSPACE when the plan's workspace
+ * (muon_adamw_workspace_size for hp->ns_precision) exceeds
+ * MA_NOALLOC_SCRATCH_BYTES, and CAPTURE under stream capture; nothing is
+ * launched then. */
+int muon_adamw_step_noalloc(const ma_plan* plan,
+                            float* const* params,
+                            const float* const* grads,
+                            ma_state* state,
+                            const ma_hparams* hp,
+                            void* stream,
+                            float* grad_norm_out,
+                            float* const* muon_update_out);
+
 /* Release a plan (NULL is a no-op).  Must not race with a step using it;
  * device work already queued does not reference plan memory after the step
  * returns... except the library's pinned staging buffers, which are freed

@@ -18,13 +18,15 @@ from . import _abi
 from ._abi import (MA_ERR_CAPTURE, MA_ERR_HIP, MA_ERR_INVALID_ARG, MA_ERR_SHAPE, MA_ERR_UNSUPPORTED,  # noqa: F401
                    MA_ERR_WORKSPACE, MA_GROUP_ADAMW, MA_GROUP_MUON, MA_GROUP_NONE,
                    MA_LR_CONSTANT, MA_LR_COSINE_MIN, MA_MODE_ADAMW, MA_MODE_MUON_ADAMW,
-                   MA_NS_BF16, MA_NS_FP32, MA_OK, MA_PARAM_BF16, MA_PARAM_FP32)
+                   MA_NOALLOC_SCRATCH_BYTES, MA_NS_BF16, MA_NS_FP32, MA_OK, MA_PARAM_BF16,
+                   MA_PARAM_FP32)
 
 __all__ = [
     "MuonAdamWError", "Plan", "State",
     "muon_adamw_default_hparams", "muon_adamw_plan", "muon_adamw_plan_size",
     "muon_adamw_plan_entry", "muon_adamw_plan_dump", "muon_adamw_workspace_size",
-    "muon_adamw_step", "muon_adamw_step_profiled", "muon_adamw_plan_free", "muon_adamw_last_error",
+    "muon_adamw_step", "muon_adamw_step_profiled", "muon_adamw_step_noalloc",
+    "muon_adamw_plan_free", "muon_adamw_last_error",
     "muon_adamw_version", "MuonAdamW", "load_library",
 ]
 
@@ -251,6 +253,14 @@ def muon_adamw_step_profiled(plan: Plan, params, grads, state: State, hp: _abi.m
           phase_events)
 
 
+def muon_adamw_step_noalloc(plan: Plan, params, grads, state: State, hp: _abi.ma_hparams,
+                            stream=None, grad_norm_out=None, muon_update_out=None) -> None:
+    """muon_adamw_step without a workspace and without any allocation: the
+    library's per-device scratch (MA_NOALLOC_SCRATCH_BYTES) serves, every
+    kernel runs on `stream`, and calls on one GPU must not overlap."""
+    _step(plan, params, grads, state, hp, None, stream, grad_norm_out, muon_update_out, None)
+
+
 def _step(plan, params, grads, state, hp, workspace, stream, grad_norm_out, muon_update_out,
           phase_events):
     n = len(plan.names)
@@ -273,7 +283,9 @@ def _step(plan, params, grads, state, hp, workspace, stream, grad_norm_out, muon
         stream = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
     elif not isinstance(stream, int):
         stream = stream.cuda_stream
-    if isinstance(workspace, tuple):
+    if workspace is None:
+        ws_ptr, ws_bytes = 0, 0          # the allocation-free step: no workspace
+    elif isinstance(workspace, tuple):
         ws_ptr, ws_bytes = int(workspace[0]), int(workspace[1])
     else:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
@@ -288,7 +300,10 @@ def _step(plan, params, grads, state, hp, workspace, stream, grad_norm_out, muon
     args = (plan.handle, pa, ga, C.byref(st), C.byref(hp), C.c_void_p(ws_ptr), ws_bytes,
             C.c_void_p(stream), C.c_void_p(_ptr(grad_norm_out, numel=1, what="grad_norm_out") or 0),
             ua)
-    if phase_events is None:
+    if workspace is None:
+        rc = _abi.load().muon_adamw_step_noalloc(args[0], args[1], args[2], args[3], args[4],
+                                                 args[7], args[8], args[9])
+    elif phase_events is None:
         rc = _abi.load().muon_adamw_step(*args)
     else:
         ev = (C.c_void_p * _abi.MA_PROFILE_EVENTS)(*[int(e) for e in phase_events])

@@ -28,6 +28,7 @@ MA_LR_CONSTANT, MA_LR_COSINE_MIN = 0, 1
 MA_PARAM_FP32, MA_PARAM_BF16 = 0, 1
 MA_MAX_NDIM = 8
 MA_PROFILE_EVENTS = 5
+MA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class ma_param_desc(C.Structure):
@@ -84,6 +85,10 @@ SIGNATURES = [
                                            C.POINTER(ma_hparams), C.c_void_p, C.c_size_t,
                                            C.c_void_p, C.c_void_p, C.POINTER(C.c_void_p),
                                            C.POINTER(C.c_void_p)]),
+    ("muon_adamw_step_noalloc", C.c_int, [C.c_void_p, C.POINTER(C.c_void_p),
+                                          C.POINTER(C.c_void_p), C.POINTER(ma_state),
+                                          C.POINTER(ma_hparams), C.c_void_p, C.c_void_p,
+                                          C.POINTER(C.c_void_p)]),
     ("muon_adamw_plan_free", None, [C.c_void_p]),
     ("muon_adamw_last_error", C.c_char_p, []),
     ("muon_adamw_version", C.c_char_p, []),

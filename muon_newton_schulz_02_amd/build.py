@@ -24,7 +24,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libmuon_adamw.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["plan.cpp", "step.cpp", "elementwise.hip", "ns_gemm.hip"]
+SOURCES = ["plan.cpp", "step.cpp", "elementwise.hip", "ns_gemm.hip", "noalloc.hip"]
 PEAKS_SOURCES = ["peaks.hip"]
 PEAKS_LIB = os.path.join(HERE, "libma_peaks.so")
 

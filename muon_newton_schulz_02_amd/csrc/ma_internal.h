@@ -61,6 +61,9 @@ constexpr size_t kNsOverlapBatchBytes = size_t(160) << 20;
 // Pinned host buffers the descriptor tables are staged in, used in rotation:
 // a step waits for the upload of the step this many calls before it.
 constexpr int kStagingSlots = 4;
+// Bytes of the per-device scratch the allocation-free step works in (the
+// largest workspace it accepts).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
@@ -196,6 +199,9 @@ struct ma_plan {
     // counter uploaded, and where: a captured step with the same tables and
     // workspace reads them from the workspace instead of uploading
     mutable std::vector<char> table_cache;
+    // host copy of the tables for the allocation-free step, sized when the
+    // plan is built (the larger of the two precisions' tables)
+    mutable std::vector<char> noalloc_tables;
     mutable const void* table_cache_ws = nullptr;
     mutable int32_t table_cache_prec = -1;
 };
@@ -236,6 +242,14 @@ void clear_error();
 
 // Build the layout of one precision (called by the plan builder).
 void build_layout(ma_plan* plan, int32_t precision);
+
+// The device address of the allocation-free step's scratch on the current
+// device (looked up once per device with hipGetSymbolAddress).  hipError_t.
+int noalloc_scratch(void** out);
+// Copies `bytes` (a multiple of 16) from host memory to device memory
+// through kernel arguments, on `stream`: the host buffer is free again when
+// this returns.  hipError_t.
+int launch_copy_args(void* dst, const void* src, size_t bytes, void* stream);
 
 // --------------------------------------------------------- launchers -----
 // Constants of the step that do not depend on the step number, formed in

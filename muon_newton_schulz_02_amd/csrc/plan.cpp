@@ -519,6 +519,8 @@ int muon_adamw_plan(const ma_param_desc* table, int32_t n, const ma_plan_opts* o
     build_tables(p);
     build_layout(p, MA_NS_BF16);
     build_layout(p, MA_NS_FP32);
+    p->noalloc_tables.assign(
+        std::max(p->layout[MA_NS_BF16].tables_bytes, p->layout[MA_NS_FP32].tables_bytes), 0);
     p->dump = make_dump(*p);
     *out = p;
     clear_error();

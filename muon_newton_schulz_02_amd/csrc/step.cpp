@@ -146,19 +146,16 @@ int get_side(const ma_plan* plan, ma_plan::Side** out) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-int muon_adamw_step(const ma_plan* plan, float* const* params, const float* const* grads,
-                    ma_state* state, const ma_hparams* hp, void* workspace, size_t ws_bytes,
-                    void* stream, float* grad_norm_out, float* const* muon_update_out) {
-    return muon_adamw_step_profiled(plan, params, grads, state, hp, workspace, ws_bytes, stream,
-                                    grad_norm_out, muon_update_out, nullptr);
-}
-
-int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const float* const* grads,
-                             ma_state* state, const ma_hparams* hp, void* workspace,
-                             size_t ws_bytes, void* stream, float* grad_norm_out,
-                             float* const* muon_update_out, void* const* phase_events) {
+// One step.  no_alloc: the allocation-free variant -- every launch on the
+// caller's stream (no library streams or events are created), the
+// descriptor tables uploaded through kernel arguments (no pinned staging),
+// and `workspace` the device scratch.
+int step_impl(const ma_plan* plan, float* const* params, const float* const* grads,
+              ma_state* state, const ma_hparams* hp, void* workspace, size_t ws_bytes,
+              void* stream, float* grad_norm_out, float* const* muon_update_out,
+              void* const* phase_events, bool no_alloc) {
     // ---------------------------------------------------------- validate --
     if (!plan || !state || !hp) {
         set_error("muon_adamw_step: plan, state and hp are required");
@@ -330,6 +327,12 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
         set_error("muon_adamw_step: a captured step needs state->device_step");
         return MA_ERR_CAPTURE;
     }
+    if (no_alloc && capturing) {
+        set_error("muon_adamw_step_noalloc: the step cannot be captured (every call on a GPU "
+                  "shares its scratch, so a replay could find another plan's data there); "
+                  "capture muon_adamw_step with a caller-owned workspace instead");
+        return MA_ERR_CAPTURE;
+    }
 
     std::lock_guard<std::mutex> lock(plan->mu);
     // ------------------------------------------------- descriptor tables --
@@ -420,7 +423,16 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     // eager steps while the graph still points at it): it relies on the
     // tables the last eager step with a device step counter put in this
     // workspace, and is refused unless those are the tables it needs.
-    if (capturing) {
+    if (no_alloc) {
+        // the plan's host copy of the tables, sized at plan time; each chunk
+        // travels in a copy kernel's arguments, which the runtime copies at
+        // enqueue time, so the buffer may be refilled by the next call
+        plan->table_cache_ws = nullptr;
+        char* hb = plan->noalloc_tables.data();
+        fill_tables(hb);
+        int er = launch_copy_args(base + L.tables_off, hb, L.tables_bytes, stream);
+        if (er) return hip_fail("table upload", er);
+    } else if (capturing) {
         std::vector<char> fresh(L.tables_bytes);
         fill_tables(fresh.data());
         const bool cached = plan->table_cache_ws == workspace && plan->table_cache_prec == prec &&
@@ -504,8 +516,8 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     guard.main = st;
     guard.side = &side;
     // (the chunk counter is an int: beyond 2^30 chunks run serially)
-    const bool overlap =
-        plan->overlap && n_adam > 0 && n_muon > 0 && plan->n_adam_chunks < (int64_t(1) << 30);
+    const bool overlap = !no_alloc && plan->overlap && n_adam > 0 && n_muon > 0 &&
+                         plan->n_adam_chunks < (int64_t(1) << 30);
     auto fork_adamw = [&]() -> int {
         int rs = get_side(plan, &side);
         if (rs != MA_OK) return rs;
@@ -538,7 +550,9 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     if (n_muon > 0) {
         static_assert(kNsStreams == 2, "one caller stream and one side stream");
         const int nb = (int)L.ns_batches.size();
-        const bool split = nb > 1;
+        // without library streams the batches run one after another on the
+        // caller's stream (each matrix's phases stay in order either way)
+        const bool split = nb > 1 && !no_alloc;
         // With two batches and nothing beside them, the second batch's
         // momentum/normalise pass (HBM-bound) runs on the side stream while
         // the first batch's Gram launches (matrix-core bound) start.  A
@@ -582,7 +596,7 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
                 for (int ph = 0; ph < 3; ++ph) {
                     for (int q = 0; q < kNsStreams && b0 + q < nb; ++q) {
                         const auto& bt = L.ns_batches[b0 + q];
-                        void* qs = q == 0 ? stream : (void*)nss;
+                        void* qs = (q == 0 || !split) ? stream : (void*)nss;
                         for (int g = 0; g < 2; ++g) {
                             err = launch_ns_phase(
                                 ph + 1, g, d_muon,
@@ -627,6 +641,51 @@ int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const fl
     if (!state->device_step) state->step = in.t_host;
     clear_error();
     return MA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int muon_adamw_step(const ma_plan* plan, float* const* params, const float* const* grads,
+                    ma_state* state, const ma_hparams* hp, void* workspace, size_t ws_bytes,
+                    void* stream, float* grad_norm_out, float* const* muon_update_out) {
+    return step_impl(plan, params, grads, state, hp, workspace, ws_bytes, stream, grad_norm_out,
+                     muon_update_out, nullptr, false);
+}
+
+int muon_adamw_step_profiled(const ma_plan* plan, float* const* params, const float* const* grads,
+                             ma_state* state, const ma_hparams* hp, void* workspace,
+                             size_t ws_bytes, void* stream, float* grad_norm_out,
+                             float* const* muon_update_out, void* const* phase_events) {
+    return step_impl(plan, params, grads, state, hp, workspace, ws_bytes, stream, grad_norm_out,
+                     muon_update_out, phase_events, false);
+}
+
+int muon_adamw_step_noalloc(const ma_plan* plan, float* const* params, const float* const* grads,
+                            ma_state* state, const ma_hparams* hp, void* stream,
+                            float* grad_norm_out, float* const* muon_update_out) {
+    if (!plan || !hp) {
+        set_error("muon_adamw_step_noalloc: plan and hp are required");
+        return MA_ERR_INVALID_ARG;
+    }
+    if (hp->ns_precision != MA_NS_BF16 && hp->ns_precision != MA_NS_FP32) {
+        set_error("muon_adamw_step_noalloc: unknown ns_precision %d", hp->ns_precision);
+        return MA_ERR_UNSUPPORTED;
+    }
+    const size_t need = plan->layout[hp->ns_precision].total;
+    if (need > kNoAllocScratchBytes) {
+        set_error("muon_adamw_step_noalloc: this plan needs %zu bytes of workspace, above the "
+                  "%zu-byte device scratch of the allocation-free step; use muon_adamw_step "
+                  "with a caller-allocated workspace",
+                  need, (size_t)kNoAllocScratchBytes);
+        return MA_ERR_WORKSPACE;
+    }
+    void* scratch = nullptr;
+    int e = noalloc_scratch(&scratch);
+    if (e) return hip_fail("hipGetSymbolAddress (scratch)", e);
+    return step_impl(plan, params, grads, state, hp, scratch, kNoAllocScratchBytes, stream,
+                     grad_norm_out, muon_update_out, nullptr, true);
 }
 
 void muon_adamw_plan_free(ma_plan* plan) {

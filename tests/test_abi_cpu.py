@@ -41,7 +41,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
     from muon_newton_schulz_02_amd import _abi
@@ -376,3 +376,22 @@ def test_binding_checks_sizes_against_the_plan(lib):
     # the right sizes get as far as the device check
     with pytest.raises(ValueError, match="GPU"):
         M.muon_adamw_step(plan, [torch.zeros(4, 6), A], [A, A], state(), hp, ws, stream=0)
+
+
+def test_noalloc_refuses_plans_beyond_its_scratch(lib):
+    """The allocation-free step accepts plans whose workspace fits its
+    per-device scratch and refuses larger ones before any GPU call
+    (fake addresses are never dereferenced)."""
+    from muon_newton_schulz_02_amd import _abi
+    text = open(HEADER).read()
+    assert "#define MA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert _abi.MA_NOALLOC_SCRATCH_BYTES == 64 << 20
+    plan = M.muon_adamw_plan([("action_expert.layers.0.q.weight", (4096, 4096), True)])
+    assert M.muon_adamw_workspace_size(plan, M.MA_NS_BF16) > M.MA_NOALLOC_SCRATCH_BYTES
+    st = M.State(1)
+    st.muon_momentum[0] = 1 << 40
+    with pytest.raises(M.MuonAdamWError) as e:
+        M.muon_adamw_step_noalloc(plan, [1 << 40], [1 << 41], st, M.muon_adamw_default_hparams())
+    assert e.value.code == M.MA_ERR_WORKSPACE
+    assert "scratch" in str(e.value)
+    assert st.step == 0
