@@ -402,7 +402,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
     const float coef = sd->coef;
     // one counter for the whole group: per-XCD counters over contiguous
     // eighths (as k_adamw maps its chunks) made the overlapped step 0.65 ms
-    // slower on the full hybrid table
+    // slower on the full hybrid table.  Claims on one address serialise
+    // (about 12 ns each), so a wave that starts after every chunk was claimed
+    // leaves after a plain read of the counter: 8192 idle waves of the
+    // finishing launch took 95 us with an atomic each.
+    {
+        int c = 0;
+        if (lane == 0) c = __hip_atomic_load(&sd->claim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        c = __builtin_amdgcn_readfirstlane(c);
+        if ((int64_t)c >= n_chunks) return;
+    }
     for (;;) {
         int c = 0;
         if (lane == 0) c = atomicAdd(&sd->claim, 1);

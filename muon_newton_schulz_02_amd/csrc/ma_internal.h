@@ -116,8 +116,15 @@ struct GemmTile {
 };
 
 // ------------------------------------------------------------ workspace --
-// Operand precision groups of the NS launches.
-enum { kGroupBf16 = 0, kGroupFp32 = 1 };
+// Launch groups of the NS tiles.  The operand precision of a matrix is
+// kGroupBf16 or kGroupFp32; fp32 matrices with at most kSmallRows padded
+// rows (in a batch of only such fp32 matrices) have their tiles in
+// kGroupFp32Small, as kSmallTile x kSmallTile pieces of the 256 x 256 tiles
+// (64 times as many workgroups, so a launch over a few such matrices still
+// spreads over the GPU).
+enum { kGroupBf16 = 0, kGroupFp32 = 1, kGroupFp32Small = 2, kNsGroups = 3 };
+constexpr int kSmallTile = 32;
+constexpr int64_t kSmallRows = 256;
 
 struct Layout {
     size_t tables_off = 0, tables_bytes = 0;
@@ -125,8 +132,8 @@ struct Layout {
     std::vector<int32_t> op_group;                   // per Muon matrix: kGroupBf16 / kGroupFp32
     // Newton-Schulz batches; batch b runs on NS stream b % kNsStreams
     struct NsBatch {
-        std::vector<GemmTile> tiles[3][2];           // [phase - 1][operand group], cost-ordered
-        size_t off[3][2] = {};                       // their offsets in the workspace
+        std::vector<GemmTile> tiles[3][kNsGroups];   // [phase - 1][launch group], cost-ordered
+        size_t off[3][kNsGroups] = {};               // their offsets in the workspace
         bool gram_split = false;                     // fp32 Gram partials to sum after the launch
     };
     std::vector<NsBatch> ns_batches;
@@ -302,7 +309,8 @@ int launch_muon_scale(const MuonMat* tab, int32_t n_tab, const float* partials, 
 // After a batch's fp32 Gram launch: A += its split reductions' partial Grams.
 int launch_gram_reduce(const MuonMat* tab, int32_t n_tab, int32_t batch, void* stream);
 // phase 1 = Gram, 2 = polynomial, 3 = X update (the parameter update when
-// `last`); group = kGroupBf16 / kGroupFp32 selects the operand type.
+// `last`); group = kGroupBf16 / kGroupFp32 / kGroupFp32Small selects the
+// operand type and tile size.
 // `ns_scale`: the per-matrix normalising factor, applied on iteration 0;
 // the last iteration's update reads its rate and decay from *sd.
 int launch_ns_phase(int phase, int32_t group, const MuonMat* tab, const GemmTile* tiles,

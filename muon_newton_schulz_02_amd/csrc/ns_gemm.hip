@@ -1353,6 +1353,166 @@ __device__ __forceinline__ void ns_gemm_tile_w8(const MuonMat* __restrict__ tab,
 #undef W8_EPI
 }
 
+// ---------------------------------------------------------------------------
+// Small fp32 tiles: 32 x 32 outputs, for matrices of at most 256 padded rows.
+//
+// A launch over a few such matrices holds only tens of 256 x 256 tiles, each
+// a long chain of matrix instructions on one CU while the rest of the GPU
+// idles.  Here a tile is 32 x 32 (64 times as many workgroups) and its
+// reduction is split four ways: wave w of the workgroup reduces over the
+// w-th quarter of K into its own accumulator block, so a wave's chain is a
+// sixteenth of a 64 x 64 tile's.  The waves read their fragments straight
+// from global memory (no operand is shared between them): lane l holds row
+// l % 32 and, of every 32-column block, the 16 columns from 16 (l / 32) on,
+// as four 16-byte loads; fragment g of the block pairs columns
+// 16 h + 4 g .. 16 h + 4 g + 3 of both operands (h = lane half), so the four
+// MFMA steps of each fragment cover the block once.  Two or four blocks are
+// in flight per wave.  Waves 1..3 then hand their sums to wave 0 through LDS;
+// wave 0 adds them in wave order (a fixed order: reruns are bitwise equal)
+// and runs the epilogue of the large tiles on its one block.
+// ---------------------------------------------------------------------------
+constexpr int kS32 = 32;
+static_assert(kS32 == kSmallTile, "small tile lists are built for 32x32 tiles");
+
+// Bytes [kb, kb + 64) of this lane's operand row (base already points at the
+// row and lane half): four 16-byte loads.
+__device__ __forceinline__ void s32_load(uint4 (&v)[4], const char* base, int64_t kb) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) v[g] = gld(base + kb + 16 * g);
+}
+
+// Blocks in flight per wave: 2 where a wave's share of K is one 64-column
+// pair (square and update steps: K = 256), deeper for the Gram, whose
+// reduction runs along the long side.
+template <int EPI>
+constexpr int kS32Depth = EPI == EPI_GRAM ? 4 : 2;
+
+__device__ __forceinline__ void s32_mma(f32x16& acc, const uint4 (&a)[4], const uint4 (&b)[4]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc = Mma<float>::run(a[g], b[g], acc);
+}
+
+template <int EPI>
+__device__ __forceinline__ void ns_gemm_tile_s32(const MuonMat* __restrict__ tab,
+                                                 const GemmTile* __restrict__ tiles,
+                                                 const NsArgs& args) {
+    constexpr bool XT = EPI == EPI_XUPD || EPI == EPI_FINAL;
+    constexpr int SLD = 36;
+    __shared__ __attribute__((aligned(16))) float red[3][16][64];  // waves 1..3: [register][lane]
+    __shared__ __attribute__((aligned(16))) float stage[32 * SLD];  // wave 0's epilogue staging
+
+    const GemmTile tile = tiles[blockIdx.x];
+    if (tile.mat < 0) return;  // padding of a shorter per-XCD list
+    const MuonMat& d = tab[tile.mat];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int cur = args.iter & 1;
+
+    // operands: fp32, row-major, reduction index contiguous (as for the
+    // large fp32 tiles)
+    const char* P;
+    const char* Q;
+    int64_t ldp, ldq;  // bytes
+    int K;
+    if (EPI == EPI_GRAM) {
+        P = Q = reinterpret_cast<const char*>(d.x[0]);
+        ldp = ldq = (int64_t)d.C * 4;
+        K = d.C;
+        if (d.gram_ks > 1) {
+            // slice tile.slice of a split reduction
+            K = d.C / d.gram_ks;
+            P += (int64_t)tile.slice * K * 4;
+            Q = P;
+        }
+    } else if (EPI == EPI_POLY) {
+        P = Q = reinterpret_cast<const char*>(d.a);
+        ldp = ldq = (int64_t)d.R * 4;
+        K = d.R;
+    } else {
+        P = reinterpret_cast<const char*>(d.b);
+        ldp = (int64_t)d.R * 4;
+        Q = reinterpret_cast<const char*>(d.xt[cur]);  // X^T: C rows of R
+        ldq = (int64_t)d.R * 4;
+        K = d.R;
+    }
+    const int m0 = tile.tm * kS32, n0 = tile.tn * kS32;
+    const int kq = K / 4;    // this wave's columns: a multiple of 64 (K is padded to 256)
+    const int nb = kq / 32;  // its 32-column blocks: at least 2
+    const int r = lane & 31, h = lane >> 5;
+    const char* pa = P + (int64_t)(m0 + r) * ldp + ((int64_t)wave * kq + 16 * h) * 4;
+    const char* qa = Q + (int64_t)(n0 + r) * ldq + ((int64_t)wave * kq + 16 * h) * 4;
+
+    // wave 0's epilogue inputs, loaded now so their latency hides behind the loop
+    EpiIn in;
+    PIn pin;
+    if (wave == 0) {
+        epi_load<float, EPI>(in, d, lane, m0, n0, cur, false, false);
+        p_load<EPI>(pin, d, lane, m0, n0);
+    }
+
+    // D blocks in flight: buffer i holds block kb + i.  Loads past the last
+    // block re-read it (cache hits) and are not multiplied, so every
+    // iteration of the loop issues the same loads and waits the same counts;
+    // the last D blocks are multiplied after it, with no further loads.
+    constexpr int D = kS32Depth<EPI>;
+    uint4 a[D][4], b[D][4];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        const int64_t o = (int64_t)min(i, nb - 1) * 128;
+        s32_load(a[i], pa, o);
+        s32_load(b[i], qa, o);
+    }
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    int kb = 0;
+    for (; kb + D < nb; kb += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            s32_mma(acc, a[i], b[i]);
+            const int64_t o = (int64_t)min(kb + i + D, nb - 1) * 128;
+            s32_load(a[i], pa, o);
+            s32_load(b[i], qa, o);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        if (kb + i < nb) s32_mma(acc, a[i], b[i]);
+
+    if (wave != 0) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) red[wave - 1][e][lane] = acc[e];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] += red[w][e][lane];
+
+    const bool mirror = (EPI == EPI_GRAM || EPI == EPI_POLY) && tile.tm != tile.tn;
+    const bool need_cols = mirror || EPI == EPI_XUPD || (EPI == EPI_FINAL && d.transposed);
+    float* out_direct = nullptr;
+    int64_t ld_direct = 0;
+    if (EPI == EPI_GRAM) {
+        out_direct = reinterpret_cast<float*>(
+            tile.slice == 0 ? d.a : d.apart + (uint64_t)(tile.slice - 1) * d.R * d.R * 4);
+        ld_direct = d.R;
+    } else if (EPI == EPI_POLY) {
+        out_direct = reinterpret_cast<float*>(d.b);
+        ld_direct = d.R;
+    }
+    const float s0 = args.iter == 0 ? args.scales[tile.mat] : 1.f;
+    const float escale = EPI == EPI_GRAM ? s0 * s0 : (XT ? s0 : 1.f);
+    Upd up{0.f, 1.f};
+    if (EPI == EPI_FINAL) {
+        up.rate = (float)(args.sd->muon_lr * (double)d.shape_scale);
+        up.decay = args.sd->muon_decay;
+    }
+    epi_block<float, EPI, SLD>(acc, in, pin, d, stage, args, escale, up, lane, m0, n0, cur,
+                               need_cols, false, out_direct, ld_direct);
+}
+
 // One kernel per phase and operand type, named for what it computes so that
 // traces and counters read directly.
 #define NS_KERNEL(NAME, T, EPI)                                                           \
@@ -1381,12 +1541,23 @@ NS_KERNEL(k_ns_poly_f32, float, EPI_POLY)
 NS_KERNEL(k_ns_xupd_f32, float, EPI_XUPD)
 NS_KERNEL(k_ns_final_f32, float, EPI_FINAL)
 #undef NS_KERNEL
+#define NS_KERNEL_S32(NAME, EPI)                                                          \
+    __global__ __launch_bounds__(256) void NAME(const MuonMat* __restrict__ tab,          \
+                                                const GemmTile* __restrict__ tiles,       \
+                                                NsArgs args) {                            \
+        ns_gemm_tile_s32<EPI>(tab, tiles, args);                                         \
+    }
+NS_KERNEL_S32(k_ns_gram_f32_s32, EPI_GRAM)
+NS_KERNEL_S32(k_ns_poly_f32_s32, EPI_POLY)
+NS_KERNEL_S32(k_ns_xupd_f32_s32, EPI_XUPD)
+NS_KERNEL_S32(k_ns_final_f32_s32, EPI_FINAL)
+#undef NS_KERNEL_S32
 
 typedef void (*NsKernel)(const MuonMat*, const GemmTile*, NsArgs);
 
 int launch_k(NsKernel k, const MuonMat* tab, const GemmTile* tiles, int64_t n, const NsArgs& a,
              int threads, hipStream_t st) {
-    static_assert(kGemmTile == 256, "tile lists are built for 256x256 tiles");
+    static_assert(kGemmTile == 256, "large tile lists are built for 256x256 tiles");
     hipLaunchKernelGGL(k, dim3((unsigned)n), dim3(threads), 0, st, tab, tiles, a);
     return (int)hipGetLastError();
 }
@@ -1429,8 +1600,11 @@ int launch_ns_phase(int phase, int32_t group, const MuonMat* tab, const GemmTile
     const int epi = phase == 1 ? EPI_GRAM : phase == 2 ? EPI_POLY : (last ? EPI_FINAL : EPI_XUPD);
     static const NsKernel bf[4] = {k_ns_gram_bf16, k_ns_poly_bf16, k_ns_xupd_bf16, k_ns_final_bf16};
     static const NsKernel f32[4] = {k_ns_gram_f32, k_ns_poly_f32, k_ns_xupd_f32, k_ns_final_f32};
-    return group == kGroupBf16 ? launch_k(bf[epi - 1], tab, tiles, n_tiles, a, kW8Waves * 64, st)
-                               : launch_k(f32[epi - 1], tab, tiles, n_tiles, a, 256, st);
+    static const NsKernel f32s[4] = {k_ns_gram_f32_s32, k_ns_poly_f32_s32, k_ns_xupd_f32_s32,
+                                     k_ns_final_f32_s32};
+    if (group == kGroupBf16) return launch_k(bf[epi - 1], tab, tiles, n_tiles, a, kW8Waves * 64, st);
+    if (group == kGroupFp32Small) return launch_k(f32s[epi - 1], tab, tiles, n_tiles, a, 256, st);
+    return launch_k(f32[epi - 1], tab, tiles, n_tiles, a, 256, st);
 }
 
 }  // namespace ma

@@ -255,17 +255,32 @@ void build_layout(ma_plan* p, int32_t precision) {
     // others fp32 partials that a reduction kernel adds to A in slice order.
     // bf16 operands keep whole reductions (their A is rounded once, from
     // the fp32 sum).
+    // The fp32 matrices of at most kSmallRows padded rows take the small
+    // tiles in a batch whose fp32 matrices are all that small; beside larger
+    // ones their 256 x 256 tiles fill the larger matrices' launches instead
+    // of adding launches of their own.
+    std::vector<char> small(nm, 0);
+    {
+        std::vector<char> big_f32(nb, 0);
+        for (size_t k = 0; k < nm; ++k)
+            if (L.op_group[k] == kGroupFp32 &&
+                round_up(p->entries[p->muon_ids[k]].r, kNsPad) > kSmallRows)
+                big_f32[L.ns_batch[k]] = 1;
+        for (size_t k = 0; k < nm; ++k)
+            small[k] = L.op_group[k] == kGroupFp32 && !big_f32[L.ns_batch[k]];
+    }
     L.gram_ks.assign(nm, 1);
     {
         std::vector<int64_t> f32_gram(nb, 0);
         for (size_t k = 0; k < nm; ++k) {
-            if (L.op_group[k] != kGroupFp32) continue;
+            if (L.op_group[k] != kGroupFp32 || small[k]) continue;
             const auto& e = p->entries[p->muon_ids[k]];
             const int64_t TR = round_up(e.r, kNsPad) / kGemmTile;
             f32_gram[L.ns_batch[k]] += TR * (TR + 1) / 2;
         }
         for (size_t k = 0; k < nm; ++k) {
-            if (L.op_group[k] != kGroupFp32 || f32_gram[L.ns_batch[k]] >= kCus) continue;
+            if (L.op_group[k] != kGroupFp32 || small[k] || f32_gram[L.ns_batch[k]] >= kCus)
+                continue;
             const auto& e = p->entries[p->muon_ids[k]];
             const int64_t blocks = round_up(e.c, kNsPad) / kGemmTile;
             int32_t ks = 1;
@@ -277,10 +292,11 @@ void build_layout(ma_plan* p, int32_t precision) {
     }
     for (size_t k = 0; k < nm; ++k) {
         const auto& e = p->entries[p->muon_ids[k]];
-        const int32_t grp = L.op_group[k];
         auto& t = L.ns_batches[L.ns_batch[k]].tiles;
         const int64_t R = round_up(e.r, kNsPad), C = round_up(e.c, kNsPad);
-        const int32_t TR = (int32_t)(R / kGemmTile), TC = (int32_t)(C / kGemmTile);
+        const int32_t grp = small[k] ? (int32_t)kGroupFp32Small : L.op_group[k];
+        const int64_t tsz = small[k] ? kSmallTile : kGemmTile;
+        const int32_t TR = (int32_t)(R / tsz), TC = (int32_t)(C / tsz);
         const int32_t ks = L.gram_ks[k];
         for (int32_t sl = 0; sl < ks; ++sl)
             for (int32_t i = 0; i < TR; ++i)
@@ -309,7 +325,7 @@ void build_layout(ma_plan* p, int32_t precision) {
     off = align256(off + sizeof(MuonMat) * p->muon_ids.size());
     for (auto& bt : L.ns_batches)
         for (int ph = 0; ph < 3; ++ph)
-            for (int g = 0; g < 2; ++g) {
+            for (int g = 0; g < kNsGroups; ++g) {
                 bt.off[ph][g] = off;
                 off = align256(off + sizeof(GemmTile) * bt.tiles[ph][g].size());
             }

@@ -408,7 +408,7 @@ int step_impl(const ma_plan* plan, float* const* params, const float* const* gra
         }
         for (const auto& bt : L.ns_batches)
             for (int ph = 0; ph < 3; ++ph)
-                for (int g = 0; g < 2; ++g)
+                for (int g = 0; g < kNsGroups; ++g)
                     std::memcpy(hb + bt.off[ph][g], bt.tiles[ph][g].data(),
                                 sizeof(GemmTile) * bt.tiles[ph][g].size());
     };
@@ -597,7 +597,7 @@ int step_impl(const ma_plan* plan, float* const* params, const float* const* gra
                     for (int q = 0; q < kNsStreams && b0 + q < nb; ++q) {
                         const auto& bt = L.ns_batches[b0 + q];
                         void* qs = (q == 0 || !split) ? stream : (void*)nss;
-                        for (int g = 0; g < 2; ++g) {
+                        for (int g = 0; g < kNsGroups; ++g) {
                             err = launch_ns_phase(
                                 ph + 1, g, d_muon,
                                 reinterpret_cast<const GemmTile*>(base + bt.off[ph][g]),
@@ -623,8 +623,11 @@ int step_impl(const ma_plan* plan, float* const* params, const float* const* gra
     }
     if (guard.adam) {
         // the chunks the side kernel has not claimed yet, at full occupancy
+        // (no more waves than chunks)
+        const int64_t groups =
+            std::min<int64_t>(kFinishAdamGroups, (plan->n_adam_chunks + 3) / 4);
         err = launch_adamw_claim(d_adam, n_adam, plan->n_adam_chunks, sd, sc, plan->param_dtype,
-                                 kFinishAdamGroups, 4, stream);
+                                 groups, 4, stream);
         if (err) return hip_fail("adamw", err);
     }
     if (guard.adam) {

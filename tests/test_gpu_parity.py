@@ -143,6 +143,23 @@ def test_tiny_hybrid_fp32_all_entries():
     _run_parity(W.tiny_hybrid_fp32(), "fp32", 3)
 
 
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_small_matrix_tiles(prec):
+    """Matrices of at most 256 rows after orientation, in both stored
+    orientations, from 1 x 1 up to reductions of 4352 padded columns: under
+    fp32 every one runs on the 32 x 32 small tiles with the four-way split
+    reduction; under bf16 the thin ones (fewer than 16 rows) do, beside bf16
+    matrices on the large tiles.  3 steps, every entry compared."""
+    shapes = [(1, 1), (2, 300), (300, 2), (31, 33), (200, 4100), (4100, 200), (256, 256),
+              (255, 1024), (1024, 255), (64, 256), (17, 17), (7, 2000)]
+    params = [W.ParamSpec("action_expert.layers.%d.s.weight" % i, sh)
+              for i, sh in enumerate(shapes)]
+    params += [W.ParamSpec("vlm.norm", (300,))]
+    w = W.Workload("small_tiles_" + prec, seed=13, steps=3, ns_precision=prec, params=params,
+                   grad_std=1e-3)
+    _run_parity(w, prec, 3)
+
+
 _ragged_workload = H.ragged_workload
 
 
