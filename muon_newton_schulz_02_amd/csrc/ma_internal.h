@@ -119,11 +119,13 @@ struct GemmTile {
 // Launch groups of the NS tiles.  The operand precision of a matrix is
 // kGroupBf16 or kGroupFp32; fp32 matrices with at most kSmallRows padded
 // rows (in a batch of only such fp32 matrices) have their tiles in
-// kGroupFp32Small, as kSmallTile x kSmallTile pieces of the 256 x 256 tiles
-// (64 times as many workgroups, so a launch over a few such matrices still
-// spreads over the GPU).
+// kGroupFp32Small: kSmallTile x kSmallTile pieces of the 256 x 256 tiles for
+// the Gram and square (64 times as many workgroups, so a launch over a few
+// such matrices still spreads over the GPU), kSmallXTile x kSmallXTile ones
+// for the X update.
 enum { kGroupBf16 = 0, kGroupFp32 = 1, kGroupFp32Small = 2, kNsGroups = 3 };
 constexpr int kSmallTile = 32;
+constexpr int kSmallXTile = 64;
 constexpr int64_t kSmallRows = 256;
 
 struct Layout {

@@ -1513,6 +1513,158 @@ __device__ __forceinline__ void ns_gemm_tile_s32(const MuonMat* __restrict__ tab
                                need_cols, false, out_direct, ld_direct);
 }
 
+// ---------------------------------------------------------------------------
+// Small fp32 X updates: 64 x 64 outputs, four waves of one 32 x 32 block
+// each over the whole reduction (K = 256 for these matrices), operands
+// shared through LDS.  Against the 32 x 32 split-reduction tiles these
+// halve the operand reads and the workgroups (two rounds of 32 x 32 update
+// tiles did not fit the GPU at once) and need no cross-wave sum.
+//
+// Operands stream through a ring of four 16 KB stages of 32 reduction
+// columns (64 rows of P, then 64 rows of Q, 128 bytes per row; 16-byte chunk
+// c of row r at slot c ^ ((r >> 1) & 7), so the sixteen rows read by each
+// quarter-wave fragment load fall in distinct banks), copied by buffer loads
+// straight into LDS three stages ahead.  The epilogue is that of the large
+// tiles, one block per wave, with its global inputs loaded before the main
+// loop.
+// ---------------------------------------------------------------------------
+constexpr int kS64 = 64;                    // output tile side
+constexpr int kS64Row = 128;                // bytes per operand row per stage
+constexpr int kS64Region = kS64 * kS64Row;  // one operand's part of a stage
+constexpr int kS64Stage = 2 * kS64Region;
+constexpr int kS64Stages = 4;               // ring depth: copies run 3 stages ahead
+static_assert(kS64 == kSmallXTile, "small update tile lists are built for 64x64 tiles");
+
+// Stage s of the ring, copied by this wave: rows 16 w .. 16 w + 15 of P and
+// of Q, as two 1 KB loads each (8 rows of 128 bytes per load).
+__device__ __forceinline__ void s64_copy(uint32_t slot, u32x4 rp, u32x4 rq, const uint32_t (&vp)[2],
+                                         const uint32_t (&vq)[2], uint32_t wbase, int s,
+                                         uint32_t ldp, uint32_t ldq) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        dma16(rp, slot + wbase + i * 1024, vp[i], (uint32_t)s * kS64Row + (uint32_t)(8 * i) * ldp);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        dma16(rq, slot + kS64Region + wbase + i * 1024, vq[i],
+              (uint32_t)s * kS64Row + (uint32_t)(8 * i) * ldq);
+}
+
+// One stage of the main loop (stage s in ring slot S): wait for its copies,
+// barrier (which also retires every wave's reads of the slot the next copy
+// overwrites), issue the copy three stages ahead, multiply.
+template <int S>
+__device__ __forceinline__ void s64_stage(f32x16& acc, const char* ring, uint32_t lring, u32x4 rp,
+                                          u32x4 rq, const uint32_t (&vp)[2],
+                                          const uint32_t (&vq)[2], const uint32_t (&fa)[4],
+                                          const uint32_t (&fb)[4], uint32_t wbase, int s, int nk,
+                                          uint32_t ldp, uint32_t ldq) {
+    // at most the copies of stages s + 1 and s + 2 (4 loads each) may still
+    // be in flight
+    wait_vm(4 * min(nk - 1 - s, kS64Stages - 2));
+    stage_barrier();
+    if (s + kS64Stages - 1 < nk)
+        s64_copy(lring + ((S + kS64Stages - 1) % kS64Stages) * kS64Stage, rp, rq, vp, vq, wbase,
+                 s + kS64Stages - 1, ldp, ldq);
+    const char* buf = ring + S * kS64Stage;
+    uint4 a[4], b[4];
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+        a[kg] = *reinterpret_cast<const uint4*>(buf + fa[kg]);
+        b[kg] = *reinterpret_cast<const uint4*>(buf + fb[kg]);
+    }
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) acc = Mma<float>::run(a[kg], b[kg], acc);
+}
+
+// X update (or final update) B X of one 64 x 64 tile: P = B (R x R), Q = X^T
+// (C x R), K = R.
+template <int EPI>
+__device__ __forceinline__ void ns_xupd_tile_s64(const MuonMat* __restrict__ tab,
+                                                 const GemmTile* __restrict__ tiles,
+                                                 const NsArgs& args) {
+    static_assert(EPI == EPI_XUPD || EPI == EPI_FINAL, "update phases only");
+    constexpr int SLD = 36;
+    __shared__ __attribute__((aligned(1024))) char ring[kS64Stages * kS64Stage];
+    static_assert(4 * 32 * SLD * 4 <= kS64Stages * kS64Stage, "epilogue staging fits in the ring");
+
+    const GemmTile tile = tiles[blockIdx.x];
+    if (tile.mat < 0) return;  // padding of a shorter per-XCD list
+    const MuonMat& d = tab[tile.mat];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int cur = args.iter & 1;
+
+    const char* P = reinterpret_cast<const char*>(d.b);
+    const char* Q = reinterpret_cast<const char*>(d.xt[cur]);
+    const int64_t ldp = (int64_t)d.R * 4, ldq = (int64_t)d.R * 4;  // bytes
+    const int m0 = tile.tm * kS64, n0 = tile.tn * kS64;
+    const int nk = d.R / 32;  // a multiple of 8: R is padded to 256
+
+    const u32x4 rp = make_rsrc(P, (int64_t)d.R * ldp);
+    const u32x4 rq = make_rsrc(Q, (int64_t)d.C * ldq);
+    const uint32_t uldp = (uint32_t)ldp, uldq = (uint32_t)ldq;
+    // copies: lane l of load i writes row 16 w + 8 i + l / 8 of the region,
+    // slot l % 8, which holds chunk (l % 8) ^ ((row >> 1) & 7)
+    // = (l % 8) ^ (l / 16) ^ 4 i
+    uint32_t vp[2], vq[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t c = (uint32_t)(((lane & 7) ^ (lane >> 4)) ^ (4 * i));
+        const uint32_t r = (uint32_t)(wave * 16 + (lane >> 3));
+        vp[i] = (uint32_t)(m0 + r) * uldp + c * 16;
+        vq[i] = (uint32_t)(n0 + r) * uldq + c * 16;
+    }
+    // fragments: lane l reads row 32 wm + l % 32 (P) or 32 wn + l % 32 (Q),
+    // chunk 2 kg + l / 32 of k-group kg
+    uint32_t fa[4], fb[4];
+    {
+        const int r32 = lane & 31, half = lane >> 5, sw = (r32 >> 1) & 7;
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg) {
+            const uint32_t slot = (uint32_t)(((2 * kg + half) ^ sw) << 4);
+            fa[kg] = (uint32_t)((wm * 32 + r32) * kS64Row) + slot;
+            fb[kg] = (uint32_t)(kS64Region + (wn * 32 + r32) * kS64Row) + slot;
+        }
+    }
+    const uint32_t wbase = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 16 * kS64Row);
+    const uint32_t lring = lds_addr(ring);
+
+    // epilogue inputs, loaded now so their latency hides behind the loop
+    const int bi = m0 + wm * 32, bj = n0 + wn * 32;
+    EpiIn in;
+    PIn pin;
+    epi_load<float, EPI>(in, d, lane, bi, bj, cur, false, false);
+    p_load<EPI>(pin, d, lane, bi, bj);
+
+#pragma unroll
+    for (int st = 0; st < kS64Stages - 1; ++st)
+        s64_copy(lring + st * kS64Stage, rp, rq, vp, vq, wbase, st, uldp, uldq);
+
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    for (int s = 0; s < nk; s += kS64Stages) {
+        s64_stage<0>(acc, ring, lring, rp, rq, vp, vq, fa, fb, wbase, s, nk, uldp, uldq);
+        s64_stage<1>(acc, ring, lring, rp, rq, vp, vq, fa, fb, wbase, s + 1, nk, uldp, uldq);
+        s64_stage<2>(acc, ring, lring, rp, rq, vp, vq, fa, fb, wbase, s + 2, nk, uldp, uldq);
+        s64_stage<3>(acc, ring, lring, rp, rq, vp, vq, fa, fb, wbase, s + 3, nk, uldp, uldq);
+    }
+    // every wave is done with the ring before it becomes the epilogue staging
+    stage_barrier();
+
+    float* S = reinterpret_cast<float*>(ring) + wave * (32 * SLD);
+    const bool need_cols = EPI == EPI_XUPD || d.transposed;
+    const float s0 = args.iter == 0 ? args.scales[tile.mat] : 1.f;
+    Upd up{0.f, 1.f};
+    if (EPI == EPI_FINAL) {
+        up.rate = (float)(args.sd->muon_lr * (double)d.shape_scale);
+        up.decay = args.sd->muon_decay;
+    }
+    epi_block<float, EPI, SLD>(acc, in, pin, d, S, args, s0, up, lane, bi, bj, cur, need_cols,
+                               false, nullptr, 0);
+}
+
 // One kernel per phase and operand type, named for what it computes so that
 // traces and counters read directly.
 #define NS_KERNEL(NAME, T, EPI)                                                           \
@@ -1549,9 +1701,16 @@ NS_KERNEL(k_ns_final_f32, float, EPI_FINAL)
     }
 NS_KERNEL_S32(k_ns_gram_f32_s32, EPI_GRAM)
 NS_KERNEL_S32(k_ns_poly_f32_s32, EPI_POLY)
-NS_KERNEL_S32(k_ns_xupd_f32_s32, EPI_XUPD)
-NS_KERNEL_S32(k_ns_final_f32_s32, EPI_FINAL)
 #undef NS_KERNEL_S32
+#define NS_KERNEL_S64(NAME, EPI)                                                          \
+    __global__ __launch_bounds__(256) void NAME(const MuonMat* __restrict__ tab,          \
+                                                const GemmTile* __restrict__ tiles,       \
+                                                NsArgs args) {                            \
+        ns_xupd_tile_s64<EPI>(tab, tiles, args);                                         \
+    }
+NS_KERNEL_S64(k_ns_xupd_f32_s64, EPI_XUPD)
+NS_KERNEL_S64(k_ns_final_f32_s64, EPI_FINAL)
+#undef NS_KERNEL_S64
 
 typedef void (*NsKernel)(const MuonMat*, const GemmTile*, NsArgs);
 
@@ -1600,8 +1759,8 @@ int launch_ns_phase(int phase, int32_t group, const MuonMat* tab, const GemmTile
     const int epi = phase == 1 ? EPI_GRAM : phase == 2 ? EPI_POLY : (last ? EPI_FINAL : EPI_XUPD);
     static const NsKernel bf[4] = {k_ns_gram_bf16, k_ns_poly_bf16, k_ns_xupd_bf16, k_ns_final_bf16};
     static const NsKernel f32[4] = {k_ns_gram_f32, k_ns_poly_f32, k_ns_xupd_f32, k_ns_final_f32};
-    static const NsKernel f32s[4] = {k_ns_gram_f32_s32, k_ns_poly_f32_s32, k_ns_xupd_f32_s32,
-                                     k_ns_final_f32_s32};
+    static const NsKernel f32s[4] = {k_ns_gram_f32_s32, k_ns_poly_f32_s32, k_ns_xupd_f32_s64,
+                                     k_ns_final_f32_s64};
     if (group == kGroupBf16) return launch_k(bf[epi - 1], tab, tiles, n_tiles, a, kW8Waves * 64, st);
     if (group == kGroupFp32Small) return launch_k(f32s[epi - 1], tab, tiles, n_tiles, a, 256, st);
     return launch_k(f32[epi - 1], tab, tiles, n_tiles, a, 256, st);

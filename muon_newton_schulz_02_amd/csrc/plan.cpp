@@ -234,6 +234,15 @@ void build_layout(ma_plan* p, int32_t precision) {
     const size_t per = batched ? kNsOverlapBatchBytes : std::max<size_t>(operand_bytes, 1);
     size_t nb = kNsStreams * ((operand_bytes + kNsStreams * per - 1) / (kNsStreams * per));
     nb = std::max<size_t>(1, std::min(nb, nm));
+    // Matrices that all take the small fp32 tiles run as one batch: their
+    // launches are bound by latency rather than by the matrix cores, and one
+    // stream of fuller launches beat two interleaved ones (tiny fp32 table:
+    // Newton-Schulz 0.278 -> 0.249 ms per step).
+    bool all_small = nm > 0;
+    for (size_t k = 0; k < nm; ++k)
+        if (L.op_group[k] != kGroupFp32 || round_up(p->entries[p->muon_ids[k]].r, kNsPad) > kSmallRows)
+            all_small = false;
+    if (all_small) nb = 1;
     std::vector<size_t> order(nm);
     for (size_t k = 0; k < nm; ++k) order[k] = k;
     std::stable_sort(order.begin(), order.end(),
@@ -296,7 +305,9 @@ void build_layout(ma_plan* p, int32_t precision) {
         const int64_t R = round_up(e.r, kNsPad), C = round_up(e.c, kNsPad);
         const int32_t grp = small[k] ? (int32_t)kGroupFp32Small : L.op_group[k];
         const int64_t tsz = small[k] ? kSmallTile : kGemmTile;
-        const int32_t TR = (int32_t)(R / tsz), TC = (int32_t)(C / tsz);
+        const int32_t TR = (int32_t)(R / tsz);
+        const int64_t xsz = small[k] ? kSmallXTile : kGemmTile;  // X-update tiles
+        const int32_t XR = (int32_t)(R / xsz), XC = (int32_t)(C / xsz);
         const int32_t ks = L.gram_ks[k];
         for (int32_t sl = 0; sl < ks; ++sl)
             for (int32_t i = 0; i < TR; ++i)
@@ -308,8 +319,8 @@ void build_layout(ma_plan* p, int32_t precision) {
         // column-major: the tiles of one column block (all readers of that
         // X panel) are consecutive, so the tiles an XCD runs together read
         // each panel once from HBM while the r x r B stays in its L2
-        for (int32_t j = 0; j < TC; ++j)
-            for (int32_t i = 0; i < TR; ++i)
+        for (int32_t j = 0; j < XC; ++j)
+            for (int32_t i = 0; i < XR; ++i)
                 t[2][grp].push_back(GemmTile{(int32_t)k, i, j, (int32_t)R, 0});
     }
     for (auto& bt : L.ns_batches)
