@@ -1354,7 +1354,8 @@ __device__ __forceinline__ void ns_gemm_tile_w8(const MuonMat* __restrict__ tab,
 }
 
 // ---------------------------------------------------------------------------
-// Small fp32 tiles: 32 x 32 outputs, for matrices of at most 256 padded rows.
+// Small fp32 Gram and square tiles: 32 x 32 outputs, for matrices of at most
+// 256 padded rows.
 //
 // A launch over a few such matrices holds only tens of 256 x 256 tiles, each
 // a long chain of matrix instructions on one CU while the rest of the GPU
@@ -1366,8 +1367,8 @@ __device__ __forceinline__ void ns_gemm_tile_w8(const MuonMat* __restrict__ tab,
 // l % 32 and, of every 32-column block, the 16 columns from 16 (l / 32) on,
 // as four 16-byte loads; fragment g of the block pairs columns
 // 16 h + 4 g .. 16 h + 4 g + 3 of both operands (h = lane half), so the four
-// MFMA steps of each fragment cover the block once.  Two or four blocks are
-// in flight per wave.  Waves 1..3 then hand their sums to wave 0 through LDS;
+// MFMA steps of each fragment cover the block once.  Two blocks are in
+// flight per wave.  Waves 1..3 then hand their sums to wave 0 through LDS;
 // wave 0 adds them in wave order (a fixed order: reruns are bitwise equal)
 // and runs the epilogue of the large tiles on its one block.
 // ---------------------------------------------------------------------------
@@ -1381,11 +1382,9 @@ __device__ __forceinline__ void s32_load(uint4 (&v)[4], const char* base, int64_
     for (int g = 0; g < 4; ++g) v[g] = gld(base + kb + 16 * g);
 }
 
-// Blocks in flight per wave: 2 where a wave's share of K is one 64-column
-// pair (square and update steps: K = 256), deeper for the Gram, whose
-// reduction runs along the long side.
-template <int EPI>
-constexpr int kS32Depth = EPI == EPI_GRAM ? 4 : 2;
+// Blocks in flight per wave (four measured no faster for the Grams of
+// 256 x 1024 matrices).
+constexpr int kS32Depth = 2;
 
 __device__ __forceinline__ void s32_mma(f32x16& acc, const uint4 (&a)[4], const uint4 (&b)[4]) {
 #pragma unroll
@@ -1396,7 +1395,7 @@ template <int EPI>
 __device__ __forceinline__ void ns_gemm_tile_s32(const MuonMat* __restrict__ tab,
                                                  const GemmTile* __restrict__ tiles,
                                                  const NsArgs& args) {
-    constexpr bool XT = EPI == EPI_XUPD || EPI == EPI_FINAL;
+    static_assert(EPI == EPI_GRAM || EPI == EPI_POLY, "Gram and square only");
     constexpr int SLD = 36;
     __shared__ __attribute__((aligned(16))) float red[3][16][64];  // waves 1..3: [register][lane]
     __shared__ __attribute__((aligned(16))) float stage[32 * SLD];  // wave 0's epilogue staging
@@ -1408,31 +1407,23 @@ __device__ __forceinline__ void ns_gemm_tile_s32(const MuonMat* __restrict__ tab
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int cur = args.iter & 1;
 
-    // operands: fp32, row-major, reduction index contiguous (as for the
-    // large fp32 tiles)
+    // operands: fp32, row-major, reduction index contiguous; both are X
+    // (Gram) or both A (square)
     const char* P;
-    const char* Q;
-    int64_t ldp, ldq;  // bytes
+    int64_t ldp;  // bytes
     int K;
     if (EPI == EPI_GRAM) {
-        P = Q = reinterpret_cast<const char*>(d.x[0]);
-        ldp = ldq = (int64_t)d.C * 4;
+        P = reinterpret_cast<const char*>(d.x[0]);
+        ldp = (int64_t)d.C * 4;
         K = d.C;
         if (d.gram_ks > 1) {
             // slice tile.slice of a split reduction
             K = d.C / d.gram_ks;
             P += (int64_t)tile.slice * K * 4;
-            Q = P;
         }
-    } else if (EPI == EPI_POLY) {
-        P = Q = reinterpret_cast<const char*>(d.a);
-        ldp = ldq = (int64_t)d.R * 4;
-        K = d.R;
     } else {
-        P = reinterpret_cast<const char*>(d.b);
+        P = reinterpret_cast<const char*>(d.a);
         ldp = (int64_t)d.R * 4;
-        Q = reinterpret_cast<const char*>(d.xt[cur]);  // X^T: C rows of R
-        ldq = (int64_t)d.R * 4;
         K = d.R;
     }
     const int m0 = tile.tm * kS32, n0 = tile.tn * kS32;
@@ -1440,21 +1431,18 @@ __device__ __forceinline__ void ns_gemm_tile_s32(const MuonMat* __restrict__ tab
     const int nb = kq / 32;  // its 32-column blocks: at least 2
     const int r = lane & 31, h = lane >> 5;
     const char* pa = P + (int64_t)(m0 + r) * ldp + ((int64_t)wave * kq + 16 * h) * 4;
-    const char* qa = Q + (int64_t)(n0 + r) * ldq + ((int64_t)wave * kq + 16 * h) * 4;
+    const char* qa = P + (int64_t)(n0 + r) * ldp + ((int64_t)wave * kq + 16 * h) * 4;
 
     // wave 0's epilogue inputs, loaded now so their latency hides behind the loop
     EpiIn in;
     PIn pin;
-    if (wave == 0) {
-        epi_load<float, EPI>(in, d, lane, m0, n0, cur, false, false);
-        p_load<EPI>(pin, d, lane, m0, n0);
-    }
+    if (wave == 0) epi_load<float, EPI>(in, d, lane, m0, n0, cur, false, false);
 
     // D blocks in flight: buffer i holds block kb + i.  Loads past the last
     // block re-read it (cache hits) and are not multiplied, so every
     // iteration of the loop issues the same loads and waits the same counts;
     // the last D blocks are multiplied after it, with no further loads.
-    constexpr int D = kS32Depth<EPI>;
+    constexpr int D = kS32Depth;
     uint4 a[D][4], b[D][4];
 #pragma unroll
     for (int i = 0; i < D; ++i) {
@@ -1490,27 +1478,17 @@ __device__ __forceinline__ void ns_gemm_tile_s32(const MuonMat* __restrict__ tab
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[e] += red[w][e][lane];
 
-    const bool mirror = (EPI == EPI_GRAM || EPI == EPI_POLY) && tile.tm != tile.tn;
-    const bool need_cols = mirror || EPI == EPI_XUPD || (EPI == EPI_FINAL && d.transposed);
-    float* out_direct = nullptr;
-    int64_t ld_direct = 0;
-    if (EPI == EPI_GRAM) {
-        out_direct = reinterpret_cast<float*>(
-            tile.slice == 0 ? d.a : d.apart + (uint64_t)(tile.slice - 1) * d.R * d.R * 4);
-        ld_direct = d.R;
-    } else if (EPI == EPI_POLY) {
-        out_direct = reinterpret_cast<float*>(d.b);
-        ld_direct = d.R;
-    }
+    // an off-diagonal tile also writes its mirror image
+    const bool mirror = tile.tm != tile.tn;
+    float* out_direct = reinterpret_cast<float*>(
+        EPI == EPI_POLY ? d.b
+                        : (tile.slice == 0 ? d.a
+                                           : d.apart + (uint64_t)(tile.slice - 1) * d.R * d.R * 4));
     const float s0 = args.iter == 0 ? args.scales[tile.mat] : 1.f;
-    const float escale = EPI == EPI_GRAM ? s0 * s0 : (XT ? s0 : 1.f);
-    Upd up{0.f, 1.f};
-    if (EPI == EPI_FINAL) {
-        up.rate = (float)(args.sd->muon_lr * (double)d.shape_scale);
-        up.decay = args.sd->muon_decay;
-    }
+    const float escale = EPI == EPI_GRAM ? s0 * s0 : 1.f;
+    const Upd up{0.f, 1.f};
     epi_block<float, EPI, SLD>(acc, in, pin, d, stage, args, escale, up, lane, m0, n0, cur,
-                               need_cols, false, out_direct, ld_direct);
+                               mirror, false, out_direct, d.R);
 }
 
 // ---------------------------------------------------------------------------
