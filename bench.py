@@ -75,14 +75,15 @@ class HipEvents:
 
 KERNEL_SOURCES = {
     "k_adamw": os.path.join(HERE, "muon_newton_schulz_02_amd", "csrc", "elementwise.hip"),
-    "k_ns_xupd_bf16": os.path.join(HERE, "muon_newton_schulz_02_amd", "csrc", "ns_gemm.hip"),
+    "k_ns_*": os.path.join(HERE, "muon_newton_schulz_02_amd", "csrc", "ns_gemm.hip"),
 }
 
 
 def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 summary
-    (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or None when
-    there is none or the kernel's source changed since it was taken."""
+    """HBM bytes per launch of `kernel` (for "k_ns_*": per serial step of all
+    Newton-Schulz launches) from the committed rocprofv3 summary (FETCH_SIZE
+    + WRITE_SIZE, calibrated against a plain copy), or None when there is
+    none or the kernel's source changed since it was taken."""
     import hashlib
     path = os.path.join(HERE, "profiles", "kernels_%s.md" % workload)
     if not os.path.exists(path):
@@ -107,16 +108,22 @@ def ns_flops(shapes, ns_steps: int) -> float:
     return tot * ns_steps
 
 
-def ns_executed_flops(shapes, ns_steps: int) -> float:
+def ns_executed_flops(shapes, ns_steps: int, ns_precision: str) -> float:
     """Flops the matrix cores execute for NS: both sides padded to 256, and
-    the symmetric Gram and square results computed over their upper 256 x 256
-    tiles only (mirrored on write), so this is below the dense count for
-    r > 256 and above it where padding dominates."""
+    the symmetric Gram and square results computed over their upper tiles
+    only (mirrored on write), so this is below the dense count for r > 256
+    and above it where padding dominates.  Tiles are 256 x 256, except for
+    fp32 operands (fp32 NS, or fewer than 16 rows) when no fp32 matrix has
+    more than 256 rows: the library then runs the Gram and square of those
+    as 32 x 32 tiles (and the X update as 64 x 64 ones, full either way)."""
+    f32 = [(min(m, n), max(m, n)) for m, n in shapes if ns_precision == "fp32" or min(m, n) < 16]
+    small = all(-(-r // 256) * 256 <= 256 for r, _ in f32)
     tot = 0.0
     for m, n in shapes:
         r, c = min(m, n), max(m, n)
         R, C = -(-r // 256) * 256, -(-c // 256) * 256
-        up = (R // 256) * (R // 256 + 1) // 2 * 256.0 * 256.0
+        t = 32 if (small and (ns_precision == "fp32" or r < 16)) else 256
+        up = (R // t) * (R // t + 1) // 2 * float(t * t)
         tot += 2.0 * up * C + 2.0 * up * R + 2.0 * R * R * C
     return tot * ns_steps
 
@@ -503,7 +510,7 @@ def main():
               if n_muon > 0 else None)
     ns_peak = PEAK_BF16_TFLOPS if w.ns_precision == "bf16" else PEAK_FP32_TFLOPS
     ns_tflops = flops / (mean["newton_schulz"] * 1e-3) / 1e12 if mean["newton_schulz"] > 0 else 0.0
-    ns_exec_tflops = (ns_executed_flops(muon_shapes, hp.muon_ns_steps) /
+    ns_exec_tflops = (ns_executed_flops(muon_shapes, hp.muon_ns_steps, w.ns_precision) /
                       (mean["newton_schulz"] * 1e-3) / 1e12 if mean["newton_schulz"] > 0 else 0.0)
     # AdamW reads p, g, m, v and writes p, m, v: 28 B per element with fp32
     # parameters, 22 B with bf16 ones (m, v fp32 either way); the clip norm
@@ -528,7 +535,8 @@ def main():
         # algorithmic rate is reported beside it
         roofline = {"kernel": "k_ns_* GEMMs (5 steps x 3 launches)", "bound": "mfma",
                     "achieved": ns_exec_tflops, "peak": ns_peak, "unit": "TFLOP/s",
-                    "frac": ns_exec_tflops / ns_peak, "traffic": None,
+                    "frac": ns_exec_tflops / ns_peak,
+                    "traffic": measured_traffic("k_ns_*", w.name),  # bytes per serial step
                     "dense_tflops": ns_tflops, "dense_frac": ns_tflops / ns_peak,
                     "b2_peak": b2_mfma, "frac_of_b2": ns_exec_tflops / b2_mfma if b2_mfma else None}
     out = {

@@ -24,11 +24,27 @@ def test_executed_ns_flops_counts_upper_tiles_and_padding():
     # 1024 x 4096: 4 x 4 tiles of 256, of which 10 are upper tiles
     up = 10 * 256 * 256
     want = 2 * up * 4096 + 2 * up * 1024 + 2 * 1024 * 1024 * 4096
-    assert bench.ns_executed_flops([(1024, 4096)], 1) == want
+    assert bench.ns_executed_flops([(1024, 4096)], 1, "bf16") == want
     # 64 x 256 pads to one 256 x 256 tile in every product
-    assert bench.ns_executed_flops([(256, 64)], 1) == 3 * 2 * 256.0 ** 3
+    assert bench.ns_executed_flops([(256, 64)], 1, "bf16") == 3 * 2 * 256.0 ** 3
     # one tile row: symmetric saving is nil, so executed == dense at r = 256
-    assert bench.ns_executed_flops([(256, 1024)], 1) == bench.ns_flops([(256, 1024)], 1)
+    assert bench.ns_executed_flops([(256, 1024)], 1, "bf16") == bench.ns_flops([(256, 1024)], 1)
+
+
+def test_executed_ns_flops_of_small_fp32_tiles():
+    # fp32 with no matrix above 256 rows: Gram and square over the 36 upper
+    # 32 x 32 tiles of the padded 256 x 256 result, the X update in full
+    up = 36 * 32 * 32
+    want = 2 * up * 1024 + 2 * up * 256 + 2 * 256 * 256 * 1024
+    assert bench.ns_executed_flops([(1024, 200)], 1, "fp32") == want
+    # beside a larger fp32 matrix they keep the 256 x 256 tiles
+    big = bench.ns_executed_flops([(512, 512)], 1, "fp32")
+    assert bench.ns_executed_flops([(1024, 200), (512, 512)], 1, "fp32") == \
+        bench.ns_flops([(1024, 256)], 1) + big
+    # under bf16 only the thin matrices (fewer than 16 rows) run in fp32
+    thin = 36 * 32 * 32
+    assert bench.ns_executed_flops([(3, 300), (256, 256)], 1, "bf16") == \
+        (2 * thin * 512 + 2 * thin * 256 + 2 * 256 * 256 * 512) + 3 * 2 * 256.0 ** 3
 
 
 def test_more_than_one_gpu_is_refused():
