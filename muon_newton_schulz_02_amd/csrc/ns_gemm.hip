@@ -21,14 +21,22 @@
 // Operands are zero-padded to multiples of 256 in both dimensions, so no
 // tile needs bounds checks.
 //
-// A workgroup (4 waves, 2 x 2 of 128 x 128 each, accumulators in the 256
-// AGPRs) computes one 256 x 256 output tile.  Operands stream through a ring
-// of 4 LDS stages of 32 reduction columns, copied by buffer loads straight
-// into LDS three stages ahead; each stage's fragment reads and copies sit
-// between its matrix instructions, since a SIMD holds only this one wave.
-// The epilogue stages each 32 x 32 accumulator block through the wave's own
-// LDS region and writes it in 16-byte runs (whole 1 KB halves of a 2 KB
-// block for the bf16 X update).
+// Three kernel families, one launch group each:
+//   * bf16 operands: a workgroup of eight waves (two per SIMD, 128 x 64
+//     each) computes one 256 x 256 output tile; operands stream through a
+//     ring of five 32 KB LDS stages, copied by buffer loads straight into
+//     LDS four stages ahead (ns_gemm_tile_w8);
+//   * fp32 operands: four waves (one per SIMD, 128 x 128 each, accumulators
+//     in the 256 AGPRs) per 256 x 256 tile, a ring of four stages copied
+//     three ahead, each stage's fragment reads and copies placed between its
+//     matrix instructions since a SIMD holds only this one wave
+//     (ns_gemm_tile);
+//   * small fp32 matrices (at most 256 padded rows): 32 x 32 Gram and square
+//     tiles with a four-way split reduction and 64 x 64 X-update tiles
+//     (ns_gemm_tile_s32, ns_xupd_tile_s64).
+// Every epilogue stages each 32 x 32 accumulator block through the wave's
+// own LDS region and writes it in 16-byte runs (whole 1 KB halves of a
+// 2 KB block for the bf16 X update).
 //
 // Method: OpenDM training-stack page, Muon/AdamW hybrid section, the
 // Newton-Schulz paragraph (a few quintic Newton-Schulz steps on the whole
