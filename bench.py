@@ -115,12 +115,18 @@ def ns_executed_flops(shapes, ns_steps: int, ns_precision: str) -> float:
     and above it where padding dominates.  Tiles are 256 x 256, except for
     fp32 operands (fp32 NS, or fewer than 16 rows) when no fp32 matrix has
     more than 256 rows: the library then runs the Gram and square of those
-    as 32 x 32 tiles (and the X update as 64 x 64 ones, full either way)."""
+    as 32 x 32 tiles (and the X update as 64 x 64 ones, full either way).
+    bf16 matrices of at most 64 x 512 run in one workgroup each, on their
+    sides rounded up to 32, every product in full."""
     f32 = [(min(m, n), max(m, n)) for m, n in shapes if ns_precision == "fp32" or min(m, n) < 16]
     small = all(-(-r // 256) * 256 <= 256 for r, _ in f32)
     tot = 0.0
     for m, n in shapes:
         r, c = min(m, n), max(m, n)
+        if ns_precision == "bf16" and 16 <= r <= 64 and -(-c // 32) * 32 <= 512:
+            R, C = -(-r // 32) * 32, -(-c // 32) * 32
+            tot += 4.0 * R * R * C + 2.0 * R ** 3
+            continue
         R, C = -(-r // 256) * 256, -(-c // 256) * 256
         t = 32 if (small and (ns_precision == "fp32" or r < 16)) else 256
         up = (R // t) * (R // t + 1) // 2 * float(t * t)

@@ -106,6 +106,8 @@ struct MuonMat {
     int32_t  p_bf16;               // p and g stored as bf16 (else float)
     int32_t  ns_batch;             // its Newton-Schulz batch
     int32_t  gram_ks;              // Gram reduction split into this many slices (fp32 only)
+    int32_t  lds_ns;               // bf16 matrix small enough for one workgroup's LDS (k_ns_lds_bf16)
+    int32_t  pad2_;
     uint64_t apart;                // gram_ks - 1 fp32 R x R partial Grams (slices 1..)
 };
 
@@ -126,6 +128,11 @@ struct GemmTile {
 enum { kGroupBf16 = 0, kGroupFp32 = 1, kGroupFp32Small = 2, kNsGroups = 3 };
 constexpr int kSmallTile = 32;
 constexpr int kSmallXTile = 64;
+// bf16 matrices of at most kLdsRows rows and kLdsCols columns (canonical
+// orientation, each rounded up to 32) run all their Newton-Schulz iterations
+// in one workgroup with X, A and B in LDS, outside the tile lists.
+constexpr int64_t kLdsRows = 64;
+constexpr int64_t kLdsCols = 512;
 constexpr int64_t kSmallRows = 256;
 
 struct Layout {
@@ -148,6 +155,8 @@ struct Layout {
     size_t ns_off = 0;                               // start of per-matrix NS buffers
     std::vector<size_t> x0, x1, lo0, lo1, xt0, xt1, a, b;  // per Muon matrix (0: unused)
     std::vector<int32_t> gram_ks;                    // per Muon matrix: Gram reduction slices
+    std::vector<int32_t> lds_ns;                     // per Muon matrix: runs in k_ns_lds_bf16
+    int32_t n_lds = 0;                               // how many do
     std::vector<size_t> apart;                       // per Muon matrix: partial Grams (0: none)
     size_t total = 0;
 };
@@ -310,6 +319,10 @@ int launch_muon_scale(const MuonMat* tab, int32_t n_tab, const float* partials, 
                       float* ns_scale, float* pre_scale, int32_t batch, void* stream);
 // After a batch's fp32 Gram launch: A += its split reductions' partial Grams.
 int launch_gram_reduce(const MuonMat* tab, int32_t n_tab, int32_t batch, void* stream);
+// Every Newton-Schulz iteration and the update of the matrices with lds_ns
+// set, one workgroup each (the others' workgroups return at once).
+int launch_ns_lds(const MuonMat* tab, int32_t n_tab, int ns_steps, const StepScalars& s,
+                  const float* ns_scale, const StepDev* sd, void* stream);
 // phase 1 = Gram, 2 = polynomial, 3 = X update (the parameter update when
 // `last`); group = kGroupBf16 / kGroupFp32 / kGroupFp32Small selects the
 // operand type and tile size.

@@ -1651,6 +1651,182 @@ __device__ __forceinline__ void ns_xupd_tile_s64(const MuonMat* __restrict__ tab
                                false, nullptr, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Small bf16 matrices (at most 64 rows and 512 columns, canonical
+// orientation): one workgroup per matrix runs every Newton-Schulz iteration
+// and the update, with X (its bf16 hi and lo halves), A and B in LDS.  On
+// 256 x 256 tiles such a matrix would execute 16 times its Gram and square
+// flops in padding and ride through 15 launches; here the whole matrix is one
+// workgroup of one launch per step.
+//
+// The arithmetic is that of the tiled path: A = bf16(s^2 X_hi X_hi^T),
+// B = bf16(b A + c A A), X' = s (a (X_hi [+ X_lo]) + B X_hi) rounded to the
+// hi / lo pair (lo kept for the first kNsLoIters iterations), s the
+// normalising factor in the first iteration only; the last iteration writes
+// p = p decay - rate X' in the stored orientation.  Rows and columns are
+// padded to multiples of 32 with the zeros the prep pass wrote.
+//
+// Work split over the four waves: one 32 x 32 block of A (or B) each (one
+// wave when the matrix has at most 32 rows); the X update by 32-column
+// blocks, wave w taking blocks w, w + 4, ...: a wave reads and writes only
+// its own columns of X, so X is updated in place.  Fragments: A-operand rows
+// (k contiguous) are 16-byte LDS reads; the X columns B X needs are gathered
+// as eight 2-byte reads.
+// ---------------------------------------------------------------------------
+constexpr int kLdsXld = (int)kLdsCols + 8;  // row pitch (bf16) of X's halves: 16 rows fall in distinct banks
+constexpr int kLdsAld = (int)kLdsRows + 8;  // row pitch of A and B
+
+struct NsLds {
+    __bf16 xhi[kLdsRows][kLdsXld];
+    __bf16 xlo[kLdsRows][kLdsXld];
+    __bf16 a[kLdsRows][kLdsAld];
+    __bf16 b[kLdsRows][kLdsAld];
+};
+static_assert(sizeof(NsLds) <= 160 * 1024, "the matrix fits in a CU's LDS");
+
+struct NsLdsArgs {
+    float a, b, c;
+    int steps;
+    const float* scales;  // per matrix 1 / (||u||_F + eps)
+    const StepDev* sd;
+};
+
+__device__ __forceinline__ uint4 lds_row8(const __bf16* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Row of A (or B) at accumulator register e of this lane: 8 (e / 4) + 4 (lane / 32) + e % 4.
+__device__ __forceinline__ int acc_row(int e, int lane) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
+
+// Stored-orientation update of one element of the matrix: p = p decay - dv,
+// delta = dv.
+__device__ __forceinline__ void lds_update(const MuonMat& d, int row, int col, float dv, float decay) {
+    const int64_t o = d.transposed ? (int64_t)col * d.n + row : (int64_t)row * d.n + col;
+    if (d.p_bf16) {
+        __bf16* p = reinterpret_cast<__bf16*>(d.p) + o;
+        *p = (__bf16)fmaf((float)*p, decay, -dv);
+    } else {
+        float* p = reinterpret_cast<float*>(d.p) + o;
+        *p = fmaf(*p, decay, -dv);
+    }
+    if (d.delta) reinterpret_cast<float*>(d.delta)[o] = dv;
+}
+
+template <int R>
+__device__ __forceinline__ void ns_lds_run(NsLds& L, const MuonMat& d, int mat,
+                                           const NsLdsArgs& args) {
+    constexpr int NB = R / 32;  // row blocks
+    const int C = (d.c + 31) & ~31;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r32 = lane & 31, h = lane >> 5;
+
+    // X0 (hi and lo as the prep pass wrote them, 32 x 32 blocks of the
+    // 256-padded operand) into LDS, 8 elements per access
+    {
+        const __bf16* ghi = reinterpret_cast<const __bf16*>(d.x[0]);
+        const __bf16* glo = reinterpret_cast<const __bf16*>(d.xlo[0]);
+        const int per_row = C / 8;
+        for (int i = tid; i < R * per_row; i += 256) {
+            const int row = i / per_row, col = (i % per_row) * 8;
+            const int64_t o = xblk(row, col, d.C);
+            *reinterpret_cast<uint4*>(&L.xhi[row][col]) = gld(ghi + o);
+            *reinterpret_cast<uint4*>(&L.xlo[row][col]) = gld(glo + o);
+        }
+    }
+    __syncthreads();
+
+    const int bi = NB == 2 ? wave >> 1 : 0, bj = NB == 2 ? wave & 1 : 0;
+    const bool sq_wave = NB == 2 || wave == 0;  // this wave owns a block of A and B
+    for (int it = 0; it < args.steps; ++it) {
+        const float s0 = it == 0 ? args.scales[mat] : 1.f;
+        const bool use_lo = it < kNsLoIters, write_lo = it + 1 < kNsLoIters;
+        const bool last = it == args.steps - 1;
+        // A = bf16(s0^2 X_hi X_hi^T), K = C
+        if (sq_wave) {
+            f32x16 acc;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+            for (int k = 0; k < C; k += 16) {
+                const uint4 fa = lds_row8(&L.xhi[bi * 32 + r32][k + 8 * h]);
+                const uint4 fb = lds_row8(&L.xhi[bj * 32 + r32][k + 8 * h]);
+                acc = Mma<__bf16>::run(fa, fb, acc);
+            }
+            const float sc = s0 * s0;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                L.a[bi * 32 + acc_row(e, lane)][bj * 32 + r32] = (__bf16)(acc[e] * sc);
+        }
+        __syncthreads();
+        // B = bf16(b A + c A A), K = R (A is symmetric: its rows are its columns)
+        if (sq_wave) {
+            f32x16 acc;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+            for (int k = 0; k < R; k += 16) {
+                const uint4 fa = lds_row8(&L.a[bi * 32 + r32][k + 8 * h]);
+                const uint4 fb = lds_row8(&L.a[bj * 32 + r32][k + 8 * h]);
+                acc = Mma<__bf16>::run(fa, fb, acc);
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = bi * 32 + acc_row(e, lane), col = bj * 32 + r32;
+                L.b[row][col] = (__bf16)fmaf(args.b, (float)L.a[row][col], args.c * acc[e]);
+            }
+        }
+        __syncthreads();
+        // X' = s0 (a X_master + B X_hi), K = R, by 32-column blocks
+        const float rate = last ? (float)(args.sd->muon_lr * (double)d.shape_scale) : 0.f;
+        const float decay = last ? args.sd->muon_decay : 1.f;
+        for (int jb = wave; jb < C / 32; jb += 4) {
+            const int col = jb * 32 + r32;
+            f32x16 acc[NB];
+#pragma unroll
+            for (int ib = 0; ib < NB; ++ib)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[ib][e] = 0.f;
+#pragma unroll
+            for (int k = 0; k < R; k += 16) {
+                // column `col` of X_hi at rows k + 8 h .. k + 8 h + 7
+                typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+                u16x8 xc;
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    xc[t] = __builtin_bit_cast(unsigned short, L.xhi[k + 8 * h + t][col]);
+                const uint4 fb = __builtin_bit_cast(uint4, xc);
+#pragma unroll
+                for (int ib = 0; ib < NB; ++ib)
+                    acc[ib] = Mma<__bf16>::run(lds_row8(&L.b[ib * 32 + r32][k + 8 * h]), fb, acc[ib]);
+            }
+#pragma unroll
+            for (int ib = 0; ib < NB; ++ib) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = ib * 32 + acc_row(e, lane);
+                    const float hi = (float)L.xhi[row][col];
+                    const float t = fmaf(args.a, hi, acc[ib][e]);
+                    const float v = use_lo ? s0 * fmaf(args.a, (float)L.xlo[row][col], t) : s0 * t;
+                    if (!last) {
+                        const __bf16 vh = (__bf16)v;
+                        L.xhi[row][col] = vh;
+                        if (write_lo) L.xlo[row][col] = (__bf16)(v - (float)vh);
+                    } else if (row < d.r && col < d.c) {
+                        lds_update(d, row, col, rate * v, decay);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void k_ns_lds_bf16(const MuonMat* __restrict__ tab, NsLdsArgs args) {
+    __shared__ __attribute__((aligned(16))) NsLds L;
+    const MuonMat& d = tab[blockIdx.x];
+    if (!d.lds_ns) return;
+    if (d.r <= 32) ns_lds_run<32>(L, d, blockIdx.x, args);
+    else ns_lds_run<64>(L, d, blockIdx.x, args);
+}
+
 // One kernel per phase and operand type, named for what it computes so that
 // traces and counters read directly.
 #define NS_KERNEL(NAME, T, EPI)                                                           \
@@ -1732,6 +1908,15 @@ int launch_gram_reduce(const MuonMat* tab, int32_t n_tab, int32_t batch, void* s
     if (n_tab == 0) return (int)hipSuccess;
     hipLaunchKernelGGL(k_gram_reduce, dim3((unsigned)n_tab * kReduceSplit), dim3(256), 0,
                        (hipStream_t)stream, tab, (int)batch);
+    return (int)hipGetLastError();
+}
+
+int launch_ns_lds(const MuonMat* tab, int32_t n_tab, int ns_steps, const StepScalars& s,
+                  const float* ns_scale, const StepDev* sd, void* stream) {
+    if (n_tab == 0) return (int)hipSuccess;
+    const NsLdsArgs a{s.ns_a, s.ns_b, s.ns_c, ns_steps, ns_scale, sd};
+    hipLaunchKernelGGL(k_ns_lds_bf16, dim3((unsigned)n_tab), dim3(256), 0, (hipStream_t)stream, tab,
+                       a);
     return (int)hipGetLastError();
 }
 

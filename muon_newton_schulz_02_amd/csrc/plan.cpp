@@ -215,12 +215,20 @@ void build_layout(ma_plan* p, int32_t precision) {
     const size_t nm = p->muon_ids.size();
     std::vector<double> cost(nm);
     size_t operand_bytes = 0;
+    L.lds_ns.assign(nm, 0);
     for (size_t k = 0; k < nm; ++k) {
         const auto& e = p->entries[p->muon_ids[k]];
         const int32_t grp =
             (precision == MA_NS_BF16 && e.r >= kBf16MinRows) ? kGroupBf16 : kGroupFp32;
         L.op_group.push_back(grp);
         const int64_t R = round_up(e.r, kNsPad), C = round_up(e.c, kNsPad);
+        if (grp == kGroupBf16 && e.r <= kLdsRows && round_up(e.c, 32) <= kLdsCols) {
+            // one workgroup through every iteration: no tiles, no batch work
+            L.lds_ns[k] = 1;
+            ++L.n_lds;
+            cost[k] = 0.0;
+            continue;
+        }
         cost[k] = (double)R * R * C + (double)R * R * R / 2.0 + (double)R * R * C;
         operand_bytes += (size_t)(R * C) * (grp == kGroupBf16 ? 4 : 8);
     }
@@ -240,7 +248,8 @@ void build_layout(ma_plan* p, int32_t precision) {
     // Newton-Schulz 0.278 -> 0.249 ms per step).
     bool all_small = nm > 0;
     for (size_t k = 0; k < nm; ++k)
-        if (L.op_group[k] != kGroupFp32 || round_up(p->entries[p->muon_ids[k]].r, kNsPad) > kSmallRows)
+        if (!L.lds_ns[k] && (L.op_group[k] != kGroupFp32 ||
+                             round_up(p->entries[p->muon_ids[k]].r, kNsPad) > kSmallRows))
             all_small = false;
     if (all_small) nb = 1;
     std::vector<size_t> order(nm);
@@ -250,6 +259,7 @@ void build_layout(ma_plan* p, int32_t precision) {
     L.ns_batch.assign(nm, 0);
     std::vector<double> bload(nb, 0.0);
     for (size_t k : order) {
+        if (L.lds_ns[k]) continue;  // batch 0: its operands are prepared with that batch's
         size_t best = 0;
         for (size_t q = 1; q < nb; ++q)
             if (bload[q] < bload[best]) best = q;
@@ -300,6 +310,7 @@ void build_layout(ma_plan* p, int32_t precision) {
         }
     }
     for (size_t k = 0; k < nm; ++k) {
+        if (L.lds_ns[k]) continue;
         const auto& e = p->entries[p->muon_ids[k]];
         auto& t = L.ns_batches[L.ns_batch[k]].tiles;
         const int64_t R = round_up(e.r, kNsPad), C = round_up(e.c, kNsPad);
@@ -361,6 +372,20 @@ void build_layout(ma_plan* p, int32_t precision) {
             off = align256(off + bytes);
             return at;
         };
+        if (L.lds_ns[k]) {
+            // only the step-0 operands, which the prep pass writes; the
+            // iterations run in LDS
+            L.x0.push_back(take(R * C * 2));
+            L.x1.push_back(0);
+            L.lo0.push_back(take(R * C * 2));
+            L.lo1.push_back(0);
+            L.xt0.push_back(0);
+            L.xt1.push_back(0);
+            L.a.push_back(0);
+            L.b.push_back(0);
+            L.apart.push_back(0);
+            continue;
+        }
         if (L.op_group[k] == kGroupBf16) {
             // X as bf16 hi / lo pairs, ping-pong; B X reads hi transposed on load
             L.x0.push_back(take(R * C * 2));

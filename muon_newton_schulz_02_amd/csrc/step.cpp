@@ -402,6 +402,8 @@ int step_impl(const ma_plan* plan, float* const* params, const float* const* gra
             d.shape_scale = e.lr_shape_scale;
             d.ns_batch = L.ns_batch[k];
             d.gram_ks = L.gram_ks[k];
+            d.lds_ns = L.lds_ns[k];
+            d.pad2_ = 0;
             d.apart = L.apart[k] ? reinterpret_cast<uint64_t>(base + L.apart[k]) : 0;
             d.op_bf16 = L.op_group[k] == kGroupBf16 ? 1 : 0;
             d.p_bf16 = bf16 ? 1 : 0;
@@ -590,6 +592,13 @@ int step_impl(const ma_plan* plan, float* const* params, const float* const* gra
             guard.ns = true;
             if (pipelined && (err = prep(1, nss)) != MA_OK) return err;
         }
+        // the matrices small enough for one workgroup each (all in batch 0,
+        // whose operands the pass above prepared): one launch for all their
+        // iterations, on the caller's stream ahead of its tiled launches
+        // (after the fork, so the side stream does not wait for it)
+        if (L.n_lds > 0 &&
+            (err = launch_ns_lds(d_muon, n_muon, hp->muon_ns_steps, sc, muon_scales, sd, st)))
+            return hip_fail("newton-schulz (lds)", err);
         for (int b0 = 0; b0 < nb; b0 += kNsStreams) {
             for (int it = 0; it < hp->muon_ns_steps; ++it) {
                 const int last = it == hp->muon_ns_steps - 1;

@@ -25,8 +25,10 @@ def test_executed_ns_flops_counts_upper_tiles_and_padding():
     up = 10 * 256 * 256
     want = 2 * up * 4096 + 2 * up * 1024 + 2 * 1024 * 1024 * 4096
     assert bench.ns_executed_flops([(1024, 4096)], 1, "bf16") == want
-    # 64 x 256 pads to one 256 x 256 tile in every product
-    assert bench.ns_executed_flops([(256, 64)], 1, "bf16") == 3 * 2 * 256.0 ** 3
+    # 64 x 256 under bf16 runs in one workgroup: every product in full on
+    # its own sides (rounded up to 32); under fp32 it pads to one 256 x 256 tile
+    assert bench.ns_executed_flops([(256, 64)], 1, "bf16") == 4 * 64 * 64 * 256 + 2 * 64 ** 3
+    assert bench.ns_executed_flops([(256, 300)], 1, "bf16") == 4 * 256.0 ** 2 * 512 + 2 * 256.0 ** 3
     # one tile row: symmetric saving is nil, so executed == dense at r = 256
     assert bench.ns_executed_flops([(256, 1024)], 1, "bf16") == bench.ns_flops([(256, 1024)], 1)
 
@@ -45,6 +47,8 @@ def test_executed_ns_flops_of_small_fp32_tiles():
     thin = 36 * 32 * 32
     assert bench.ns_executed_flops([(3, 300), (256, 256)], 1, "bf16") == \
         (2 * thin * 512 + 2 * thin * 256 + 2 * 256 * 256 * 512) + 3 * 2 * 256.0 ** 3
+    # 33 x 65 under bf16: one workgroup on 64 x 96
+    assert bench.ns_executed_flops([(65, 33)], 1, "bf16") == 4 * 64 * 64 * 96 + 2 * 64 ** 3
 
 
 def test_more_than_one_gpu_is_refused():
