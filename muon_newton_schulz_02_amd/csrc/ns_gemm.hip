@@ -1696,18 +1696,31 @@ __device__ __forceinline__ uint4 lds_row8(const __bf16* p) { return *reinterpret
 // Row of A (or B) at accumulator register e of this lane: 8 (e / 4) + 4 (lane / 32) + e % 4.
 __device__ __forceinline__ int acc_row(int e, int lane) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
 
-// Stored-orientation update of one element of the matrix: p = p decay - dv,
-// delta = dv.
-__device__ __forceinline__ void lds_update(const MuonMat& d, int row, int col, float dv, float decay) {
-    const int64_t o = d.transposed ? (int64_t)col * d.n + row : (int64_t)row * d.n + col;
-    if (d.p_bf16) {
-        __bf16* p = reinterpret_cast<__bf16*>(d.p) + o;
-        *p = (__bf16)fmaf((float)*p, decay, -dv);
-    } else {
-        float* p = reinterpret_cast<float*>(d.p) + o;
-        *p = fmaf(*p, decay, -dv);
+// Stored-orientation update of the 16 elements of one accumulator block
+// that a lane holds (canonical rows row0 + acc_row(e), column col): p = p
+// decay - dv, delta = dv, for the elements inside the matrix.  All 16 old
+// values are loaded before the first store, so their latencies overlap.
+template <typename P>
+__device__ __forceinline__ void lds_update16(const MuonMat& d, int row0, int col, int lane,
+                                             const float (&dv)[16], float decay) {
+    typedef __attribute__((address_space(1))) P g_P;
+    g_P* p = (g_P*)reinterpret_cast<P*>(d.p);
+    int64_t o[16];
+    float pv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int row = row0 + acc_row(e, lane);
+        o[e] = d.transposed ? (int64_t)col * d.n + row : (int64_t)row * d.n + col;
+        pv[e] = row < d.r && col < d.c ? (float)p[o[e]] : 0.f;
     }
-    if (d.delta) reinterpret_cast<float*>(d.delta)[o] = dv;
+    g_float* dl = (g_float*)reinterpret_cast<float*>(d.delta);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        if (row0 + acc_row(e, lane) < d.r && col < d.c) {
+            p[o[e]] = (P)fmaf(pv[e], decay, -dv[e]);
+            if (dl) dl[o[e]] = dv[e];
+        }
+    }
 }
 
 template <int R>
@@ -1799,6 +1812,7 @@ __device__ __forceinline__ void ns_lds_run(NsLds& L, const MuonMat& d, int mat,
             }
 #pragma unroll
             for (int ib = 0; ib < NB; ++ib) {
+                float dv[16];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int row = ib * 32 + acc_row(e, lane);
@@ -1809,9 +1823,12 @@ __device__ __forceinline__ void ns_lds_run(NsLds& L, const MuonMat& d, int mat,
                         const __bf16 vh = (__bf16)v;
                         L.xhi[row][col] = vh;
                         if (write_lo) L.xlo[row][col] = (__bf16)(v - (float)vh);
-                    } else if (row < d.r && col < d.c) {
-                        lds_update(d, row, col, rate * v, decay);
                     }
+                    dv[e] = rate * v;
+                }
+                if (last) {
+                    if (d.p_bf16) lds_update16<__bf16>(d, ib * 32, col, lane, dv, decay);
+                    else lds_update16<float>(d, ib * 32, col, lane, dv, decay);
                 }
             }
         }

@@ -595,7 +595,10 @@ int step_impl(const ma_plan* plan, float* const* params, const float* const* gra
         // the matrices small enough for one workgroup each (all in batch 0,
         // whose operands the pass above prepared): one launch for all their
         // iterations, on the caller's stream ahead of its tiled launches
-        // (after the fork, so the side stream does not wait for it)
+        // (after the fork above, so the other stream does not wait for it).
+        // On a stream of its own it ran five times longer beside the tiled
+        // launches and slowed the second batch's momentum pass: 16.9 ->
+        // 17.8 ms per step on the stress table.
         if (L.n_lds > 0 &&
             (err = launch_ns_lds(d_muon, n_muon, hp->muon_ns_steps, sc, muon_scales, sd, st)))
             return hip_fail("newton-schulz (lds)", err);
