@@ -377,7 +377,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(every matrix is held whole on one device); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
