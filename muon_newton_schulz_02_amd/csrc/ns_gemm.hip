@@ -1391,8 +1391,11 @@ __device__ __forceinline__ void s32_load(uint4 (&v)[4], const char* base, int64_
 }
 
 // Blocks in flight per wave (four measured no faster for the Grams of
-// 256 x 1024 matrices).
+// 256 x 1024 matrices), and waves per workgroup: the reduction is split
+// kS32Waves ways (K is a multiple of 256, so each wave gets whole 32-column
+// blocks; eight waves made the tiny table's Newton-Schulz 0.20 -> 0.23 ms).
 constexpr int kS32Depth = 2;
+constexpr int kS32Waves = 4;
 
 __device__ __forceinline__ void s32_mma(f32x16& acc, const uint4 (&a)[4], const uint4 (&b)[4]) {
 #pragma unroll
@@ -1405,7 +1408,8 @@ __device__ __forceinline__ void ns_gemm_tile_s32(const MuonMat* __restrict__ tab
                                                  const NsArgs& args) {
     static_assert(EPI == EPI_GRAM || EPI == EPI_POLY, "Gram and square only");
     constexpr int SLD = 36;
-    __shared__ __attribute__((aligned(16))) float red[3][16][64];  // waves 1..3: [register][lane]
+    constexpr int W = kS32Waves;
+    __shared__ __attribute__((aligned(16))) float red[W - 1][16][64];  // waves 1..: [register][lane]
     __shared__ __attribute__((aligned(16))) float stage[32 * SLD];  // wave 0's epilogue staging
 
     const GemmTile tile = tiles[blockIdx.x];
@@ -1435,8 +1439,8 @@ __device__ __forceinline__ void ns_gemm_tile_s32(const MuonMat* __restrict__ tab
         K = d.R;
     }
     const int m0 = tile.tm * kS32, n0 = tile.tn * kS32;
-    const int kq = K / 4;    // this wave's columns: a multiple of 64 (K is padded to 256)
-    const int nb = kq / 32;  // its 32-column blocks: at least 2
+    const int kq = K / W;    // this wave's columns: a multiple of 32 (K is padded to 256)
+    const int nb = kq / 32;  // its 32-column blocks: at least 1
     const int r = lane & 31, h = lane >> 5;
     const char* pa = P + (int64_t)(m0 + r) * ldp + ((int64_t)wave * kq + 16 * h) * 4;
     const char* qa = P + (int64_t)(n0 + r) * ldp + ((int64_t)wave * kq + 16 * h) * 4;
@@ -1482,7 +1486,7 @@ __device__ __forceinline__ void ns_gemm_tile_s32(const MuonMat* __restrict__ tab
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
-    for (int w = 0; w < 3; ++w)
+    for (int w = 0; w < W - 1; ++w)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[e] += red[w][e][lane];
 
@@ -1873,7 +1877,7 @@ NS_KERNEL(k_ns_xupd_f32, float, EPI_XUPD)
 NS_KERNEL(k_ns_final_f32, float, EPI_FINAL)
 #undef NS_KERNEL
 #define NS_KERNEL_S32(NAME, EPI)                                                          \
-    __global__ __launch_bounds__(256) void NAME(const MuonMat* __restrict__ tab,          \
+    __global__ __launch_bounds__(kS32Waves * 64) void NAME(const MuonMat* __restrict__ tab, \
                                                 const GemmTile* __restrict__ tiles,       \
                                                 NsArgs args) {                            \
         ns_gemm_tile_s32<EPI>(tab, tiles, args);                                         \
@@ -1950,7 +1954,8 @@ int launch_ns_phase(int phase, int32_t group, const MuonMat* tab, const GemmTile
     static const NsKernel f32s[4] = {k_ns_gram_f32_s32, k_ns_poly_f32_s32, k_ns_xupd_f32_s64,
                                      k_ns_final_f32_s64};
     if (group == kGroupBf16) return launch_k(bf[epi - 1], tab, tiles, n_tiles, a, kW8Waves * 64, st);
-    if (group == kGroupFp32Small) return launch_k(f32s[epi - 1], tab, tiles, n_tiles, a, 256, st);
+    if (group == kGroupFp32Small)
+        return launch_k(f32s[epi - 1], tab, tiles, n_tiles, a, epi <= 2 ? kS32Waves * 64 : 256, st);
     return launch_k(f32[epi - 1], tab, tiles, n_tiles, a, 256, st);
 }
 
