@@ -526,6 +526,10 @@ def main():
     norm_bytes = esz * n_train
     adam_gbps = adam_bytes / (mean["adamw"] * 1e-3) / 1e9 if mean["adamw"] > 0 else 0.0
     norm_gbps = norm_bytes / (mean["clip_norm"] * 1e-3) / 1e9 if mean["clip_norm"] > 0 else 0.0
+    # the bf16 GEMMs copy 32 KB of operands into LDS per 256 x 256 x 32
+    # product (4.19 M executed flops): 128 executed flops per staged byte
+    ns_dma_gbps = (ns_exec_tflops * 1e3 / 128.0
+                   if (n_muon > 0 and w.ns_precision == "bf16") else None)
     b2_mfma = (b2 or {}).get("mfma_bf16_tflops" if w.ns_precision == "bf16" else "mfma_fp32_tflops")
     b2_mix = (b2 or {}).get("hbm_adamw_mix_gbps")
     if n_adam > 0 and mean["adamw"] >= mean["newton_schulz"]:
@@ -579,6 +583,9 @@ def main():
         "ns_executed_tflops": ns_exec_tflops,
         "ns_mfma_frac": ns_exec_tflops / ns_peak,
         "ns_mfma_frac_of_b2": ns_exec_tflops / b2_mfma if b2_mfma else None,
+        "ns_lds_dma_gbps": ns_dma_gbps,
+        "ns_lds_dma_frac_of_b2_l2": (ns_dma_gbps / b2["lds_dma_l2_gbps"]) if (b2 and ns_dma_gbps) else None,
+        "ns_lds_dma_frac_of_b2_far": (ns_dma_gbps / b2["lds_dma_far_gbps"]) if (b2 and ns_dma_gbps) else None,
         "ns_library_ms": lib_ms,
         "ns_library_tflops": flops / (lib_ms * 1e-3) / 1e12 if lib_ms else None,
         "gemm_tflops_measured": gemm,

@@ -14,6 +14,11 @@
 //                      (1 read : 1 write), and the AdamW mix (read four
 //                      streams, write three of them back in place: 16 : 12
 //                      bytes per element)
+//   ma_peaks_dma       global memory straight into LDS (buffer loads that
+//                      write LDS), staged as the bf16 GEMMs stage their
+//                      operands: eight waves copy 32 KB stages into a ring of
+//                      five, four stages ahead, with a wait and a workgroup
+//                      barrier per stage; no matrix instructions, no LDS reads
 //
 // Not part of the optimizer's C ABI: measurement only.  Every entry point
 // launches on the given stream and returns a hipError_t (0 on success); the
@@ -159,6 +164,74 @@ __global__ __launch_bounds__(256) void k_peak_stream(f32x4* __restrict__ a, f32x
     if (KIND == 0) sink[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+// LDS-DMA probe.  Workgroup b copies stage s from the 32 KB chunk
+// (b * 7919 + s) mod (src_bytes / 32 KB) of the source: a source of a few MB
+// stays in every XCD's L2, a large one streams from the memory-side cache or
+// HBM.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kDmaStage = 32768;
+constexpr int kDmaSlots = 5;
+constexpr int kDmaWaves = 8;
+
+__device__ __forceinline__ void dma_copy16(u32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+// vmcnt(n) for n in {0, 4, 8, 12}, the other counters unconstrained
+__device__ __forceinline__ void dma_wait(int n) {
+    if (n <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+    else if (n == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
+    else if (n == 8) __builtin_amdgcn_s_waitcnt(0x0F78);
+    else __builtin_amdgcn_s_waitcnt(0x0F7C);
+}
+
+__global__ __launch_bounds__(kDmaWaves * 64) void k_peak_dma(const char* __restrict__ src,
+                                                              uint32_t src_bytes, int stages,
+                                                              uint64_t* clocks) {
+    __shared__ __attribute__((aligned(1024))) char ring[kDmaSlots * kDmaStage];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t a = (uint64_t)src;
+    u32x4 rsrc;
+    rsrc.x = (uint32_t)a;
+    rsrc.y = (uint32_t)(a >> 32) & 0xffffu;
+    rsrc.z = src_bytes;
+    rsrc.w = 0x00020000u;
+    const uint32_t lring = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)ring;
+    const uint32_t chunks = src_bytes / kDmaStage;
+    const uint32_t voff = (uint32_t)lane * 16;
+    // this wave's 4 KB of stage s: four 1 KB copies
+    auto copy = [&](int s) {
+        const uint32_t chunk = ((uint32_t)blockIdx.x * 7919u + (uint32_t)s) % chunks;
+        const uint32_t from = chunk * kDmaStage + (uint32_t)wave * 4096;
+        const uint32_t to = lring + (uint32_t)(s % kDmaSlots) * kDmaStage + (uint32_t)wave * 4096;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma_copy16(rsrc, to + i * 1024, voff, from + i * 1024);
+    };
+    const uint64_t t0 = __builtin_readcyclecounter();
+    const uint64_t w0 = __builtin_amdgcn_s_memrealtime();
+    for (int s = 0; s < kDmaSlots - 1 && s < stages; ++s) copy(s);
+    for (int s = 0; s < stages; ++s) {
+        // stage s + 1 has landed once at most the copies of stages s + 2,
+        // s + 3 are outstanding; the barrier frees the slot of stage s - 1
+        const int ahead = stages - 2 - s;
+        dma_wait(4 * (ahead < 2 ? ahead : 2));
+        __builtin_amdgcn_s_barrier();
+        if (s + kDmaSlots - 1 < stages) copy(s + kDmaSlots - 1);
+    }
+    dma_wait(0);
+    __builtin_amdgcn_s_barrier();
+    const uint64_t t1 = __builtin_readcyclecounter();
+    const uint64_t w1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+        clocks[2 * blockIdx.x] = t1 - t0;
+        clocks[2 * blockIdx.x + 1] = w1 - w0;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -210,6 +283,20 @@ int ma_peaks_stream(int kind, void* a, void* b, void* c, void* d, int64_t n_vec,
     if (kind == 0) hipLaunchKernelGGL(k_peak_stream<0>, grid, dim3(256), 0, st, A, B, Cc, D, n_vec, sink);
     else if (kind == 1) hipLaunchKernelGGL(k_peak_stream<1>, grid, dim3(256), 0, st, A, B, Cc, D, n_vec, sink);
     else hipLaunchKernelGGL(k_peak_stream<2>, grid, dim3(256), 0, st, A, B, Cc, D, n_vec, sink);
+    return (int)hipGetLastError();
+}
+
+// `blocks` workgroups of eight waves (160 KB of LDS each, so one per CU)
+// copy `stages` 32 KB stages each from src (src_bytes: a multiple of 32 KB,
+// at most 2 GiB - 32 KB) into LDS.  Bytes per launch: blocks * stages *
+// 32768.  clocks: 2 * blocks uint64, as for ma_peaks_mfma.
+int ma_peaks_dma(const void* src, int64_t src_bytes, int64_t blocks, int stages,
+                 uint64_t* clocks, void* stream) {
+    if (!src || !clocks || blocks < 1 || stages < 1 || src_bytes < kDmaStage ||
+        src_bytes % kDmaStage != 0 || src_bytes > 0x7fffffffLL)
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_peak_dma, dim3((unsigned)blocks), dim3(kDmaWaves * 64), 0,
+                       (hipStream_t)stream, (const char*)src, (uint32_t)src_bytes, stages, clocks);
     return (int)hipGetLastError();
 }
 

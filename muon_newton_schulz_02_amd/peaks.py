@@ -1,8 +1,9 @@
 """Ceilings of this GPU, measured by the hand-written probes of
 libma_peaks.so (csrc/peaks.hip) in the calling process: the matrix-core
 issue rate (bf16 and fp32 MFMA, with the shader clock they ran at), the LDS
-read bandwidth per compute unit, and HBM streams (read only, copy, and the
-AdamW 16:12 read/write mix).  Each probe is launched on torch's current
+read bandwidth per compute unit, HBM streams (read only, copy, and the
+AdamW 16:12 read/write mix), and the rate at which a CU copies global memory
+straight into LDS the way the bf16 GEMMs stage their operands.  Each probe is launched on torch's current
 stream and timed with events on it; the best of `reps` launches is kept.
 
 Measurement only: nothing here is on the optimizer's path.
@@ -32,7 +33,9 @@ def load(path: str = LIB_PATH):
                                  C.c_void_p]
     lib.ma_peaks_stream.argtypes = [C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.c_int64, C.c_void_p, C.c_void_p]
-    for f in (lib.ma_peaks_mfma, lib.ma_peaks_lds, lib.ma_peaks_stream):
+    lib.ma_peaks_dma.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_int, C.c_void_p,
+                                 C.c_void_p]
+    for f in (lib.ma_peaks_mfma, lib.ma_peaks_lds, lib.ma_peaks_stream, lib.ma_peaks_dma):
         f.restype = C.c_int
     _lib = lib
     return lib
@@ -126,6 +129,31 @@ def stream(torch, kind: str, gib: float = 1.0, reps: int = 3) -> dict:
     return {"gbps": per_vec * n_vec / (ms * 1e-3) / 1e9}
 
 
+def dma(torch, src_mib: int, blocks: int = CUS, stages: int = 2048, reps: int = 3) -> dict:
+    """Global memory into LDS as the bf16 GEMMs stage operands (one
+    workgroup per CU, 32 KB stages, a wait and a barrier per stage), from a
+    source of `src_mib` MiB: a few MiB stay in L2, a large source streams
+    from the memory-side cache or HBM.  GB/s, shader clock, bytes per shader
+    cycle per CU."""
+    lib = load()
+    nbytes_src = src_mib << 20
+    src = torch.ones(nbytes_src // 4, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+
+    def go():
+        _check(lib.ma_peaks_dma(src.data_ptr(), nbytes_src, blocks, stages, clocks.data_ptr(), st),
+               "ma_peaks_dma")
+
+    ms = _timed(torch, go, reps)
+    nbytes = blocks * float(stages) * 32768.0
+    cyc = clocks.view(-1, 2).double()
+    mhz = float((cyc[:, 0] / (cyc[:, 1] / 100.0)).median())
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    del src
+    return {"gbps": gbps, "sclk_mhz": mhz, "bytes_per_clk_per_cu": gbps * 1e9 / (mhz * 1e6) / CUS}
+
+
 def measure_all(torch) -> dict:
     """Every probe, with the derived per-CU LDS figure."""
     bf = mfma(torch, False)
@@ -144,5 +172,13 @@ def measure_all(torch) -> dict:
         "hbm_copy_gbps": stream(torch, "copy", 2.0)["gbps"],
         "hbm_adamw_mix_gbps": stream(torch, "adamw_mix", 1.0)["gbps"],
     }
+    near, far = dma(torch, 4), dma(torch, 1024)
+    out.update({
+        "lds_dma_l2_gbps": near["gbps"],
+        "lds_dma_l2_bytes_per_clk_per_cu": near["bytes_per_clk_per_cu"],
+        "lds_dma_far_gbps": far["gbps"],
+        "lds_dma_far_bytes_per_clk_per_cu": far["bytes_per_clk_per_cu"],
+        "lds_dma_sclk_mhz": far["sclk_mhz"],
+    })
     torch.cuda.empty_cache()
     return out
