@@ -279,7 +279,7 @@ int muon_adamw_workspace_size(const ma_plan* plan, int32_t ns_precision, size_t*
  * pointer NULL, hp values out of range, or two of the buffers the step
  * touches overlapping: parameters, gradients, states, update outputs,
  * grad_norm_out, device_step and the workspace must be pairwise disjoint,
- * judged from their addresses and sizes), UNSUPPORTED (ns_steps < 1 or > 64,
+ * as address ranges), UNSUPPORTED (ns_steps < 1 or > 64,
  * unknown precision), WORKSPACE (null, too small, misaligned), CAPTURE (the
  * stream is capturing and the descriptor tables would have to be uploaded:
  * run one eager step with the same pointers and workspace first, with
