@@ -464,20 +464,28 @@ __device__ __forceinline__ int find_matrix(const MuonMat* tab, int n, int64_t bl
 // hi = RNE(x), lo = RNE(x - hi), each stored in 32x32 blocks of 2 KB
 // (row-major inside a block, block-row-major outside), the layout the
 // Newton-Schulz launches read and write.
+// A thread writes eight consecutive elements of a canonical row (16 bytes of
+// hi and of lo: one run inside a 32x32 block) per store.
 __device__ __forceinline__ void write_operands_bf16(const MuonMat& d,
                                                     const float (*tile)[kOrientTile + 1], int i0,
                                                     int j0) {
     constexpr int TS = kOrientTile;
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
     __bf16* hi = reinterpret_cast<__bf16*>(d.x[0]);
     __bf16* lo = reinterpret_cast<__bf16*>(d.xlo[0]);
-    for (int idx = threadIdx.x; idx < TS * TS; idx += kThreads) {
-        const int a_ = idx / TS, b_ = idx % TS;
-        const float v = d.transposed ? tile[b_][a_] : tile[a_][b_];
-        const int i = i0 + a_, j = j0 + b_;
+    for (int c = threadIdx.x; c < TS * TS / 8; c += kThreads) {
+        const int a_ = c / (TS / 8), b0 = (c % (TS / 8)) * 8;
+        const int i = i0 + a_, j = j0 + b0;
         const int64_t o = ((int64_t)(i >> 5) * (d.C >> 5) + (j >> 5)) * 1024 + (i & 31) * 32 + (j & 31);
-        const __bf16 h = (__bf16)v;
-        hi[o] = h;
-        lo[o] = (__bf16)(v - (float)h);
+        bf16x8_t h, l;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float v = d.transposed ? tile[b0 + e][a_] : tile[a_][b0 + e];
+            h[e] = (__bf16)v;
+            l[e] = (__bf16)(v - (float)h[e]);
+        }
+        *reinterpret_cast<bf16x8_t*>(hi + o) = h;
+        *reinterpret_cast<bf16x8_t*>(lo + o) = l;
     }
 }
 
@@ -528,18 +536,31 @@ __global__ __launch_bounds__(kThreads) void k_muon_prep(const MuonMat* __restric
     const int sc0 = d.transposed ? i0 : j0;
     float acc = 0.f;
     if (d.vec_ok && sr0 + TS <= d.m && sc0 + TS <= d.n) {
-        // whole tile inside the matrix: 16-byte accesses, 4 per thread
-        for (int q = threadIdx.x; q < TS * TS / 4; q += kThreads) {
+        // whole tile inside the matrix: 16-byte accesses, NQ of each stream
+        // per thread, all loads issued before the first store
+        constexpr int NQ = TS * TS / 4 / kThreads;
+        static_assert(NQ * kThreads * 4 == TS * TS, "the tile splits evenly over the threads");
+        f4 gg[NQ];
+        float4 bb[NQ];
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            const int q = threadIdx.x + k * kThreads;
             const int lr = q / (TS / 4), lc = (q % (TS / 4)) * 4;
             const int64_t o = (int64_t)(sr0 + lr) * d.n + (sc0 + lc);
-            const f4 gg = d.p_bf16 ? Quad<__bf16>::get(*reinterpret_cast<const u32x2*>(gh + o))
-                                   : *reinterpret_cast<const f4*>(g + o);
-            float4 bb = *reinterpret_cast<const float4*>(buf + o);
-            const float u0 = momentum_elem(gg[0], bb.x, coef, a);
-            const float u1 = momentum_elem(gg[1], bb.y, coef, a);
-            const float u2 = momentum_elem(gg[2], bb.z, coef, a);
-            const float u3 = momentum_elem(gg[3], bb.w, coef, a);
-            *reinterpret_cast<float4*>(buf + o) = bb;
+            gg[k] = d.p_bf16 ? Quad<__bf16>::get(*reinterpret_cast<const u32x2*>(gh + o))
+                             : *reinterpret_cast<const f4*>(g + o);
+            bb[k] = *reinterpret_cast<const float4*>(buf + o);
+        }
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            const int q = threadIdx.x + k * kThreads;
+            const int lr = q / (TS / 4), lc = (q % (TS / 4)) * 4;
+            const int64_t o = (int64_t)(sr0 + lr) * d.n + (sc0 + lc);
+            const float u0 = momentum_elem(gg[k][0], bb[k].x, coef, a);
+            const float u1 = momentum_elem(gg[k][1], bb[k].y, coef, a);
+            const float u2 = momentum_elem(gg[k][2], bb[k].z, coef, a);
+            const float u3 = momentum_elem(gg[k][3], bb[k].w, coef, a);
+            *reinterpret_cast<float4*>(buf + o) = bb[k];
             tile[lr][lc] = u0;
             tile[lr][lc + 1] = u1;
             tile[lr][lc + 2] = u2;
